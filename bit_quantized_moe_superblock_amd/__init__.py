@@ -1,0 +1,15 @@
+"""Q4_K MoE expert path for AMD MI355X (gfx950).
+
+The compute lives in ``libq4kmoe.so`` (HIP kernels behind the C ABI in
+``include/q4kmoe.h``); ``_lib`` is its ctypes binding with the same names.
+Importing the package does not load the library; the first call does, and
+raises if it has not been built.
+"""
+from . import _lib
+from ._lib import (  # noqa: F401
+    MOE_SHARED_NONE, MOE_SHARED_SIGMOID, MOE_SHARED_UNSCALED, Q4K_BUCKET_AUTO, Q4K_BUCKET_OFF,
+    Q4K_BUCKET_ON, Q4K_BUCKET_PREBUILT, Q4KError, moe_bucket, moe_bucket_workspace_bytes, moe_combine_residual,
+    moe_expert_ffn, q4k_abi_version, q4k_dequantize, q4k_matrix_bytes, q4k_moe_id_gemv,
+    q4k_moe_gate_up_silu,
+    q4k_quantize, q4tp_matvec, q4tp_quantize, q4tp_tensor_bytes, status_string,
+)

@@ -1,0 +1,285 @@
+// C ABI of the library (declared and documented in include/q4kmoe.h).
+// Validation happens here, on the host, before any HIP call; the kernels
+// assume validated arguments.
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/q4kmoe.h"
+#include "launch.hpp"
+
+using namespace q4k;
+
+namespace {
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int launched(hipError_t e) { return e == hipSuccess ? Q4K_OK : Q4K_ERR_LAUNCH; }
+
+bool k_ok(int64_t k) { return k >= 256 && k % 256 == 0 && k <= Q4K_MAX_IN; }
+
+int check_gemv_shape(int64_t n, int64_t k, int64_t m, int64_t top_k, int64_t E) {
+    if (!k_ok(k) || n < 1 || n > (1 << 30) || m < 1 || top_k < 1 || top_k > Q4K_MAX_TOP_K ||
+        E < 1 || E > Q4K_MAX_EXPERTS)
+        return Q4K_ERR_SHAPE;
+    if (m * top_k > 65535)   // one workgroup row per pair in the grid
+        return Q4K_ERR_SHAPE;
+    return Q4K_OK;
+}
+
+// Bucketed mode decision and workspace check; *use set on success.
+int bucket_mode(int flag, int64_t m, int64_t P, int64_t E, void *ws, int64_t ws_bytes,
+                bool *use) {
+    if (flag != Q4K_BUCKET_AUTO && flag != Q4K_BUCKET_OFF && flag != Q4K_BUCKET_ON &&
+        flag != Q4K_BUCKET_PREBUILT)
+        return Q4K_ERR_ARG;
+    *use = flag == Q4K_BUCKET_ON || flag == Q4K_BUCKET_PREBUILT ||
+           (flag == Q4K_BUCKET_AUTO && m > 1);
+    if (!*use)
+        return Q4K_OK;
+    if (P > Q4K_MAX_PAIRS)
+        return Q4K_ERR_SHAPE;
+    if (!ws || !aligned4(ws) || ws_bytes < moe_bucket_workspace_bytes(P, E))
+        return Q4K_ERR_WORKSPACE;
+    return Q4K_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *q4k_status_string(int status) {
+    switch (status) {
+    case Q4K_OK: return "ok";
+    case Q4K_ERR_SHAPE: return "size out of range or not a required multiple";
+    case Q4K_ERR_NULL: return "required pointer is NULL or misaligned";
+    case Q4K_ERR_STRIDE: return "activation stride is negative";
+    case Q4K_ERR_WORKSPACE: return "workspace missing or too small";
+    case Q4K_ERR_LAUNCH: return "HIP launch failed";
+    case Q4K_ERR_ARG: return "unknown enum argument";
+    default: return "unknown status";
+    }
+}
+
+int q4k_abi_version(void) { return 1; }
+
+int64_t q4k_matrix_bytes(int64_t n, int64_t k) {
+    if (n < 0 || k <= 0 || k % Q4K_BLOCK_WEIGHTS)
+        return -1;
+    return n * (k / Q4K_BLOCK_WEIGHTS) * Q4K_BLOCK_BYTES;
+}
+
+int q4k_dequantize(const void *blocks, float *out, int64_t n_blocks, void *stream) {
+    if (n_blocks < 0)
+        return Q4K_ERR_SHAPE;
+    if (n_blocks == 0)
+        return Q4K_OK;
+    if (!blocks || !out || !aligned16(blocks) || !aligned16(out))
+        return Q4K_ERR_NULL;
+    return launched(launch_q4k_dequant(blocks, out, n_blocks, as_stream(stream)));
+}
+
+int q4k_quantize(const float *w, void *blocks, int64_t n_rows, int64_t k, void *stream) {
+    if (n_rows < 0 || k <= 0 || k % Q4K_BLOCK_WEIGHTS)
+        return Q4K_ERR_SHAPE;
+    if (n_rows == 0)
+        return Q4K_OK;
+    if (!w || !blocks || !aligned16(blocks) || !aligned4(w))
+        return Q4K_ERR_NULL;
+    return launched(launch_q4k_quant(w, blocks, n_rows * (k / Q4K_BLOCK_WEIGHTS),
+                                     as_stream(stream)));
+}
+
+int64_t moe_bucket_workspace_bytes(int64_t n_pairs, int64_t num_experts) {
+    if (n_pairs < 0 || num_experts < 1)
+        return -1;
+    return bucket_ws_words(n_pairs, num_experts) * 4;
+}
+
+int moe_bucket(const int32_t *ids, int64_t n_pairs, int64_t num_experts, void *ws,
+               int64_t ws_bytes, void *stream) {
+    if (n_pairs < 1 || n_pairs > Q4K_MAX_PAIRS || num_experts < 1 ||
+        num_experts > Q4K_MAX_EXPERTS)
+        return Q4K_ERR_SHAPE;
+    if (!ids || !aligned4(ids))
+        return Q4K_ERR_NULL;
+    if (!ws || !aligned4(ws) || ws_bytes < moe_bucket_workspace_bytes(n_pairs, num_experts))
+        return Q4K_ERR_WORKSPACE;
+    return launched(launch_moe_bucket(ids, n_pairs, num_experts, (int32_t *)ws,
+                                      as_stream(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+int id_gemv_entry(const void *w0, const void *w1, const float *src1, const int32_t *ids,
+                  float *dst, int64_t n, int64_t k, int64_t m, int64_t top_k,
+                  int64_t src1_outer_stride, int64_t src1_inner_stride, int64_t num_experts,
+                  int bucket_flag, void *ws, int64_t ws_bytes, void *stream) {
+    const void *w_stacked = w0;
+    int rc = check_gemv_shape(n, k, m, top_k, num_experts);
+    if (rc)
+        return rc;
+    if (!w_stacked || !src1 || !ids || !dst || !aligned16(w_stacked) || !aligned4(src1) ||
+        !aligned4(ids) || !aligned4(dst))
+        return Q4K_ERR_NULL;
+    if (w1 && !aligned16(w1))
+        return Q4K_ERR_NULL;
+    if (src1_outer_stride < 0 || src1_inner_stride < 0)
+        return Q4K_ERR_STRIDE;
+    const int64_t P = m * top_k;
+    bool use = false;
+    rc = bucket_mode(bucket_flag, m, P, num_experts, ws, ws_bytes, &use);
+    if (rc)
+        return rc;
+    hipStream_t st = as_stream(stream);
+    if (use && bucket_flag != Q4K_BUCKET_PREBUILT) {
+        rc = launched(launch_moe_bucket(ids, P, num_experts, (int32_t *)ws, st));
+        if (rc)
+            return rc;
+    }
+    GemvLaunch L{};
+    L.w0 = w_stacked;
+    L.w1 = w1;
+    L.src1 = src1;
+    L.ids = ids;
+    L.bucket_ws = use ? (const int32_t *)ws : nullptr;
+    L.dst = dst;
+    L.n = n;
+    L.k = k;
+    L.top_k = top_k;
+    L.num_experts = num_experts;
+    L.n_pairs = P;
+    L.outer = src1_outer_stride;
+    L.inner = src1_inner_stride;
+    L.fused_swiglu = w1 != nullptr;
+    return launched(launch_q4k_gemv(L, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int q4k_moe_id_gemv(const void *w_stacked, const float *src1, const int32_t *ids, float *dst,
+                    int64_t n, int64_t k, int64_t m, int64_t top_k,
+                    int64_t src1_outer_stride, int64_t src1_inner_stride,
+                    int64_t num_experts, int bucket_flag, void *ws, int64_t ws_bytes,
+                    void *stream) {
+    return id_gemv_entry(w_stacked, nullptr, src1, ids, dst, n, k, m, top_k, src1_outer_stride,
+                         src1_inner_stride, num_experts, bucket_flag, ws, ws_bytes, stream);
+}
+
+int q4k_moe_gate_up_silu(const void *w_gate, const void *w_up, const float *src1,
+                         const int32_t *ids, float *out, int64_t n, int64_t k, int64_t m,
+                         int64_t top_k, int64_t src1_outer_stride, int64_t src1_inner_stride,
+                         int64_t num_experts, int bucket_flag, void *ws, int64_t ws_bytes,
+                         void *stream) {
+    if (!w_up)
+        return Q4K_ERR_NULL;
+    return id_gemv_entry(w_gate, w_up, src1, ids, out, n, k, m, top_k, src1_outer_stride,
+                         src1_inner_stride, num_experts, bucket_flag, ws, ws_bytes, stream);
+}
+
+int moe_expert_ffn(const void *w_gate, const void *w_up, const void *w_down,
+                   const float *h_post, const int32_t *ids, float *act, float *expert_out,
+                   int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
+                   int64_t top_k, int bucket_flag, void *ws, int64_t ws_bytes, void *stream) {
+    int rc = check_gemv_shape(inter, hidden, m, top_k, num_experts);
+    if (rc)
+        return rc;
+    rc = check_gemv_shape(hidden, inter, m, top_k, num_experts);
+    if (rc)
+        return rc;
+    if (!w_gate || !w_up || !w_down || !h_post || !ids || !act || !expert_out ||
+        !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned4(h_post) ||
+        !aligned4(ids) || !aligned4(act) || !aligned4(expert_out))
+        return Q4K_ERR_NULL;
+    const int64_t P = m * top_k;
+    bool use = false;
+    rc = bucket_mode(bucket_flag, m, P, num_experts, ws, ws_bytes, &use);
+    if (rc)
+        return rc;
+    hipStream_t st = as_stream(stream);
+    if (use && bucket_flag != Q4K_BUCKET_PREBUILT) {
+        rc = launched(launch_moe_bucket(ids, P, num_experts, (int32_t *)ws, st));
+        if (rc)
+            return rc;
+    }
+    GemvLaunch L{};
+    L.w0 = w_gate;
+    L.w1 = w_up;
+    L.src1 = h_post;
+    L.ids = ids;
+    L.bucket_ws = use ? (const int32_t *)ws : nullptr;
+    L.dst = act;
+    L.n = inter;
+    L.k = hidden;
+    L.top_k = top_k;
+    L.num_experts = num_experts;
+    L.n_pairs = P;
+    L.outer = hidden;
+    L.inner = 0;
+    L.fused_swiglu = true;
+    rc = launched(launch_q4k_gemv(L, st));
+    if (rc)
+        return rc;
+    GemvLaunch D = L;
+    D.w0 = w_down;
+    D.w1 = nullptr;
+    D.src1 = act;
+    D.dst = expert_out;
+    D.n = hidden;
+    D.k = inter;
+    D.outer = top_k * inter;
+    D.inner = inter;
+    D.fused_swiglu = false;
+    return launched(launch_q4k_gemv(D, st));
+}
+
+int moe_combine_residual(const float *h_mid, const float *expert_out, const float *route_w,
+                         const float *shared_out, const float *shared_gate_logit, float *out,
+                         int64_t hidden, int64_t m, int64_t top_k, int shared_mode,
+                         void *stream) {
+    if (hidden < 1 || m < 1 || top_k < 1 || top_k > Q4K_MAX_TOP_K)
+        return Q4K_ERR_SHAPE;
+    if (shared_mode != MOE_SHARED_NONE && shared_mode != MOE_SHARED_SIGMOID &&
+        shared_mode != MOE_SHARED_UNSCALED)
+        return Q4K_ERR_ARG;
+    if (!h_mid || !expert_out || !route_w || !out)
+        return Q4K_ERR_NULL;
+    if (shared_mode != MOE_SHARED_NONE && !shared_out)
+        return Q4K_ERR_NULL;
+    if (shared_mode == MOE_SHARED_SIGMOID && !shared_gate_logit)
+        return Q4K_ERR_NULL;
+    return launched(launch_moe_combine(h_mid, expert_out, route_w, shared_out, shared_gate_logit,
+                                       out, hidden, m, top_k, shared_mode, as_stream(stream)));
+}
+
+int64_t q4tp_tensor_bytes(int64_t rows, int64_t cols) {
+    if (rows < 1 || cols < 32 || cols % 32)
+        return -1;
+    const int64_t gpr = cols / 32;
+    return rows * gpr * 16 + rows * 4 + rows * ((5 * gpr + 7) / 8);
+}
+
+int q4tp_matvec(const void *tensor, const float *x, float *y, int64_t rows, int64_t cols,
+                void *stream) {
+    if (rows < 1 || rows > (1 << 30) || cols < 32 || cols % 32 || cols > Q4TP_MAX_COLS)
+        return Q4K_ERR_SHAPE;
+    if (!tensor || !x || !y || !aligned16(tensor) || !aligned4(x) || !aligned4(y))
+        return Q4K_ERR_NULL;
+    return launched(launch_q4tp_matvec(tensor, x, y, rows, cols, as_stream(stream)));
+}
+
+int q4tp_quantize(const float *w, void *tensor, int64_t rows, int64_t cols, void *stream) {
+    if (rows < 1 || rows > (1 << 30) || cols < 32 || cols % 32 || cols > Q4TP_MAX_COLS)
+        return Q4K_ERR_SHAPE;
+    if (!w || !tensor || !aligned16(tensor) || !aligned4(w))
+        return Q4K_ERR_NULL;
+    return launched(launch_q4tp_quant(w, tensor, rows, cols, as_stream(stream)));
+}
+
+}  // extern "C"

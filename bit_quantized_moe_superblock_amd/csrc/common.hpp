@@ -1,0 +1,123 @@
+// Device-side helpers for the Q4_K and Q4TiledP kernels (gfx950, wave64).
+//
+// Q4_K superblock (ferrum-kernels q4_k_moe_id_gemv_batched.rs: 256 weights in
+// 144 bytes; GGML's layout by way of candle): bytes 0-1 d, 2-3 dmin (fp16),
+// 4-15 eight 6-bit scales and mins, 16-143 nibbles where byte 32c+l holds
+// weight 64c+l (low nibble) and 64c+32+l (high nibble).
+//
+// Work unit of one lane: one 32-byte nibble chunk c of one superblock, i.e. 64
+// weights = sub-block 2c (the low nibbles) and sub-block 2c+1 (the high ones).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4k {
+
+constexpr int kBlockWeights = 256;
+constexpr int kBlockBytes = 144;
+constexpr int kThreads = 256;   // threads of every GEMV workgroup (4 waves)
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Half lanes of a packed register widened to float.  Feeding them straight into
+// fmaf lets the compiler emit v_fma_mix_f32, which converts and multiplies in
+// one instruction.
+__device__ __forceinline__ float lo_half(uint32_t v) {
+    return (float)__builtin_bit_cast(half2v, v).x;
+}
+__device__ __forceinline__ float hi_half(uint32_t v) {
+    return (float)__builtin_bit_cast(half2v, v).y;
+}
+
+// Index of float i of an activation row in LDS: every 64 floats (one lane's
+// unit) are followed by 4 pad floats, so lanes of a row start 68 floats apart
+// and their 16-byte LDS reads fall in different banks.
+__device__ __forceinline__ int xpad(int i) { return i + ((i >> 6) << 2); }
+__host__ __device__ constexpr int xpad_len(int k) { return k + (k >> 4); }
+
+// Scale and min of the lane's two sub-blocks (2c and 2c+1) from the 12 packed
+// bytes (header words y, z, w):
+//   j < 4 : scale = s[j] & 63, min = s[j+4] & 63
+//   j >= 4: scale = (s[j+4] & 15) | (s[j-4] >> 6) << 4,
+//           min   = (s[j+4] >> 4) | (s[j]   >> 6) << 4
+struct UnitScale {
+    float kA, kB;   // d*scale of sub-blocks A and B
+    float mA, mB;   // dmin*min of sub-blocks A and B
+};
+
+__device__ __forceinline__ UnitScale unit_scale(uint4 h, int c) {
+    const uint32_t sh = (c & 1) << 4;   // bytes 2c and 2c+1, modulo 4
+    const uint32_t b0 = h.y >> sh, b1 = h.z >> sh, b2 = h.w >> sh;
+    uint32_t scA, scB, mA, mB;
+    if (c >= 2) {
+        scA = (b2 & 15u) | ((b0 >> 2) & 0x30u);
+        scB = ((b2 >> 8) & 15u) | ((b0 >> 10) & 0x30u);
+        mA = ((b2 >> 4) & 15u) | ((b1 >> 2) & 0x30u);
+        mB = ((b2 >> 12) & 15u) | ((b1 >> 10) & 0x30u);
+    } else {
+        scA = b0 & 63u;
+        scB = (b0 >> 8) & 63u;
+        mA = b1 & 63u;
+        mB = (b1 >> 8) & 63u;
+    }
+    const float d = lo_half(h.x), dmin = hi_half(h.x);
+    UnitScale s;
+    s.kA = d * (float)scA;
+    s.kB = d * (float)scB;
+    s.mA = dmin * (float)mA;
+    s.mB = dmin * (float)mB;
+    return s;
+}
+
+// Nibble dot products of one unit against the lane's 64 activations in LDS.
+// The masked nibbles are used in place as fp16 subnormals: (v & 0x000F000F)
+// holds q*2^-24 in each half and (v & 0x00F000F0) holds q*2^-20, so one
+// v_fma_mix_f32 per weight converts and accumulates with the product exact.
+// accA = 2^-24 * sum q_i x_i over sub-block A, accB = 2^-20 * sum over B.
+// Elements are accumulated in ascending order, one fp32 rounding per step.
+struct UnitAcc {
+    float a, b;
+};
+
+__device__ __forceinline__ void nib_fma(uint32_t v, float4 xa, float4 xb, UnitAcc &acc) {
+    const uint32_t s = v >> 8;
+    const uint32_t r0 = v & 0x000F000Fu, r2 = s & 0x000F000Fu;   // low nibbles: A
+    const uint32_t r1 = v & 0x00F000F0u, r3 = s & 0x00F000F0u;   // high nibbles: B
+    acc.a = __builtin_fmaf(lo_half(r0), xa.x, acc.a);
+    acc.a = __builtin_fmaf(lo_half(r2), xa.y, acc.a);
+    acc.a = __builtin_fmaf(hi_half(r0), xa.z, acc.a);
+    acc.a = __builtin_fmaf(hi_half(r2), xa.w, acc.a);
+    acc.b = __builtin_fmaf(lo_half(r1), xb.x, acc.b);
+    acc.b = __builtin_fmaf(lo_half(r3), xb.y, acc.b);
+    acc.b = __builtin_fmaf(hi_half(r1), xb.z, acc.b);
+    acc.b = __builtin_fmaf(hi_half(r3), xb.w, acc.b);
+}
+
+// Unit value: sum over the 64 weights of (d*sc*q - dmin*m) * x, evaluated as
+// d*sc_A*(sum q x)_A + d*sc_B*(sum q x)_B - (dmin*m_A*Sx_A + dmin*m_B*Sx_B).
+__device__ __forceinline__ float unit_value(const UnitScale &s, const UnitAcc &acc, float sxA,
+                                            float sxB) {
+    const float dotA = acc.a * 16777216.0f;   // 2^24, exact
+    const float dotB = acc.b * 1048576.0f;    // 2^20, exact
+    const float pos = __builtin_fmaf(s.kA, dotA, s.kB * dotB);
+    const float neg = __builtin_fmaf(s.mA, sxA, s.mB * sxB);
+    return pos - neg;
+}
+
+// Sum over groups of LPR consecutive lanes inside a wave (LPR <= 64), xor
+// butterfly in ascending distance; every lane of the group ends with the same
+// bits because fp32 addition is commutative.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int off = 1; off < W; off <<= 1)
+        v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g / (1.0f + expf(-g)) * u;
+}
+
+}  // namespace q4k

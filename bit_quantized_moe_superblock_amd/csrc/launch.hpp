@@ -1,0 +1,41 @@
+// Internal launch interface between the C ABI (api.hip) and the kernel files.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4k {
+
+struct GemvLaunch {
+    const void *w0;            // stacked experts; the gate stack when fused_swiglu
+    const void *w1;            // up stack (fused_swiglu only)
+    const float *src1;
+    const int32_t *ids;
+    const int32_t *bucket_ws;  // non-null selects the bucketed mode
+    float *dst;
+    int64_t n, k, top_k, num_experts, n_pairs;
+    int64_t outer, inner;
+    bool fused_swiglu;
+};
+
+hipError_t launch_q4k_gemv(const GemvLaunch &L, hipStream_t st);
+hipError_t launch_q4k_dequant(const void *blocks, float *out, int64_t n_blocks, hipStream_t st);
+hipError_t launch_q4k_quant(const float *w, void *blocks, int64_t n_blocks, hipStream_t st);
+hipError_t launch_moe_bucket(const int32_t *ids, int64_t n_pairs, int64_t num_experts,
+                             int32_t *ws, hipStream_t st);
+hipError_t launch_moe_combine(const float *h_mid, const float *expert_out, const float *route_w,
+                              const float *shared_out, const float *shared_gate_logit, float *out,
+                              int64_t hidden, int64_t m, int64_t top_k, int shared_mode,
+                              hipStream_t st);
+hipError_t launch_q4tp_matvec(const void *t, const float *x, float *y, int64_t rows,
+                              int64_t cols, hipStream_t st);
+hipError_t launch_q4tp_quant(const float *w, void *t, int64_t rows, int64_t cols,
+                             hipStream_t st);
+
+// Workspace of the bucketing kernel in int32 words (layout in q4kmoe.h).
+inline int64_t bucket_ws_words(int64_t n_pairs, int64_t num_experts) {
+    return (num_experts + 1) + (num_experts + 2) + n_pairs + (num_experts + 1) + 1;
+}
+
+}  // namespace q4k

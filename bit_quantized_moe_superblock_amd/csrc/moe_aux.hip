@@ -1,0 +1,150 @@
+// Expert bucketing and the weighted residual combine.
+//
+// Bucketing (moeflux expert_forward.rs, encode_moe_gather_id_fuse step 1 and
+// the ExpertBuckets CSR): one workgroup of 1024 threads counts pairs per
+// expert, scans the counts, lists the non-empty buckets, and orders the pairs
+// by sorting the unique keys (bucket << 13 | pair) with a bitonic network in
+// LDS, so each bucket lists its pairs in ascending pair order and the result is
+// the same on every run.  Bucket E collects ids outside [0, E).
+//
+// Combine (moeflux module doc and encode_moe_combine_residual_n_tokens):
+// out[t,i] = h_mid[t,i] + sum_s w[t,s]*expert_out[t,s,i] + g_t*shared_out[t,i],
+// slots in order, one thread per output element.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace q4k {
+
+constexpr int kBucketThreads = 1024;
+constexpr int kMaxPairsPow2 = 8192;
+
+__global__ __launch_bounds__(kBucketThreads) void k_moe_bucket(const int32_t *__restrict__ ids,
+                                                               int P, int E, int32_t *ws) {
+    __shared__ int cnt[kBucketThreads];
+    __shared__ uint32_t keys[kMaxPairsPow2];
+    __shared__ int wsum_c[16], wsum_f[16];
+    const int tid = threadIdx.x;
+    int32_t *counts = ws;
+    int32_t *offsets = counts + (E + 1);
+    int32_t *pairs = offsets + (E + 2);
+    int32_t *active = pairs + P;
+    int32_t *n_active = active + (E + 1);
+
+    int N = 1;
+    while (N < P)
+        N <<= 1;
+    cnt[tid] = 0;
+    __syncthreads();
+    for (int p = tid; p < N; p += kBucketThreads) {
+        if (p < P) {
+            const int e = ids[p];
+            const int b = ((unsigned)e < (unsigned)E) ? e : E;
+            atomicAdd(&cnt[b], 1);
+            keys[p] = ((uint32_t)b << 13) | (uint32_t)p;
+        } else {
+            keys[p] = 0xFFFFFFFFu;
+        }
+    }
+    __syncthreads();
+
+    // Exclusive scans of the counts and of the non-empty flags over buckets.
+    const int c = tid <= E ? cnt[tid] : 0;
+    const int f = c > 0 ? 1 : 0;
+    int ic = c, iff = f;   // inclusive wave scans
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int tc = __shfl_up(ic, off, 64);
+        const int tf = __shfl_up(iff, off, 64);
+        if (lane >= off) {
+            ic += tc;
+            iff += tf;
+        }
+    }
+    if (lane == 63) {
+        wsum_c[wave] = ic;
+        wsum_f[wave] = iff;
+    }
+    __syncthreads();
+    int base_c = 0, base_f = 0;
+    for (int w = 0; w < wave; w++) {
+        base_c += wsum_c[w];
+        base_f += wsum_f[w];
+    }
+    const int ex_c = base_c + ic - c;
+    const int ex_f = base_f + iff - f;
+    if (tid <= E) {
+        counts[tid] = c;
+        offsets[tid] = ex_c;
+        if (f)
+            active[ex_f] = tid;
+    }
+    if (tid == E) {
+        offsets[E + 1] = ex_c + c;
+        *n_active = ex_f + f;
+    }
+
+    // Bitonic sort of the keys (ascending).
+    for (int size = 2; size <= N; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < (N >> 1); i += kBucketThreads) {
+                const int j = 2 * stride * (i / stride) + (i % stride);
+                const int l = j + stride;
+                const bool up = (j & size) == 0;
+                const uint32_t a = keys[j], b = keys[l];
+                if ((a > b) == up) {
+                    keys[j] = b;
+                    keys[l] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int q = tid; q < P; q += kBucketThreads)
+        pairs[q] = (int32_t)(keys[q] & 8191u);
+}
+
+hipError_t launch_moe_bucket(const int32_t *ids, int64_t n_pairs, int64_t num_experts,
+                             int32_t *ws, hipStream_t st) {
+    hipLaunchKernelGGL(k_moe_bucket, dim3(1), dim3(kBucketThreads), 0, st, ids, (int)n_pairs,
+                       (int)num_experts, ws);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_moe_combine(const float *__restrict__ h_mid,
+                                                     const float *__restrict__ eo,
+                                                     const float *__restrict__ w,
+                                                     const float *__restrict__ shared,
+                                                     const float *__restrict__ logit,
+                                                     float *out, int64_t H, int64_t m, int K,
+                                                     int mode) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= H * m)
+        return;
+    const int64_t t = idx / H, i = idx - t * H;
+    float acc = h_mid[idx];
+    for (int s = 0; s < K; s++)
+        acc = __builtin_fmaf(w[t * K + s], eo[(t * K + s) * H + i], acc);
+    if (mode == 1) {
+        const float g = 1.0f / (1.0f + expf(-logit[t]));
+        acc = __builtin_fmaf(g, shared[idx], acc);
+    } else if (mode == 2) {
+        acc += shared[idx];
+    }
+    out[idx] = acc;
+}
+
+hipError_t launch_moe_combine(const float *h_mid, const float *expert_out, const float *route_w,
+                              const float *shared_out, const float *shared_gate_logit, float *out,
+                              int64_t hidden, int64_t m, int64_t top_k, int shared_mode,
+                              hipStream_t st) {
+    const int64_t n = hidden * m;
+    if (n == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, h_mid,
+                       expert_out, route_w, shared_out, shared_gate_logit, out, hidden, m,
+                       (int)top_k, shared_mode);
+    return hipGetLastError();
+}
+
+}  // namespace q4k

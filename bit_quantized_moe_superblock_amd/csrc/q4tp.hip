@@ -1,0 +1,267 @@
+// Q4TiledP dense matvec and encoder (cortiq-engine mv_lab.rs, kernel `cur`).
+//
+// Tensor layout, rows x cols, gpr = cols/32:
+//   [0, rows*gpr*16)      group (r,g) at (r*gpr+g)*16: byte i holds element 2i
+//                         (low nibble) and 2i+1 (high nibble), value nibble-8;
+//   params_off = rows*gpr*16: per row fp16 base then fp16 step;
+//   codes_off = params_off + rows*4: per row ceil(5*gpr/8) bytes of 5-bit
+//                         codes, group g at bit 5g, least significant bit first;
+//   scale(r,g) = 2^(base + code*step).
+// y[r] = sum_g scale(r,g) * (sum_j nib*x[32g+j] - 8*sum_j x[32g+j]).
+//
+// LPR lanes (a power of two >= gpr, at most 256) cover a row, one 16-byte
+// group per lane per step; x is staged in LDS with per-group sums.  The group
+// scale uses the hardware exp2 (about one ulp), as the page's kernel does.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace q4k {
+
+// Group g's 32 activations start at 36*g floats in LDS (4 pad floats per
+// group keeps the 16-byte reads of neighbouring lanes in different banks).
+__device__ __forceinline__ int gpad(int i) { return i + ((i >> 5) << 2); }
+
+template <int LPR, int ITERS>
+__global__ __launch_bounds__(256) void k_q4tp_matvec(const uint8_t *__restrict__ t,
+                                                     const float *__restrict__ x,
+                                                     float *__restrict__ y, int rows, int cols) {
+    extern __shared__ float lds[];
+    constexpr int RPI = 256 / LPR;
+    constexpr int WL = LPR < 64 ? LPR : 64;
+    constexpr int WPR = LPR / WL;
+    const int gpr = cols >> 5;
+    float *xs = lds;
+    float *sx = xs + cols + (gpr << 2);
+    float *red = sx + gpr;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < cols; i += 256)
+        xs[gpad(i)] = x[i];
+    __syncthreads();
+    for (int g = tid; g < gpr; g += 256) {
+        const float *p = xs + 36 * g;
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; i++)
+            s += p[i];
+        sx[g] = s;
+    }
+    __syncthreads();
+
+    const int64_t params_off = (int64_t)rows * gpr * 16;
+    const int64_t codes_off = params_off + (int64_t)rows * 4;
+    const int64_t stride = (5 * gpr + 7) >> 3;
+    const int u = tid % LPR;
+    const int rsub = tid / LPR;
+    const int row0 = blockIdx.x * (ITERS * RPI);
+#pragma unroll
+    for (int it = 0; it < ITERS; it++) {
+        const int r = row0 + it * RPI + rsub;
+        const bool rok = r < rows;
+        float acc = 0.0f;
+        if (rok) {
+            const uint32_t pb = *(const uint32_t *)(t + params_off + (int64_t)r * 4);
+            const float base = lo_half(pb), step = hi_half(pb);
+            const uint8_t *cp = t + codes_off + (int64_t)r * stride;
+            for (int g = u; g < gpr; g += LPR) {
+                const uint4 q = *(const uint4 *)(t + ((int64_t)r * gpr + g) * 16);
+                const int bit = 5 * g;
+                const int cb = bit >> 3, shf = bit & 7;
+                uint32_t cw = cp[cb];
+                if (shf > 3)
+                    cw |= (uint32_t)cp[cb + 1] << 8;
+                const uint32_t code = (cw >> shf) & 31u;
+                const float scale = exp2f(__builtin_fmaf((float)code, step, base));
+                const float4 *xv = (const float4 *)(xs + 36 * g);
+                // element 8d+e of dword d: even e in the low nibbles, odd in the high
+                float lo = 0.0f, hi = 0.0f;
+                const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int d = 0; d < 4; d++) {
+                    const uint32_t v = w4[d], s = v >> 8;
+                    const float4 x0 = xv[2 * d], x1 = xv[2 * d + 1];
+                    const uint32_t r0 = v & 0x000F000Fu, r2 = s & 0x000F000Fu;
+                    const uint32_t r1 = v & 0x00F000F0u, r3 = s & 0x00F000F0u;
+                    lo = __builtin_fmaf(lo_half(r0), x0.x, lo);   // element 0
+                    hi = __builtin_fmaf(lo_half(r1), x0.y, hi);   // element 1
+                    lo = __builtin_fmaf(lo_half(r2), x0.z, lo);   // element 2
+                    hi = __builtin_fmaf(lo_half(r3), x0.w, hi);   // element 3
+                    lo = __builtin_fmaf(hi_half(r0), x1.x, lo);   // element 4
+                    hi = __builtin_fmaf(hi_half(r1), x1.y, hi);   // element 5
+                    lo = __builtin_fmaf(hi_half(r2), x1.z, lo);   // element 6
+                    hi = __builtin_fmaf(hi_half(r3), x1.w, hi);   // element 7
+                }
+                // lo = 2^-24 * sum over even elements, hi = 2^-20 * sum over odd ones
+                const float dot = __builtin_fmaf(lo, 16777216.0f, hi * 1048576.0f);
+                acc = __builtin_fmaf(scale, __builtin_fmaf(-8.0f, sx[g], dot), acc);
+            }
+        }
+        acc = group_sum<WL>(acc);
+        if constexpr (WPR > 1) {
+            const int wave = tid >> 6;
+            if ((tid & 63) == 0)
+                red[wave] = acc;
+            __syncthreads();
+            if (u == 0) {
+                float s = red[wave];
+                for (int w = 1; w < WPR; w++)
+                    s += red[wave + w];
+                acc = s;
+            }
+            __syncthreads();
+        }
+        if (u == 0 && rok)
+            y[r] = acc;
+    }
+}
+
+static int tp_lanes(int gpr) {
+    int l = 4;
+    while (l < gpr && l < 256)
+        l <<= 1;
+    return l;
+}
+
+template <int LPR>
+static hipError_t tp_launch(const void *t, const float *x, float *y, int rows, int cols,
+                            hipStream_t st) {
+    constexpr int RPI = 256 / LPR;
+    const int gpr = cols >> 5;
+    const size_t lds = (size_t)(cols + 4 * gpr + gpr + 8) * sizeof(float);
+    constexpr int IT = 2;
+    auto kern = k_q4tp_matvec<LPR, IT>;
+    if (lds > 65536)
+        hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds);
+    dim3 grid((rows + IT * RPI - 1) / (IT * RPI));
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const uint8_t *)t, x, y, rows, cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_q4tp_matvec(const void *t, const float *x, float *y, int64_t rows,
+                              int64_t cols, hipStream_t st) {
+    const int gpr = (int)(cols >> 5);
+    switch (tp_lanes(gpr)) {
+    case 4: return tp_launch<4>(t, x, y, (int)rows, (int)cols, st);
+    case 8: return tp_launch<8>(t, x, y, (int)rows, (int)cols, st);
+    case 16: return tp_launch<16>(t, x, y, (int)rows, (int)cols, st);
+    case 32: return tp_launch<32>(t, x, y, (int)rows, (int)cols, st);
+    case 64: return tp_launch<64>(t, x, y, (int)rows, (int)cols, st);
+    case 128: return tp_launch<128>(t, x, y, (int)rows, (int)cols, st);
+    default: return tp_launch<256>(t, x, y, (int)rows, (int)cols, st);
+    }
+}
+
+// ------------------------------------------------------------- encoder ----
+// One workgroup (256 threads) per row; thread g-loop over groups.  Steps:
+// t_g = max|w|/7; lt_g = float(log2(double t_g)) for t_g > 0;
+// base = fp16(min lt), step = fp16(max(0, max lt - base)/31);
+// code_g = clamp(rne((lt_g - base)/step), 0, 31);
+// scale = float(exp2(double(base + code*step)));
+// nibble = clamp(rne(w/scale), -8, 7) + 8.  log2/exp2 in double, rest fp32.
+__global__ __launch_bounds__(256) void k_q4tp_quant(const float *__restrict__ w,
+                                                    uint8_t *__restrict__ t, int rows, int cols) {
+    __shared__ float lmin_s[256], lmax_s[256];
+    __shared__ int any_s[256];
+    __shared__ uint32_t codes_w[(5 * 512 + 31) / 32 + 1];
+    const int r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int gpr = cols >> 5;
+    const float *x = w + (int64_t)r * cols;
+    const int64_t params_off = (int64_t)rows * gpr * 16;
+    const int64_t codes_off = params_off + (int64_t)rows * 4;
+    const int stride = (5 * gpr + 7) >> 3;
+    float lmin = 0.0f, lmax = 0.0f;
+    int any = 0;
+    for (int g = tid; g < gpr; g += 256) {
+        float amax = 0.0f;
+        for (int e = 0; e < 32; e++) {
+            const float a = fabsf(x[32 * g + e]);
+            if (a > amax) amax = a;
+        }
+        const float tg = amax / 7.0f;
+        if (tg > 0.0f) {
+            const float lt = (float)log2((double)tg);
+            if (!any || lt < lmin) lmin = lt;
+            if (!any || lt > lmax) lmax = lt;
+            any = 1;
+        }
+    }
+    lmin_s[tid] = lmin;
+    lmax_s[tid] = lmax;
+    any_s[tid] = any;
+    for (int i = tid; i < (int)(sizeof(codes_w) / 4); i += 256)
+        codes_w[i] = 0u;
+    __syncthreads();
+    if (tid == 0) {
+        int a = 0;
+        float mn = 0.0f, mx = 0.0f;
+        for (int i = 0; i < 256; i++) {
+            if (!any_s[i]) continue;
+            if (!a || lmin_s[i] < mn) mn = lmin_s[i];
+            if (!a || lmax_s[i] > mx) mx = lmax_s[i];
+            a = 1;
+        }
+        uint32_t base = 0, step = 0;
+        if (a) {
+            const _Float16 bh = (_Float16)mn;
+            base = __builtin_bit_cast(uint16_t, bh);
+            float span = mx - (float)bh;
+            if (span < 0.0f) span = 0.0f;
+            step = __builtin_bit_cast(uint16_t, (_Float16)(span / 31.0f));
+        }
+        *(uint32_t *)(t + params_off + (int64_t)r * 4) = base | (step << 16);
+        lmin_s[0] = __builtin_bit_cast(float, base | (step << 16));
+    }
+    __syncthreads();
+    const uint32_t pb = __builtin_bit_cast(uint32_t, lmin_s[0]);
+    const float bf = lo_half(pb), sf = hi_half(pb);
+    for (int g = tid; g < gpr; g += 256) {
+        float amax = 0.0f;
+        for (int e = 0; e < 32; e++) {
+            const float a = fabsf(x[32 * g + e]);
+            if (a > amax) amax = a;
+        }
+        const float tg = amax / 7.0f;
+        const bool has = tg > 0.0f;
+        int code = 0;
+        if (has && sf > 0.0f) {
+            const float lt = (float)log2((double)tg);
+            code = (int)__builtin_rintf((lt - bf) / sf);
+            code = code < 0 ? 0 : (code > 31 ? 31 : code);
+        }
+        const float L = (float)exp2((double)(bf + (float)code * sf));
+        uint8_t grp[16];
+        for (int i = 0; i < 16; i++) {
+            int nib[2];
+            for (int h = 0; h < 2; h++) {
+                int q = 0;
+                if (has && L > 0.0f) {
+                    q = (int)__builtin_rintf(x[32 * g + 2 * i + h] / L);
+                    q = q < -8 ? -8 : (q > 7 ? 7 : q);
+                }
+                nib[h] = q + 8;
+            }
+            grp[i] = (uint8_t)(nib[0] | (nib[1] << 4));
+        }
+        uint4 v;
+        __builtin_memcpy(&v, grp, 16);
+        *(uint4 *)(t + ((int64_t)r * gpr + g) * 16) = v;
+        const int bit = 5 * g;
+        atomicOr(&codes_w[bit >> 5], (uint32_t)code << (bit & 31));
+        if ((bit & 31) > 27)
+            atomicOr(&codes_w[(bit >> 5) + 1], (uint32_t)code >> (32 - (bit & 31)));
+    }
+    __syncthreads();
+    uint8_t *cp = t + codes_off + (int64_t)r * stride;
+    for (int i = tid; i < stride; i += 256)
+        cp[i] = (uint8_t)(codes_w[i >> 2] >> (8 * (i & 3)));
+}
+
+hipError_t launch_q4tp_quant(const float *w, void *t, int64_t rows, int64_t cols,
+                             hipStream_t st) {
+    hipLaunchKernelGGL(k_q4tp_quant, dim3((unsigned)rows), dim3(256), 0, st, w, (uint8_t *)t,
+                       (int)rows, (int)cols);
+    return hipGetLastError();
+}
+
+}  // namespace q4k

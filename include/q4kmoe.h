@@ -1,0 +1,196 @@
+/*
+ * q4kmoe.h -- C ABI of the Q4_K MoE expert library for AMD MI355X (gfx950).
+ *
+ * Sources (the three pages this library implements):
+ *   [FK] ferrum-kernels 0.7.7, src/backend/metal/q4_k_moe_id_gemv_batched.rs
+ *   [MF] moeflux 0.1.0-pre.3, src/riir/moe/expert_forward.rs
+ *   [CE] cortiq-engine 0.7.7, examples/mv_lab.rs
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronizes.  Scratch memory is a caller
+ *     buffer (`ws`, `ws_bytes`) where a call needs one.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it and the call returns; results are visible to
+ *     later work on the same stream.
+ *   - Arguments are validated on the host before any HIP call; a bad argument
+ *     returns a nonzero status and enqueues nothing.  A failed launch returns
+ *     Q4K_ERR_LAUNCH.  q4k_status_string() names every status.
+ *   - Strides are in elements (floats), as in [FK]'s module doc.
+ *   - Activations and outputs are fp32, row-major.
+ *   - Calls are stateless and may be issued from several host threads.
+ */
+#ifndef Q4KMOE_H
+#define Q4KMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    Q4K_OK = 0,
+    Q4K_ERR_SHAPE = 1,     /* a size is out of range or not a required multiple */
+    Q4K_ERR_NULL = 2,      /* a required pointer is NULL                        */
+    Q4K_ERR_STRIDE = 3,    /* an activation stride is negative                  */
+    Q4K_ERR_WORKSPACE = 4, /* workspace missing or smaller than required        */
+    Q4K_ERR_LAUNCH = 5,    /* the HIP runtime rejected a launch                 */
+    Q4K_ERR_ARG = 6        /* an enum argument has an unknown value             */
+};
+
+/* Bucketing flag of the id-GEMV entry points ([MF]
+ * encode_moe_batched_permute_fuse: group (token, slot) pairs by expert so each
+ * expert's weights are read once).  AUTO buckets when more than one token is
+ * in the batch.  PREBUILT runs the bucketed kernels on a workspace that
+ * moe_bucket (or an earlier call) already filled for the same ids, so gate/up
+ * and down pay for one bucketing pass.  The output is identical bit for bit
+ * in every mode. */
+enum { Q4K_BUCKET_AUTO = 0, Q4K_BUCKET_OFF = 1, Q4K_BUCKET_ON = 2, Q4K_BUCKET_PREBUILT = 3 };
+
+/* Shared-expert term of the combine ([MF] combine_kernel_name and the
+ * variant comment: sigmoid-gated for Qwen3 MoE, added unscaled for
+ * DeepSeek-V3-style models, or absent). */
+enum { MOE_SHARED_NONE = 0, MOE_SHARED_SIGMOID = 1, MOE_SHARED_UNSCALED = 2 };
+
+#define Q4K_BLOCK_WEIGHTS 256 /* [FK] test: QK_K                          */
+#define Q4K_BLOCK_BYTES 144   /* [FK] test: BLOCK_BYTES                    */
+#define Q4K_MAX_TOP_K 16      /* [MF] MAX_K                                */
+#define Q4K_MAX_IN 16384      /* largest in-features (k) of one GEMV       */
+#define Q4K_MAX_EXPERTS 1023  /* bucketing keeps E+1 buckets in one block  */
+#define Q4K_MAX_PAIRS 8192    /* m*top_k handled by one bucketing launch   */
+#define Q4TP_MAX_COLS 16384   /* largest Q4TiledP row                       */
+
+const char *q4k_status_string(int status);
+int q4k_abi_version(void);
+
+/* Bytes of an n x k Q4_K matrix: n*(k/256)*144 ([FK]
+ * dispatch_gemv_q4k_moe_id_batched_on_encoder, nb01 and nb02).  -1 when k is
+ * not a positive multiple of 256 or n < 0. */
+int64_t q4k_matrix_bytes(int64_t n, int64_t k);
+
+/* Q4_K superblock layout (reading of [FK]: 256 weights in 144 bytes, GGML's
+ * Q4_K by way of candle):
+ *   bytes 0-1 d (fp16), 2-3 dmin (fp16), 4-15 eight 6-bit scales and eight
+ *   6-bit mins packed in 12 bytes, 16-143 nibbles: byte 32c+l holds weight
+ *   64c+l (low nibble) and 64c+32+l (high nibble);
+ *   w_i = d*scale_j*q_i - dmin*min_j with j = i/32.
+ *
+ * q4k_dequantize: `blocks` (n_blocks*144 bytes) -> `out` (n_blocks*256 fp32).
+ * The fp32 result is exact (every product fits in 24 bits), so it is
+ * bit-identical to any correct evaluation.  n_blocks >= 0. */
+int q4k_dequantize(const void *blocks, float *out, int64_t n_blocks, void *stream);
+
+/* q4k_quantize: `w` fp32 [n_rows, k] -> `blocks` [n_rows, k/256] superblocks,
+ * k % 256 == 0.  The pages quantize with candle and print no encoder; this is
+ * a plain min/max affine encoder whose steps are single IEEE float operations
+ * (per sub-block lo = min(0, min w), hi = max w, a = (hi-lo)/15, b = -lo;
+ * d = fp16(max a / 63), dmin = fp16(max b / 63); scale = rne(a/d),
+ * min = rne(b/dmin), q = rne((w + dmin*min)/(d*scale)), all clamped). */
+int q4k_quantize(const float *w, void *blocks, int64_t n_rows, int64_t k, void *stream);
+
+/* Scratch bytes that the bucketed modes need for `n_pairs` (token, slot)
+ * pairs over `num_experts` experts. */
+int64_t moe_bucket_workspace_bytes(int64_t n_pairs, int64_t num_experts);
+
+/* Expert bucketing ([MF] encode_moe_gather_id_fuse step 1, map0; and
+ * ExpertBuckets, CSR by expert).  Writes into `ws` (int32 words):
+ *   counts[E+1] | offsets[E+2] | pairs[P] | active[E+1] | n_active[1]
+ * where bucket E collects ids outside [0, E), offsets is the exclusive prefix
+ * sum of counts, pairs lists pair indices grouped by bucket in ascending order
+ * inside a bucket, and active lists the non-empty buckets ascending.
+ * The layout above is what the bucketed GEMV reads; callers need not read it. */
+int moe_bucket(const int32_t *ids, int64_t n_pairs, int64_t num_experts, void *ws,
+               int64_t ws_bytes, void *stream);
+
+/* Batched indirect-dispatch Q4_K GEMV ([FK]
+ * dispatch_gemv_q4k_moe_id_batched_on_encoder and module doc).
+ *   w_stacked : [num_experts, n, k/256] superblocks; expert e starts at byte
+ *               e*n*(k/256)*144.  The caller pre-offsets the pointer if the
+ *               stack starts inside a larger buffer ([FK] weights_byte_offset).
+ *   src1      : activations; pair p = token*top_k + slot reads the k floats at
+ *               src1 + token*src1_outer_stride + slot*src1_inner_stride.
+ *               gate/up: outer = k, inner = 0; down: outer = top_k*k, inner = k.
+ *   ids       : [m*top_k] int32 expert ids.  An id outside [0, num_experts)
+ *               gives a zero output row (the pages leave it undefined).
+ *   dst       : [m*top_k, n] fp32.
+ *   Requires k % 256 == 0, 256 <= k <= Q4K_MAX_IN, n >= 1, m >= 1,
+ *   1 <= top_k <= Q4K_MAX_TOP_K, 1 <= num_experts <= Q4K_MAX_EXPERTS, strides
+ *   >= 0.  ([FK] asserts k%256 and n%4; n%4 is not needed here.)
+ *   bucket_flag: Q4K_BUCKET_*; the bucketed mode needs
+ *   ws_bytes >= moe_bucket_workspace_bytes(m*top_k, num_experts), otherwise ws
+ *   may be NULL.  Output is independent of bucketing and of m bit for bit. */
+int q4k_moe_id_gemv(const void *w_stacked, const float *src1, const int32_t *ids, float *dst,
+                    int64_t n, int64_t k, int64_t m, int64_t top_k,
+                    int64_t src1_outer_stride, int64_t src1_inner_stride,
+                    int64_t num_experts, int bucket_flag, void *ws, int64_t ws_bytes,
+                    void *stream);
+
+/* Fused gate + up id-GEMV with SiLU ([FK] test module:
+ * dispatch_gemv_q4k_moe_id_gate_up_silu_batched_on_encoder, which writes
+ * [m*top_k, n] rows of silu(gate.x) * (up.x); [MF] swiglu_fused).
+ *   w_gate, w_up : two stacks of the same shape [num_experts, n, k/256]
+ *   out          : [m*top_k, n] fp32, out[p,r] = silu(g)*u with
+ *                  g = W_gate[ids[p]][r].x, u = W_up[ids[p]][r].x, x the
+ *                  pair's activation row (strides as in q4k_moe_id_gemv).
+ *   Same requirements and bucketing as q4k_moe_id_gemv. */
+int q4k_moe_gate_up_silu(const void *w_gate, const void *w_up, const float *src1,
+                         const int32_t *ids, float *out, int64_t n, int64_t k, int64_t m,
+                         int64_t top_k, int64_t src1_outer_stride, int64_t src1_inner_stride,
+                         int64_t num_experts, int bucket_flag, void *ws, int64_t ws_bytes,
+                         void *stream);
+
+/* Expert FFN for all (token, slot) pairs ([MF] module doc: gate and up
+ * matvecs, SwiGLU, down matvec; encode_moe_gather_id_fuse for the strides).
+ *   w_gate, w_up : [num_experts, inter, hidden/256] superblocks
+ *   w_down       : [num_experts, hidden, inter/256] superblocks
+ *   h_post       : [m, hidden] fp32 (one row per token, shared by its slots)
+ *   ids          : [m*top_k] int32
+ *   act          : [m*top_k, inter] fp32 out: silu(gate.x) * (up.x)
+ *   expert_out   : [m*top_k, hidden] fp32 out: down applied to act
+ *   hidden and inter: multiples of 256, at most Q4K_MAX_IN.
+ *   The shared expert is this call on a one-expert stack with ids = 0 and
+ *   top_k = 1.  Workspace as for q4k_moe_id_gemv. */
+int moe_expert_ffn(const void *w_gate, const void *w_up, const void *w_down,
+                   const float *h_post, const int32_t *ids, float *act, float *expert_out,
+                   int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
+                   int64_t top_k, int bucket_flag, void *ws, int64_t ws_bytes, void *stream);
+
+/* Weighted combine with residual ([MF] module doc and
+ * encode_moe_combine_residual_n_tokens):
+ *   out[t,i] = h_mid[t,i] + sum_{s<top_k} route_w[t*top_k+s]*expert_out[t*top_k+s,i]
+ *              + g_t*shared_out[t,i]
+ * with g_t = sigmoid(shared_gate_logit[t]) (MOE_SHARED_SIGMOID), 1
+ * (MOE_SHARED_UNSCALED) or no shared term (MOE_SHARED_NONE; shared_out and
+ * shared_gate_logit may be NULL).  Slots are summed in order, so the result
+ * does not depend on the batch.  `out` may alias `h_mid`. */
+int moe_combine_residual(const float *h_mid, const float *expert_out, const float *route_w,
+                         const float *shared_out, const float *shared_gate_logit, float *out,
+                         int64_t hidden, int64_t m, int64_t top_k, int shared_mode,
+                         void *stream);
+
+/* Q4TiledP dense tensor ([CE] kernel `cur`): rows x cols, cols % 32 == 0,
+ * gpr = cols/32 groups of 32 signed nibbles (value = nibble - 8, byte i of a
+ * group holds elements 2i and 2i+1), 16 bytes per group at (r*gpr+g)*16; then
+ * per row an fp16 pair (base, step); then per row ceil(5*gpr/8) bytes of 5-bit
+ * group codes, least significant bit first.  Group scale = 2^(base+code*step).
+ * q4tp_tensor_bytes returns the byte size, -1 on bad shape. */
+int64_t q4tp_tensor_bytes(int64_t rows, int64_t cols);
+
+/* y[r] = sum_g scale(r,g) * sum_j (nibble-8) * x[32g+j]  ([CE] kernel `cur`).
+ * x: [cols] fp32, y: [rows] fp32.  1 <= cols <= Q4TP_MAX_COLS. */
+int q4tp_matvec(const void *tensor, const float *x, float *y, int64_t rows, int64_t cols,
+                void *stream);
+
+/* q4tp_quantize: fp32 [rows, cols] -> Q4TiledP.  The page prints no encoder;
+ * reading: t_g = max|w|/7, lt_g = log2(t_g); base = fp16(min lt),
+ * step = fp16((max lt - base)/31); code = rne((lt-base)/step);
+ * nibble = clamp(rne(w/scale), -8, 7) + 8. */
+int q4tp_quantize(const float *w, void *tensor, int64_t rows, int64_t cols, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4KMOE_H */

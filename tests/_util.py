@@ -1,0 +1,27 @@
+"""Shared helpers for the parity tests (no arithmetic of the method here)."""
+import numpy as np
+
+# The band the pages use for GPU kernels against a C-side oracle (moeflux
+# expert_forward.rs, module doc, Tolerance regime).
+BAND_MAX_ABS_REL = 1e-3
+BAND_COSINE = 0.9999
+
+
+def band(got, want, what=""):
+    """Assert the fp32 parity band and return (max_abs_diff / max|want|, cosine)."""
+    got = np.asarray(got, np.float64).reshape(-1)
+    want = np.asarray(want, np.float64).reshape(-1)
+    assert got.shape == want.shape, what
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    mx = np.abs(want).max()
+    diff = np.abs(got - want).max()
+    rel = diff / mx if mx > 0 else diff
+    nrm = np.linalg.norm(got) * np.linalg.norm(want)
+    cos = float(got @ want / nrm) if nrm > 0 else 1.0
+    assert rel <= BAND_MAX_ABS_REL, f"{what}: max_abs_diff/max|out| = {rel:.3g}"
+    assert cos >= BAND_COSINE, f"{what}: cosine {cos:.8f}"
+    return rel, cos
+
+
+def bits(a):
+    return np.ascontiguousarray(a, np.float32).view(np.uint32)

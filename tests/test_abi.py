@@ -1,0 +1,131 @@
+"""The C-ABI library loads and exports every entry point include/q4kmoe.h
+declares, and rejects bad arguments on the host before any HIP call (so these
+run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_moe_superblock_amd as q4
+from bit_quantized_moe_superblock_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4kmoe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = _declared()
+    assert len(names) >= 12, names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, f"{n} has no Python binding"
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_constants_match_header(lib):
+    src = open(HEADER).read()
+    for name, val in [("Q4K_BLOCK_WEIGHTS", 256), ("Q4K_BLOCK_BYTES", 144), ("Q4K_MAX_TOP_K", 16),
+                      ("Q4K_MAX_IN", _lib.Q4K_MAX_IN), ("Q4K_MAX_EXPERTS", _lib.Q4K_MAX_EXPERTS),
+                      ("Q4K_MAX_PAIRS", _lib.Q4K_MAX_PAIRS), ("Q4TP_MAX_COLS", _lib.Q4TP_MAX_COLS)]:
+        assert re.search(rf"#define {name} {val}\b", src), name
+    assert q4.q4k_abi_version() == 1
+
+
+def test_size_helpers(lib):
+    assert q4.q4k_matrix_bytes(768, 2048) == 884_736
+    assert q4.q4k_matrix_bytes(7168, 2048) == 8_257_536
+    assert q4.q4k_matrix_bytes(4, 100) == -1
+    assert q4.q4tp_tensor_bytes(1, 4096) == 2132
+    assert q4.q4tp_tensor_bytes(1, 14336) == 7452
+    assert q4.q4tp_tensor_bytes(3, 33) == -1
+    assert q4.moe_bucket_workspace_bytes(128, 128) == 4 * (129 + 130 + 128 + 129 + 1)
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert q4.status_string(s) and q4.status_string(s) != "unknown status"
+    assert q4.status_string(99) == "unknown status"
+
+
+FAKE = 1 << 20   # a non-null, 16-byte aligned address that is never dereferenced
+
+
+def _err(fn, *args):
+    with pytest.raises(q4.Q4KError) as e:
+        fn(*args, stream=0)
+    return e.value.status
+
+
+def test_id_gemv_validation(lib):
+    g = q4.q4k_moe_id_gemv
+    ok = dict(n=64, k=256, m=3, top_k=2, outer=256, inner=0, E=4)
+
+    def call(w=FAKE, x=FAKE, ids=FAKE, dst=FAKE, n=64, k=256, m=3, top_k=2, outer=256, inner=0,
+             E=4, flag=q4.Q4K_BUCKET_OFF, ws=None, wsb=0):
+        return _err(g, w, x, ids, dst, n, k, m, top_k, outer, inner, E, flag, ws, wsb)
+
+    assert call(k=100) == _lib.Q4K_ERR_SHAPE
+    assert call(k=0) == _lib.Q4K_ERR_SHAPE
+    assert call(k=16384 + 256) == _lib.Q4K_ERR_SHAPE
+    assert call(n=0) == _lib.Q4K_ERR_SHAPE
+    assert call(m=0) == _lib.Q4K_ERR_SHAPE
+    assert call(top_k=0) == _lib.Q4K_ERR_SHAPE
+    assert call(top_k=17) == _lib.Q4K_ERR_SHAPE
+    assert call(E=0) == _lib.Q4K_ERR_SHAPE
+    assert call(E=1024) == _lib.Q4K_ERR_SHAPE
+    assert call(w=None) == _lib.Q4K_ERR_NULL
+    assert call(w=FAKE + 8) == _lib.Q4K_ERR_NULL       # weights need 16-byte alignment
+    assert call(dst=None) == _lib.Q4K_ERR_NULL
+    assert call(outer=-1) == _lib.Q4K_ERR_STRIDE
+    assert call(inner=-5) == _lib.Q4K_ERR_STRIDE
+    assert call(flag=7) == _lib.Q4K_ERR_ARG
+    assert call(flag=q4.Q4K_BUCKET_ON) == _lib.Q4K_ERR_WORKSPACE
+    assert call(flag=q4.Q4K_BUCKET_ON, ws=FAKE, wsb=8) == _lib.Q4K_ERR_WORKSPACE
+    assert call(flag=q4.Q4K_BUCKET_AUTO) == _lib.Q4K_ERR_WORKSPACE   # m > 1 buckets
+
+
+def test_ffn_combine_bucket_q4tp_validation(lib):
+    f = q4.moe_expert_ffn
+    base = [FAKE] * 7
+    assert _err(f, *base, 2048, 700, 8, 1, 8) == _lib.Q4K_ERR_SHAPE       # inter % 256
+    assert _err(f, *base, 2048, 768, 8, 1, 0) == _lib.Q4K_ERR_SHAPE
+    bad = list(base)
+    bad[4] = None
+    assert _err(f, *bad, 2048, 768, 8, 1, 8) == _lib.Q4K_ERR_NULL
+    c = q4.moe_combine_residual
+    assert _err(c, FAKE, FAKE, FAKE, None, None, FAKE, 64, 1, 8, 3) == _lib.Q4K_ERR_ARG
+    assert _err(c, FAKE, FAKE, FAKE, None, None, FAKE, 64, 1, 8, 1) == _lib.Q4K_ERR_NULL
+    assert _err(c, FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 1, 8, 1) == _lib.Q4K_ERR_NULL
+    assert _err(c, FAKE, FAKE, FAKE, None, None, FAKE, 0, 1, 8, 0) == _lib.Q4K_ERR_SHAPE
+    b = q4.moe_bucket
+    assert _err(b, FAKE, 0, 8, FAKE, 1 << 20) == _lib.Q4K_ERR_SHAPE
+    assert _err(b, FAKE, 8193, 8, FAKE, 1 << 20) == _lib.Q4K_ERR_SHAPE
+    assert _err(b, FAKE, 16, 8, FAKE, 4) == _lib.Q4K_ERR_WORKSPACE
+    m = q4.q4tp_matvec
+    assert _err(m, FAKE, FAKE, FAKE, 4, 48) == _lib.Q4K_ERR_SHAPE
+    assert _err(m, FAKE, FAKE, FAKE, 4, 16384 + 32) == _lib.Q4K_ERR_SHAPE
+    assert _err(m, None, FAKE, FAKE, 4, 64) == _lib.Q4K_ERR_NULL
+    assert _err(q4.q4k_quantize, FAKE, FAKE, 2, 300) == _lib.Q4K_ERR_SHAPE
+    assert _err(q4.q4k_dequantize, FAKE, FAKE, -1) == _lib.Q4K_ERR_SHAPE
+    assert _err(q4.q4tp_quantize, FAKE, FAKE, 2, 40) == _lib.Q4K_ERR_SHAPE
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    with pytest.raises(ValueError):
+        q4.q4k_dequantize(torch.zeros(144, dtype=torch.uint8), FAKE, 1, stream=0)
