@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Benchmark of one Q4_K MoE decode layer on one MI355X.
+
+A step is one whole MoE layer on one batch of synthetic decode input:
+expert bucketing (when m > 1), the fused gate/up id-GEMV with SiLU over the
+routed experts, the down id-GEMV, the shared expert's gate/up and down, and the
+weighted residual combine -- every kernel of the hot path.
+
+Workload (the throughput line): hidden 2048, expert intermediate 768, 128
+experts, top_k 8, m = 1 token, sigmoid-gated shared expert of the same shape
+(a Qwen3-30B-A3B-class layer; ferrum-kernels q4_k_moe_id_gemv_batched.rs
+microbench shape, moeflux expert_forward.rs combine).  A second object reports
+m = 16 tokens with Zipf(1.1) routing, where bucketing lets tokens that share
+an expert read it once.
+
+Cold-cache protocol: the weights exist as R independent replicas (each a full
+128-expert layer, 340 MB) and G id sets; consecutive steps use different
+replicas, so a graph replay of G steps touches far more distinct bytes than the
+256 MB Infinity Cache holds.  Steps are captured into HIP graphs (one launch
+per G layers) so host overhead does not pace the GPU.
+
+value = unique expert-weight bytes read per layer (distinct routed experts
+plus the shared expert, three matrices each) / wall time per layer.
+roofline = the layer's first kernel (fused gate/up + SiLU over the routed
+experts with the shared expert in the same launch), timed by a graph of only
+its launches over the same rotation (in-graph launches run back to back, so
+the per-launch time is the kernel's duration), against the 8 TB/s HBM peak.
+cpu_baseline = the CPU oracle's layer forward, single-threaded, on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE id-GEMV effective HBM GB/s (% of peak) + µs/MoE layer at M=1,16"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Layer:
+    """Device-resident weight replicas and per-step inputs of one MoE workload."""
+
+    def __init__(self, torch, q4, wl, cfg, replicas, stacks=None):
+        self.torch, self.q4, self.cfg = torch, q4, cfg
+        dev = torch.device("cuda")
+        H, I, E = cfg.hidden, cfg.inter, cfg.num_experts
+        self.mat_bytes = q4.q4k_matrix_bytes(I, H)           # one expert matrix
+        self.expert_bytes = 3 * self.mat_bytes
+        if stacks is None:
+            stacks = []
+            for r in range(replicas):
+                st = []
+                for t, (rows, cols, n_exp) in enumerate([(I, H, E), (I, H, E), (H, I, E),
+                                                          (I, H, 1), (I, H, 1), (H, I, 1)]):
+                    w = wl.device_normal((n_exp * rows, cols), cfg.w_std, seed=1000 * r + t)
+                    b = torch.empty(n_exp * q4.q4k_matrix_bytes(rows, cols), dtype=torch.uint8,
+                                    device=dev)
+                    q4.q4k_quantize(w, b, n_exp * rows, cols)
+                    del w
+                    st.append(b)
+                stacks.append(st)
+            torch.cuda.synchronize()
+        self.stacks = stacks
+
+    def inputs(self, wl, n_sets):
+        torch, cfg = self.torch, self.cfg
+        dev = torch.device("cuda")
+        self.sets = []
+        self.unique = []
+        for s in range(n_sets):
+            a = wl.moe_activations(cfg, index=s)
+            self.sets.append(dict(
+                h_post=torch.from_numpy(a.h_post).to(dev),
+                h_mid=torch.from_numpy(a.h_mid).to(dev),
+                ids=torch.from_numpy(a.ids).to(dev),
+                route_w=torch.from_numpy(a.route_w).to(dev),
+                logit=torch.from_numpy(a.shared_logit).to(dev)))
+            self.unique.append(len(set(a.ids.tolist())))
+        m, K, H, I = cfg.m, cfg.top_k, cfg.hidden, cfg.inter
+        P = m * K
+        self.act = torch.empty(P, I, device=dev)
+        self.eo = torch.empty(P, H, device=dev)
+        self.s_act = torch.empty(m, I, device=dev)
+        self.s_out = torch.empty(m, H, device=dev)
+        self.out = torch.empty(m, H, device=dev)
+        self.lwsb = self.q4.moe_layer_workspace_bytes(H, I, cfg.num_experts, m, K)
+        self.lws = torch.empty(self.lwsb, dtype=torch.uint8, device=dev)
+        self.wsb = self.q4.moe_bucket_workspace_bytes(P, cfg.num_experts)
+        # one bucket workspace per id set, filled here, so a graph of gate/up
+        # launches alone still reads the buckets of its own routing
+        self.ws_sets = []
+        for x in self.sets:
+            ws = torch.empty(self.wsb, dtype=torch.uint8, device=dev)
+            if m > 1:
+                self.q4.moe_bucket(x["ids"], P, cfg.num_experts, ws, self.wsb)
+            self.ws_sets.append(ws)
+        torch.cuda.synchronize()
+
+    def step_of(self, i):
+        return i % len(self.stacks), i % len(self.sets)
+
+    def bucketed(self):
+        return self.cfg.m > 2    # moe_layer_forward's AUTO rule
+
+    def gate_up(self, i):
+        """The layer's first kernel alone: fused gate/up + SiLU over the routed
+        pairs with the shared expert in the same launch (buckets pre-built)."""
+        q4, cfg = self.q4, self.cfg
+        r, s = self.step_of(i)
+        st, x = self.stacks[r], self.sets[s]
+        flag = q4.Q4K_BUCKET_PREBUILT if self.bucketed() else q4.Q4K_BUCKET_OFF
+        q4.q4k_moe_gate_up_silu(st[0], st[1], x["h_post"], x["ids"], self.act, cfg.inter,
+                                cfg.hidden, cfg.m, cfg.top_k, cfg.hidden, 0, cfg.num_experts,
+                                st[3], st[4], self.s_act, flag, self.ws_sets[s], self.wsb)
+
+    def layer(self, i):
+        """One whole MoE layer (every kernel of the hot path)."""
+        q4, cfg = self.q4, self.cfg
+        r, s = self.step_of(i)
+        st, x = self.stacks[r], self.sets[s]
+        q4.moe_layer_forward(st[0], st[1], st[2], st[3], st[4], st[5], x["h_post"], x["h_mid"],
+                             x["ids"], x["route_w"], x["logit"], self.out, cfg.hidden, cfg.inter,
+                             cfg.num_experts, cfg.m, cfg.top_k, cfg.shared_mode,
+                             q4.Q4K_BUCKET_AUTO, self.lws, self.lwsb)
+
+    def layer_bytes(self, i):
+        r, s = self.step_of(i)
+        return (self.unique[s] + 1) * self.expert_bytes
+
+    def gate_up_bytes(self, i):
+        r, s = self.step_of(i)
+        return (self.unique[s] + 1) * 2 * self.mat_bytes
+
+
+def capture(torch, fn, n):
+    """HIP graph of fn(0..n-1), warmed up on a side stream first."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(n):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, replays, warmup):
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / 1e3, wall
+
+
+def run_workload(torch, q4, wl, cfg, args, stacks=None):
+    G = args.group
+    layer = Layer(torch, q4, wl, cfg, args.replicas, stacks)
+    layer.inputs(wl, args.id_sets)
+    steps = max(G, (args.steps + G - 1) // G * G)
+    replays = steps // G
+    warm = max(1, (args.warmup + G - 1) // G)
+    log(f"{cfg.name}: capturing {G} layers per graph, {replays} replays timed")
+    g_layer = capture(torch, layer.layer, G)
+    gpu_s, wall_s = time_graph(torch, g_layer, replays, warm)
+    g_gu = capture(torch, layer.gate_up, G)
+    gu_s, _ = time_graph(torch, g_gu, replays, warm)
+    bytes_per_replay = sum(layer.layer_bytes(i) for i in range(G))
+    gu_bytes = sum(layer.gate_up_bytes(i) for i in range(G))
+    us_layer = gpu_s / steps * 1e6
+    gbs = bytes_per_replay * replays / gpu_s / 1e9
+    gu_us = gu_s / steps * 1e6
+    gu_gbs = gu_bytes * replays / gu_s / 1e9
+    res = dict(steps=steps, warmup=warm * G, gpu_s=gpu_s, wall_s=wall_s, us_per_layer=us_layer,
+               gbs=gbs, bytes_per_layer=bytes_per_replay / G, gate_up_us=gu_us,
+               gate_up_gbs=gu_gbs, gate_up_bytes=gu_bytes / G,
+               mean_unique_experts=sum(layer.unique[:G]) / G if G <= len(layer.unique) else None)
+    del g_layer, g_gu
+    return res, layer.stacks
+
+
+def cpu_baseline(wl, cfg, seconds):
+    """The oracle's layer forward (routed FFN, shared expert, combine), one
+    thread, repeated on one id set until `seconds` of work is done."""
+    import numpy as np
+
+    import oracle
+    a = wl.moe_activations(cfg, index=0)
+    H, I, E, K, m = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.m
+    experts = sorted(set(a.ids.tolist()))
+    mb = oracle.q4k_matrix_bytes(I, H)
+    stk = [np.zeros(E * mb, np.uint8) for _ in range(3)]
+    for t, (rows, cols) in enumerate([(I, H), (I, H), (H, I)]):
+        for e in experts:
+            stk[t][e * mb:(e + 1) * mb] = oracle.q4k_quantize(wl.expert_weight(cfg, t, e, rows, cols))
+    sh = [oracle.q4k_quantize(wl.expert_weight(cfg, wl.T_SH_GATE + t, 0, rows, cols))
+          for t, (rows, cols) in enumerate([(I, H), (I, H), (H, I)])]
+    zeros = np.zeros(m, np.int32)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        _, _, _, eo = oracle.moe_expert_ffn(*stk, E, H, I, a.h_post, a.ids, m, K)
+        _, _, _, so = oracle.moe_expert_ffn(*sh, 1, H, I, a.h_post, zeros, m, 1)
+        oracle.moe_combine_residual(a.h_mid, eo, a.route_w, so, a.shared_logit, H, m, K,
+                                    cfg.shared_mode)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 10000:
+            break
+    layer_bytes = (len(experts) + 1) * 3 * mb
+    return dict(value=round(layer_bytes * n / el / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"{n} layer forwards of {cfg.name} (id set 0: {len(experts)} routed + 1 "
+                       f"shared expert, oracle-encoded weights), {el:.1f} s, one thread; "
+                       f"{el / n * 1e6:.0f} us/layer")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024, help="timed layers")
+    ap.add_argument("--warmup", type=int, default=128, help="untimed layers")
+    ap.add_argument("--group", type=int, default=64, help="layers captured per graph")
+    ap.add_argument("--replicas", type=int, default=16, help="weight replicas rotated")
+    ap.add_argument("--id-sets", type=int, default=64, help="routing draws rotated")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-m16", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: every box here has one MI355X and this path has no "
+              f"multi-GPU mode (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_quantized_moe_superblock_amd as q4
+    from bit_quantized_moe_superblock_amd import workloads as wl
+    q4._lib.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    res1, stacks = run_workload(torch, q4, wl, wl.CFG2, args)
+    log(f"m=1: {res1['us_per_layer']:.2f} us/layer, {res1['gbs']:.1f} GB/s; gate/up "
+        f"{res1['gate_up_us']:.2f} us, {res1['gate_up_gbs']:.1f} GB/s")
+    res16 = None
+    if not args.no_m16:
+        res16, _ = run_workload(torch, q4, wl, wl.CFG3, args, stacks)
+        log(f"m=16: {res16['us_per_layer']:.2f} us/layer, {res16['gbs']:.1f} GB/s; gate/up "
+            f"{res16['gate_up_us']:.2f} us, {res16['gate_up_gbs']:.1f} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, wl.CFG2, args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value']} GB/s")
+
+    cfg = wl.CFG2
+    line = {
+        "metric": METRIC,
+        "value": round(res1["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": res1["steps"],
+        "warmup": res1["warmup"],
+        "ms_per_step": round(res1["us_per_layer"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "single-token MoE FFN decode layer: hidden 2048, expert intermediate 768, "
+                        "128 experts, top_k 8, m=1, Q4_K weights N(0,0.02^2), sigmoid-gated "
+                        "shared expert, weighted residual combine",
+            "hidden": cfg.hidden, "inter": cfg.inter, "experts": cfg.num_experts,
+            "top_k": cfg.top_k, "m": cfg.m, "weight_replicas": args.replicas,
+            "id_sets": args.id_sets, "layers_per_graph": args.group,
+            "bytes_per_layer": int(res1["bytes_per_layer"]),
+        },
+        "us_per_layer": round(res1["us_per_layer"], 3),
+        "frac_hbm_peak": round(res1["gbs"] / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "fused gate/up id-GEMV + SiLU (routed + shared experts)",
+            "achieved": round(res1["gate_up_gbs"], 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(res1["gate_up_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "us_per_launch": round(res1["gate_up_us"], 3),
+            "bytes_per_launch": int(res1["gate_up_bytes"]),
+        },
+        "cpu_baseline": cpu,
+    }
+    if res16 is not None:
+        line["m16"] = {
+            "workload": "same layer, m=16 tokens, Zipf(1.1) routing, bucketed",
+            "value": round(res16["gbs"], 2), "unit": "GB/s",
+            "us_per_layer": round(res16["us_per_layer"], 3),
+            "frac_hbm_peak": round(res16["gbs"] / HBM_PEAK_GBS, 4),
+            "bytes_per_layer": int(res16["bytes_per_layer"]),
+            "gate_up_gbs": round(res16["gate_up_gbs"], 2),
+            "gate_up_us": round(res16["gate_up_us"], 3),
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -33,9 +33,12 @@ SIGNATURES = {
     "q4k_moe_id_gemv": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _I, _P,
                              _I64, _P]),
     "q4k_moe_gate_up_silu": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
-                                  _I, _P, _I64, _P]),
+                                  _P, _P, _P, _I, _P, _I64, _P]),
     "moe_expert_ffn": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P,
                             _I64, _P]),
+    "moe_layer_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64]),
+    "moe_layer_forward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64,
+                               _I64, _I64, _I, _I, _P, _I64, _P]),
     "moe_combine_residual": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
     "q4tp_tensor_bytes": (_I64, [_I64, _I64]),
     "q4tp_matvec": (_I, [_P, _P, _P, _I64, _I64, _P]),
@@ -140,11 +143,12 @@ def q4k_moe_id_gemv(w_stacked, src1, ids, dst, n: int, k: int, m: int, top_k: in
 
 def q4k_moe_gate_up_silu(w_gate, w_up, src1, ids, out, n: int, k: int, m: int, top_k: int,
                          src1_outer_stride: int, src1_inner_stride: int, num_experts: int,
+                         sh_gate=None, sh_up=None, sh_out=None,
                          bucket_flag: int = Q4K_BUCKET_AUTO, ws=None, ws_bytes: int = 0,
                          stream=None):
     _call("q4k_moe_gate_up_silu", _ptr(w_gate), _ptr(w_up), _ptr(src1), _ptr(ids), _ptr(out), n,
-          k, m, top_k, src1_outer_stride, src1_inner_stride, num_experts, bucket_flag, _ptr(ws),
-          ws_bytes, _stream(stream))
+          k, m, top_k, src1_outer_stride, src1_inner_stride, num_experts, _ptr(sh_gate),
+          _ptr(sh_up), _ptr(sh_out), bucket_flag, _ptr(ws), ws_bytes, _stream(stream))
 
 
 def moe_expert_ffn(w_gate, w_up, w_down, h_post, ids, act, expert_out, hidden: int, inter: int,
@@ -153,6 +157,21 @@ def moe_expert_ffn(w_gate, w_up, w_down, h_post, ids, act, expert_out, hidden: i
     _call("moe_expert_ffn", _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(h_post), _ptr(ids),
           _ptr(act), _ptr(expert_out), hidden, inter, num_experts, m, top_k, bucket_flag,
           _ptr(ws), ws_bytes, _stream(stream))
+
+
+def moe_layer_workspace_bytes(hidden: int, inter: int, num_experts: int, m: int,
+                              top_k: int) -> int:
+    return load().moe_layer_workspace_bytes(hidden, inter, num_experts, m, top_k)
+
+
+def moe_layer_forward(w_gate, w_up, w_down, sh_gate, sh_up, sh_down, h_post, h_mid, ids, route_w,
+                      shared_gate_logit, out, hidden: int, inter: int, num_experts: int, m: int,
+                      top_k: int, shared_mode: int, bucket_flag: int = Q4K_BUCKET_AUTO, ws=None,
+                      ws_bytes: int = 0, stream=None):
+    _call("moe_layer_forward", _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(sh_gate),
+          _ptr(sh_up), _ptr(sh_down), _ptr(h_post), _ptr(h_mid), _ptr(ids), _ptr(route_w),
+          _ptr(shared_gate_logit), _ptr(out), hidden, inter, num_experts, m, top_k, shared_mode,
+          bucket_flag, _ptr(ws), ws_bytes, _stream(stream))
 
 
 def moe_combine_residual(h_mid, expert_out, route_w, shared_out, shared_gate_logit, out,

@@ -4,7 +4,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
-#include "../../include/q4kmoe.h"
+#include "q4kmoe.h"
 #include "launch.hpp"
 
 using namespace q4k;
@@ -118,6 +118,7 @@ namespace {
 int id_gemv_entry(const void *w0, const void *w1, const float *src1, const int32_t *ids,
                   float *dst, int64_t n, int64_t k, int64_t m, int64_t top_k,
                   int64_t src1_outer_stride, int64_t src1_inner_stride, int64_t num_experts,
+                  const void *s0, const void *s1, float *sh_out,
                   int bucket_flag, void *ws, int64_t ws_bytes, void *stream) {
     const void *w_stacked = w0;
     int rc = check_gemv_shape(n, k, m, top_k, num_experts);
@@ -127,6 +128,10 @@ int id_gemv_entry(const void *w0, const void *w1, const float *src1, const int32
         !aligned4(ids) || !aligned4(dst))
         return Q4K_ERR_NULL;
     if (w1 && !aligned16(w1))
+        return Q4K_ERR_NULL;
+    const bool has_sh = s0 != nullptr;
+    if (has_sh && (!sh_out || !aligned16(s0) || !aligned4(sh_out) || (w1 && !s1) ||
+                   (s1 && !aligned16(s1))))
         return Q4K_ERR_NULL;
     if (src1_outer_stride < 0 || src1_inner_stride < 0)
         return Q4K_ERR_STRIDE;
@@ -155,6 +160,12 @@ int id_gemv_entry(const void *w0, const void *w1, const float *src1, const int32
     L.n_pairs = P;
     L.outer = src1_outer_stride;
     L.inner = src1_inner_stride;
+    L.s0 = s0;
+    L.s1 = has_sh ? s1 : nullptr;
+    L.src1_sh = src1;
+    L.outer_sh = src1_outer_stride;
+    L.dst_sh = sh_out;
+    L.m_sh = has_sh ? m : 0;
     L.fused_swiglu = w1 != nullptr;
     return launched(launch_q4k_gemv(L, st));
 }
@@ -169,18 +180,23 @@ int q4k_moe_id_gemv(const void *w_stacked, const float *src1, const int32_t *ids
                     int64_t num_experts, int bucket_flag, void *ws, int64_t ws_bytes,
                     void *stream) {
     return id_gemv_entry(w_stacked, nullptr, src1, ids, dst, n, k, m, top_k, src1_outer_stride,
-                         src1_inner_stride, num_experts, bucket_flag, ws, ws_bytes, stream);
+                         src1_inner_stride, num_experts, nullptr, nullptr, nullptr, bucket_flag,
+                         ws, ws_bytes, stream);
 }
 
 int q4k_moe_gate_up_silu(const void *w_gate, const void *w_up, const float *src1,
                          const int32_t *ids, float *out, int64_t n, int64_t k, int64_t m,
                          int64_t top_k, int64_t src1_outer_stride, int64_t src1_inner_stride,
-                         int64_t num_experts, int bucket_flag, void *ws, int64_t ws_bytes,
+                         int64_t num_experts, const void *sh_gate, const void *sh_up,
+                         float *sh_out, int bucket_flag, void *ws, int64_t ws_bytes,
                          void *stream) {
     if (!w_up)
         return Q4K_ERR_NULL;
+    if ((sh_gate == nullptr) != (sh_up == nullptr))
+        return Q4K_ERR_NULL;
     return id_gemv_entry(w_gate, w_up, src1, ids, out, n, k, m, top_k, src1_outer_stride,
-                         src1_inner_stride, num_experts, bucket_flag, ws, ws_bytes, stream);
+                         src1_inner_stride, num_experts, sh_gate, sh_up, sh_out, bucket_flag, ws,
+                         ws_bytes, stream);
 }
 
 int moe_expert_ffn(const void *w_gate, const void *w_up, const void *w_down,
@@ -237,6 +253,116 @@ int moe_expert_ffn(const void *w_gate, const void *w_up, const void *w_down,
     D.inner = inter;
     D.fused_swiglu = false;
     return launched(launch_q4k_gemv(D, st));
+}
+
+int64_t moe_layer_workspace_bytes(int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
+                                  int64_t top_k) {
+    if (hidden < 1 || inter < 1 || num_experts < 1 || m < 1 || top_k < 1)
+        return -1;
+    const int64_t P = m * top_k;
+    auto up16 = [](int64_t b) { return (b + 255) / 256 * 256; };
+    // act [P+m, inter] | expert_out [P, hidden] | shared_out [m, hidden] | buckets
+    return up16((P + m) * inter * 4) + up16(P * hidden * 4) + up16(m * hidden * 4) +
+           up16(moe_bucket_workspace_bytes(P, num_experts));
+}
+
+int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
+                      const void *sh_gate, const void *sh_up, const void *sh_down,
+                      const float *h_post, const float *h_mid, const int32_t *ids,
+                      const float *route_w, const float *shared_gate_logit, float *out,
+                      int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
+                      int64_t top_k, int shared_mode, int bucket_flag, void *ws,
+                      int64_t ws_bytes, void *stream) {
+    int rc = check_gemv_shape(inter, hidden, m, top_k, num_experts);
+    if (rc)
+        return rc;
+    rc = check_gemv_shape(hidden, inter, m, top_k, num_experts);
+    if (rc)
+        return rc;
+    if (shared_mode != MOE_SHARED_NONE && shared_mode != MOE_SHARED_SIGMOID &&
+        shared_mode != MOE_SHARED_UNSCALED)
+        return Q4K_ERR_ARG;
+    if (bucket_flag != Q4K_BUCKET_AUTO && bucket_flag != Q4K_BUCKET_OFF &&
+        bucket_flag != Q4K_BUCKET_ON && bucket_flag != Q4K_BUCKET_PREBUILT)
+        return Q4K_ERR_ARG;
+    if (!w_gate || !w_up || !w_down || !h_post || !h_mid || !ids || !route_w || !out ||
+        !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned4(h_post) ||
+        !aligned4(h_mid) || !aligned4(ids) || !aligned4(route_w) || !aligned4(out))
+        return Q4K_ERR_NULL;
+    const bool has_sh = shared_mode != MOE_SHARED_NONE;
+    if (has_sh && (!sh_gate || !sh_up || !sh_down || !aligned16(sh_gate) ||
+                   !aligned16(sh_up) || !aligned16(sh_down)))
+        return Q4K_ERR_NULL;
+    if (shared_mode == MOE_SHARED_SIGMOID && !shared_gate_logit)
+        return Q4K_ERR_NULL;
+    const int64_t P = m * top_k;
+    if (P > Q4K_MAX_PAIRS)
+        return Q4K_ERR_SHAPE;
+    const int64_t need = moe_layer_workspace_bytes(hidden, inter, num_experts, m, top_k);
+    if (!ws || !aligned16(ws) || ws_bytes < need)
+        return Q4K_ERR_WORKSPACE;
+    auto up16 = [](int64_t b) { return (b + 255) / 256 * 256; };
+    char *base = (char *)ws;
+    float *act = (float *)base;
+    float *eo = (float *)(base + up16((P + m) * inter * 4));
+    float *s_out = (float *)((char *)eo + up16(P * hidden * 4));
+    int32_t *bws = (int32_t *)((char *)s_out + up16(m * hidden * 4));
+    const int64_t m_sh = has_sh ? m : 0;
+    const bool bucketed = bucket_flag == Q4K_BUCKET_ON || bucket_flag == Q4K_BUCKET_PREBUILT ||
+                          (bucket_flag == Q4K_BUCKET_AUTO && m > 2);
+    hipStream_t st = as_stream(stream);
+    if (bucketed) {
+        rc = launched(launch_moe_bucket(ids, P, num_experts, bws, st));
+        if (rc)
+            return rc;
+    }
+    GemvLaunch G{};
+    G.w0 = w_gate;
+    G.w1 = w_up;
+    G.s0 = has_sh ? sh_gate : nullptr;
+    G.s1 = has_sh ? sh_up : nullptr;
+    G.src1 = h_post;
+    G.src1_sh = h_post;
+    G.ids = ids;
+    G.bucket_ws = bucketed ? bws : nullptr;
+    G.dst = act;
+    G.dst_sh = act + P * inter;
+    G.n = inter;
+    G.k = hidden;
+    G.top_k = top_k;
+    G.num_experts = num_experts;
+    G.n_pairs = P;
+    G.m_sh = m_sh;
+    G.outer = hidden;
+    G.inner = 0;
+    G.outer_sh = hidden;
+    G.fused_swiglu = true;
+    rc = launched(launch_q4k_gemv(G, st));
+    if (rc)
+        return rc;
+    GemvLaunch D = G;
+    D.w0 = w_down;
+    D.w1 = nullptr;
+    D.s0 = has_sh ? sh_down : nullptr;
+    D.s1 = nullptr;
+    D.src1 = act;
+    D.src1_sh = act + P * inter;
+    D.dst = eo;
+    D.dst_sh = s_out;
+    D.n = hidden;
+    D.k = inter;
+    D.outer = top_k * inter;
+    D.inner = inter;
+    D.outer_sh = inter;
+    D.fused_swiglu = false;
+    if (!bucketed)
+        return launched(launch_q4k_down_combine(D, h_mid, route_w, shared_gate_logit, out,
+                                                nullptr, shared_mode, st));
+    rc = launched(launch_q4k_gemv(D, st));
+    if (rc)
+        return rc;
+    return launched(launch_moe_combine(h_mid, eo, route_w, has_sh ? s_out : nullptr,
+                                       shared_gate_logit, out, hidden, m, top_k, shared_mode, st));
 }
 
 int moe_combine_residual(const float *h_mid, const float *expert_out, const float *route_w,

@@ -17,6 +17,8 @@ namespace q4k {
 constexpr int kBlockWeights = 256;
 constexpr int kBlockBytes = 144;
 constexpr int kThreads = 256;   // threads of every GEMV workgroup (4 waves)
+constexpr int kMaxTopK = 16;    // largest top_k
+constexpr int kBucketChunk = 4; // pairs per bucketed work item
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
@@ -105,14 +107,38 @@ __device__ __forceinline__ float unit_value(const UnitScale &s, const UnitAcc &a
     return pos - neg;
 }
 
-// Sum over groups of LPR consecutive lanes inside a wave (LPR <= 64), xor
-// butterfly in ascending distance; every lane of the group ends with the same
-// bits because fp32 addition is commutative.
+// Cross-lane moves for the row reductions.  DPP quad_perm / row mirrors
+// exchange within 16-lane rows in one v_add_f32_dpp each; rows are then
+// combined through v_readlane (scalar broadcast), not through LDS.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_value(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over groups of W consecutive lanes of a wave (W a power of two <= 64).
+// Within 16 lanes: xor-1, xor-2, half-row mirror, row mirror, each step adding
+// the partner's value, so every lane of a 16-lane row holds the row sum.
+// Wider groups add the 16-lane row sums in row order.  The result is exact
+// for the group's first lane (and for every lane when W <= 16).
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int off = 1; off < W; off <<= 1)
-        v += __shfl_xor(v, off, 64);
+    if constexpr (W >= 2) v += dpp_move<0xB1>(v);    // quad_perm [1,0,3,2]
+    if constexpr (W >= 4) v += dpp_move<0x4E>(v);    // quad_perm [2,3,0,1]
+    if constexpr (W >= 8) v += dpp_move<0x141>(v);   // row_half_mirror
+    if constexpr (W >= 16) v += dpp_move<0x140>(v);  // row_mirror
+    if constexpr (W == 32) {
+        const float r0 = lane_value(v, 0), r1 = lane_value(v, 16);
+        const float r2 = lane_value(v, 32), r3 = lane_value(v, 48);
+        v = (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
+    } else if constexpr (W == 64) {
+        const float r0 = lane_value(v, 0), r1 = lane_value(v, 16);
+        const float r2 = lane_value(v, 32), r3 = lane_value(v, 48);
+        v = (r0 + r1) + (r2 + r3);
+    }
     return v;
 }
 

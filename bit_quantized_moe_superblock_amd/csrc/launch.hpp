@@ -10,16 +10,24 @@ namespace q4k {
 struct GemvLaunch {
     const void *w0;            // stacked experts; the gate stack when fused_swiglu
     const void *w1;            // up stack (fused_swiglu only)
+    const void *s0, *s1;       // shared expert (one-expert stacks) or null
     const float *src1;
+    const float *src1_sh;      // shared activations, token t at src1_sh + t*outer_sh
     const int32_t *ids;
     const int32_t *bucket_ws;  // non-null selects the bucketed mode
     float *dst;
-    int64_t n, k, top_k, num_experts, n_pairs;
-    int64_t outer, inner;
+    float *dst_sh;             // [m_sh, n] shared-expert rows
+    int64_t n, k, top_k, num_experts, n_pairs, m_sh;
+    int64_t outer, inner, outer_sh;
     bool fused_swiglu;
 };
 
 hipError_t launch_q4k_gemv(const GemvLaunch &L, hipStream_t st);
+// Down projection fused with the weighted residual combine, one workgroup row
+// of tiles per token (few tokens).  expert_out may be null.
+hipError_t launch_q4k_down_combine(const GemvLaunch &L, const float *h_mid, const float *route_w,
+                                   const float *shared_logit, float *out, float *expert_out,
+                                   int shared_mode, hipStream_t st);
 hipError_t launch_q4k_dequant(const void *blocks, float *out, int64_t n_blocks, hipStream_t st);
 hipError_t launch_q4k_quant(const float *w, void *blocks, int64_t n_blocks, hipStream_t st);
 hipError_t launch_moe_bucket(const int32_t *ids, int64_t n_pairs, int64_t num_experts,
@@ -35,7 +43,8 @@ hipError_t launch_q4tp_quant(const float *w, void *t, int64_t rows, int64_t cols
 
 // Workspace of the bucketing kernel in int32 words (layout in q4kmoe.h).
 inline int64_t bucket_ws_words(int64_t n_pairs, int64_t num_experts) {
-    return (num_experts + 1) + (num_experts + 2) + n_pairs + (num_experts + 1) + 1;
+    return (num_experts + 1) + (num_experts + 2) + n_pairs + (num_experts + 1) + 1 + 1 +
+           2 * n_pairs;
 }
 
 }  // namespace q4k

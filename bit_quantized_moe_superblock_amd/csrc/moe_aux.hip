@@ -2,7 +2,8 @@
 //
 // Bucketing (moeflux expert_forward.rs, encode_moe_gather_id_fuse step 1 and
 // the ExpertBuckets CSR): one workgroup of 1024 threads counts pairs per
-// expert, scans the counts, lists the non-empty buckets, and orders the pairs
+// expert, scans the counts, lists the non-empty buckets and the work chunks
+// (at most kBucketChunk pairs of one bucket each), and orders the pairs
 // by sorting the unique keys (bucket << 13 | pair) with a bitonic network in
 // LDS, so each bucket lists its pairs in ascending pair order and the result is
 // the same on every run.  Bucket E collects ids outside [0, E).
@@ -22,13 +23,15 @@ __global__ __launch_bounds__(kBucketThreads) void k_moe_bucket(const int32_t *__
                                                                int P, int E, int32_t *ws) {
     __shared__ int cnt[kBucketThreads];
     __shared__ uint32_t keys[kMaxPairsPow2];
-    __shared__ int wsum_c[16], wsum_f[16];
+    __shared__ int wsum_c[16], wsum_f[16], wsum_h[16];
     const int tid = threadIdx.x;
     int32_t *counts = ws;
     int32_t *offsets = counts + (E + 1);
     int32_t *pairs = offsets + (E + 2);
     int32_t *active = pairs + P;
     int32_t *n_active = active + (E + 1);
+    int32_t *n_chunks = n_active + 1;
+    int32_t *chunks = n_chunks + 1;
 
     int N = 1;
     while (N < P)
@@ -48,40 +51,54 @@ __global__ __launch_bounds__(kBucketThreads) void k_moe_bucket(const int32_t *__
     __syncthreads();
 
     // Exclusive scans of the counts and of the non-empty flags over buckets.
+    // Exclusive scans over buckets of the counts, of the non-empty flags and of
+    // the chunk counts (kBucketChunk pairs per chunk).
     const int c = tid <= E ? cnt[tid] : 0;
     const int f = c > 0 ? 1 : 0;
-    int ic = c, iff = f;   // inclusive wave scans
+    const int h = (c + kBucketChunk - 1) / kBucketChunk;
+    int ic = c, iff = f, ih = h;   // inclusive wave scans
     const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const int tc = __shfl_up(ic, off, 64);
         const int tf = __shfl_up(iff, off, 64);
+        const int th = __shfl_up(ih, off, 64);
         if (lane >= off) {
             ic += tc;
             iff += tf;
+            ih += th;
         }
     }
     if (lane == 63) {
         wsum_c[wave] = ic;
         wsum_f[wave] = iff;
+        wsum_h[wave] = ih;
     }
     __syncthreads();
-    int base_c = 0, base_f = 0;
+    int base_c = 0, base_f = 0, base_h = 0;
     for (int w = 0; w < wave; w++) {
         base_c += wsum_c[w];
         base_f += wsum_f[w];
+        base_h += wsum_h[w];
     }
     const int ex_c = base_c + ic - c;
     const int ex_f = base_f + iff - f;
+    const int ex_h = base_h + ih - h;
     if (tid <= E) {
         counts[tid] = c;
         offsets[tid] = ex_c;
         if (f)
             active[ex_f] = tid;
+        for (int i = 0; i < h; i++) {
+            const int n = c - i * kBucketChunk < kBucketChunk ? c - i * kBucketChunk : kBucketChunk;
+            chunks[2 * (ex_h + i)] = tid;
+            chunks[2 * (ex_h + i) + 1] = (ex_c + i * kBucketChunk) | (n << 24);
+        }
     }
     if (tid == E) {
         offsets[E + 1] = ex_c + c;
         *n_active = ex_f + f;
+        *n_chunks = ex_h + h;
     }
 
     // Bitonic sort of the keys (ascending).

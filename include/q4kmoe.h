@@ -61,6 +61,7 @@ enum { MOE_SHARED_NONE = 0, MOE_SHARED_SIGMOID = 1, MOE_SHARED_UNSCALED = 2 };
 #define Q4K_MAX_EXPERTS 1023  /* bucketing keeps E+1 buckets in one block  */
 #define Q4K_MAX_PAIRS 8192    /* m*top_k handled by one bucketing launch   */
 #define Q4TP_MAX_COLS 16384   /* largest Q4TiledP row                       */
+#define Q4K_BUCKET_CHUNK 4    /* pairs per bucketed work item               */
 
 const char *q4k_status_string(int status);
 int q4k_abi_version(void);
@@ -96,10 +97,14 @@ int64_t moe_bucket_workspace_bytes(int64_t n_pairs, int64_t num_experts);
 
 /* Expert bucketing ([MF] encode_moe_gather_id_fuse step 1, map0; and
  * ExpertBuckets, CSR by expert).  Writes into `ws` (int32 words):
- *   counts[E+1] | offsets[E+2] | pairs[P] | active[E+1] | n_active[1]
+ *   counts[E+1] | offsets[E+2] | pairs[P] | active[E+1] | n_active[1] |
+ *   n_chunks[1] | chunks[2*P]
  * where bucket E collects ids outside [0, E), offsets is the exclusive prefix
  * sum of counts, pairs lists pair indices grouped by bucket in ascending order
- * inside a bucket, and active lists the non-empty buckets ascending.
+ * inside a bucket, active lists the non-empty buckets ascending, and chunks
+ * lists the work items of at most Q4K_BUCKET_CHUNK pairs each, buckets
+ * ascending (n_chunks of them), as (bucket, first | count << 24) where first
+ * indexes pairs and count is the item's number of pairs.
  * The layout above is what the bucketed GEMV reads; callers need not read it. */
 int moe_bucket(const int32_t *ids, int64_t n_pairs, int64_t num_experts, void *ws,
                int64_t ws_bytes, void *stream);
@@ -134,11 +139,17 @@ int q4k_moe_id_gemv(const void *w_stacked, const float *src1, const int32_t *ids
  *   out          : [m*top_k, n] fp32, out[p,r] = silu(g)*u with
  *                  g = W_gate[ids[p]][r].x, u = W_up[ids[p]][r].x, x the
  *                  pair's activation row (strides as in q4k_moe_id_gemv).
- *   Same requirements and bucketing as q4k_moe_id_gemv. */
+ *   sh_gate, sh_up, sh_out : optional shared expert ([MF] ExpertPayload
+ *                  shared_out) run in the same launch: one-expert stacks of
+ *                  the same shape and sh_out [m, n] = silu(G.x_t)*(U.x_t)
+ *                  with x_t = src1 + t*src1_outer_stride.  All NULL: none.
+ *   Same requirements and bucketing as q4k_moe_id_gemv (bucketed, the shared
+ *   expert is one more bucket holding every token). */
 int q4k_moe_gate_up_silu(const void *w_gate, const void *w_up, const float *src1,
                          const int32_t *ids, float *out, int64_t n, int64_t k, int64_t m,
                          int64_t top_k, int64_t src1_outer_stride, int64_t src1_inner_stride,
-                         int64_t num_experts, int bucket_flag, void *ws, int64_t ws_bytes,
+                         int64_t num_experts, const void *sh_gate, const void *sh_up,
+                         float *sh_out, int bucket_flag, void *ws, int64_t ws_bytes,
                          void *stream);
 
 /* Expert FFN for all (token, slot) pairs ([MF] module doc: gate and up
@@ -156,6 +167,34 @@ int moe_expert_ffn(const void *w_gate, const void *w_up, const void *w_down,
                    const float *h_post, const int32_t *ids, float *act, float *expert_out,
                    int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
                    int64_t top_k, int bucket_flag, void *ws, int64_t ws_bytes, void *stream);
+
+/* Whole MoE layer for a decode batch: routed experts, optional shared expert
+ * and the weighted residual combine ([MF] gpu_batched_experts_forward and
+ * emit_batched_experts: gate/up, SwiGLU, down for every selected expert and
+ * the shared one, then moe_combine_residual), in the fewest launches:
+ *   few tokens : fused gate/up+SiLU over routed and shared pairs, then the
+ *                down projection fused with the combine (2 launches);
+ *   more tokens: bucketing, bucketed gate/up+SiLU and down (the shared expert
+ *                as one more bucket holding every token), then the combine.
+ *   w_gate, w_up, w_down : routed stacks as in moe_expert_ffn
+ *   sh_gate, sh_up, sh_down : one-expert stacks of the same row shapes, or
+ *                all NULL with shared_mode == MOE_SHARED_NONE
+ *   h_post [m,hidden], h_mid [m,hidden], ids [m*top_k], route_w [m*top_k],
+ *   shared_gate_logit [m] (MOE_SHARED_SIGMOID only), out [m,hidden] fp32.
+ *   ws: scratch of at least moe_layer_workspace_bytes(...) bytes, 16-byte
+ *   aligned; its contents are not meaningful after the call.
+ *   bucket_flag: AUTO picks by m; OFF forces the few-token path; ON (or
+ *   PREBUILT, treated as ON) forces bucketing.  Output bits do not depend on
+ *   the path. */
+int64_t moe_layer_workspace_bytes(int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
+                                  int64_t top_k);
+int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
+                      const void *sh_gate, const void *sh_up, const void *sh_down,
+                      const float *h_post, const float *h_mid, const int32_t *ids,
+                      const float *route_w, const float *shared_gate_logit, float *out,
+                      int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
+                      int64_t top_k, int shared_mode, int bucket_flag, void *ws,
+                      int64_t ws_bytes, void *stream);
 
 /* Weighted combine with residual ([MF] module doc and
  * encode_moe_combine_residual_n_tokens):

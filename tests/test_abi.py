@@ -41,7 +41,8 @@ def test_constants_match_header(lib):
     src = open(HEADER).read()
     for name, val in [("Q4K_BLOCK_WEIGHTS", 256), ("Q4K_BLOCK_BYTES", 144), ("Q4K_MAX_TOP_K", 16),
                       ("Q4K_MAX_IN", _lib.Q4K_MAX_IN), ("Q4K_MAX_EXPERTS", _lib.Q4K_MAX_EXPERTS),
-                      ("Q4K_MAX_PAIRS", _lib.Q4K_MAX_PAIRS), ("Q4TP_MAX_COLS", _lib.Q4TP_MAX_COLS)]:
+                      ("Q4K_MAX_PAIRS", _lib.Q4K_MAX_PAIRS), ("Q4TP_MAX_COLS", _lib.Q4TP_MAX_COLS),
+                      ("Q4K_BUCKET_CHUNK", 4)]:
         assert re.search(rf"#define {name} {val}\b", src), name
     assert q4.q4k_abi_version() == 1
 
@@ -53,7 +54,7 @@ def test_size_helpers(lib):
     assert q4.q4tp_tensor_bytes(1, 4096) == 2132
     assert q4.q4tp_tensor_bytes(1, 14336) == 7452
     assert q4.q4tp_tensor_bytes(3, 33) == -1
-    assert q4.moe_bucket_workspace_bytes(128, 128) == 4 * (129 + 130 + 128 + 129 + 1)
+    assert q4.moe_bucket_workspace_bytes(128, 128) == 4 * (129 + 130 + 128 + 129 + 1 + 1 + 256)
 
 
 def test_status_strings(lib):

@@ -242,9 +242,12 @@ def _bucket_gpu(dev, ids, E):
     counts = w[:E + 1]
     offsets = w[E + 1:2 * E + 3]
     pairs = w[2 * E + 3:2 * E + 3 + P]
-    nact = w[2 * E + 3 + P + E + 1]
-    active = w[2 * E + 3 + P:2 * E + 3 + P + nact]
-    return counts, offsets, pairs, active, nact
+    base = 2 * E + 3 + P
+    nact = w[base + E + 1]
+    active = w[base:base + nact]
+    nch = w[base + E + 2]
+    chunks = w[base + E + 3:base + E + 3 + 2 * nch].reshape(-1, 2)
+    return counts, offsets, pairs, active, nact, chunks
 
 
 @pytest.mark.parametrize("P,E,seed", [(128, 128, 0), (8, 128, 1), (256, 256, 2), (8192, 1023, 3),
@@ -253,16 +256,20 @@ def test_bucket_matches_oracle(dev, P, E, seed):
     say(f"bucket P={P} E={E}")
     g = np.random.default_rng(seed)
     ids = g.integers(-3, E + 3, P).astype(np.int32)
-    c, o, p, act, nact = _bucket_gpu(dev, ids, E)
+    c, o, p, act, nact, chunks = _bucket_gpu(dev, ids, E)
     wc, wo, wp = oracle.moe_bucket(ids, E)
     assert np.array_equal(c, wc) and np.array_equal(o, wo) and np.array_equal(p, wp)
     assert act.tolist() == [b for b in range(E + 1) if wc[b] > 0] and nact == (wc > 0).sum()
+    # work chunks: each non-empty bucket split into pieces of at most 4 pairs
+    want = [(b, (wo[b] + i) | (min(4, wc[b] - i) << 24)) for b in range(E + 1)
+            for i in range(0, wc[b], 4)]
+    assert [tuple(x) for x in chunks.tolist()] == want
 
 
 def test_bucket_zipf_workload(dev):
     cfg = wl.CFG3
     ids = wl.moe_ids(cfg)
-    c, o, p, act, nact = _bucket_gpu(dev, ids, cfg.num_experts)
+    c, o, p, act, nact, _ = _bucket_gpu(dev, ids, cfg.num_experts)
     wc, wo, wp = oracle.moe_bucket(ids, cfg.num_experts)
     assert np.array_equal(p, wp) and np.array_equal(o, wo)
     say(f"  zipf m=16: {nact} distinct experts, largest bucket {wc.max()}")
@@ -432,3 +439,145 @@ def test_q4tp_unit_probe_and_ragged(dev):
         y = torch.empty(rows, device=dev)
         q4.q4tp_matvec(d_t, T(x, dev), y, rows, cols)
         band(sync_np(y), oracle.q4tp_matvec(t, rows, cols, x), f"{rows}x{cols}")
+
+
+# ------------------------------------------------------ whole-layer entry ----
+
+def _layer_gpu(dev, cfg, d_st, sd, a, ids, flag, shared=True):
+    H, I, E, K, m = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.m
+    wsb = q4.moe_layer_workspace_bytes(H, I, E, m, K)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    out = torch.empty(m, H, device=dev)
+    mode = cfg.shared_mode if shared else q4.MOE_SHARED_NONE
+    sh = sd if shared else (None, None, None)
+    q4.moe_layer_forward(*d_st, *sh, T(a.h_post, dev), T(a.h_mid, dev), T(ids, dev),
+                         T(a.route_w, dev), T(a.shared_logit, dev), out, H, I, E, m, K, mode,
+                         flag, ws, wsb)
+    return sync_np(out)
+
+
+def _layer_oracle(cfg, h_st, sh_h, a, ids, shared=True):
+    H, I, E, K, m = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.m
+    _, _, _, eo = oracle.moe_expert_ffn(*h_st, E, H, I, a.h_post, ids, m, K)
+    if not shared:
+        return oracle.moe_combine_residual(a.h_mid, eo, a.route_w, None, None, H, m, K, 0)
+    _, _, _, so = oracle.moe_expert_ffn(*sh_h, 1, H, I, a.h_post, np.zeros(m, np.int32), m, 1)
+    return oracle.moe_combine_residual(a.h_mid, eo, a.route_w, so, a.shared_logit, H, m, K,
+                                       cfg.shared_mode)
+
+
+@pytest.mark.parametrize("cfg", [wl.CFG2, wl.CFG3], ids=lambda c: c.name)
+def test_layer_forward_matches_oracle_and_unfused(dev, cfg):
+    """moe_layer_forward (few-token path and bucketed path) against the
+    oracle, and bit for bit against moe_expert_ffn + shared FFN + combine."""
+    say(f"moe_layer_forward {cfg.name}")
+    H, I, E, K, m = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.m
+    a, ids, d_st, h_st = _ffn_case(cfg, dev)
+    sd, sh = _shared_stacks(cfg, dev)
+    outs = {f: _layer_gpu(dev, cfg, d_st, sd, a, ids, f)
+            for f in (q4.Q4K_BUCKET_AUTO, q4.Q4K_BUCKET_OFF, q4.Q4K_BUCKET_ON)}
+    want = _layer_oracle(cfg, h_st, sh, a, ids)
+    r = band(outs[q4.Q4K_BUCKET_AUTO], want, "layer")
+    say(f"  layer rel {r[0]:.3g} cos {r[1]:.9f}")
+    for f in (q4.Q4K_BUCKET_OFF, q4.Q4K_BUCKET_ON):
+        assert np.array_equal(bits(outs[f]), bits(outs[q4.Q4K_BUCKET_AUTO])), f
+    # unfused composition of the same layer
+    d_h = T(a.h_post, dev)
+    act, eo = _run_ffn(dev, d_st, d_h, T(ids, dev), H, I, E, m, K, q4.Q4K_BUCKET_AUTO)
+    s_act, s_out = _run_ffn(dev, sd, d_h, T(np.zeros(m, np.int32), dev), H, I, 1, m, 1,
+                            q4.Q4K_BUCKET_OFF)
+    out = torch.empty(m, H, device=dev)
+    q4.moe_combine_residual(T(a.h_mid, dev), eo, T(a.route_w, dev), s_out, T(a.shared_logit, dev),
+                            out, H, m, K, cfg.shared_mode)
+    assert np.array_equal(bits(sync_np(out)), bits(outs[q4.Q4K_BUCKET_AUTO]))
+    # without a shared expert
+    o2 = _layer_gpu(dev, cfg, d_st, sd, a, ids, q4.Q4K_BUCKET_AUTO, shared=False)
+    band(o2, _layer_oracle(cfg, h_st, sh, a, ids, shared=False), "layer, no shared")
+
+
+def test_gate_up_with_shared_rides_along(dev):
+    say("gate/up with the shared expert in the same launch")
+    cfg = wl.CFG3
+    H, I, E, K, m = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.m
+    a, ids, d_st, _ = _ffn_case(cfg, dev)
+    sd, _ = _shared_stacks(cfg, dev)
+    d_h, d_ids = T(a.h_post, dev), T(ids, dev)
+    wsb = q4.moe_bucket_workspace_bytes(m * K, E)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    for flag in (q4.Q4K_BUCKET_OFF, q4.Q4K_BUCKET_ON):
+        act = torch.empty(m * K, I, device=dev)
+        sact = torch.empty(m, I, device=dev)
+        q4.q4k_moe_gate_up_silu(d_st[0], d_st[1], d_h, d_ids, act, I, H, m, K, H, 0, E, sd[0],
+                                sd[1], sact, flag, ws, wsb)
+        act_ref = torch.empty(m * K, I, device=dev)
+        q4.q4k_moe_gate_up_silu(d_st[0], d_st[1], d_h, d_ids, act_ref, I, H, m, K, H, 0, E,
+                                bucket_flag=flag, ws=ws, ws_bytes=wsb)
+        sact_ref = torch.empty(m, I, device=dev)
+        q4.q4k_moe_gate_up_silu(sd[0], sd[1], d_h, T(np.zeros(m, np.int32), dev), sact_ref, I, H,
+                                m, 1, H, 0, 1, bucket_flag=q4.Q4K_BUCKET_OFF)
+        assert np.array_equal(bits(sync_np(act)), bits(sync_np(act_ref)))
+        assert np.array_equal(bits(sync_np(sact)), bits(sync_np(sact_ref)))
+
+
+def test_layer_invalid_ids_and_token_mode_edges(dev):
+    """Few-token path with an invalid id (zero contribution), top_k 1 and 16,
+    hidden sizes that are not multiples of the tile."""
+    g = np.random.default_rng(50)
+    for H, I, E, K, m in [(512, 256, 6, 3, 2), (1280, 512, 20, 16, 1), (768, 768, 3, 1, 2)]:
+        say(f"layer edges H={H} I={I} E={E} K={K} m={m}")
+        st = [np.concatenate(quantize_many([(g.standard_normal((r, c)) * 0.05).astype(np.float32)
+                                            for _ in range(E)]))
+              for r, c in [(I, H), (I, H), (H, I)]]
+        sh = [oracle.q4k_quantize((g.standard_normal((r, c)) * 0.05).astype(np.float32))
+              for r, c in [(I, H), (I, H), (H, I)]]
+        h = g.standard_normal((m, H)).astype(np.float32)
+        hm = g.standard_normal((m, H)).astype(np.float32)
+        ids = g.integers(0, E, m * K).astype(np.int32)
+        ids[0] = E + 5
+        rw = g.random(m * K).astype(np.float32)
+        lg = g.standard_normal(m).astype(np.float32)
+        _, _, _, eo = oracle.moe_expert_ffn(*st, E, H, I, h, ids, m, K)
+        _, _, _, so = oracle.moe_expert_ffn(*sh, 1, H, I, h, np.zeros(m, np.int32), m, 1)
+        want = oracle.moe_combine_residual(hm, eo, rw, so, lg, H, m, K, 1)
+        wsb = q4.moe_layer_workspace_bytes(H, I, E, m, K)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        res = []
+        for flag in (q4.Q4K_BUCKET_OFF, q4.Q4K_BUCKET_ON):
+            out = torch.empty(m, H, device=dev)
+            q4.moe_layer_forward(*[T(s, dev) for s in st], *[T(s, dev) for s in sh], T(h, dev),
+                                 T(hm, dev), T(ids, dev), T(rw, dev), T(lg, dev), out, H, I, E, m,
+                                 K, 1, flag, ws, wsb)
+            res.append(sync_np(out))
+        band(res[0], want, "token mode")
+        assert np.array_equal(bits(res[0]), bits(res[1]))
+
+
+@pytest.mark.parametrize("cfg,sample", [(wl.CFG4_M1, None), (wl.CFG4_M32, [0, 13, 31])],
+                         ids=["m1", "m32"])
+def test_large_layer_deepseek_class(dev, cfg, sample):
+    """hidden 7168, inter 2048, 256 experts, unscaled shared expert, at full
+    stack size (6.3 GB of Q4_K).  m=32 runs all tokens on the GPU and checks
+    the sampled tokens, whose experts carry oracle-encoded weights."""
+    say(f"large layer {cfg.name}")
+    H, I, E, K, m = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.m
+    a = wl.moe_activations(cfg)
+    ids = a.ids
+    toks = list(range(m)) if sample is None else sample
+    experts = np.unique(np.concatenate([ids[t * K:(t + 1) * K] for t in toks]))
+    g_d, g_h = touched_stack(cfg, wl.T_GATE, I, H, experts, dev)
+    u_d, u_h = touched_stack(cfg, wl.T_UP, I, H, experts, dev)
+    d_d, d_h = touched_stack(cfg, wl.T_DOWN, H, I, experts, dev)
+    sd, sh = _shared_stacks(cfg, dev)
+    outs = {f: _layer_gpu(dev, cfg, (g_d, u_d, d_d), sd, a, ids, f)
+            for f in (q4.Q4K_BUCKET_AUTO, q4.Q4K_BUCKET_OFF if m <= 2 else q4.Q4K_BUCKET_ON)}
+    vals = list(outs.values())
+    assert np.array_equal(bits(vals[0]), bits(vals[-1]))
+    for t in toks:
+        sub = wl.MoeActivations(a.h_post[t:t + 1], a.h_mid[t:t + 1], ids[t * K:(t + 1) * K],
+                                a.route_w[t * K:(t + 1) * K], a.shared_logit[t:t + 1])
+        c1 = wl.MoeConfig("tok", cfg.cfg_id, H, I, E, K, 1, shared_mode=cfg.shared_mode)
+        want = _layer_oracle(c1, (g_h, u_h, d_h), sh, sub, sub.ids)
+        r = band(vals[0][t:t + 1], want, f"token {t}")
+    say(f"  last token rel {r[0]:.3g} cos {r[1]:.9f}")
+    del g_d, u_d, d_d
+    torch.cuda.empty_cache()
