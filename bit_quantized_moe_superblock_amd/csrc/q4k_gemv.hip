@@ -96,6 +96,17 @@ __device__ __forceinline__ const float *pair_x(const GemvArgs &a, int q) {
     return a.src1_sh + (q - a.n_pairs) * a.outer_sh;
 }
 
+// Same, when the caller knows (uniformly across the workgroup) whether the
+// pair is a shared-expert pair.  A lane-varying choice between the two
+// argument fields compiles into a per-lane load from the argument segment,
+// whose wait would also wait for every weight load in flight.
+__device__ __forceinline__ const float *pair_x_known(const GemvArgs &a, bool shared, int q) {
+    if (shared)
+        return a.src1_sh + (q - a.n_pairs) * a.outer_sh;
+    const int t = q / a.top_k, s = q - t * a.top_k;
+    return a.src1 + t * a.outer + s * a.inner;
+}
+
 // ------------------------------------------------------------ staging ----
 // LDS image of one activation row: xpad_len(k) floats (64 + 4 pad per unit),
 // then k/32 sub-block sums.  Each sub-block of 32 floats is loaded and summed
@@ -114,18 +125,21 @@ __device__ __forceinline__ void stage_issue(XOf x_of, int base, int total, int k
                                             StageBatch &b) {
     const int nsub = k >> 5;
     b.f = base + (int)threadIdx.x;
-    if (b.f < total) {
-        const int row = b.f / nsub, j = b.f - row * nsub;
-        const float *src = x_of(row) + 32 * j;
-        if (vec) {
+    if (total <= 0)
+        return;
+    // Threads past the end re-load the last sub-block (clamped, never
+    // committed) so the loads need no lane-divergent branch.
+    const int f = b.f < total ? b.f : total - 1;
+    const int row = f / nsub, j = f - row * nsub;
+    const float *src = x_of(row) + 32 * j;
+    if (vec) {   // uniform
 #pragma unroll
-            for (int q = 0; q < 8; q++)
-                b.v[q] = *(const float4 *)(src + 4 * q);
-        } else {
+        for (int q = 0; q < 8; q++)
+            b.v[q] = *(const float4 *)(src + 4 * q);
+    } else {
 #pragma unroll
-            for (int q = 0; q < 8; q++)
-                b.v[q] = make_float4(src[4 * q], src[4 * q + 1], src[4 * q + 2], src[4 * q + 3]);
-        }
+        for (int q = 0; q < 8; q++)
+            b.v[q] = make_float4(src[4 * q], src[4 * q + 1], src[4 * q + 2], src[4 * q + 3]);
     }
 }
 
@@ -259,30 +273,38 @@ __device__ __forceinline__ void load_rows(const uint8_t *w0, const uint8_t *w1, 
                                           int row0, bool valid, Tile<NT, ITERS> &t) {
     constexpr int RPI = kThreads / LPR;
     const int tid = threadIdx.x;
-    const int u = tid % LPR;
-    const int rsub = tid / LPR;
     const int nb = k >> 8;
-    const bool active = valid && u < 4 * nb;
+    // Lanes past the row's units and row groups past n load a clamped, valid
+    // address instead of branching: their results never reach a reduction or
+    // a store, and a lane-divergent load makes the compiler wait for it at the
+    // join (register copies out of the loaded registers).
+    const int u0 = tid % LPR;
+    const int u = u0 < 4 * nb ? u0 : 0;
+    const int rsub = tid / LPR;
     const int64_t nb01 = (int64_t)nb * kBlockBytes;
     const int64_t uoff = (int64_t)(u >> 2) * kBlockBytes;
     const int c = u & 3;
+    if (!valid) {   // uniform: nothing to load
 #pragma unroll
-    for (int it = 0; it < ITERS; it++) {
-        const int r = row0 + it * RPI + rsub;
-        const bool ok = active && r < n;
+        for (int it = 0; it < ITERS; it++)
 #pragma unroll
-        for (int nt = 0; nt < NT; nt++) {
-            const uint8_t *w = nt == 0 ? w0 : w1;
-            if (ok) {
-                const uint8_t *rp = w + uoff + (int64_t)r * nb01;
-                t.hdr[nt][it] = *(const uint4 *)rp;
-                t.qa[nt][it] = *(const uint4 *)(rp + 16 + 32 * c);
-                t.qb[nt][it] = *(const uint4 *)(rp + 32 + 32 * c);
-            } else {
+            for (int nt = 0; nt < NT; nt++) {
                 t.hdr[nt][it] = make_uint4(0, 0, 0, 0);
                 t.qa[nt][it] = make_uint4(0, 0, 0, 0);
                 t.qb[nt][it] = make_uint4(0, 0, 0, 0);
             }
+        return;
+    }
+#pragma unroll
+    for (int it = 0; it < ITERS; it++) {
+        const int r0 = row0 + it * RPI + rsub;
+        const int r = r0 < n ? r0 : n - 1;
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++) {
+            const uint8_t *rp = (nt == 0 ? w0 : w1) + uoff + (int64_t)r * nb01;
+            t.hdr[nt][it] = *(const uint4 *)rp;
+            t.qa[nt][it] = *(const uint4 *)(rp + 16 + 32 * c);
+            t.qb[nt][it] = *(const uint4 *)(rp + 32 + 32 * c);
         }
     }
 }
@@ -415,7 +437,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket(GemvArgs a) {
     const int rl = row_lds_floats(a.k);
     float *red = lds + a.pc * rl;
     const int first = cnt < a.pc ? cnt : a.pc;
-    auto xq = [&](int i) { return pair_x(a, pair_of(i)); };
+    auto xq = [&](int i) { return pair_x_known(a, shared, pair_of(i)); };
     const int total = first * (a.k >> 5);
     StageBatch sb;
     stage_issue(xq, 0, total, a.k, a.vec, sb);
@@ -435,7 +457,8 @@ __global__ __launch_bounds__(kThreads) void k_bucket(GemvArgs a) {
         const int cl = cnt - c0 < a.pc ? cnt - c0 : a.pc;
         if (c0 > 0) {
             __syncthreads();   // the previous pass is consumed
-            stage_rows([&](int i) { return pair_x(a, pair_of(c0 + i)); }, cl, a.k, a.vec, lds);
+            stage_rows([&](int i) { return pair_x_known(a, shared, pair_of(c0 + i)); }, cl, a.k,
+                       a.vec, lds);
         }
         __syncthreads();
         for (int i = 0; i < cl; i++) {
@@ -565,13 +588,13 @@ __global__ __launch_bounds__(kThreads) void k_bucket_persist(GemvArgs a, int n_t
         const uint8_t *w1 = shared ? a.s1 : (a.w1 ? a.w1 + (zero ? 0 : (int64_t)bkt * mat) : nullptr);
         load_rows<LPR, NT, ITERS>(w0, w1, a.n, a.k, it.tile * ITERS * RPI, !zero, it.t);
         const int cl = cnt < a.pc ? cnt : a.pc;
-        stage_issue([&](int i) { return pair_x(a, pair_at(shared, first, i)); }, 0,
+        stage_issue([&](int i) { return pair_x_known(a, shared, pair_at(shared, first, i)); }, 0,
                     zero ? 0 : cl * (a.k >> 5), a.k, a.vec, it.xb);
     };
 
-    Item<NT, ITERS> cur, nxt;
-    issue(blockIdx.x, cur);
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    // Two item buffers in ping-pong: the next item loads into the buffer the
+    // current one does not use (copying it over would wait for its loads).
+    auto step = [&](int item, Item<NT, ITERS> &cur, Item<NT, ITERS> &nxt) {
         int bkt, first, cnt;
         bool shared;
         chunk_info(cur.chunk, bkt, first, cnt, shared);
@@ -599,8 +622,9 @@ __global__ __launch_bounds__(kThreads) void k_bucket_persist(GemvArgs a, int n_t
                 const int cl = cnt - c0 < a.pc ? cnt - c0 : a.pc;
                 if (c0 > 0) {
                     __syncthreads();
-                    stage_rows([&](int i) { return pair_x(a, pair_at(shared, first, c0 + i)); },
-                               cl, a.k, a.vec, xs);
+                    stage_rows([&](int i) {
+                        return pair_x_known(a, shared, pair_at(shared, first, c0 + i));
+                    }, cl, a.k, a.vec, xs);
                 }
                 __syncthreads();
                 for (int i = 0; i < cl; i++) {
@@ -654,7 +678,13 @@ __global__ __launch_bounds__(kThreads) void k_bucket_persist(GemvArgs a, int n_t
                 }
             }
         }
-        cur = nxt;
+            };
+    Item<NT, ITERS> A, B;
+    issue(blockIdx.x, A);
+    for (int item = blockIdx.x; item < n_items; item += 2 * gridDim.x) {
+        step(item, A, B);
+        if (item + gridDim.x < n_items)
+            step(item + gridDim.x, B, A);
     }
 }
 
@@ -696,6 +726,8 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineAr
     Tile<1, ITERS> t;
     int sp[ITERS], sr[ITERS];
     bool sok[ITERS];
+    const int ul = active ? u : 0;   // clamped unit (see load_rows)
+    const int cl = ul & 3;
 #pragma unroll
     for (int it = 0; it < ITERS; it++) {
         const int slot = it * RPI + rsub;
@@ -708,32 +740,31 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineAr
 #pragma unroll
             for (int s = 1; s < kMaxTopK; s++)
                 e = sp[it] == s ? ex[s] : e;
-            ok = ok && (unsigned)e < (unsigned)a.num_experts;
-            base = a.w0 + (ok ? (int64_t)e * a.n * nb01 : 0);
+            const bool ev = (unsigned)e < (unsigned)a.num_experts;
+            ok = ok && ev;
+            base = a.w0 + (ev ? (int64_t)e * a.n * nb01 : 0);
         } else {
             base = a.s0;
         }
         sok[it] = ok;
-        if (ok && active) {
-            const uint8_t *rp = base + (int64_t)(u >> 2) * kBlockBytes +
-                                (int64_t)(row0 + sr[it]) * nb01;
-            t.hdr[0][it] = *(const uint4 *)rp;
-            t.qa[0][it] = *(const uint4 *)(rp + 16 + 32 * c);
-            t.qb[0][it] = *(const uint4 *)(rp + 32 + 32 * c);
-        } else {
-            t.hdr[0][it] = make_uint4(0, 0, 0, 0);
-            t.qa[0][it] = make_uint4(0, 0, 0, 0);
-            t.qb[0][it] = make_uint4(0, 0, 0, 0);
-        }
+        const int r0 = row0 + sr[it];
+        const int r = r0 < a.n ? r0 : a.n - 1;
+        const uint8_t *rp = base + (int64_t)(ul >> 2) * kBlockBytes + (int64_t)r * nb01;
+        t.hdr[0][it] = *(const uint4 *)rp;
+        t.qa[0][it] = *(const uint4 *)(rp + 16 + 32 * cl);
+        t.qb[0][it] = *(const uint4 *)(rp + 32 + 32 * cl);
     }
     // 3. combine inputs of this thread's output row, prefetched
     const int ri = tid;
     const int64_t o = (int64_t)tok * a.n + row0 + ri;
     const bool rowok = ri < trt && row0 + ri < a.n;
     const float hm = rowok ? cb.h_mid[o] : 0.0f;
-    // 4. activation rows of the token's pairs
-    auto qof = [&](int s) { return s < K ? tok * K + s : a.n_pairs + tok; };
-    stage_rows([&](int s) { return pair_x(a, qof(s)); }, np, a.k, a.vec, lds);
+    // 4. activation rows of the token's pairs (routed rows, then the shared
+    //    row); both bases are uniform, lanes pick between the two values
+    const float *xr = a.src1 + tok * a.outer;
+    const float *xsh = a.m_sh > 0 ? a.src1_sh + tok * a.outer_sh : xr;
+    const int64_t inner = a.inner;
+    stage_rows([&](int s) { return s < K ? xr + s * inner : xsh; }, np, a.k, a.vec, lds);
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < ITERS; it++) {
