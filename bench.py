@@ -41,6 +41,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE id-GEMV effective HBM GB/s (% of peak) + µs/MoE layer at M=1,16"
 HBM_PEAK_GBS = 8000.0
+# FETCH_SIZE + WRITE_SIZE of the dominant kernel, scaled by a plain copy
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gate_up_silu_m1_hbm_traffic.md")
 
 
 def log(msg):
@@ -175,30 +177,115 @@ def time_graph(torch, g, replays, warmup):
     return e0.elapsed_time(e1) / 1e3, wall
 
 
+def largest_divisor_at_most(k, cap):
+    for g in range(min(k, cap), 0, -1):
+        if k % g == 0:
+            return g
+    return 1
+
+
+def time_eager(torch, fn, steps, warmup, start=0):
+    """fn(i) launched one by one (no graph), timed with events on the launch
+    stream; used under hardware-counter profiling."""
+    for i in range(warmup):
+        fn(start + i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        fn(start + warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3, time.perf_counter() - t0
+
+
 def run_workload(torch, q4, wl, cfg, args, stacks=None):
-    G = args.group
+    """Times exactly args.steps layers (and, separately, args.steps launches
+    of the layer's first kernel) after args.warmup untimed ones."""
+    steps = args.steps
     layer = Layer(torch, q4, wl, cfg, args.replicas, stacks)
     layer.inputs(wl, args.id_sets)
-    steps = max(G, (args.steps + G - 1) // G * G)
-    replays = steps // G
-    warm = max(1, (args.warmup + G - 1) // G)
-    log(f"{cfg.name}: capturing {G} layers per graph, {replays} replays timed")
-    g_layer = capture(torch, layer.layer, G)
-    gpu_s, wall_s = time_graph(torch, g_layer, replays, warm)
-    g_gu = capture(torch, layer.gate_up, G)
-    gu_s, _ = time_graph(torch, g_gu, replays, warm)
-    bytes_per_replay = sum(layer.layer_bytes(i) for i in range(G))
-    gu_bytes = sum(layer.gate_up_bytes(i) for i in range(G))
-    us_layer = gpu_s / steps * 1e6
-    gbs = bytes_per_replay * replays / gpu_s / 1e9
-    gu_us = gu_s / steps * 1e6
-    gu_gbs = gu_bytes * replays / gu_s / 1e9
-    res = dict(steps=steps, warmup=warm * G, gpu_s=gpu_s, wall_s=wall_s, us_per_layer=us_layer,
-               gbs=gbs, bytes_per_layer=bytes_per_replay / G, gate_up_us=gu_us,
-               gate_up_gbs=gu_gbs, gate_up_bytes=gu_bytes / G,
-               mean_unique_experts=sum(layer.unique[:G]) / G if G <= len(layer.unique) else None)
-    del g_layer, g_gu
+    if args.eager:
+        log(f"{cfg.name}: {steps} eager layers timed")
+        gpu_s, wall_s = time_eager(torch, layer.layer, steps, args.warmup)
+        gu_s, _ = time_eager(torch, layer.gate_up, steps, args.warmup)
+        G, warm = 1, args.warmup
+        idx = range(steps)
+        mode = "eager launches"
+    else:
+        G = largest_divisor_at_most(steps, args.group)
+        replays = steps // G
+        warm_replays = max(1, -(-args.warmup // G))
+        warm = warm_replays * G
+        log(f"{cfg.name}: capturing {G} layers per graph, {replays} replays timed")
+        g_layer = capture(torch, layer.layer, G)
+        gpu_s, wall_s = time_graph(torch, g_layer, replays, warm_replays)
+        g_gu = capture(torch, layer.gate_up, G)
+        gu_s, _ = time_graph(torch, g_gu, replays, warm_replays)
+        del g_layer, g_gu
+        idx = [i % G for i in range(steps)]
+        mode = f"HIP graphs of {G} layers"
+    total_bytes = sum(layer.layer_bytes(i) for i in idx)
+    gu_bytes = sum(layer.gate_up_bytes(i) for i in idx)
+    res = dict(steps=steps, warmup=warm, gpu_s=gpu_s, wall_s=wall_s, mode=mode, group=G,
+               us_per_layer=gpu_s / steps * 1e6, gbs=total_bytes / gpu_s / 1e9,
+               bytes_per_layer=total_bytes / steps, gate_up_us=gu_s / steps * 1e6,
+               gate_up_gbs=gu_bytes / gu_s / 1e9, gate_up_bytes=gu_bytes / steps)
     return res, layer.stacks
+
+
+def copy_calibration(torch, mib):
+    """A plain device-to-device copy of a known size, the yardstick that the
+    FETCH_SIZE / WRITE_SIZE counters are scaled by."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 10}), flush=True)
+
+
+def source_digest(files):
+    """sha256 over the named kernel sources (paths relative to the repository
+    root): a stored counter figure is reported only while the code it was
+    taken from is unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in files:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(path):
+    """HBM bytes per launch of the dominant kernel from a profile summary
+    (lines `traffic_bytes_per_launch: N`, `source_files: F...` and
+    `source_sha256: H`), or None when the summary is absent or was taken on
+    other kernel sources."""
+    try:
+        with open(path) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = {}
+    for ln in text.splitlines():
+        if ":" in ln:
+            k, v = ln.split(":", 1)
+            fields[k.strip().strip("-* `")] = v.strip().strip("`")
+    files = fields.get("source_files", "").split()
+    try:
+        if not files or fields.get("source_sha256") != source_digest(files):
+            return None
+    except OSError:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(wl, cfg, seconds):
@@ -241,7 +328,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1024, help="timed layers")
     ap.add_argument("--warmup", type=int, default=128, help="untimed layers")
-    ap.add_argument("--group", type=int, default=64, help="layers captured per graph")
+    ap.add_argument("--group", type=int, default=64,
+                    help="layers captured per graph (a divisor of --steps)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every kernel directly instead of through graphs")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter yardstick)")
     ap.add_argument("--replicas", type=int, default=16, help="weight replicas rotated")
     ap.add_argument("--id-sets", type=int, default=64, help="routing draws rotated")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -259,6 +351,9 @@ def main():
     from bit_quantized_moe_superblock_amd import workloads as wl
     q4._lib.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        copy_calibration(torch, args.calibrate_copy)
+        return
 
     res1, stacks = run_workload(torch, q4, wl, wl.CFG2, args)
     log(f"m=1: {res1['us_per_layer']:.2f} us/layer, {res1['gbs']:.1f} GB/s; gate/up "
@@ -293,7 +388,7 @@ def main():
                         "shared expert, weighted residual combine",
             "hidden": cfg.hidden, "inter": cfg.inter, "experts": cfg.num_experts,
             "top_k": cfg.top_k, "m": cfg.m, "weight_replicas": args.replicas,
-            "id_sets": args.id_sets, "layers_per_graph": args.group,
+            "id_sets": args.id_sets, "launch": res1["mode"],
             "bytes_per_layer": int(res1["bytes_per_layer"]),
         },
         "us_per_layer": round(res1["us_per_layer"], 3),
@@ -305,7 +400,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(res1["gate_up_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": stored_traffic(TRAFFIC_PROFILE),
             "us_per_launch": round(res1["gate_up_us"], 3),
             "bytes_per_launch": int(res1["gate_up_bytes"]),
         },

@@ -829,6 +829,22 @@ static int pick_iters(int64_t pairs, int n, int rpi) {
     return 1;
 }
 
+// Compute units of the current device (256 on MI355X), cached per device.
+static int cu_count() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n < 1)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 static size_t set_lds(const void *kern, size_t bytes) {
     if (bytes > 65536)
         hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
@@ -857,8 +873,15 @@ static hipError_t launch_lpr(GemvArgs a, bool bucketed, hipStream_t st) {
         const size_t lds = set_lds((const void *)kern,
                                    ((size_t)3 * a.n_pairs + (size_t)a.pc * rl + 8) * sizeof(float));
         const int n_tiles = (a.n + IT * RPI - 1) / (IT * RPI);
+        // every workgroup of a persistent grid must be resident at once
+        int fit = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, (const void *)kern, kThreads,
+                                                         lds) != hipSuccess || fit < 1)
+            fit = 1;
         static const int per_cu = env_int("Q4KMOE_PERSIST_WG", 2);
-        hipLaunchKernelGGL(kern, dim3(256 * per_cu), dim3(kThreads), lds, st, a, n_tiles);
+        const int wg = per_cu < fit ? per_cu : fit;
+        hipLaunchKernelGGL(kern, dim3(cu_count() * (wg < 1 ? 1 : wg)), dim3(kThreads), lds, st,
+                           a, n_tiles);
         return hipGetLastError();
     }
     if (bucketed) {
