@@ -96,7 +96,7 @@ class Layer:
         self.s_out = torch.empty(m, H, device=dev)
         self.out = torch.empty(m, H, device=dev)
         self.lwsb = self.q4.moe_layer_workspace_bytes(H, I, cfg.num_experts, m, K)
-        self.lws = torch.empty(self.lwsb, dtype=torch.uint8, device=dev)
+        self.lws = torch.zeros(self.lwsb, dtype=torch.uint8, device=dev)   # barrier words zero
         self.wsb = self.q4.moe_bucket_workspace_bytes(P, cfg.num_experts)
         # one bucket workspace per id set, filled here, so a graph of gate/up
         # launches alone still reads the buckets of its own routing

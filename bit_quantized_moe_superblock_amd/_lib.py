@@ -37,6 +37,7 @@ SIGNATURES = {
     "moe_expert_ffn": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P,
                             _I64, _P]),
     "moe_layer_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64]),
+    "moe_layer_workspace_init": (_I, [_P, _I64, _P]),
     "moe_layer_forward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64,
                                _I64, _I64, _I, _I, _P, _I64, _P]),
     "moe_combine_residual": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
@@ -162,6 +163,10 @@ def moe_expert_ffn(w_gate, w_up, w_down, h_post, ids, act, expert_out, hidden: i
 def moe_layer_workspace_bytes(hidden: int, inter: int, num_experts: int, m: int,
                               top_k: int) -> int:
     return load().moe_layer_workspace_bytes(hidden, inter, num_experts, m, top_k)
+
+
+def moe_layer_workspace_init(ws, ws_bytes: int, stream=None):
+    _call("moe_layer_workspace_init", _ptr(ws), ws_bytes, _stream(stream))
 
 
 def moe_layer_forward(w_gate, w_up, w_down, sh_gate, sh_up, sh_down, h_post, h_mid, ids, route_w,

@@ -63,7 +63,7 @@ const char *q4k_status_string(int status) {
     }
 }
 
-int q4k_abi_version(void) { return 1; }
+int q4k_abi_version(void) { return 2; }
 
 int64_t q4k_matrix_bytes(int64_t n, int64_t k) {
     if (n < 0 || k <= 0 || k % Q4K_BLOCK_WEIGHTS)
@@ -261,9 +261,17 @@ int64_t moe_layer_workspace_bytes(int64_t hidden, int64_t inter, int64_t num_exp
         return -1;
     const int64_t P = m * top_k;
     auto up16 = [](int64_t b) { return (b + 255) / 256 * 256; };
-    // act [P+m, inter] | expert_out [P, hidden] | shared_out [m, hidden] | buckets
-    return up16((P + m) * inter * 4) + up16(P * hidden * 4) + up16(m * hidden * 4) +
-           up16(moe_bucket_workspace_bytes(P, num_experts));
+    // sync words | act [P+m, inter] | expert_out [P, hidden] | shared_out [m, hidden] | buckets
+    return MOE_LAYER_SYNC_BYTES + up16((P + m) * inter * 4) + up16(P * hidden * 4) +
+           up16(m * hidden * 4) + up16(moe_bucket_workspace_bytes(P, num_experts));
+}
+
+int moe_layer_workspace_init(void *ws, int64_t ws_bytes, void *stream) {
+    if (!ws || !aligned16(ws))
+        return Q4K_ERR_NULL;
+    if (ws_bytes < MOE_LAYER_SYNC_BYTES)
+        return Q4K_ERR_WORKSPACE;
+    return launched(hipMemsetAsync(ws, 0, MOE_LAYER_SYNC_BYTES, as_stream(stream)));
 }
 
 int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
@@ -302,7 +310,8 @@ int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
     if (!ws || !aligned16(ws) || ws_bytes < need)
         return Q4K_ERR_WORKSPACE;
     auto up16 = [](int64_t b) { return (b + 255) / 256 * 256; };
-    char *base = (char *)ws;
+    uint32_t *sync = (uint32_t *)ws;
+    char *base = (char *)ws + MOE_LAYER_SYNC_BYTES;
     float *act = (float *)base;
     float *eo = (float *)(base + up16((P + m) * inter * 4));
     float *s_out = (float *)((char *)eo + up16(P * hidden * 4));
@@ -311,6 +320,34 @@ int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
     const bool bucketed = bucket_flag == Q4K_BUCKET_ON || bucket_flag == Q4K_BUCKET_PREBUILT ||
                           (bucket_flag == Q4K_BUCKET_AUTO && m > 2);
     hipStream_t st = as_stream(stream);
+    // The one-launch single-token layer is opt-in (Q4KMOE_FUSED_LAYER=1): on
+    // MI355X its device-wide barrier and one-workgroup-per-CU phases cost more
+    // than the second launch they save.
+    const char *fused_env = getenv("Q4KMOE_FUSED_LAYER");
+    const bool fused_ok = fused_env != nullptr && atoi(fused_env) != 0;
+    if (m == 1 && !bucketed && fused_ok && layer_m1_supported(hidden, inter, top_k, has_sh)) {
+        LayerLaunch L{};
+        L.w_gate = w_gate;
+        L.w_up = w_up;
+        L.w_down = w_down;
+        L.sh_gate = has_sh ? sh_gate : nullptr;
+        L.sh_up = has_sh ? sh_up : nullptr;
+        L.sh_down = has_sh ? sh_down : nullptr;
+        L.h_post = h_post;
+        L.h_mid = h_mid;
+        L.ids = ids;
+        L.route_w = route_w;
+        L.shared_logit = shared_gate_logit;
+        L.out = out;
+        L.act = act;
+        L.sync = sync;
+        L.hidden = hidden;
+        L.inter = inter;
+        L.num_experts = num_experts;
+        L.top_k = top_k;
+        L.shared_mode = shared_mode;
+        return launched(launch_layer_m1(L, st));
+    }
     if (bucketed) {
         rc = launched(launch_moe_bucket(ids, P, num_experts, bws, st));
         if (rc)
@@ -337,10 +374,18 @@ int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
     G.inner = 0;
     G.outer_sh = hidden;
     G.fused_swiglu = true;
+    if (!bucketed) {   // the down launch reads these next: have them cached
+        G.pf = w_down;
+        G.pf_sh = has_sh ? sh_down : nullptr;
+        G.pf_mat = q4k_matrix_bytes(hidden, inter);
+    }
     rc = launched(launch_q4k_gemv(G, st));
     if (rc)
         return rc;
     GemvLaunch D = G;
+    D.pf = nullptr;
+    D.pf_sh = nullptr;
+    D.pf_mat = 0;
     D.w0 = w_down;
     D.w1 = nullptr;
     D.s0 = has_sh ? sh_down : nullptr;

@@ -48,21 +48,17 @@ struct UnitScale {
     float mA, mB;   // dmin*min of sub-blocks A and B
 };
 
+// Both decodings are computed and one is selected: with a branch on c the
+// compiler sinks the load of the header's last word into the c >= 2 side, and
+// waiting for that late load drains every load still in flight.
 __device__ __forceinline__ UnitScale unit_scale(uint4 h, int c) {
     const uint32_t sh = (c & 1) << 4;   // bytes 2c and 2c+1, modulo 4
     const uint32_t b0 = h.y >> sh, b1 = h.z >> sh, b2 = h.w >> sh;
-    uint32_t scA, scB, mA, mB;
-    if (c >= 2) {
-        scA = (b2 & 15u) | ((b0 >> 2) & 0x30u);
-        scB = ((b2 >> 8) & 15u) | ((b0 >> 10) & 0x30u);
-        mA = ((b2 >> 4) & 15u) | ((b1 >> 2) & 0x30u);
-        mB = ((b2 >> 12) & 15u) | ((b1 >> 10) & 0x30u);
-    } else {
-        scA = b0 & 63u;
-        scB = (b0 >> 8) & 63u;
-        mA = b1 & 63u;
-        mB = (b1 >> 8) & 63u;
-    }
+    const bool hi = c >= 2;
+    const uint32_t scA = hi ? (b2 & 15u) | ((b0 >> 2) & 0x30u) : b0 & 63u;
+    const uint32_t scB = hi ? ((b2 >> 8) & 15u) | ((b0 >> 10) & 0x30u) : (b0 >> 8) & 63u;
+    const uint32_t mA = hi ? ((b2 >> 4) & 15u) | ((b1 >> 2) & 0x30u) : b1 & 63u;
+    const uint32_t mB = hi ? ((b2 >> 12) & 15u) | ((b1 >> 10) & 0x30u) : (b1 >> 8) & 63u;
     const float d = lo_half(h.x), dmin = hi_half(h.x);
     UnitScale s;
     s.kA = d * (float)scA;
@@ -140,6 +136,14 @@ __device__ __forceinline__ float group_sum(float v) {
         v = (r0 + r1) + (r2 + r3);
     }
     return v;
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations have
+// completed, then all waves meet.  __syncthreads() also waits for every
+// global load still in flight (its release fence covers global memory), which
+// would stall a kernel that has issued loads for later work.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {

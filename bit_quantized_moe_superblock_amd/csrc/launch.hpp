@@ -20,6 +20,10 @@ struct GemvLaunch {
     int64_t n, k, top_k, num_experts, n_pairs, m_sh;
     int64_t outer, inner, outer_sh;
     bool fused_swiglu;
+    // Stacks the next launch reads for the same pairs (touched by pair mode
+    // so they are cached), bytes per expert; null for none.
+    const void *pf = nullptr, *pf_sh = nullptr;
+    int64_t pf_mat = 0;
 };
 
 hipError_t launch_q4k_gemv(const GemvLaunch &L, hipStream_t st);
@@ -40,6 +44,22 @@ hipError_t launch_q4tp_matvec(const void *t, const float *x, float *y, int64_t r
                               int64_t cols, hipStream_t st);
 hipError_t launch_q4tp_quant(const float *w, void *t, int64_t rows, int64_t cols,
                              hipStream_t st);
+
+// One whole single-token layer in one launch (q4k_layer.hip).
+struct LayerLaunch {
+    const void *w_gate, *w_up, *w_down;
+    const void *sh_gate, *sh_up, *sh_down;   // null when there is no shared expert
+    const float *h_post, *h_mid;
+    const int32_t *ids;
+    const float *route_w, *shared_logit;
+    float *out;
+    float *act;        // [top_k (+1), inter] scratch
+    uint32_t *sync;    // barrier words (zero before first use, left zero)
+    int64_t hidden, inter, num_experts, top_k;
+    int shared_mode;
+};
+bool layer_m1_supported(int64_t hidden, int64_t inter, int64_t top_k, int has_shared);
+hipError_t launch_layer_m1(const LayerLaunch &L, hipStream_t st);
 
 // Workspace of the bucketing kernel in int32 words (layout in q4kmoe.h).
 inline int64_t bucket_ws_words(int64_t n_pairs, int64_t num_experts) {

@@ -11,7 +11,7 @@
 // An optional shared expert (moeflux: the shared_out term of the combine) runs
 // in the same launch as extra pairs, one per token, on its own one-expert stack.
 //
-// Device layout common to all kernels:
+// Device layout common to all kernels (helpers in gemv_core.hpp):
 //   - 256 threads per workgroup; LPR consecutive lanes cover one weight row,
 //     lane u owning unit u = (superblock u/4, 32-byte nibble chunk u%4), i.e.
 //     64 weights: sub-block 2c in the low nibbles and 2c+1 in the high ones.
@@ -34,309 +34,20 @@
 //             (moeflux moe_combine_residual).
 // Every kernel runs the same per-unit arithmetic in the same order, so pair,
 // bucketed and token modes give identical bits.
-#include "common.hpp"
-#include "launch.hpp"
+#include <stdint.h>
+
+#include "gemv_core.hpp"
 
 namespace q4k {
-
-enum { EPI_STORE = 0, EPI_SWIGLU = 1 };
-
-struct GemvArgs {
-    const uint8_t *w0, *w1;   // routed stacks (w1: the up stack of the fused kernel)
-    const uint8_t *s0, *s1;   // shared one-expert stacks (null when m_sh == 0)
-    const float *src1;        // routed activations
-    const float *src1_sh;     // shared activations: token t at src1_sh + t*outer_sh
-    const int32_t *ids;
-    const int32_t *bucket;    // bucket workspace (bucketed mode)
-    float *dst;               // [n_pairs, n]
-    float *dst_sh;            // [m_sh, n]
-    int64_t outer, inner, outer_sh;
-    int n, k, top_k, num_experts, n_pairs, m_sh;
-    int pc;                   // pairs per LDS chunk (bucketed mode)
-    int vec;                  // activation rows 16-byte aligned (float4 staging)
-};
-
-// Where pair q (q >= n_pairs: shared pair of token q - n_pairs) reads and writes.
-struct PairRef {
-    const uint8_t *w0, *w1;   // expert base of the stacks
-    const float *x;
-    float *out;
-    bool valid;
-};
-
-__device__ __forceinline__ PairRef pair_ref(const GemvArgs &a, int q) {
-    PairRef r;
-    const int64_t nb01 = (int64_t)(a.k >> 8) * kBlockBytes;
-    if (q < a.n_pairs) {
-        const int e = a.ids[q];
-        const int t = q / a.top_k, s = q - t * a.top_k;
-        r.valid = (unsigned)e < (unsigned)a.num_experts;
-        const int64_t off = r.valid ? (int64_t)e * a.n * nb01 : 0;
-        r.w0 = a.w0 + off;
-        r.w1 = a.w1 ? a.w1 + off : nullptr;
-        r.x = a.src1 + t * a.outer + s * a.inner;
-        r.out = a.dst + (int64_t)q * a.n;
-    } else {
-        const int t = q - a.n_pairs;
-        r.valid = true;
-        r.w0 = a.s0;
-        r.w1 = a.s1;
-        r.x = a.src1_sh + t * a.outer_sh;
-        r.out = a.dst_sh + (int64_t)t * a.n;
-    }
-    return r;
-}
-
-// Activation row of pair q (no id lookup needed).
-__device__ __forceinline__ const float *pair_x(const GemvArgs &a, int q) {
-    if (q < a.n_pairs) {
-        const int t = q / a.top_k, s = q - t * a.top_k;
-        return a.src1 + t * a.outer + s * a.inner;
-    }
-    return a.src1_sh + (q - a.n_pairs) * a.outer_sh;
-}
-
-// Same, when the caller knows (uniformly across the workgroup) whether the
-// pair is a shared-expert pair.  A lane-varying choice between the two
-// argument fields compiles into a per-lane load from the argument segment,
-// whose wait would also wait for every weight load in flight.
-__device__ __forceinline__ const float *pair_x_known(const GemvArgs &a, bool shared, int q) {
-    if (shared)
-        return a.src1_sh + (q - a.n_pairs) * a.outer_sh;
-    const int t = q / a.top_k, s = q - t * a.top_k;
-    return a.src1 + t * a.outer + s * a.inner;
-}
-
-// ------------------------------------------------------------ staging ----
-// LDS image of one activation row: xpad_len(k) floats (64 + 4 pad per unit),
-// then k/32 sub-block sums.  Each sub-block of 32 floats is loaded and summed
-// (ascending, one thread) by one thread, which fixes the rounding of the sums.
-__host__ __device__ constexpr int row_lds_floats(int k) { return xpad_len(k) + (k >> 5); }
-
-// One staging batch: thread tid owns flattened sub-block base + tid of the
-// rows being staged (row-major over (row, sub-block)).
-struct StageBatch {
-    float4 v[8];
-    int f;
-};
-
-template <typename XOf>
-__device__ __forceinline__ void stage_issue(XOf x_of, int base, int total, int k, bool vec,
-                                            StageBatch &b) {
-    const int nsub = k >> 5;
-    b.f = base + (int)threadIdx.x;
-    if (total <= 0)
-        return;
-    // Threads past the end re-load the last sub-block (clamped, never
-    // committed) so the loads need no lane-divergent branch.
-    const int f = b.f < total ? b.f : total - 1;
-    const int row = f / nsub, j = f - row * nsub;
-    const float *src = x_of(row) + 32 * j;
-    if (vec) {   // uniform
-#pragma unroll
-        for (int q = 0; q < 8; q++)
-            b.v[q] = *(const float4 *)(src + 4 * q);
-    } else {
-#pragma unroll
-        for (int q = 0; q < 8; q++)
-            b.v[q] = make_float4(src[4 * q], src[4 * q + 1], src[4 * q + 2], src[4 * q + 3]);
-    }
-}
-
-__device__ __forceinline__ void stage_commit(const StageBatch &b, int total, int k, float *lds) {
-    if (b.f < total) {
-        const int nsub = k >> 5;
-        const int row = b.f / nsub, j = b.f - row * nsub;
-        float *dstrow = lds + row * row_lds_floats(k);
-        float4 *d = (float4 *)(dstrow + xpad(32 * j));
-        float s = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 8; q++) {
-            d[q] = b.v[q];
-            s += b.v[q].x;
-            s += b.v[q].y;
-            s += b.v[q].z;
-            s += b.v[q].w;
-        }
-        dstrow[xpad_len(k) + j] = s;
-    }
-}
-
-// Stage rows [0, cl) starting at flattened sub-block `from` (batches of 256).
-// No barrier.
-template <typename XOf>
-__device__ __forceinline__ void stage_rows(XOf x_of, int cl, int k, bool vec, float *lds,
-                                           int from = 0) {
-    const int total = cl * (k >> 5);
-    for (int base = from; base < total; base += kThreads) {
-        StageBatch b;
-        stage_issue(x_of, base, total, k, vec, b);
-        stage_commit(b, total, k, lds);
-    }
-}
-
-// ------------------------------------------------------- unit arithmetic ----
-
-// Masked nibbles of one 32-byte chunk: for each of its 8 dwords, the four
-// fp16-subnormal pairs (low nibbles of bytes 0,2 and 1,3; high nibbles of the
-// same).
-struct Masks {
-    uint32_t m[8][4];
-};
-
-__device__ __forceinline__ void make_masks(const uint4 &qa, const uint4 &qb, Masks &k) {
-    const uint32_t w[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-#pragma unroll
-    for (int d = 0; d < 8; d++) {
-        const uint32_t v = w[d], s = v >> 8;
-        k.m[d][0] = v & 0x000F000Fu;
-        k.m[d][1] = s & 0x000F000Fu;
-        k.m[d][2] = v & 0x00F000F0u;
-        k.m[d][3] = s & 0x00F000F0u;
-    }
-}
-
-// Accumulate one 8-weight step d of a unit (see nib_fma in common.hpp for the
-// element order) from precomputed masks.
-__device__ __forceinline__ void masked_fma(const uint32_t (&r)[4], float4 xa, float4 xb,
-                                           UnitAcc &acc) {
-    acc.a = __builtin_fmaf(lo_half(r[0]), xa.x, acc.a);
-    acc.a = __builtin_fmaf(lo_half(r[1]), xa.y, acc.a);
-    acc.a = __builtin_fmaf(hi_half(r[0]), xa.z, acc.a);
-    acc.a = __builtin_fmaf(hi_half(r[1]), xa.w, acc.a);
-    acc.b = __builtin_fmaf(lo_half(r[2]), xb.x, acc.b);
-    acc.b = __builtin_fmaf(lo_half(r[3]), xb.y, acc.b);
-    acc.b = __builtin_fmaf(hi_half(r[2]), xb.z, acc.b);
-    acc.b = __builtin_fmaf(hi_half(r[3]), xb.w, acc.b);
-}
-
-// Reduce a per-lane unit value over the LPR lanes of its row.  For rows wider
-// than a wave the wave sums go through `red` (2 barriers); `slot_lane0` is true
-// on the lane that receives the row total.
-template <int LPR>
-__device__ __forceinline__ float row_reduce(float v, float *red, int nt_index) {
-    constexpr int WL = LPR < 64 ? LPR : 64;
-    constexpr int WPR = LPR / WL;
-    v = group_sum<WL>(v);
-    if constexpr (WPR > 1) {
-        const int tid = threadIdx.x;
-        const int wave = tid >> 6;
-        if ((tid & 63) == 0)
-            red[nt_index * 4 + wave] = v;
-        __syncthreads();
-        if ((tid % LPR) == 0) {
-            float s = red[nt_index * 4 + wave];
-            for (int w = 1; w < WPR; w++)
-                s += red[nt_index * 4 + wave + w];
-            v = s;
-        }
-        __syncthreads();
-    }
-    return v;
-}
-
-template <int EPI, int NT>
-__device__ __forceinline__ float epilogue(const float (&part)[NT]) {
-    if constexpr (EPI == EPI_SWIGLU)
-        return silu_mul(part[0], part[NT - 1]);
-    else
-        return part[0];
-}
-
-// Row tile of one lane: ITERS row groups, NT tensors.
-template <int NT, int ITERS>
-struct Tile {
-    uint4 hdr[NT][ITERS];
-    uint4 qa[NT][ITERS];
-    uint4 qb[NT][ITERS];
-};
-
-// Hide a tile's registers from loop-invariant code motion.  Without this the
-// compiler hoists the masked and fp32-converted weights out of a per-pair loop
-// into (accumulation) registers, which costs a register read plus an fma per
-// weight and pair instead of one v_fma_mix_f32 that decodes as it multiplies.
-template <int NT, int ITERS>
-__device__ __forceinline__ void opaque(Tile<NT, ITERS> &t) {
-#pragma unroll
-    for (int nt = 0; nt < NT; nt++)
-#pragma unroll
-        for (int it = 0; it < ITERS; it++) {
-            asm volatile("" : "+v"(t.qa[nt][it].x), "+v"(t.qa[nt][it].y), "+v"(t.qa[nt][it].z),
-                         "+v"(t.qa[nt][it].w));
-            asm volatile("" : "+v"(t.qb[nt][it].x), "+v"(t.qb[nt][it].y), "+v"(t.qb[nt][it].z),
-                         "+v"(t.qb[nt][it].w));
-        }
-}
-
-template <int LPR, int NT, int ITERS>
-__device__ __forceinline__ void load_rows(const uint8_t *w0, const uint8_t *w1, int n, int k,
-                                          int row0, bool valid, Tile<NT, ITERS> &t) {
-    constexpr int RPI = kThreads / LPR;
-    const int tid = threadIdx.x;
-    const int nb = k >> 8;
-    // Lanes past the row's units and row groups past n load a clamped, valid
-    // address instead of branching: their results never reach a reduction or
-    // a store, and a lane-divergent load makes the compiler wait for it at the
-    // join (register copies out of the loaded registers).
-    const int u0 = tid % LPR;
-    const int u = u0 < 4 * nb ? u0 : 0;
-    const int rsub = tid / LPR;
-    const int64_t nb01 = (int64_t)nb * kBlockBytes;
-    const int64_t uoff = (int64_t)(u >> 2) * kBlockBytes;
-    const int c = u & 3;
-    if (!valid) {   // uniform: nothing to load
-#pragma unroll
-        for (int it = 0; it < ITERS; it++)
-#pragma unroll
-            for (int nt = 0; nt < NT; nt++) {
-                t.hdr[nt][it] = make_uint4(0, 0, 0, 0);
-                t.qa[nt][it] = make_uint4(0, 0, 0, 0);
-                t.qb[nt][it] = make_uint4(0, 0, 0, 0);
-            }
-        return;
-    }
-#pragma unroll
-    for (int it = 0; it < ITERS; it++) {
-        const int r0 = row0 + it * RPI + rsub;
-        const int r = r0 < n ? r0 : n - 1;
-#pragma unroll
-        for (int nt = 0; nt < NT; nt++) {
-            const uint8_t *rp = (nt == 0 ? w0 : w1) + uoff + (int64_t)r * nb01;
-            t.hdr[nt][it] = *(const uint4 *)rp;
-            t.qa[nt][it] = *(const uint4 *)(rp + 16 + 32 * c);
-            t.qb[nt][it] = *(const uint4 *)(rp + 32 + 32 * c);
-        }
-    }
-}
-
-// Unit value of tensor (nt, it) of the tile against the staged row at xrow.
-template <int NT, int ITERS>
-__device__ __forceinline__ float unit_from_tile(const Tile<NT, ITERS> &t, int nt, int it,
-                                                const float *xrow, int u, int c, int k) {
-    const float *xl = xrow + 68 * u;   // xpad(64u)
-    const float4 *xa = (const float4 *)xl;
-    const float4 *xb = (const float4 *)(xl + 32);
-    UnitAcc acc{0.0f, 0.0f};
-    const uint32_t w[8] = {t.qa[nt][it].x, t.qa[nt][it].y, t.qa[nt][it].z, t.qa[nt][it].w,
-                           t.qb[nt][it].x, t.qb[nt][it].y, t.qb[nt][it].z, t.qb[nt][it].w};
-#pragma unroll
-    for (int d = 0; d < 8; d++) {
-        const uint32_t v = w[d], s = v >> 8;
-        const uint32_t r[4] = {v & 0x000F000Fu, s & 0x000F000Fu, v & 0x00F000F0u,
-                               s & 0x00F000F0u};
-        masked_fma(r, xa[d], xb[d], acc);
-    }
-    const float *sx = xrow + xpad_len(k);
-    return unit_value(unit_scale(t.hdr[nt][it], c), acc, sx[2 * u], sx[2 * u + 1]);
-}
 
 // ------------------------------------------------------------ pair mode ----
 
 template <int LPR, int NT, int ITERS, int EPI>
 __global__ __launch_bounds__(kThreads) void k_rows(GemvArgs a) {
     extern __shared__ float lds[];
+    fetch_args(a);
     constexpr int RPI = kThreads / LPR;
-    float *red = lds + row_lds_floats(a.k);
+    float *red = lds;   // cross-wave row sums (rows wider than a wave)
     const int q = blockIdx.y;
     const int row0 = blockIdx.x * (ITERS * RPI);
     const PairRef pr = pair_ref(a, q);
@@ -347,30 +58,52 @@ __global__ __launch_bounds__(kThreads) void k_rows(GemvArgs a) {
                 pr.out[row0 + i] = 0.0f;
         return;
     }
-    Tile<NT, ITERS> t;
-    // Activation loads first, then the weights, then the LDS writes: the
-    // weight loads are in flight while the activations are committed.
-    const int total = a.k >> 5;
-    StageBatch sb;
-    stage_issue([&](int) { return pr.x; }, 0, total, a.k, a.vec, sb);
-    load_rows<LPR, NT, ITERS>(pr.w0, pr.w1, a.n, a.k, row0, true, t);
-    stage_commit(sb, total, a.k, lds);
-    stage_rows([&](int) { return pr.x; }, 1, a.k, a.vec, lds, kThreads);
-    __syncthreads();
+    // Each lane reads its unit's 64 activations straight into registers (the
+    // rows of a workgroup share them through the cache), then its weights.
     const int u = tid % LPR, rsub = tid / LPR, c = u & 3;
     const bool active = u < 4 * (a.k >> 8);
+    LaneX lx;
+    lane_x_issue(pr.x, active ? u : 0, a.vec, lx);
+    Tile<NT, ITERS> t;
+    load_rows<LPR, NT, ITERS>(pr.w0, pr.w1, a.n, a.k, row0, true, t);
+    // Touch this workgroup's share of the pair's next-launch stack (8 x 16
+    // bytes per lane, after the weights so those arrive first).  Without a
+    // stack to touch the same loads re-read this pair's first weight bytes,
+    // which keeps the loads unconditional (a branch around loads makes every
+    // later wait drain the whole queue).
+    uint32_t pfx = 0;
+    {
+        const int64_t span = a.pf ? a.pf_mat : 16;
+        const int64_t per_wg = ((span / gridDim.x + 15) >> 4) << 4;
+        const int64_t beg = (int64_t)blockIdx.x * per_wg;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            int64_t off = beg + (int64_t)(j * kThreads + tid) * 16;
+            off = off < beg + per_wg - 16 ? off : beg + per_wg - 16;
+            off = off < span - 16 ? off : span - 16;
+            off = off > 0 ? off : 0;
+            const uint4 v = *(const uint4 *)(pr.pf + off);
+            pfx ^= v.x ^ v.y ^ v.z ^ v.w;
+        }
+    }
+    lane_x_sums(lx);
 #pragma unroll
     for (int it = 0; it < ITERS; it++) {
         float part[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; nt++) {
-            float v = active ? unit_from_tile<NT, ITERS>(t, nt, it, lds, u, c, a.k) : 0.0f;
-            part[nt] = row_reduce<LPR>(v, red, nt);
+            // Computed on every lane (inactive lanes hold a clamped, valid
+            // unit) and then selected: under a branch the compiler sinks part
+            // of the weight loads into it, and their wait drains the queue.
+            const float uv = unit_from_regs<NT, ITERS>(t, nt, it, lx, c);
+            part[nt] = row_reduce<LPR>(active ? uv : 0.0f, red, nt);
         }
         const int r = row0 + it * RPI + rsub;
         if (u == 0 && r < a.n)
             pr.out[r] = epilogue<EPI, NT>(part);
     }
+    if (a.pf_mat < 0)   // never: keeps the touching loads alive
+        pr.out[0] = __builtin_bit_cast(float, pfx);
 }
 
 // -------------------------------------------------------- bucketed mode ----
@@ -397,6 +130,7 @@ struct BucketView {
 template <int LPR, int NT, int ITERS, int EPI>
 __global__ __launch_bounds__(kThreads) void k_bucket(GemvArgs a) {
     extern __shared__ float lds[];
+    fetch_args(a);
     constexpr int RPI = kThreads / LPR;
     const BucketView bv(a.bucket, a.num_experts, a.n_pairs);
     const int y = blockIdx.y;
@@ -531,6 +265,7 @@ struct Item {
 template <int LPR, int NT, int ITERS, int EPI>
 __global__ __launch_bounds__(kThreads) void k_bucket_persist(GemvArgs a, int n_tiles) {
     extern __shared__ float lds[];
+    fetch_args(a);
     constexpr int RPI = kThreads / LPR;
     const int tid = threadIdx.x;
     const int P = a.n_pairs, E = a.num_experts;
@@ -704,6 +439,9 @@ struct CombineArgs {
 template <int LPR, int ITERS>
 __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineArgs cb, int trt) {
     extern __shared__ float lds[];
+    fetch_args(a);
+    asm volatile("" ::"s"(cb.h_mid), "s"(cb.route_w), "s"(cb.shared_logit), "s"(cb.out),
+                 "s"(cb.expert_out), "s"(cb.shared_mode), "s"(trt));
     constexpr int RPI = kThreads / LPR;
     const int tok = blockIdx.y;
     const int K = a.top_k;
@@ -713,12 +451,19 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineAr
     float *red = ybuf + trt * np;
     const int tid = threadIdx.x;
     const int row0 = blockIdx.x * trt;
-    // 1. the token's experts: uniform (scalar) loads, issued first
-    int ex[kMaxTopK];
-#pragma unroll
-    for (int s = 0; s < kMaxTopK; s++)
-        ex[s] = s < K ? a.ids[tok * K + s] : 0;
-    // 2. slot it*RPI + rsub -> (row row0 + slot/np, pair slot%np); weight loads
+    // 1. the token's experts into LDS (-1 for ids outside [0, E)): one load
+    //    per thread, unconditional with a clamped index (a load under a
+    //    divergent branch makes later waits drain the whole queue), the only
+    //    load in flight when it is waited for.  A per-lane select over the
+    //    ids held in registers would become an indexed array in scratch.
+    __shared__ int ex_lds[kMaxTopK];
+    const int e_own = a.ids[tok * K + (tid < K ? tid : K - 1)];
+    if (tid < K)
+        ex_lds[tid] = (unsigned)e_own < (unsigned)a.num_experts ? e_own : -1;
+    lds_barrier();
+    // 2. slot it*RPI + rsub -> (row row0 + slot/np, pair slot%np); weight
+    //    loads, branch-free (clamped addresses; the shared pair selects its
+    //    own stack)
     const int u = tid % LPR, rsub = tid / LPR, c = u & 3;
     const int nb = a.k >> 8;
     const bool active = u < 4 * nb;
@@ -733,20 +478,11 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineAr
         const int slot = it * RPI + rsub;
         sr[it] = slot / np;
         sp[it] = slot - sr[it] * np;
-        bool ok = sr[it] < trt && row0 + sr[it] < a.n;
-        const uint8_t *base;
-        if (sp[it] < K) {
-            int e = ex[0];
-#pragma unroll
-            for (int s = 1; s < kMaxTopK; s++)
-                e = sp[it] == s ? ex[s] : e;
-            const bool ev = (unsigned)e < (unsigned)a.num_experts;
-            ok = ok && ev;
-            base = a.w0 + (ev ? (int64_t)e * a.n * nb01 : 0);
-        } else {
-            base = a.s0;
-        }
-        sok[it] = ok;
+        const bool routed = sp[it] < K;
+        const int e = ex_lds[routed ? sp[it] : 0];
+        sok[it] = sr[it] < trt && row0 + sr[it] < a.n && (!routed || e >= 0);
+        const int64_t eoff = routed && e >= 0 ? (int64_t)e * a.n * nb01 : 0;
+        const uint8_t *base = (routed ? a.w0 : a.s0) + eoff;
         const int r0 = row0 + sr[it];
         const int r = r0 < a.n ? r0 : a.n - 1;
         const uint8_t *rp = base + (int64_t)(ul >> 2) * kBlockBytes + (int64_t)r * nb01;
@@ -769,8 +505,9 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineAr
 #pragma unroll
     for (int it = 0; it < ITERS; it++) {
         const float *xrow = lds + sp[it] * rl;
-        float v = (active && sok[it]) ? unit_from_tile<1, ITERS>(t, 0, it, xrow, u, c, a.k) : 0.0f;
-        v = row_reduce<LPR>(v, red, 0);
+        // computed on every lane, then selected (see k_rows)
+        const float uv = unit_from_tile<1, ITERS>(t, 0, it, xrow, ul, cl, a.k);
+        const float v = row_reduce<LPR>((active && sok[it]) ? uv : 0.0f, red, 0);
         if (u == 0 && sr[it] < trt)
             ybuf[sr[it] * np + sp[it]] = v;
     }
@@ -801,61 +538,37 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineAr
 
 // ------------------------------------------------------------------ host ---
 
-static int lanes_per_row(int k) {
-    const int units = 4 * (k >> 8);
-    int l = 4;
-    while (l < units)
-        l <<= 1;
-    return l;
-}
-
-static int env_int(const char *name, int dflt) {
-    const char *s = getenv(name);
-    return s ? atoi(s) : dflt;
-}
-
 // Row groups per workgroup in pair mode: as tall as possible while the grid
 // still gives every CU a workgroup (256 CUs on MI355X).
-static int pick_iters(int64_t pairs, int n, int rpi) {
+static int pick_iters(int64_t pairs, int n, int rpi, int max_it) {
     static const int forced = env_int("Q4KMOE_ITERS", 0);
     if (forced == 1 || forced == 2 || forced == 3 || forced == 4 || forced == 6 || forced == 8)
         return forced;
-    const int cand[] = {8, 6, 4, 3, 2};
+    // Smallest (waves of workgroups over the CUs) x (row groups per
+    // workgroup), ties to the taller tile: a grid just past a multiple of the
+    // CU count leaves some CUs with twice the work of the rest.
+    const int64_t cus = cu_count();
+    const int cand[] = {1, 2, 3, 4, 6, 8};
+    int best = 1;
+    int64_t best_cost = INT64_MAX;
     for (int it : cand) {
+        if (it > max_it)
+            break;
         const int64_t tiles = (n + it * rpi - 1) / (it * rpi);
-        if (tiles * pairs >= 256)
-            return it;
+        const int64_t cost = (tiles * pairs + cus - 1) / cus * it;
+        if (cost <= best_cost) {
+            best = it;
+            best_cost = cost;
+        }
     }
-    return 1;
-}
-
-// Compute units of the current device (256 on MI355X), cached per device.
-static int cu_count() {
-    static int cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n < 1)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
-static size_t set_lds(const void *kern, size_t bytes) {
-    if (bytes > 65536)
-        hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    return bytes;
+    return best;
 }
 
 template <int LPR, int NT, int EPI, int IT>
 static hipError_t go_rows(const GemvArgs &a, hipStream_t st) {
     constexpr int RPI = kThreads / LPR;
     auto kern = k_rows<LPR, NT, IT, EPI>;
-    const size_t lds = set_lds((const void *)kern, (row_lds_floats(a.k) + 8) * sizeof(float));
+    const size_t lds = 8 * sizeof(float);
     dim3 grid((a.n + IT * RPI - 1) / (IT * RPI), a.n_pairs + a.m_sh);
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a);
     return hipGetLastError();
@@ -898,9 +611,7 @@ static hipError_t launch_lpr(GemvArgs a, bool bucketed, hipStream_t st) {
         hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a);
         return hipGetLastError();
     }
-    int it = pick_iters(a.n_pairs + a.m_sh, a.n, RPI);
-    if (NT == 2 && it > 4)
-        it = 4;
+    const int it = pick_iters(a.n_pairs + a.m_sh, a.n, RPI, NT == 2 ? 4 : 8);
     switch (it) {
     case 8: return go_rows<LPR, NT, EPI, (NT == 2 ? 4 : 8)>(a, st);
     case 6: return go_rows<LPR, NT, EPI, (NT == 2 ? 4 : 6)>(a, st);
@@ -950,6 +661,9 @@ static GemvArgs make_args(const GemvLaunch &L) {
     a.m_sh = (int)L.m_sh;
     a.vec = al16(L.src1) && L.outer % 4 == 0 && L.inner % 4 == 0 &&
             (L.m_sh == 0 || (al16(L.src1_sh) && L.outer_sh % 4 == 0));
+    a.pf = (const uint8_t *)L.pf;
+    a.pf_sh = (const uint8_t *)L.pf_sh;
+    a.pf_mat = L.pf ? L.pf_mat : 0;
     return a;
 }
 

@@ -62,6 +62,8 @@ enum { MOE_SHARED_NONE = 0, MOE_SHARED_SIGMOID = 1, MOE_SHARED_UNSCALED = 2 };
 #define Q4K_MAX_PAIRS 8192    /* m*top_k handled by one bucketing launch   */
 #define Q4TP_MAX_COLS 16384   /* largest Q4TiledP row                       */
 #define Q4K_BUCKET_CHUNK 4    /* pairs per bucketed work item               */
+#define MOE_LAYER_SYNC_BYTES 4096 /* synchronisation header of a layer workspace */
+#define MOE_LAYER_SYNC_TIMEOUT_WORD 576 /* 32-bit word of that header: barrier timed out */
 
 const char *q4k_status_string(int status);
 int q4k_abi_version(void);
@@ -172,6 +174,10 @@ int moe_expert_ffn(const void *w_gate, const void *w_up, const void *w_down,
  * and the weighted residual combine ([MF] gpu_batched_experts_forward and
  * emit_batched_experts: gate/up, SwiGLU, down for every selected expert and
  * the shared one, then moe_combine_residual), in the fewest launches:
+ *   one token  : the whole layer in one launch (gate/up+SiLU, a device-wide
+ *                barrier, down fused with the combine), for the shapes this
+ *                kernel tiles (hidden 1024..4096 and inter up to 2048 at
+ *                top_k <= 16 on a 256-CU device); otherwise as few tokens;
  *   few tokens : fused gate/up+SiLU over routed and shared pairs, then the
  *                down projection fused with the combine (2 launches);
  *   more tokens: bucketing, bucketed gate/up+SiLU and down (the shared expert
@@ -181,13 +187,24 @@ int moe_expert_ffn(const void *w_gate, const void *w_up, const void *w_down,
  *                all NULL with shared_mode == MOE_SHARED_NONE
  *   h_post [m,hidden], h_mid [m,hidden], ids [m*top_k], route_w [m*top_k],
  *   shared_gate_logit [m] (MOE_SHARED_SIGMOID only), out [m,hidden] fp32.
- *   ws: scratch of at least moe_layer_workspace_bytes(...) bytes, 16-byte
- *   aligned; its contents are not meaningful after the call.
+ *   ws: at least moe_layer_workspace_bytes(...) bytes, 16-byte aligned.  Its
+ *   first MOE_LAYER_SYNC_BYTES hold the one-launch path's barrier words: they
+ *   must be zero before the first call with this workspace (allocate it
+ *   zeroed, or call moe_layer_workspace_init once, outside graph capture).
+ *   Calls advance per-workgroup generation words there.
+ *   32-bit word MOE_LAYER_SYNC_TIMEOUT_WORD is set to 1 if a barrier wait
+ *   ever timed out (the grid was not resident at once, e.g. the device was
+ *   shared with a kernel that held its CUs); the output of that call is then
+ *   not valid.  The rest is scratch.  Calls that may overlap in time must not
+ *   share a workspace.
  *   bucket_flag: AUTO picks by m; OFF forces the few-token path; ON (or
  *   PREBUILT, treated as ON) forces bucketing.  Output bits do not depend on
  *   the path. */
 int64_t moe_layer_workspace_bytes(int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
                                   int64_t top_k);
+/* Zeroes the synchronisation header of a layer workspace (an asynchronous
+ * memset on `stream`).  ws_bytes < MOE_LAYER_SYNC_BYTES -> Q4K_ERR_WORKSPACE. */
+int moe_layer_workspace_init(void *ws, int64_t ws_bytes, void *stream);
 int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
                       const void *sh_gate, const void *sh_up, const void *sh_down,
                       const float *h_post, const float *h_mid, const int32_t *ids,

@@ -42,9 +42,10 @@ def test_constants_match_header(lib):
     for name, val in [("Q4K_BLOCK_WEIGHTS", 256), ("Q4K_BLOCK_BYTES", 144), ("Q4K_MAX_TOP_K", 16),
                       ("Q4K_MAX_IN", _lib.Q4K_MAX_IN), ("Q4K_MAX_EXPERTS", _lib.Q4K_MAX_EXPERTS),
                       ("Q4K_MAX_PAIRS", _lib.Q4K_MAX_PAIRS), ("Q4TP_MAX_COLS", _lib.Q4TP_MAX_COLS),
-                      ("Q4K_BUCKET_CHUNK", 4)]:
+                      ("Q4K_BUCKET_CHUNK", 4), ("MOE_LAYER_SYNC_BYTES", 4096),
+                      ("MOE_LAYER_SYNC_TIMEOUT_WORD", 576)]:
         assert re.search(rf"#define {name} {val}\b", src), name
-    assert q4.q4k_abi_version() == 1
+    assert q4.q4k_abi_version() == 2
 
 
 def test_size_helpers(lib):
@@ -55,6 +56,9 @@ def test_size_helpers(lib):
     assert q4.q4tp_tensor_bytes(1, 14336) == 7452
     assert q4.q4tp_tensor_bytes(3, 33) == -1
     assert q4.moe_bucket_workspace_bytes(128, 128) == 4 * (129 + 130 + 128 + 129 + 1 + 1 + 256)
+    # sync header | act [9, 768] | expert_out [8, 2048] | shared_out [1, 2048] | buckets
+    assert q4.moe_layer_workspace_bytes(2048, 768, 128, 1, 8) == \
+        4096 + 27648 + 65536 + 8192 + 1792
 
 
 def test_status_strings(lib):
@@ -124,6 +128,9 @@ def test_ffn_combine_bucket_q4tp_validation(lib):
     assert _err(q4.q4k_quantize, FAKE, FAKE, 2, 300) == _lib.Q4K_ERR_SHAPE
     assert _err(q4.q4k_dequantize, FAKE, FAKE, -1) == _lib.Q4K_ERR_SHAPE
     assert _err(q4.q4tp_quantize, FAKE, FAKE, 2, 40) == _lib.Q4K_ERR_SHAPE
+    w = q4.moe_layer_workspace_init
+    assert _err(w, None, 1024) == _lib.Q4K_ERR_NULL
+    assert _err(w, FAKE, 4095) == _lib.Q4K_ERR_WORKSPACE
 
 
 def test_binding_refuses_host_tensors(lib):

@@ -446,7 +446,7 @@ def test_q4tp_unit_probe_and_ragged(dev):
 def _layer_gpu(dev, cfg, d_st, sd, a, ids, flag, shared=True):
     H, I, E, K, m = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.m
     wsb = q4.moe_layer_workspace_bytes(H, I, E, m, K)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)   # barrier words start at zero
     out = torch.empty(m, H, device=dev)
     mode = cfg.shared_mode if shared else q4.MOE_SHARED_NONE
     sh = sd if shared else (None, None, None)
@@ -541,6 +541,7 @@ def test_layer_invalid_ids_and_token_mode_edges(dev):
         want = oracle.moe_combine_residual(hm, eo, rw, so, lg, H, m, K, 1)
         wsb = q4.moe_layer_workspace_bytes(H, I, E, m, K)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        q4.moe_layer_workspace_init(ws, wsb)
         res = []
         for flag in (q4.Q4K_BUCKET_OFF, q4.Q4K_BUCKET_ON):
             out = torch.empty(m, H, device=dev)
@@ -550,6 +551,131 @@ def test_layer_invalid_ids_and_token_mode_edges(dev):
             res.append(sync_np(out))
         band(res[0], want, "token mode")
         assert np.array_equal(bits(res[0]), bits(res[1]))
+
+
+@pytest.fixture
+def one_launch_layer():
+    """Selects the opt-in one-launch single-token layer for one test."""
+    old = os.environ.get("Q4KMOE_FUSED_LAYER")
+    os.environ["Q4KMOE_FUSED_LAYER"] = "1"
+    yield
+    if old is None:
+        del os.environ["Q4KMOE_FUSED_LAYER"]
+    else:
+        os.environ["Q4KMOE_FUSED_LAYER"] = old
+
+
+@pytest.mark.parametrize("cfg", [wl.CFG2], ids=lambda c: c.name)
+def test_one_launch_layer_matches_two_launch_and_oracle(dev, cfg, one_launch_layer):
+    """The opt-in one-launch layer against the oracle and bit for bit against
+    the default two-launch layer, with and without a shared expert, and with
+    an invalid id at top_k 16."""
+    say("one-launch layer vs two-launch and oracle")
+    H, I, E, K, m = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.m
+    a, ids, d_st, h_st = _ffn_case(cfg, dev)
+    sd, sh = _shared_stacks(cfg, dev)
+    for shared in (True, False):
+        one = _layer_gpu(dev, cfg, d_st, sd, a, ids, q4.Q4K_BUCKET_AUTO, shared)
+        os.environ["Q4KMOE_FUSED_LAYER"] = "0"
+        two = _layer_gpu(dev, cfg, d_st, sd, a, ids, q4.Q4K_BUCKET_AUTO, shared)
+        os.environ["Q4KMOE_FUSED_LAYER"] = "1"
+        band(one, _layer_oracle(cfg, h_st, sh, a, ids, shared), f"one launch, shared={shared}")
+        assert np.array_equal(bits(one), bits(two)), shared
+    g = np.random.default_rng(51)
+    H, I, E, K = 1280, 512, 20, 16
+    st = [np.concatenate(quantize_many([(g.standard_normal((r, c)) * 0.05).astype(np.float32)
+                                        for _ in range(E)]))
+          for r, c in [(I, H), (I, H), (H, I)]]
+    shs = [oracle.q4k_quantize((g.standard_normal((r, c)) * 0.05).astype(np.float32))
+           for r, c in [(I, H), (I, H), (H, I)]]
+    h = g.standard_normal((1, H)).astype(np.float32)
+    hm = g.standard_normal((1, H)).astype(np.float32)
+    ids2 = g.integers(0, E, K).astype(np.int32)
+    ids2[3] = -2
+    rw = g.random(K).astype(np.float32)
+    lg = g.standard_normal(1).astype(np.float32)
+    _, _, _, eo = oracle.moe_expert_ffn(*st, E, H, I, h, ids2, 1, K)
+    _, _, _, so = oracle.moe_expert_ffn(*shs, 1, H, I, h, np.zeros(1, np.int32), 1, 1)
+    want = oracle.moe_combine_residual(hm, eo, rw, so, lg, H, 1, K, 1)
+    wsb = q4.moe_layer_workspace_bytes(H, I, E, 1, K)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    res = []
+    for fused in ("1", "0"):
+        os.environ["Q4KMOE_FUSED_LAYER"] = fused
+        out = torch.empty(1, H, device=dev)
+        q4.moe_layer_forward(*[T(x, dev) for x in st], *[T(x, dev) for x in shs], T(h, dev),
+                             T(hm, dev), T(ids2, dev), T(rw, dev), T(lg, dev), out, H, I, E, 1, K,
+                             1, q4.Q4K_BUCKET_AUTO, ws, wsb)
+        res.append(sync_np(out))
+    os.environ["Q4KMOE_FUSED_LAYER"] = "1"
+    band(res[0], want, "one launch, top_k 16, invalid id")
+    assert np.array_equal(bits(res[0]), bits(res[1]))
+
+
+def test_one_launch_layer_graph_replays_and_barrier_words(dev, one_launch_layer):
+    """The single-token layer in one launch: a HIP graph of the call replayed
+    with new inputs copied in between (each replay checked against the eager
+    result for those inputs), 40 eager calls in a row on one workspace, and
+    the workspace's barrier words as documented, with the timeout word clear."""
+    cfg = wl.CFG2
+    H, I, E, K, m = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.m
+    say("one-launch layer: graph replays and barrier words")
+    a, ids, d_st, h_st = _ffn_case(cfg, dev)
+    sd, sh = _shared_stacks(cfg, dev)
+    wsb = q4.moe_layer_workspace_bytes(H, I, E, m, K)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    g = np.random.default_rng(77)
+    draws = []
+    for i in range(4):
+        hp = (g.standard_normal((m, H))).astype(np.float32)
+        hm = (g.standard_normal((m, H))).astype(np.float32)
+        draws.append((hp, hm))
+    d_hp, d_hm = T(draws[0][0], dev), T(draws[0][1], dev)
+    d_ids, d_rw, d_lg = T(ids, dev), T(a.route_w, dev), T(a.shared_logit, dev)
+    out = torch.empty(m, H, device=dev)
+
+    def call():
+        q4.moe_layer_forward(*d_st, *sd, d_hp, d_hm, d_ids, d_rw, d_lg, out, H, I, E, m, K,
+                             cfg.shared_mode, q4.Q4K_BUCKET_AUTO, ws, wsb)
+
+    eager = []
+    for hp, hm in draws:
+        d_hp.copy_(T(hp, dev))
+        d_hm.copy_(T(hm, dev))
+        call()
+        eager.append(sync_np(out).copy())
+    for i, (hp, hm) in enumerate(draws):
+        sub = wl.MoeActivations(hp, hm, ids, a.route_w, a.shared_logit)
+        band(eager[i], _layer_oracle(cfg, h_st, sh, sub, ids), f"draw {i}")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for rep in range(3):
+        for i, (hp, hm) in enumerate(draws):
+            d_hp.copy_(T(hp, dev))
+            d_hm.copy_(T(hm, dev))
+            torch.cuda.synchronize()
+            graph.replay()
+            got = sync_np(out)
+            assert np.array_equal(bits(got), bits(eager[i])), (rep, i)
+    for _ in range(40):
+        call()
+    assert np.array_equal(bits(sync_np(out)), bits(eager[-1]))
+    words = ws[:4096].view(torch.int32).cpu().numpy()
+    grid = torch.cuda.get_device_properties(0).multi_processor_count   # one workgroup per CU
+    launches = 4 + 1 + 12 + 40
+    assert (words[:grid] == launches).all(), np.unique(words[:grid])   # per-workgroup flags
+    assert words[544] == launches                                    # release word
+    assert words[576] == 0                                           # MOE_LAYER_SYNC_TIMEOUT_WORD
+    rest = np.delete(words, list(range(grid)) + [544])
+    assert not rest.any(), np.nonzero(rest)
+    del graph
 
 
 @pytest.mark.parametrize("cfg,sample", [(wl.CFG4_M1, None), (wl.CFG4_M32, [0, 13, 31])],
