@@ -437,6 +437,9 @@ __device__ __forceinline__ float unit_from_tile(const Tile<NT, ITERS> &t, int nt
 
 // ------------------------------------------------------------ host side ---
 
+// Bucketed mode on the matrix cores (q4k_mfma.hip).
+hipError_t launch_q4k_gemv_mfma(const GemvArgs &a, bool fused_swiglu, hipStream_t st);
+
 static inline int lanes_per_row(int k) {
     const int units = 4 * (k >> 8);
     int l = 4;
