@@ -435,6 +435,20 @@ __device__ __forceinline__ float unit_from_tile(const Tile<NT, ITERS> &t, int nt
     return unit_value(unit_scale(t.hdr[nt][it], c), acc, sx[2 * u], sx[2 * u + 1]);
 }
 
+// Bucket workspace views (layout documented with moe_bucket in q4kmoe.h).
+struct BucketView {
+    const int32_t *counts, *offsets, *pairs, *active, *n_active, *n_chunks, *chunks;
+    __device__ BucketView(const int32_t *ws, int E, int P) {
+        counts = ws;
+        offsets = counts + (E + 1);
+        pairs = offsets + (E + 2);
+        active = pairs + P;
+        n_active = active + (E + 1);
+        n_chunks = n_active + 1;
+        chunks = n_chunks + 1;
+    }
+};
+
 // ------------------------------------------------------------ host side ---
 
 // Bucketed mode on the matrix cores (q4k_mfma.hip).

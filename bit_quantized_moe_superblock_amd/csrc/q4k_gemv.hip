@@ -108,19 +108,6 @@ __global__ __launch_bounds__(kThreads) void k_rows(GemvArgs a) {
 
 // -------------------------------------------------------- bucketed mode ----
 
-// Bucket workspace views (layout documented with moe_bucket in q4kmoe.h).
-struct BucketView {
-    const int32_t *counts, *offsets, *pairs, *active, *n_active, *n_chunks, *chunks;
-    __device__ BucketView(const int32_t *ws, int E, int P) {
-        counts = ws;
-        offsets = counts + (E + 1);
-        pairs = offsets + (E + 2);
-        active = pairs + P;
-        n_active = active + (E + 1);
-        n_chunks = n_active + 1;
-        chunks = n_chunks + 1;
-    }
-};
 
 // Work item = one chunk (at most kBucketChunk pairs of one bucket, listed by
 // the bucketing kernel) x one tile of ITERS*RPI rows.  The chunk's activation

@@ -39,9 +39,10 @@ namespace q4k {
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 
-constexpr int kMP = 16;        // pairs per MFMA group (the A rows)
-constexpr int kMRows = 64;     // weight rows per workgroup (4 waves x 16)
-constexpr int kSubB = 2048;    // LDS bytes per staged sub-block: 2 parts x 4 groups x 16 pairs x 16 B
+constexpr int kMP = kBucketChunk;   // pairs per workgroup (A rows 8..15 repeat 0..7)
+constexpr int kMRows = 64;          // weight rows per workgroup (4 waves x 16)
+constexpr int kSubB = 2 * 4 * kMP * 16;   // LDS bytes per staged sub-block: parts x groups x pairs x 16 B
+static_assert(kMP == 8, "A-row mapping assumes 8 pairs per workgroup");
 
 // LDS bytes of one slab of SB superblocks: the split activations, then the
 // sub-block sums [sub-block][pair].
@@ -104,8 +105,8 @@ __device__ __forceinline__ void mfma_stage(XOf x_of, int cnt, int j0, int nsub_t
                 hi[i] = h;
                 lo[i] = (_Float16)(x - (float)h);
             }
-            *(h8v *)(dst + (size_t)(0 * 4 + g) * 256 + p * 16) = hi;
-            *(h8v *)(dst + (size_t)(1 * 4 + g) * 256 + p * 16) = lo;
+            *(h8v *)(dst + (size_t)(0 * 4 + g) * (kMP * 16) + p * 16) = hi;
+            *(h8v *)(dst + (size_t)(1 * 4 + g) * (kMP * 16) + p * 16) = lo;
         }
     }
 }
@@ -164,10 +165,13 @@ __device__ __forceinline__ void mfma_superblock(const MfmaTile (&t)[NT], const u
         for (int half = 0; half < 2; half++) {
             const int jl = jl0 + 2 * c + half;   // sub-block within the slab
             const int j = 2 * c + half;          // sub-block within the superblock
-            const uint8_t *xs = lds + (size_t)jl * kSubB + lane * 16;
+            // A row l % 16 is pair (l % 16) % 8: rows 8..15 repeat 0..7 and
+            // their D rows are not used
+            const uint8_t *xs = lds + (size_t)jl * kSubB + (lane >> 4) * (kMP * 16) +
+                                (lane & 7) * 16;
             const h8v ahi = *(const h8v *)xs;
-            const h8v alo = *(const h8v *)(xs + 1024);
-            const float4 sx = *(const float4 *)(sxs + jl * kMP + 4 * gp);
+            const h8v alo = *(const h8v *)(xs + 4 * kMP * 16);
+            const float4 sx = *(const float4 *)(sxs + jl * kMP + 4 * (gp & 1));
 #pragma unroll
             for (int nt = 0; nt < NT; nt++) {
                 const h8v b = __builtin_bit_cast(h8v, half ? bhi[nt] : blo[nt]);
@@ -184,9 +188,9 @@ __device__ __forceinline__ void mfma_superblock(const MfmaTile (&t)[NT], const u
     }
 }
 
-// Grid (row tiles of 64, bucket slots + shared groups).  Slot y < n_slots is
-// the y-th non-empty bucket (its pairs in groups of 16); slot n_slots + s is
-// the shared expert's tokens 16 s .. 16 s + 15.
+// Grid (row tiles of 64, chunk slots + shared chunks).  Slot y < n_slots is
+// chunk y of the bucketing kernel's list (at most 8 pairs of one bucket);
+// slot n_slots + s is the shared expert's tokens 8 s .. 8 s + 7.
 template <int NT, int EPI, int SB>
 __global__ __launch_bounds__(kThreads) void k_bucket_mfma(GemvArgs a, int n_slots) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_b[];
@@ -196,16 +200,17 @@ __global__ __launch_bounds__(kThreads) void k_bucket_mfma(GemvArgs a, int n_slot
     const int E = a.num_experts, P = a.n_pairs;
     const int y = blockIdx.y;
     const int32_t *ws = a.bucket;
-    const int32_t *counts = ws, *offsets = ws + (E + 1), *pairs = offsets + (E + 2);
-    const int32_t *active = pairs + P, *n_active = active + (E + 1);
+    const BucketView bv(ws, E, P);
+    const int32_t *pairs = bv.pairs;
     int cnt, first, bkt;
     bool shared;
     if (y < n_slots) {
-        if (y >= *n_active)
+        if (y >= *bv.n_chunks)
             return;
-        bkt = active[y];
-        cnt = counts[bkt];
-        first = offsets[bkt];
+        bkt = bv.chunks[2 * y];
+        const int packed = bv.chunks[2 * y + 1];
+        first = packed & 0xFFFFFF;
+        cnt = packed >> 24;
         shared = false;
     } else {
         const int s = y - n_slots;
@@ -237,8 +242,8 @@ __global__ __launch_bounds__(kThreads) void k_bucket_mfma(GemvArgs a, int n_slot
     const float *sxs = (const float *)(lds_b + (size_t)SB * 8 * kSubB);
     const int nsub_total = a.k >> 5;
 
-    for (int g0 = 0; g0 < cnt; g0 += kMP) {
-        const int gc = cnt - g0 < kMP ? cnt - g0 : kMP;
+    {   // one chunk: at most kMP pairs
+        const int g0 = 0, gc = cnt;
         auto x_of = [&](int i) { return pair_x_known(a, shared, pair_q(g0 + i)); };
         float yv[NT][4];
 #pragma unroll
@@ -271,11 +276,12 @@ __global__ __launch_bounds__(kThreads) void k_bucket_mfma(GemvArgs a, int n_slot
                     issue(i + 3);
             }
         }
-        // D rows 4g .. 4g+3 are pairs g0 + 4g + j; this lane's column is row r0
+        // D rows 4g .. 4g+3 are pairs g0 + 4g + j (rows 8..15 repeat 0..7);
+        // this lane's column is row r0
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const int i = 4 * g + j;
-            if (i < gc && r0 < a.n) {
+            if (g < 2 && i < gc && r0 < a.n) {
                 const int q = pair_q(g0 + i);
                 float *out = q < P ? a.dst + (int64_t)q * a.n : a.dst_sh + (int64_t)(q - P) * a.n;
                 float part[NT];
@@ -294,9 +300,9 @@ template <int NT, int EPI, int SB>
 static hipError_t go_mfma(const GemvArgs &a, hipStream_t st) {
     auto kern = k_bucket_mfma<NT, EPI, SB>;
     const size_t lds = set_lds((const void *)kern, mfma_lds_bytes(SB));
-    const int n_slots = (int)((int64_t)a.n_pairs < (int64_t)a.num_experts + 1
-                                  ? a.n_pairs
-                                  : a.num_experts + 1);
+    // chunks of the list: at most one partial chunk per non-empty bucket
+    const int64_t nb_max = a.n_pairs < (int64_t)a.num_experts + 1 ? a.n_pairs : a.num_experts + 1;
+    const int n_slots = (int)(nb_max + a.n_pairs / kMP);
     const int sh_groups = (a.m_sh + kMP - 1) / kMP;
     dim3 grid((a.n + kMRows - 1) / kMRows, n_slots + sh_groups);
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a, n_slots);

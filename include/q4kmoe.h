@@ -61,7 +61,7 @@ enum { MOE_SHARED_NONE = 0, MOE_SHARED_SIGMOID = 1, MOE_SHARED_UNSCALED = 2 };
 #define Q4K_MAX_EXPERTS 1023  /* bucketing keeps E+1 buckets in one block  */
 #define Q4K_MAX_PAIRS 8192    /* m*top_k handled by one bucketing launch   */
 #define Q4TP_MAX_COLS 16384   /* largest Q4TiledP row                       */
-#define Q4K_BUCKET_CHUNK 4    /* pairs per bucketed work item               */
+#define Q4K_BUCKET_CHUNK 8    /* pairs per bucketed work item               */
 #define MOE_LAYER_SYNC_BYTES 4096 /* synchronisation header of a layer workspace */
 #define MOE_LAYER_SYNC_TIMEOUT_WORD 576 /* 32-bit word of that header: barrier timed out */
 

@@ -42,7 +42,7 @@ def test_constants_match_header(lib):
     for name, val in [("Q4K_BLOCK_WEIGHTS", 256), ("Q4K_BLOCK_BYTES", 144), ("Q4K_MAX_TOP_K", 16),
                       ("Q4K_MAX_IN", _lib.Q4K_MAX_IN), ("Q4K_MAX_EXPERTS", _lib.Q4K_MAX_EXPERTS),
                       ("Q4K_MAX_PAIRS", _lib.Q4K_MAX_PAIRS), ("Q4TP_MAX_COLS", _lib.Q4TP_MAX_COLS),
-                      ("Q4K_BUCKET_CHUNK", 4), ("MOE_LAYER_SYNC_BYTES", 4096),
+                      ("Q4K_BUCKET_CHUNK", 8), ("MOE_LAYER_SYNC_BYTES", 4096),
                       ("MOE_LAYER_SYNC_TIMEOUT_WORD", 576)]:
         assert re.search(rf"#define {name} {val}\b", src), name
     assert q4.q4k_abi_version() == 2

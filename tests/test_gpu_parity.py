@@ -19,6 +19,7 @@ from _util import band, bits
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+CH = 8   # Q4K_BUCKET_CHUNK: pairs per bucketed work item
 POOL = cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4))
 
 
@@ -264,8 +265,8 @@ def test_bucket_matches_oracle(dev, P, E, seed):
     assert np.array_equal(c, wc) and np.array_equal(o, wo) and np.array_equal(p, wp)
     assert act.tolist() == [b for b in range(E + 1) if wc[b] > 0] and nact == (wc > 0).sum()
     # work chunks: each non-empty bucket split into pieces of at most 4 pairs
-    want = [(b, (wo[b] + i) | (min(4, wc[b] - i) << 24)) for b in range(E + 1)
-            for i in range(0, wc[b], 4)]
+    want = [(b, (wo[b] + i) | (min(CH, wc[b] - i) << 24)) for b in range(E + 1)
+            for i in range(0, wc[b], CH)]
     assert [tuple(x) for x in chunks.tolist()] == want
 
 
