@@ -18,6 +18,7 @@ SOURCES = ["api.hip", "q4k_gemv.hip", "q4k_mfma.hip", "q4k_layer.hip", "q4k_code
            "q4tp.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-result", "-I", INCLUDE]
 

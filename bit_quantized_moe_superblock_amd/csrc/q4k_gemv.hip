@@ -658,9 +658,10 @@ hipError_t launch_q4k_gemv(const GemvLaunch &L, hipStream_t st) {
     const GemvArgs a = make_args(L);
     const bool bucketed = L.bucket_ws != nullptr;
     // Bucketed mode runs on the matrix cores unless Q4KMOE_MFMA=0 selects the
-    // vector-unit kernels.
+    // vector-unit kernels; the matrix-core kernel reads activations as float4,
+    // so rows and strides must be 16-byte aligned.
     static const bool mfma = env_int("Q4KMOE_MFMA", 1) != 0;
-    if (bucketed && mfma)
+    if (bucketed && mfma && a.vec)
         return launch_q4k_gemv_mfma(a, L.fused_swiglu, st);
     if (L.fused_swiglu)
         return launch_any<2, EPI_SWIGLU>(a, bucketed, st);

@@ -21,13 +21,17 @@
 //     (0x00F000F0 gives the high nibbles, * 2^-20); the matrix core takes
 //     fp16 subnormals exactly, so the weights enter with no conversion.  The
 //     k order inside each group of 8 is therefore (0,2,1,3,4,6,5,7).
-//   - A is the activation split exactly into two fp16 parts,
-//     x = hi + lo, hi = fp16(x), lo = fp16(x - hi), staged once per
-//     workgroup in LDS in the same k order; D = A_hi B + A_lo B.
+//   - A is the activation split into two fp16 parts, x = hi + lo,
+//     hi = fp16(x), lo = fp16(x - hi), staged once per workgroup in LDS in
+//     the same k order: A rows 0..7 are the 8 pairs' hi parts, rows 8..15
+//     their lo parts, so one MFMA per sub-block covers both and the halves
+//     are added once at the end.
 //   - Each lane's D column is one weight row: the lane decodes that row's
 //     header itself (d, dmin, six-bit scales and mins) and applies, per
-//     sub-block j, y += d sc_j 2^24 D - dmin m_j sum_j(x) (2^20 for the high
-//     nibbles), the factored form of the superblock formula.
+//     sub-block j, y += d sc_j 2^24 D_j (2^20 for the high nibbles); the min
+//     term -dmin sum_j m_j sum_j(x), the other half of the factored
+//     superblock formula, is one more MFMA per superblock over the split
+//     sub-block sums and the mins.
 //
 // Rounding differs from the vector-unit kernels (the matrix core's own sum
 // order, x carried as hi + lo), so this mode matches them within the fp32
@@ -39,15 +43,15 @@ namespace q4k {
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 
-constexpr int kMP = kBucketChunk;   // pairs per workgroup (A rows 8..15 repeat 0..7)
+constexpr int kMP = kBucketChunk;   // pairs per workgroup (A rows: 8 hi parts, 8 lo parts)
 constexpr int kMRows = 64;          // weight rows per workgroup (4 waves x 16)
 constexpr int kSubB = 2 * 4 * kMP * 16;   // LDS bytes per staged sub-block: parts x groups x pairs x 16 B
 static_assert(kMP == 8, "A-row mapping assumes 8 pairs per workgroup");
 
-// LDS bytes of one slab of SB superblocks: the split activations, then the
-// sub-block sums [sub-block][pair].
+// LDS bytes of one slab of SB superblocks: the split activations, then per
+// superblock the split sub-block sums (16 rows x 8 sub-blocks of fp16).
 __host__ __device__ constexpr size_t mfma_lds_bytes(int sb) {
-    return (size_t)sb * 8 * kSubB + (size_t)sb * 8 * kMP * 4;
+    return (size_t)sb * 8 * kSubB + (size_t)sb * 256;
 }
 
 struct MfmaTile {
@@ -55,44 +59,63 @@ struct MfmaTile {
     uint2 q[4];   // 8 bytes of each 32-byte chunk: bytes 8g..8g+7
 };
 
-// Stage pairs [0, cnt) of one slab (sub-blocks j0 .. j0 + 8 SB) into LDS.
-// Task (pair, sub-block) loads 32 activations, sums them in ascending order
-// from 0, splits each into fp16 hi + lo, and writes the four k groups.
-template <int SB, typename XOf>
-__device__ __forceinline__ void mfma_stage(XOf x_of, int cnt, int j0, int nsub_total, bool vec,
-                                           uint8_t *lds) {
-    float *sxs = (float *)(lds + (size_t)SB * 8 * kSubB);
-    const int nsub = SB * 8;
-    for (int task = threadIdx.x; task < cnt * nsub; task += kThreads) {
+// A thread's share of one slab's activations: tasks (pair, sub-block)
+// tid, tid + 256, ..., 32 activations each.  The loads are issued before the
+// weights so that staging waits on them alone.
+template <int SB>
+struct XRegs {
+    static constexpr int U = (kMP * SB * 8 + kThreads - 1) / kThreads;   // tasks per thread
+    float4 v[U][8];
+};
+
+template <int SB>
+__device__ __forceinline__ void mfma_x_issue(const float *const (&xrow)[XRegs<SB>::U], int cnt,
+                                             int j0, int nsub_total, XRegs<SB> &xr) {
+    constexpr int nsub = SB * 8;
+#pragma unroll
+    for (int u = 0; u < XRegs<SB>::U; u++) {
+        const int task = threadIdx.x + u * kThreads;
+        const int jl = task % nsub;
+        const bool ok = task < cnt * nsub && j0 + jl < nsub_total;
+        const float *src = xrow[u] + 32 * (ok ? j0 + jl : 0);   // clamped
+#pragma unroll
+        for (int q = 0; q < 8; q++)
+            xr.v[u][q] = *(const float4 *)(src + 4 * q);
+    }
+}
+
+// Task (pair p, sub-block jl) sums its 32 activations in ascending order from
+// 0, splits each activation and the sum into fp16 hi + lo, and writes the
+// four k groups of both parts and the two sums.  Sub-blocks past the end of
+// the row are zeros.
+template <int SB>
+__device__ __forceinline__ void mfma_x_commit(const XRegs<SB> &xr, int cnt, int j0,
+                                              int nsub_total, uint8_t *lds) {
+    constexpr int nsub = SB * 8;
+    uint8_t *sxa = lds + (size_t)SB * 8 * kSubB;
+#pragma unroll
+    for (int u = 0; u < XRegs<SB>::U; u++) {
+        const int task = threadIdx.x + u * kThreads;
+        if (task >= cnt * nsub)
+            continue;
         const int p = task / nsub, jl = task - p * nsub;
-        const int j = j0 + jl;
+        const bool live = j0 + jl < nsub_total;
         float v[32];
-        if (j < nsub_total) {   // uniform per task row; past the end: zeros
-            const float *src = x_of(p) + 32 * j;
-            if (vec) {
 #pragma unroll
-                for (int q = 0; q < 8; q++) {
-                    const float4 f = *(const float4 *)(src + 4 * q);
-                    v[4 * q] = f.x;
-                    v[4 * q + 1] = f.y;
-                    v[4 * q + 2] = f.z;
-                    v[4 * q + 3] = f.w;
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 32; q++)
-                    v[q] = src[q];
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 32; q++)
-                v[q] = 0.0f;
+        for (int q = 0; q < 8; q++) {
+            v[4 * q] = live ? xr.v[u][q].x : 0.0f;
+            v[4 * q + 1] = live ? xr.v[u][q].y : 0.0f;
+            v[4 * q + 2] = live ? xr.v[u][q].z : 0.0f;
+            v[4 * q + 3] = live ? xr.v[u][q].w : 0.0f;
         }
         float s = 0.0f;
 #pragma unroll
         for (int q = 0; q < 32; q++)
             s += v[q];
-        sxs[jl * kMP + p] = s;
+        const _Float16 sh = (_Float16)s;
+        _Float16 *sx = (_Float16 *)(sxa + (size_t)(jl >> 3) * 256) + (jl & 7);
+        sx[p * 8] = sh;
+        sx[(8 + p) * 8] = (_Float16)(s - (float)sh);
         uint8_t *dst = lds + (size_t)jl * kSubB;
 #pragma unroll
         for (int g = 0; g < 4; g++) {
@@ -119,36 +142,52 @@ __device__ __forceinline__ void mfma_load(const uint8_t *row, int sb, int g, Mfm
         t.q[c] = *(const uint2 *)(b + 16 + 32 * c + 8 * g);
 }
 
-// Per-sub-block factors of the lane's row: k[j] = d sc_j 2^24 (2^20 for the
-// odd, high-nibble sub-blocks), m[j] = dmin m_j.
-__device__ __forceinline__ void mfma_scales(const uint4 &h, float (&k)[8], float (&m)[8]) {
-    const float d = lo_half(h.x), dmin = hi_half(h.x);
-    const uint32_t s[3] = {h.y, h.z, h.w};
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        uint32_t sc, mn;
-        if (j < 4) {
-            sc = (s[0] >> (8 * j)) & 63u;
-            mn = (s[1] >> (8 * j)) & 63u;
-        } else {
-            const int i = j - 4;
-            sc = ((s[2] >> (8 * i)) & 15u) | (((s[0] >> (8 * i)) >> 6) << 4 & 0x30u);
-            mn = ((s[2] >> (8 * i + 4)) & 15u) | (((s[1] >> (8 * i)) >> 6) << 4 & 0x30u);
-        }
-        k[j] = d * (float)sc * ((j & 1) ? 1048576.0f : 16777216.0f);
-        m[j] = dmin * (float)mn;
-    }
-}
-
+// One superblock of the lane's row against the staged pairs.  A rows 0..7
+// are the pairs' hi parts and rows 8..15 their lo parts, so one MFMA per
+// sub-block gives both; D rows 8..15 (lanes 32..63) accumulate the lo half,
+// which the caller adds to the hi half once at the end.
+//
+//   y += d sc_j 2^24 D_j        (2^20 for the odd, high-nibble sub-blocks)
+//   y -= dmin 2^24 D_min,  D_min = sum_j (sum of x over sub-block j) m_j 2^-24
+//
+// D_min is one more MFMA: its A holds the split sub-block sums in k = 0..7
+// (lanes 0..15; zero elsewhere) and its B the six-bit mins as fp16
+// subnormals m_j 2^-24, both exact.
 template <int NT>
 __device__ __forceinline__ void mfma_superblock(const MfmaTile (&t)[NT], const uint8_t *lds,
-                                                const float *sxs, int jl0, float (&y)[NT][4]) {
+                                                const uint8_t *sxa, int s, float (&y)[NT][4]) {
     const int lane = threadIdx.x & 63;
-    const int gp = lane >> 4;   // D rows (pairs) 4 gp .. 4 gp + 3
-    float ks[NT][8], ms[NT][8];
+    const int aoff = (((lane >> 3) & 1) * 4 + (lane >> 4)) * (kMP * 16) + (lane & 7) * 16;
+    const h8v a_sx = *(const h8v *)(sxa + (size_t)s * 256 + (lane & 15) * 16);
+    const h8v zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    const h8v amin = lane < 16 ? a_sx : zero8;
+    float kd[NT][8];
 #pragma unroll
-    for (int nt = 0; nt < NT; nt++)
-        mfma_scales(t[nt].hdr, ks[nt], ms[nt]);
+    for (int nt = 0; nt < NT; nt++) {
+        const uint4 h = t[nt].hdr;
+        const float d = lo_half(h.x), dmin = hi_half(h.x);
+        const uint32_t sc03 = h.y & 0x3F3F3F3Fu;
+        const uint32_t sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+        const uint32_t mn03 = h.z & 0x3F3F3F3Fu;
+        const uint32_t mn47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+        const float d24 = d * 16777216.0f, d20 = d * 1048576.0f;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const uint32_t w = j < 4 ? sc03 : sc47;
+            kd[nt][j] = ((j & 1) ? d20 : d24) * (float)((w >> (8 * (j & 3))) & 0xFFu);
+        }
+        const uint4 bm = make_uint4(__builtin_amdgcn_perm(0u, mn03, 0x0c010c00u),
+                                    __builtin_amdgcn_perm(0u, mn03, 0x0c030c02u),
+                                    __builtin_amdgcn_perm(0u, mn47, 0x0c010c00u),
+                                    __builtin_amdgcn_perm(0u, mn47, 0x0c030c02u));
+        const f4v zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+        const f4v dm = __builtin_amdgcn_mfma_f32_16x16x32_f16(amin, __builtin_bit_cast(h8v, bm),
+                                                              zero4, 0, 0, 0);
+        const float dm24 = -dmin * 16777216.0f;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            y[nt][i] = __builtin_fmaf(dm24, dm[i], y[nt][i]);
+    }
 #pragma unroll
     for (int c = 0; c < 4; c++) {
         uint4 blo[NT], bhi[NT];
@@ -163,26 +202,16 @@ __device__ __forceinline__ void mfma_superblock(const MfmaTile (&t)[NT], const u
         }
 #pragma unroll
         for (int half = 0; half < 2; half++) {
-            const int jl = jl0 + 2 * c + half;   // sub-block within the slab
-            const int j = 2 * c + half;          // sub-block within the superblock
-            // A row l % 16 is pair (l % 16) % 8: rows 8..15 repeat 0..7 and
-            // their D rows are not used
-            const uint8_t *xs = lds + (size_t)jl * kSubB + (lane >> 4) * (kMP * 16) +
-                                (lane & 7) * 16;
-            const h8v ahi = *(const h8v *)xs;
-            const h8v alo = *(const h8v *)(xs + 4 * kMP * 16);
-            const float4 sx = *(const float4 *)(sxs + jl * kMP + 4 * (gp & 1));
+            const int j = 2 * c + half;   // sub-block within the superblock
+            const h8v ax = *(const h8v *)(lds + (size_t)(s * 8 + j) * kSubB + aoff);
 #pragma unroll
             for (int nt = 0; nt < NT; nt++) {
                 const h8v b = __builtin_bit_cast(h8v, half ? bhi[nt] : blo[nt]);
-                f4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, b, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, b, acc, 0, 0, 0);
-                const float kk = ks[nt][j], mm = ms[nt][j];
-                y[nt][0] = __builtin_fmaf(-mm, sx.x, __builtin_fmaf(kk, acc[0], y[nt][0]));
-                y[nt][1] = __builtin_fmaf(-mm, sx.y, __builtin_fmaf(kk, acc[1], y[nt][1]));
-                y[nt][2] = __builtin_fmaf(-mm, sx.z, __builtin_fmaf(kk, acc[2], y[nt][2]));
-                y[nt][3] = __builtin_fmaf(-mm, sx.w, __builtin_fmaf(kk, acc[3], y[nt][3]));
+                const f4v zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+                const f4v acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, b, zero4, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    y[nt][i] = __builtin_fmaf(kd[nt][j], acc[i], y[nt][i]);
             }
         }
     }
@@ -192,7 +221,8 @@ __device__ __forceinline__ void mfma_superblock(const MfmaTile (&t)[NT], const u
 // chunk y of the bucketing kernel's list (at most 8 pairs of one bucket);
 // slot n_slots + s is the shared expert's tokens 8 s .. 8 s + 7.
 template <int NT, int EPI, int SB>
-__global__ __launch_bounds__(kThreads) void k_bucket_mfma(GemvArgs a, int n_slots) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SB <= 4 ? 3 : 2)))
+void k_bucket_mfma(GemvArgs a, int n_slots) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_b[];
     fetch_args(a);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -239,12 +269,20 @@ __global__ __launch_bounds__(kThreads) void k_bucket_mfma(GemvArgs a, int n_slot
     wrow[0] = (shared ? a.s0 : a.w0 + (int64_t)bkt * mat) + (int64_t)r * rowb;
     if (NT == 2)
         wrow[NT - 1] = (shared ? a.s1 : a.w1 + (int64_t)bkt * mat) + (int64_t)r * rowb;
-    const float *sxs = (const float *)(lds_b + (size_t)SB * 8 * kSubB);
+    const uint8_t *sxa = lds_b + (size_t)SB * 8 * kSubB;
     const int nsub_total = a.k >> 5;
 
     {   // one chunk: at most kMP pairs
         const int g0 = 0, gc = cnt;
         auto x_of = [&](int i) { return pair_x_known(a, shared, pair_q(g0 + i)); };
+        // activation rows of this thread's staging tasks (pair = task / (8 SB),
+        // clamped to the chunk), looked up once
+        const float *xrow[XRegs<SB>::U];
+#pragma unroll
+        for (int u = 0; u < XRegs<SB>::U; u++) {
+            const int p = (tid + u * kThreads) / (SB * 8);
+            xrow[u] = x_of(p < gc ? p : gc - 1);
+        }
         float yv[NT][4];
 #pragma unroll
         for (int nt = 0; nt < NT; nt++)
@@ -263,21 +301,32 @@ __global__ __launch_bounds__(kThreads) void k_bucket_mfma(GemvArgs a, int n_slot
                 for (int nt = 0; nt < NT; nt++)
                     mfma_load(wrow[nt], sb, g, tt[i % 3][nt]);
             };
+            XRegs<SB> xr;
+            mfma_x_issue<SB>(xrow, gc, sb0 * 8, nsub_total, xr);
+            // the activations ahead of the weights: staging waits on them alone
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < (SB < 3 ? SB : 3); i++)
                 issue(i);
-            mfma_stage<SB>(x_of, gc, sb0 * 8, nsub_total, a.vec, lds_b);
+            mfma_x_commit<SB>(xr, gc, sb0 * 8, nsub_total, lds_b);
             lds_barrier();
 #pragma unroll
             for (int i = 0; i < SB; i++) {
                 if (sb0 + i < nb)   // uniform
-                    mfma_superblock<NT>(tt[i % 3], lds_b, sxs, i * 8, yv);
+                    mfma_superblock<NT>(tt[i % 3], lds_b, sxa, i, yv);
                 if (i + 3 < SB)
                     issue(i + 3);
             }
         }
-        // D rows 4g .. 4g+3 are pairs g0 + 4g + j (rows 8..15 repeat 0..7);
-        // this lane's column is row r0
+        // hi half (D rows 0..7, lanes 0..31) plus lo half (rows 8..15, lanes
+        // 32..63)
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                yv[nt][j] += __shfl_xor(yv[nt][j], 32);
+        // D rows 4g .. 4g+3 (g < 2) are pairs g0 + 4g + j; this lane's column
+        // is row r0
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const int i = 4 * g + j;
@@ -311,7 +360,9 @@ static hipError_t go_mfma(const GemvArgs &a, hipStream_t st) {
 
 template <int NT, int EPI>
 static hipError_t mfma_sb(const GemvArgs &a, hipStream_t st) {
-    switch (a.k >> 8 < 8 ? a.k >> 8 : 8) {
+    static const int slab = env_int("Q4KMOE_MFMA_SLAB", 8);
+    const int sb_max = slab < 1 ? 1 : slab > 8 ? 8 : slab;
+    switch (a.k >> 8 < sb_max ? a.k >> 8 : sb_max) {
     case 1: return go_mfma<NT, EPI, 1>(a, st);
     case 2: return go_mfma<NT, EPI, 2>(a, st);
     case 3: return go_mfma<NT, EPI, 3>(a, st);
