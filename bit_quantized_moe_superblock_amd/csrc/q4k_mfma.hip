@@ -16,22 +16,27 @@
 // i < 8, and D[4 (l / 16) + j][l % 16] for j < 4.
 //
 //   - B comes straight from the nibbles: with v the dword of bytes b0..b3,
-//     (v & 0x000F000F) is the fp16 pair (q(b0), q(b2)) * 2^-24 and
-//     ((v >> 8) & 0x000F000F) is (q(b1), q(b3)) * 2^-24 as subnormals
-//     (0x00F000F0 gives the high nibbles, * 2^-20); the matrix core takes
-//     fp16 subnormals exactly, so the weights enter with no conversion.  The
-//     k order inside each group of 8 is therefore (0,2,1,3,4,6,5,7).
+//     (v & 0x000F000F) holds (q(b0), q(b2)) and ((v >> 8) & 0x000F000F)
+//     (q(b1), q(b3)) as 16-bit integers (shifts by 4 and 12 give the high
+//     nibbles).  One packed 16-bit multiply by the sub-block's six-bit scale
+//     makes them q sc <= 945, which read as fp16 are the subnormals
+//     q sc 2^-24; the matrix core takes fp16 subnormals exactly.  The k order
+//     inside each group of 8 is therefore (0,2,1,3,4,6,5,7).
+//   - With the scales inside B, one MFMA may mix sub-blocks of a superblock,
+//     so each lane loads contiguous bytes (16 of each 64-byte half of the
+//     nibbles; a row's 4 lanes read 64 contiguous bytes per load) and the
+//     activations are staged in the matching k order.
 //   - A is the activation split into two fp16 parts, x = hi + lo,
 //     hi = fp16(x), lo = fp16(x - hi), staged once per workgroup in LDS in
 //     the same k order: A rows 0..7 are the 8 pairs' hi parts, rows 8..15
 //     their lo parts, so one MFMA per sub-block covers both and the halves
 //     are added once at the end.
 //   - Each lane's D column is one weight row: the lane decodes that row's
-//     header itself (d, dmin, six-bit scales and mins) and applies, per
-//     sub-block j, y += d sc_j 2^24 D_j (2^20 for the high nibbles); the min
-//     term -dmin sum_j m_j sum_j(x), the other half of the factored
-//     superblock formula, is one more MFMA per superblock over the split
-//     sub-block sums and the mins.
+//     header itself (d, dmin, six-bit scales and mins), and the superblock's
+//     eight MFMAs accumulate into one D with y += d 2^24 D; the min term
+//     -dmin sum_j m_j sum_j(x), the other half of the factored superblock
+//     formula, is one more MFMA per superblock over the split sub-block sums
+//     and the mins.
 //
 // Rounding differs from the vector-unit kernels (the matrix core's own sum
 // order, x carried as hi + lo), so this mode matches them within the fp32
@@ -45,6 +50,10 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr int kMP = kBucketChunk;   // pairs per workgroup (A rows: 8 hi parts, 8 lo parts)
 constexpr int kMRows = 64;          // weight rows per workgroup (4 waves x 16)
+#ifndef Q4K_MFMA_DEPTH
+#define Q4K_MFMA_DEPTH 3
+#endif
+constexpr int kDepth = Q4K_MFMA_DEPTH;   // superblocks of weights in flight per wave
 constexpr int kSubB = 2 * 4 * kMP * 16;   // LDS bytes per staged sub-block: parts x groups x pairs x 16 B
 static_assert(kMP == 8, "A-row mapping assumes 8 pairs per workgroup");
 
@@ -54,9 +63,12 @@ __host__ __device__ constexpr size_t mfma_lds_bytes(int sb) {
     return (size_t)sb * 8 * kSubB + (size_t)sb * 256;
 }
 
+// One superblock of a lane's row: the header and 32 of the 128 nibble bytes,
+// qs[16 g, 16 g + 16) and qs[64 + 16 g, 64 + 16 g + 16) for lane group g, so
+// that the 4 lanes of a row read 64 contiguous bytes per load.
 struct MfmaTile {
     uint4 hdr;
-    uint2 q[4];   // 8 bytes of each 32-byte chunk: bytes 8g..8g+7
+    uint4 u[2];
 };
 
 // A thread's share of one slab's activations: tasks (pair, sub-block)
@@ -116,20 +128,26 @@ __device__ __forceinline__ void mfma_x_commit(const XRegs<SB> &xr, int cnt, int 
         _Float16 *sx = (_Float16 *)(sxa + (size_t)(jl >> 3) * 256) + (jl & 7);
         sx[p * 8] = sh;
         sx[(8 + p) * 8] = (_Float16)(s - (float)sh);
-        uint8_t *dst = lds + (size_t)jl * kSubB;
+        // sub-block j = 2c + hh (c = 2hu + gg) of superblock jl / 8: its
+        // positions 8 q8 .. 8 q8 + 7 are the k group g = 2 gg + q8 / 2 of MFMA
+        // t = 4hu + 2hh + q8 % 2 (the nibbles a lane of group g holds)
+        const int j = jl & 7, c = j >> 1, hh = j & 1, hu = c >> 1, gg = c & 1;
+        uint8_t *dst = lds + (size_t)(jl >> 3) * 8 * kSubB;
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
+        for (int q8 = 0; q8 < 4; q8++) {
             const int ord[8] = {0, 2, 1, 3, 4, 6, 5, 7};
             h8v hi, lo;
 #pragma unroll
             for (int i = 0; i < 8; i++) {
-                const float x = v[8 * g + ord[i]];
+                const float x = v[8 * q8 + ord[i]];
                 const _Float16 h = (_Float16)x;
                 hi[i] = h;
                 lo[i] = (_Float16)(x - (float)h);
             }
-            *(h8v *)(dst + (size_t)(0 * 4 + g) * (kMP * 16) + p * 16) = hi;
-            *(h8v *)(dst + (size_t)(1 * 4 + g) * (kMP * 16) + p * 16) = lo;
+            const int g = 2 * gg + (q8 >> 1), t = 4 * hu + 2 * hh + (q8 & 1);
+            uint8_t *blk = dst + (size_t)t * kSubB;
+            *(h8v *)(blk + (size_t)(0 * 4 + g) * (kMP * 16) + p * 16) = hi;
+            *(h8v *)(blk + (size_t)(1 * 4 + g) * (kMP * 16) + p * 16) = lo;
         }
     }
 }
@@ -137,83 +155,108 @@ __device__ __forceinline__ void mfma_x_commit(const XRegs<SB> &xr, int cnt, int 
 __device__ __forceinline__ void mfma_load(const uint8_t *row, int sb, int g, MfmaTile &t) {
     const uint8_t *b = row + (size_t)sb * kBlockBytes;
     t.hdr = *(const uint4 *)b;
-#pragma unroll
-    for (int c = 0; c < 4; c++)
-        t.q[c] = *(const uint2 *)(b + 16 + 32 * c + 8 * g);
+    t.u[0] = *(const uint4 *)(b + 16 + 16 * g);
+    t.u[1] = *(const uint4 *)(b + 80 + 16 * g);
 }
 
 // One superblock of the lane's row against the staged pairs.  A rows 0..7
-// are the pairs' hi parts and rows 8..15 their lo parts, so one MFMA per
-// sub-block gives both; D rows 8..15 (lanes 32..63) accumulate the lo half,
-// which the caller adds to the hi half once at the end.
+// are the pairs' hi parts and rows 8..15 their lo parts; D rows 8..15 (lanes
+// 32..63) accumulate the lo half, which the caller adds to the hi half once
+// at the end.
 //
-//   y += d sc_j 2^24 D_j        (2^20 for the odd, high-nibble sub-blocks)
-//   y -= dmin 2^24 D_min,  D_min = sum_j (sum of x over sub-block j) m_j 2^-24
+// Lane group g holds nibble bytes 16 g .. 16 g + 15 of the two 64-byte
+// halves u of the block: sub-blocks j = 4u + 2gg + hh (gg = g / 2, hh = 0
+// low nibbles, 1 high nibbles), positions 16 (g % 2) .. + 15.  Each of its
+// B values is the nibble times the sub-block's six-bit scale, an integer
+// q sc <= 945 taken as the fp16 subnormal q sc 2^-24 (exact), so the eight
+// MFMAs of the superblock accumulate into one D and
 //
-// D_min is one more MFMA: its A holds the split sub-block sums in k = 0..7
-// (lanes 0..15; zero elsewhere) and its B the six-bit mins as fp16
-// subnormals m_j 2^-24, both exact.
+//   y += d 2^24 D - dmin 2^24 D_min
+//
+// where D_min is one more MFMA: its A holds the split sub-block sums in
+// k = 0..7 (lanes 0..15; zero elsewhere) and its B the six-bit mins as fp16
+// subnormals m_j 2^-24.
 template <int NT>
 __device__ __forceinline__ void mfma_superblock(const MfmaTile (&t)[NT], const uint8_t *lds,
                                                 const uint8_t *sxa, int s, float (&y)[NT][4]) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
     const int lane = threadIdx.x & 63;
     const int aoff = (((lane >> 3) & 1) * 4 + (lane >> 4)) * (kMP * 16) + (lane & 7) * 16;
     const h8v a_sx = *(const h8v *)(sxa + (size_t)s * 256 + (lane & 15) * 16);
     const h8v zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
     const h8v amin = lane < 16 ? a_sx : zero8;
-    float kd[NT][8];
+    // scale byte 2gg + hh of a packed scale word, into both 16-bit halves
+    const uint32_t gg2 = (uint32_t)(lane >> 5) * 2u;
+    const uint32_t sel0 = 0x0c000c00u | gg2 | (gg2 << 16);
+    const uint32_t sel1 = sel0 + 0x00010001u;
+    const f4v zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    f4v acc[NT];
+    uint32_t scp[NT][2][2];   // [u][hh]
 #pragma unroll
     for (int nt = 0; nt < NT; nt++) {
         const uint4 h = t[nt].hdr;
-        const float d = lo_half(h.x), dmin = hi_half(h.x);
         const uint32_t sc03 = h.y & 0x3F3F3F3Fu;
         const uint32_t sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
         const uint32_t mn03 = h.z & 0x3F3F3F3Fu;
         const uint32_t mn47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
-        const float d24 = d * 16777216.0f, d20 = d * 1048576.0f;
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const uint32_t w = j < 4 ? sc03 : sc47;
-            kd[nt][j] = ((j & 1) ? d20 : d24) * (float)((w >> (8 * (j & 3))) & 0xFFu);
-        }
+        scp[nt][0][0] = __builtin_amdgcn_perm(0u, sc03, sel0);
+        scp[nt][0][1] = __builtin_amdgcn_perm(0u, sc03, sel1);
+        scp[nt][1][0] = __builtin_amdgcn_perm(0u, sc47, sel0);
+        scp[nt][1][1] = __builtin_amdgcn_perm(0u, sc47, sel1);
         const uint4 bm = make_uint4(__builtin_amdgcn_perm(0u, mn03, 0x0c010c00u),
                                     __builtin_amdgcn_perm(0u, mn03, 0x0c030c02u),
                                     __builtin_amdgcn_perm(0u, mn47, 0x0c010c00u),
                                     __builtin_amdgcn_perm(0u, mn47, 0x0c030c02u));
-        const f4v zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-        const f4v dm = __builtin_amdgcn_mfma_f32_16x16x32_f16(amin, __builtin_bit_cast(h8v, bm),
-                                                              zero4, 0, 0, 0);
-        const float dm24 = -dmin * 16777216.0f;
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(amin, __builtin_bit_cast(h8v, bm),
+                                                         zero4, 0, 0, 0);
+    }
+    // the min term first; the accumulators then restart for D
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++) {
+        const float dm24 = -hi_half(t[nt].hdr.x) * 16777216.0f;
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            y[nt][i] = __builtin_fmaf(dm24, dm[i], y[nt][i]);
+            y[nt][i] = __builtin_fmaf(dm24, acc[nt][i], y[nt][i]);
+        acc[nt] = zero4;
     }
+    auto scaled = [](uint32_t v, uint32_t sc) {
+        return __builtin_bit_cast(uint32_t,
+                                  __builtin_bit_cast(u16x2, v) * __builtin_bit_cast(u16x2, sc));
+    };
 #pragma unroll
-    for (int c = 0; c < 4; c++) {
-        uint4 blo[NT], bhi[NT];
+    for (int u = 0; u < 2; u++) {
 #pragma unroll
-        for (int nt = 0; nt < NT; nt++) {
-            const uint32_t w0 = t[nt].q[c].x, w1 = t[nt].q[c].y;
-            const uint32_t s0 = w0 >> 8, s1 = w1 >> 8;
-            blo[nt] = make_uint4(w0 & 0x000F000Fu, s0 & 0x000F000Fu, w1 & 0x000F000Fu,
-                                 s1 & 0x000F000Fu);
-            bhi[nt] = make_uint4(w0 & 0x00F000F0u, s0 & 0x00F000F0u, w1 & 0x00F000F0u,
-                                 s1 & 0x00F000F0u);
-        }
-#pragma unroll
-        for (int half = 0; half < 2; half++) {
-            const int j = 2 * c + half;   // sub-block within the superblock
-            const h8v ax = *(const h8v *)(lds + (size_t)(s * 8 + j) * kSubB + aoff);
+        for (int e = 0; e < 2; e++) {
+            uint4 blo[NT], bhi[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; nt++) {
-                const h8v b = __builtin_bit_cast(h8v, half ? bhi[nt] : blo[nt]);
-                const f4v zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-                const f4v acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, b, zero4, 0, 0, 0);
+                const uint32_t w0 = e ? t[nt].u[u].z : t[nt].u[u].x;
+                const uint32_t w1 = e ? t[nt].u[u].w : t[nt].u[u].y;
+                const uint32_t s0 = scp[nt][u][0], s1 = scp[nt][u][1];
+                blo[nt] = make_uint4(scaled(w0 & 0x000F000Fu, s0), scaled((w0 >> 8) & 0x000F000Fu, s0),
+                                     scaled(w1 & 0x000F000Fu, s0), scaled((w1 >> 8) & 0x000F000Fu, s0));
+                bhi[nt] = make_uint4(scaled((w0 >> 4) & 0x000F000Fu, s1),
+                                     scaled((w0 >> 12) & 0x000F000Fu, s1),
+                                     scaled((w1 >> 4) & 0x000F000Fu, s1),
+                                     scaled((w1 >> 12) & 0x000F000Fu, s1));
+            }
 #pragma unroll
-                for (int i = 0; i < 4; i++)
-                    y[nt][i] = __builtin_fmaf(kd[nt][j], acc[i], y[nt][i]);
+            for (int hh = 0; hh < 2; hh++) {
+                const int tk = 4 * u + 2 * hh + e;   // MFMA within the superblock
+                const h8v ax = *(const h8v *)(lds + (size_t)(s * 8 + tk) * kSubB + aoff);
+#pragma unroll
+                for (int nt = 0; nt < NT; nt++)
+                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        ax, __builtin_bit_cast(h8v, hh ? bhi[nt] : blo[nt]), acc[nt], 0, 0, 0);
             }
         }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++) {
+        const float d24 = lo_half(t[nt].hdr.x) * 16777216.0f;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            y[nt][i] = __builtin_fmaf(d24, acc[nt][i], y[nt][i]);
     }
 }
 
@@ -292,30 +335,30 @@ void k_bucket_mfma(GemvArgs a, int n_slots) {
         for (int sb0 = 0; sb0 < nb; sb0 += SB) {
             __syncthreads();   // the previous slab's LDS is consumed
             // weights of the slab's first superblocks in flight while staging
-            // (three superblocks in flight; indices are constants once the
+            // (kDepth superblocks in flight; indices are constants once the
             // loop is unrolled, so the tiles stay in registers)
-            MfmaTile tt[3][NT];
+            MfmaTile tt[kDepth][NT];
             auto issue = [&](int i) {
                 const int sb = sb0 + i < nb ? sb0 + i : nb - 1;   // clamped
 #pragma unroll
                 for (int nt = 0; nt < NT; nt++)
-                    mfma_load(wrow[nt], sb, g, tt[i % 3][nt]);
+                    mfma_load(wrow[nt], sb, g, tt[i % kDepth][nt]);
             };
             XRegs<SB> xr;
             mfma_x_issue<SB>(xrow, gc, sb0 * 8, nsub_total, xr);
             // the activations ahead of the weights: staging waits on them alone
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < (SB < 3 ? SB : 3); i++)
+            for (int i = 0; i < (SB < kDepth ? SB : kDepth); i++)
                 issue(i);
             mfma_x_commit<SB>(xr, gc, sb0 * 8, nsub_total, lds_b);
             lds_barrier();
 #pragma unroll
             for (int i = 0; i < SB; i++) {
                 if (sb0 + i < nb)   // uniform
-                    mfma_superblock<NT>(tt[i % 3], lds_b, sxa, i, yv);
-                if (i + 3 < SB)
-                    issue(i + 3);
+                    mfma_superblock<NT>(tt[i % kDepth], lds_b, sxa, i, yv);
+                if (i + kDepth < SB)
+                    issue(i + kDepth);
             }
         }
         // hi half (D rows 0..7, lanes 0..31) plus lo half (rows 8..15, lanes
