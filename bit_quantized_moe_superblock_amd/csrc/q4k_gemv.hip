@@ -532,20 +532,25 @@ static int pick_iters(int64_t pairs, int n, int rpi, int max_it) {
     if (forced == 1 || forced == 2 || forced == 3 || forced == 4 || forced == 6 || forced == 8)
         return forced;
     // Smallest (waves of workgroups over the CUs) x (row groups per
-    // workgroup), ties to the taller tile: a grid just past a multiple of the
-    // CU count leaves some CUs with twice the work of the rest.
+    // workgroup): a grid just past a multiple of the CU count leaves some CUs
+    // with twice the work of the rest.  Ties go to a grid that gives every CU
+    // a workgroup (one workgroup alone on a CU leaves one wave per SIMD, with
+    // nothing to hide its latency), then to the taller tile.
     const int64_t cus = cu_count();
     const int cand[] = {1, 2, 3, 4, 6, 8};
     int best = 1;
     int64_t best_cost = INT64_MAX;
+    bool best_fills = false;
     for (int it : cand) {
         if (it > max_it)
             break;
         const int64_t tiles = (n + it * rpi - 1) / (it * rpi);
         const int64_t cost = (tiles * pairs + cus - 1) / cus * it;
-        if (cost <= best_cost) {
+        const bool fills = tiles * pairs >= cus;
+        if (cost < best_cost || (cost == best_cost && (fills || !best_fills))) {
             best = it;
             best_cost = cost;
+            best_fills = fills;
         }
     }
     return best;
