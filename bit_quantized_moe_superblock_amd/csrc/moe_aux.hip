@@ -3,10 +3,12 @@
 // Bucketing (moeflux expert_forward.rs, encode_moe_gather_id_fuse step 1 and
 // the ExpertBuckets CSR): one workgroup of 1024 threads counts pairs per
 // expert, scans the counts, lists the non-empty buckets and the work chunks
-// (at most kBucketChunk pairs of one bucket each), and orders the pairs
-// by sorting the unique keys (bucket << 13 | pair) with a bitonic network in
-// LDS, so each bucket lists its pairs in ascending pair order and the result is
-// the same on every run.  Bucket E collects ids outside [0, E).
+// (at most kBucketChunk pairs of one bucket each), and places the pairs in
+// pair order: one wave takes 64 pairs at a time, finds the lanes that share a
+// bucket by ballots over the bucket's bits, and writes each pair at its
+// bucket's running cursor plus its rank among those lanes.  Each bucket thus
+// lists its pairs in ascending pair order (a stable counting sort), the same on
+// every run.  Bucket E collects ids outside [0, E).
 //
 // Combine (moeflux module doc and encode_moe_combine_residual_n_tokens):
 // out[t,i] = h_mid[t,i] + sum_s w[t,s]*expert_out[t,s,i] + g_t*shared_out[t,i],
@@ -17,12 +19,12 @@
 namespace q4k {
 
 constexpr int kBucketThreads = 1024;
-constexpr int kMaxPairsPow2 = 8192;
+constexpr int kMaxPairs = 8192;
 
 __global__ __launch_bounds__(kBucketThreads) void k_moe_bucket(const int32_t *__restrict__ ids,
                                                                int P, int E, int32_t *ws) {
     __shared__ int cnt[kBucketThreads];
-    __shared__ uint32_t keys[kMaxPairsPow2];
+    __shared__ int bk[kMaxPairs];   // bucket of each pair
     __shared__ int wsum_c[16], wsum_f[16], wsum_h[16];
     const int tid = threadIdx.x;
     int32_t *counts = ws;
@@ -33,20 +35,13 @@ __global__ __launch_bounds__(kBucketThreads) void k_moe_bucket(const int32_t *__
     int32_t *n_chunks = n_active + 1;
     int32_t *chunks = n_chunks + 1;
 
-    int N = 1;
-    while (N < P)
-        N <<= 1;
     cnt[tid] = 0;
     __syncthreads();
-    for (int p = tid; p < N; p += kBucketThreads) {
-        if (p < P) {
-            const int e = ids[p];
-            const int b = ((unsigned)e < (unsigned)E) ? e : E;
-            atomicAdd(&cnt[b], 1);
-            keys[p] = ((uint32_t)b << 13) | (uint32_t)p;
-        } else {
-            keys[p] = 0xFFFFFFFFu;
-        }
+    for (int p = tid; p < P; p += kBucketThreads) {
+        const int e = ids[p];
+        const int b = ((unsigned)e < (unsigned)E) ? e : E;
+        atomicAdd(&cnt[b], 1);
+        bk[p] = b;
     }
     __syncthreads();
 
@@ -101,24 +96,35 @@ __global__ __launch_bounds__(kBucketThreads) void k_moe_bucket(const int32_t *__
         *n_chunks = ex_h + h;
     }
 
-    // Bitonic sort of the keys (ascending).
-    for (int size = 2; size <= N; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < (N >> 1); i += kBucketThreads) {
-                const int j = 2 * stride * (i / stride) + (i % stride);
-                const int l = j + stride;
-                const bool up = (j & size) == 0;
-                const uint32_t a = keys[j], b = keys[l];
-                if ((a > b) == up) {
-                    keys[j] = b;
-                    keys[l] = a;
-                }
-            }
-            __syncthreads();
+    // Stable placement, one wave.  The cursors start at the offsets (cnt is
+    // reused; every wave has read its count above).
+    __syncthreads();
+    if (tid <= E)
+        cnt[tid] = ex_c;
+    __syncthreads();
+    if (wave != 0)
+        return;
+    int nbits = 1;
+    while ((1 << nbits) <= E)
+        nbits++;
+    const uint64_t below = lane ? ~0ull >> (64 - lane) : 0ull;   // lanes under this one
+    for (int p0 = 0; p0 < P; p0 += 64) {
+        const int p = p0 + lane;
+        const bool live = p < P;
+        const int b = live ? bk[p] : 0;
+        uint64_t same = __ballot(live);
+        for (int bit = 0; bit < nbits; bit++) {
+            const bool on = (b >> bit) & 1;
+            const uint64_t m = __ballot(on);
+            same &= on ? m : ~m;
+        }
+        if (live) {
+            const int rank = __popcll(same & below);
+            pairs[cnt[b] + rank] = p;
+            if (rank == 0)   // one lane per bucket of this step
+                cnt[b] += __popcll(same);
         }
     }
-    for (int q = tid; q < P; q += kBucketThreads)
-        pairs[q] = (int32_t)(keys[q] & 8191u);
 }
 
 hipError_t launch_moe_bucket(const int32_t *ids, int64_t n_pairs, int64_t num_experts,
