@@ -374,18 +374,10 @@ int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
     G.inner = 0;
     G.outer_sh = hidden;
     G.fused_swiglu = true;
-    if (!bucketed) {   // the down launch reads these next: have them cached
-        G.pf = w_down;
-        G.pf_sh = has_sh ? sh_down : nullptr;
-        G.pf_mat = q4k_matrix_bytes(hidden, inter);
-    }
     rc = launched(launch_q4k_gemv(G, st));
     if (rc)
         return rc;
     GemvLaunch D = G;
-    D.pf = nullptr;
-    D.pf_sh = nullptr;
-    D.pf_mat = 0;
     D.w0 = w_down;
     D.w1 = nullptr;
     D.s0 = has_sh ? sh_down : nullptr;

@@ -37,12 +37,6 @@ struct GemvArgs {
     int n, k, top_k, num_experts, n_pairs, m_sh;
     int pc;                   // pairs per LDS chunk (bucketed mode)
     int vec;                  // activation rows 16-byte aligned (float4 staging)
-    // Optional stacks the next launch will read for the same pairs (the down
-    // projection after gate/up): pair mode touches them so they are in the
-    // device's last-level cache when that launch starts.  pf_mat = bytes per
-    // expert; null pf = nothing to touch.
-    const uint8_t *pf, *pf_sh;
-    int64_t pf_mat;
 };
 
 // Reads every argument field into scalar registers at kernel entry.  Left to
@@ -56,13 +50,11 @@ __device__ __forceinline__ void fetch_args(const GemvArgs &a) {
     asm volatile("" ::"s"(a.dst), "s"(a.dst_sh), "s"(a.outer), "s"(a.inner), "s"(a.outer_sh),
                  "s"(a.n), "s"(a.k), "s"(a.top_k), "s"(a.num_experts), "s"(a.n_pairs),
                  "s"(a.m_sh), "s"(a.pc), "s"(a.vec));
-    asm volatile("" ::"s"(a.pf), "s"(a.pf_sh), "s"(a.pf_mat));
 }
 
 // Where pair q (q >= n_pairs: shared pair of token q - n_pairs) reads and writes.
 struct PairRef {
     const uint8_t *w0, *w1;   // expert base of the stacks
-    const uint8_t *pf;        // expert base of the stack to touch (or w0)
     const float *x;
     float *out;
     bool valid;
@@ -78,7 +70,6 @@ __device__ __forceinline__ PairRef pair_ref(const GemvArgs &a, int q) {
         const int64_t off = r.valid ? (int64_t)e * a.n * nb01 : 0;
         r.w0 = a.w0 + off;
         r.w1 = a.w1 ? a.w1 + off : nullptr;
-        r.pf = a.pf ? a.pf + (r.valid ? (int64_t)e * a.pf_mat : 0) : r.w0;
         r.x = a.src1 + t * a.outer + s * a.inner;
         r.out = a.dst + (int64_t)q * a.n;
     } else {
@@ -86,7 +77,6 @@ __device__ __forceinline__ PairRef pair_ref(const GemvArgs &a, int q) {
         r.valid = true;
         r.w0 = a.s0;
         r.w1 = a.s1;
-        r.pf = a.pf ? a.pf_sh : r.w0;
         r.x = a.src1_sh + t * a.outer_sh;
         r.out = a.dst_sh + (int64_t)t * a.n;
     }

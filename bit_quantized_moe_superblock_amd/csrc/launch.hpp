@@ -20,10 +20,6 @@ struct GemvLaunch {
     int64_t n, k, top_k, num_experts, n_pairs, m_sh;
     int64_t outer, inner, outer_sh;
     bool fused_swiglu;
-    // Stacks the next launch reads for the same pairs (touched by pair mode
-    // so they are cached), bytes per expert; null for none.
-    const void *pf = nullptr, *pf_sh = nullptr;
-    int64_t pf_mat = 0;
 };
 
 hipError_t launch_q4k_gemv(const GemvLaunch &L, hipStream_t st);

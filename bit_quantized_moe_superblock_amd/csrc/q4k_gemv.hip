@@ -66,26 +66,6 @@ __global__ __launch_bounds__(kThreads) void k_rows(GemvArgs a) {
     lane_x_issue(pr.x, active ? u : 0, a.vec, lx);
     Tile<NT, ITERS> t;
     load_rows<LPR, NT, ITERS>(pr.w0, pr.w1, a.n, a.k, row0, true, t);
-    // Touch this workgroup's share of the pair's next-launch stack (8 x 16
-    // bytes per lane, after the weights so those arrive first).  Without a
-    // stack to touch the same loads re-read this pair's first weight bytes,
-    // which keeps the loads unconditional (a branch around loads makes every
-    // later wait drain the whole queue).
-    uint32_t pfx = 0;
-    {
-        const int64_t span = a.pf ? a.pf_mat : 16;
-        const int64_t per_wg = ((span / gridDim.x + 15) >> 4) << 4;
-        const int64_t beg = (int64_t)blockIdx.x * per_wg;
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            int64_t off = beg + (int64_t)(j * kThreads + tid) * 16;
-            off = off < beg + per_wg - 16 ? off : beg + per_wg - 16;
-            off = off < span - 16 ? off : span - 16;
-            off = off > 0 ? off : 0;
-            const uint4 v = *(const uint4 *)(pr.pf + off);
-            pfx ^= v.x ^ v.y ^ v.z ^ v.w;
-        }
-    }
     lane_x_sums(lx);
 #pragma unroll
     for (int it = 0; it < ITERS; it++) {
@@ -102,8 +82,6 @@ __global__ __launch_bounds__(kThreads) void k_rows(GemvArgs a) {
         if (u == 0 && r < a.n)
             pr.out[r] = epilogue<EPI, NT>(part);
     }
-    if (a.pf_mat < 0)   // never: keeps the touching loads alive
-        pr.out[0] = __builtin_bit_cast(float, pfx);
 }
 
 // -------------------------------------------------------- bucketed mode ----
@@ -653,9 +631,6 @@ static GemvArgs make_args(const GemvLaunch &L) {
     a.m_sh = (int)L.m_sh;
     a.vec = al16(L.src1) && L.outer % 4 == 0 && L.inner % 4 == 0 &&
             (L.m_sh == 0 || (al16(L.src1_sh) && L.outer_sh % 4 == 0));
-    a.pf = (const uint8_t *)L.pf;
-    a.pf_sh = (const uint8_t *)L.pf_sh;
-    a.pf_mat = L.pf ? L.pf_mat : 0;
     return a;
 }
 
