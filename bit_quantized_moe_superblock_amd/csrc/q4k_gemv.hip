@@ -423,6 +423,28 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineAr
     //    ids held in registers would become an indexed array in scratch.
     __shared__ int ex_lds[kMaxTopK];
     const int e_own = a.ids[tok * K + (tid < K ? tid : K - 1)];
+    // The first staging batch of the token's activation rows (routed rows,
+    // then the shared row; both bases are uniform, lanes pick between the two
+    // values) is issued next, ahead of the weights, as float4 loads with a
+    // clamped index and no branch: waiting for the ids above leaves it in
+    // flight, and committing it below waits for it alone.  The host launches
+    // this kernel only on 16-byte aligned rows.
+    const float *xr = a.src1 + tok * a.outer;
+    const float *xsh = a.m_sh > 0 ? a.src1_sh + tok * a.outer_sh : xr;
+    const int64_t inner = a.inner;
+    auto x_of = [&](int s) { return s < K ? xr + s * inner : xsh; };
+    const int nsub = a.k >> 5;
+    const int total = np * nsub;
+    StageBatch xb;
+    {
+        xb.f = tid;
+        const int f = tid < total ? tid : total - 1;
+        const int xrow = f / nsub, j = f - xrow * nsub;
+        const float *src = x_of(xrow) + 32 * j;
+#pragma unroll
+        for (int q = 0; q < 8; q++)
+            xb.v[q] = *(const float4 *)(src + 4 * q);
+    }
     if (tid < K)
         ex_lds[tid] = (unsigned)e_own < (unsigned)a.num_experts ? e_own : -1;
     lds_barrier();
@@ -460,13 +482,11 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineAr
     const int64_t o = (int64_t)tok * a.n + row0 + ri;
     const bool rowok = ri < trt && row0 + ri < a.n;
     const float hm = rowok ? cb.h_mid[o] : 0.0f;
-    // 4. activation rows of the token's pairs (routed rows, then the shared
-    //    row); both bases are uniform, lanes pick between the two values
-    const float *xr = a.src1 + tok * a.outer;
-    const float *xsh = a.m_sh > 0 ? a.src1_sh + tok * a.outer_sh : xr;
-    const int64_t inner = a.inner;
-    stage_rows([&](int s) { return s < K ? xr + s * inner : xsh; }, np, a.k, a.vec, lds);
-    __syncthreads();
+    // 4. activation rows of the token's pairs into LDS (first batch, then any
+    //    further ones)
+    stage_commit(xb, total, a.k, lds);
+    stage_rows(x_of, np, a.k, true, lds, kThreads);
+    lds_barrier();
 #pragma unroll
     for (int it = 0; it < ITERS; it++) {
         const float *xrow = lds + sp[it] * rl;
@@ -666,13 +686,15 @@ static hipError_t dc_lpr(const GemvArgs &a, const CombineArgs &cb, hipStream_t s
     constexpr int RPI = kThreads / LPR;
     const int np = a.top_k + (a.m_sh > 0 ? 1 : 0);
     const int m = a.n_pairs / a.top_k;
-    // rows per workgroup: the tallest tile that still gives two workgroups
-    // per CU (256 CUs) and at most 8 row groups per lane
+    // rows per workgroup: the tallest tile that still gives every CU a
+    // workgroup, with at most 8 row groups per lane (every workgroup stages
+    // all of the token's activation rows, so taller tiles stage less in all)
     static const int forced = env_int("Q4KMOE_DC_ROWS", 0);
+    const int64_t cus = cu_count();
     int trt = 1;
     for (int cand = 64; cand >= 1; cand >>= 1) {
         const int its = (cand * np + RPI - 1) / RPI;
-        if (its <= 8 && (int64_t)((a.n + cand - 1) / cand) * m >= 512) {
+        if (its <= 8 && (int64_t)((a.n + cand - 1) / cand) * m >= cus) {
             trt = cand;
             break;
         }
@@ -691,6 +713,8 @@ hipError_t launch_q4k_down_combine(const GemvLaunch &L, const float *h_mid, cons
                                    const float *shared_logit, float *out, float *expert_out,
                                    int shared_mode, hipStream_t st) {
     const GemvArgs a = make_args(L);
+    if (!a.vec)   // the kernel stages activations as float4
+        return hipErrorInvalidValue;
     CombineArgs cb{h_mid, route_w, shared_logit, out, expert_out, shared_mode};
     switch (lanes_per_row(a.k)) {
     case 4: return dc_lpr<4>(a, cb, st);
