@@ -42,12 +42,19 @@ namespace q4k {
 
 // ------------------------------------------------------------ pair mode ----
 
-template <int LPR, int NT, int ITERS, int EPI>
+// XLDS: the pair's activation row is staged once per workgroup in LDS (a
+// thread per 32-float sub-block, float4 loads issued ahead of the weights,
+// committed with its sub-block sum) and every lane reads its unit's 64
+// activations from there; otherwise (rows not 16-byte aligned) each lane loads
+// them into registers itself.  Both give the same bits: the sub-block sums are
+// taken in ascending order from 0 either way.
+template <int LPR, int NT, int ITERS, int EPI, bool XLDS>
 __global__ __launch_bounds__(kThreads) void k_rows(GemvArgs a) {
     extern __shared__ float lds[];
     fetch_args(a);
     constexpr int RPI = kThreads / LPR;
-    float *red = lds;   // cross-wave row sums (rows wider than a wave)
+    float *red = lds;        // cross-wave row sums (rows wider than a wave)
+    float *xs = lds + 16;    // staged activation row (XLDS)
     const int q = blockIdx.y;
     const int row0 = blockIdx.x * (ITERS * RPI);
     const PairRef pr = pair_ref(a, q);
@@ -58,29 +65,66 @@ __global__ __launch_bounds__(kThreads) void k_rows(GemvArgs a) {
                 pr.out[row0 + i] = 0.0f;
         return;
     }
-    // Each lane reads its unit's 64 activations straight into registers (the
-    // rows of a workgroup share them through the cache), then its weights.
-    const int u = tid % LPR, rsub = tid / LPR, c = u & 3;
+    const int u = tid % LPR, rsub = tid / LPR;
     const bool active = u < 4 * (a.k >> 8);
-    LaneX lx;
-    lane_x_issue(pr.x, active ? u : 0, a.vec, lx);
-    Tile<NT, ITERS> t;
-    load_rows<LPR, NT, ITERS>(pr.w0, pr.w1, a.n, a.k, row0, true, t);
-    lane_x_sums(lx);
+    const int ul = active ? u : 0, cl = ul & 3;   // clamped unit (see load_rows)
+    if constexpr (XLDS) {
+        const int nsub = a.k >> 5;
+        StageBatch xb;
+        xb.f = tid;
+        {
+            const int f = tid < nsub ? tid : nsub - 1;   // clamped, no branch
 #pragma unroll
-    for (int it = 0; it < ITERS; it++) {
-        float part[NT];
+            for (int q = 0; q < 8; q++)
+                xb.v[q] = *(const float4 *)(pr.x + 32 * f + 4 * q);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep them ahead of the weights
+        Tile<NT, ITERS> t;
+        load_rows<LPR, NT, ITERS>(pr.w0, pr.w1, a.n, a.k, row0, true, t);
+        stage_commit(xb, nsub, a.k, xs);
+        stage_rows([&](int) { return pr.x; }, 1, a.k, true, xs, kThreads);   // k > 8192
+        lds_barrier();
 #pragma unroll
-        for (int nt = 0; nt < NT; nt++) {
+        for (int it = 0; it < ITERS; it++) {
             // Computed on every lane (inactive lanes hold a clamped, valid
             // unit) and then selected: under a branch the compiler sinks part
             // of the weight loads into it, and their wait drains the queue.
-            const float uv = unit_from_regs<NT, ITERS>(t, nt, it, lx, c);
-            part[nt] = row_reduce<LPR>(active ? uv : 0.0f, red, nt);
+            float part[NT];
+            if constexpr (NT == 2) {
+                float v0, v1;
+                unit_pair_from_tile<ITERS>(t, it, xs, ul, cl, a.k, v0, v1);
+                part[0] = row_reduce<LPR>(active ? v0 : 0.0f, red, 0);
+                part[1] = row_reduce<LPR>(active ? v1 : 0.0f, red, 1);
+            } else {
+                const float uv = unit_from_tile<NT, ITERS>(t, 0, it, xs, ul, cl, a.k);
+                part[0] = row_reduce<LPR>(active ? uv : 0.0f, red, 0);
+            }
+            const int r = row0 + it * RPI + rsub;
+            if (u == 0 && r < a.n)
+                pr.out[r] = epilogue<EPI, NT>(part);
         }
-        const int r = row0 + it * RPI + rsub;
-        if (u == 0 && r < a.n)
-            pr.out[r] = epilogue<EPI, NT>(part);
+    } else {
+        // each lane reads its unit's 64 activations straight into registers
+        // (the rows of a workgroup share them through the cache), then its
+        // weights
+        const int c = u & 3;
+        LaneX lx;
+        lane_x_issue(pr.x, ul, a.vec, lx);
+        Tile<NT, ITERS> t;
+        load_rows<LPR, NT, ITERS>(pr.w0, pr.w1, a.n, a.k, row0, true, t);
+        lane_x_sums(lx);
+#pragma unroll
+        for (int it = 0; it < ITERS; it++) {
+            float part[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; nt++) {
+                const float uv = unit_from_regs<NT, ITERS>(t, nt, it, lx, c);
+                part[nt] = row_reduce<LPR>(active ? uv : 0.0f, red, nt);
+            }
+            const int r = row0 + it * RPI + rsub;
+            if (u == 0 && r < a.n)
+                pr.out[r] = epilogue<EPI, NT>(part);
+        }
     }
 }
 
@@ -557,10 +601,15 @@ static int pick_iters(int64_t pairs, int n, int rpi, int max_it) {
 template <int LPR, int NT, int EPI, int IT>
 static hipError_t go_rows(const GemvArgs &a, hipStream_t st) {
     constexpr int RPI = kThreads / LPR;
-    auto kern = k_rows<LPR, NT, IT, EPI>;
-    const size_t lds = 8 * sizeof(float);
     dim3 grid((a.n + IT * RPI - 1) / (IT * RPI), a.n_pairs + a.m_sh);
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a);
+    if (a.vec) {
+        auto kern = k_rows<LPR, NT, IT, EPI, true>;
+        const size_t lds = set_lds((const void *)kern, (16 + (size_t)row_lds_floats(a.k)) * sizeof(float));
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a);
+    } else {
+        auto kern = k_rows<LPR, NT, IT, EPI, false>;
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 8 * sizeof(float), st, a);
+    }
     return hipGetLastError();
 }
 
