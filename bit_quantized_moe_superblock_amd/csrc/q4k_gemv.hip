@@ -598,6 +598,28 @@ static int pick_iters(int64_t pairs, int n, int rpi, int max_it) {
     return best;
 }
 
+// Row groups per workgroup when the activation row is staged in LDS: the
+// shortest tile whose staged row (4k bytes, read from the cache) is at most
+// half of its weight bytes and whose grid still gives every CU a workgroup
+// (more, smaller workgroups hide each other's latency); otherwise the rule
+// above.
+static int pick_iters_staged(int64_t pairs, int n, int rpi, int max_it, int k, int nt) {
+    static const int forced = env_int("Q4KMOE_ITERS", 0);
+    if (forced == 1 || forced == 2 || forced == 3 || forced == 4 || forced == 6 || forced == 8)
+        return forced;
+    const int64_t cus = cu_count();
+    const int64_t rowb = (int64_t)(k >> 8) * kBlockBytes;
+    const int cand[] = {1, 2, 3, 4, 6, 8};
+    for (int it : cand) {
+        if (it > max_it)
+            break;
+        const int64_t tiles = (n + it * rpi - 1) / (it * rpi);
+        if (8 * (int64_t)k <= (int64_t)it * rpi * nt * rowb && tiles * pairs >= cus)
+            return it;
+    }
+    return pick_iters(pairs, n, rpi, max_it);
+}
+
 template <int LPR, int NT, int EPI, int IT>
 static hipError_t go_rows(const GemvArgs &a, hipStream_t st) {
     constexpr int RPI = kThreads / LPR;
@@ -650,7 +672,9 @@ static hipError_t launch_lpr(GemvArgs a, bool bucketed, hipStream_t st) {
         hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a);
         return hipGetLastError();
     }
-    const int it = pick_iters(a.n_pairs + a.m_sh, a.n, RPI, NT == 2 ? 4 : 8);
+    const int max_it = NT == 2 ? 4 : 8;
+    const int it = a.vec ? pick_iters_staged(a.n_pairs + a.m_sh, a.n, RPI, max_it, a.k, NT)
+                         : pick_iters(a.n_pairs + a.m_sh, a.n, RPI, max_it);
     switch (it) {
     case 8: return go_rows<LPR, NT, EPI, (NT == 2 ? 4 : 8)>(a, st);
     case 6: return go_rows<LPR, NT, EPI, (NT == 2 ? 4 : 6)>(a, st);
