@@ -775,11 +775,15 @@ static hipError_t dc_lpr(const GemvArgs &a, const CombineArgs &cb, hipStream_t s
     if (forced > 0 && forced <= 64 && (forced * np + RPI - 1) / RPI <= 8)
         trt = forced;
     const int its = (trt * np + RPI - 1) / RPI;
-    if (its <= 1) return go_dc<LPR, 1>(a, cb, trt, st);
-    if (its <= 2) return go_dc<LPR, 2>(a, cb, trt, st);
-    if (its <= 4) return go_dc<LPR, 4>(a, cb, trt, st);
-    if (its <= 6) return go_dc<LPR, 6>(a, cb, trt, st);
-    return go_dc<LPR, 8>(a, cb, trt, st);
+    switch (its) {
+    case 1: return go_dc<LPR, 1>(a, cb, trt, st);
+    case 2: return go_dc<LPR, 2>(a, cb, trt, st);
+    case 3: return go_dc<LPR, 3>(a, cb, trt, st);
+    case 4: return go_dc<LPR, 4>(a, cb, trt, st);
+    case 5: return go_dc<LPR, 5>(a, cb, trt, st);
+    case 6: return go_dc<LPR, 6>(a, cb, trt, st);
+    default: return go_dc<LPR, 8>(a, cb, trt, st);
+    }
 }
 
 hipError_t launch_q4k_down_combine(const GemvLaunch &L, const float *h_mid, const float *route_w,
