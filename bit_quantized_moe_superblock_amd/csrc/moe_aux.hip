@@ -134,6 +134,11 @@ hipError_t launch_moe_bucket(const int32_t *ids, int64_t n_pairs, int64_t num_ex
     return hipGetLastError();
 }
 
+// One thread per output element.  The top_k expert rows and weights are all
+// loaded before the first use (slots past top_k re-load the last one, clamped,
+// and are skipped), so the loads are in flight together; the sum then runs in
+// slot order, one fma per slot, as the pages' combine does.
+template <int KMAX>
 __global__ __launch_bounds__(256) void k_moe_combine(const float *__restrict__ h_mid,
                                                      const float *__restrict__ eo,
                                                      const float *__restrict__ w,
@@ -145,14 +150,25 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float *__restrict__ h
     if (idx >= H * m)
         return;
     const int64_t t = idx / H, i = idx - t * H;
+    float e[KMAX], wv[KMAX];
+#pragma unroll
+    for (int s = 0; s < KMAX; s++) {
+        const int sc = s < K ? s : K - 1;
+        e[s] = eo[(t * K + sc) * H + i];
+        wv[s] = w[t * K + sc];
+    }
+    const float sh = mode != 0 ? shared[idx] : 0.0f;
+    const float lg = mode == 1 ? logit[t] : 0.0f;
     float acc = h_mid[idx];
-    for (int s = 0; s < K; s++)
-        acc = __builtin_fmaf(w[t * K + s], eo[(t * K + s) * H + i], acc);
+#pragma unroll
+    for (int s = 0; s < KMAX; s++)
+        if (s < K)
+            acc = __builtin_fmaf(wv[s], e[s], acc);
     if (mode == 1) {
-        const float g = 1.0f / (1.0f + expf(-logit[t]));
-        acc = __builtin_fmaf(g, shared[idx], acc);
+        const float g = 1.0f / (1.0f + expf(-lg));
+        acc = __builtin_fmaf(g, sh, acc);
     } else if (mode == 2) {
-        acc += shared[idx];
+        acc += sh;
     }
     out[idx] = acc;
 }
@@ -164,9 +180,14 @@ hipError_t launch_moe_combine(const float *h_mid, const float *expert_out, const
     const int64_t n = hidden * m;
     if (n == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, h_mid,
-                       expert_out, route_w, shared_out, shared_gate_logit, out, hidden, m,
-                       (int)top_k, shared_mode);
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (top_k <= 8)
+        hipLaunchKernelGGL(k_moe_combine<8>, grid, dim3(256), 0, st, h_mid, expert_out, route_w,
+                           shared_out, shared_gate_logit, out, hidden, m, (int)top_k, shared_mode);
+    else
+        hipLaunchKernelGGL(k_moe_combine<kMaxTopK>, grid, dim3(256), 0, st, h_mid, expert_out,
+                           route_w, shared_out, shared_gate_logit, out, hidden, m, (int)top_k,
+                           shared_mode);
     return hipGetLastError();
 }
 
