@@ -201,6 +201,38 @@ def time_eager(torch, fn, steps, warmup, start=0):
     return e0.elapsed_time(e1) / 1e3, time.perf_counter() - t0
 
 
+def run_walk(torch, q4, wl, replicas, walks, warmup):
+    """The dense Q4TiledP decode walk (one layer's q, k, v, o, gate, up and down
+    matvecs, then the head) over `replicas` device-encoded copies of its
+    tensors, rotated so that consecutive walks do not find them in cache.
+    Returns microseconds per walk and its tensor bytes."""
+    dev = torch.device("cuda")
+    shapes = [(rows, cols) for _, rows, cols, _ in wl.walk_tensors(1, True)]
+    reps = []
+    for r in range(replicas):
+        ts = []
+        for i, (rows, cols) in enumerate(shapes):
+            w = wl.device_normal((rows, cols), 0.02, seed=50000 + 100 * r + i)
+            t = torch.empty(q4.q4tp_tensor_bytes(rows, cols), dtype=torch.uint8, device=dev)
+            q4.q4tp_quantize(w, t, rows, cols)
+            del w
+            ts.append(t)
+        reps.append(ts)
+    x = wl.device_normal((wl.WALK_X_LEN,), 1.0, seed=59999)
+    ys = [torch.empty(rows, device=dev) for rows, _ in shapes]
+    torch.cuda.synchronize()
+
+    def walk(i):
+        ts = reps[i % replicas]
+        for (rows, cols), t, y in zip(shapes, ts, ys):
+            q4.q4tp_matvec(t, x, y, rows, cols)
+
+    g = capture(torch, walk, walks)
+    sec, _ = time_graph(torch, g, 4, warmup)
+    nbytes = sum(q4.q4tp_tensor_bytes(rows, cols) for rows, cols in shapes)
+    return sec / (4 * walks) * 1e6, nbytes
+
+
 def run_workload(torch, q4, wl, cfg, args, stacks=None):
     """Times exactly args.steps layers (and, separately, args.steps launches
     of the layer's first kernel) after args.warmup untimed ones."""
@@ -339,6 +371,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-m16", action="store_true")
+    ap.add_argument("--no-walk", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: every box here has one MI355X and this path has no "
@@ -363,6 +396,10 @@ def main():
         res16, _ = run_workload(torch, q4, wl, wl.CFG3, args, stacks)
         log(f"m=16: {res16['us_per_layer']:.2f} us/layer, {res16['gbs']:.1f} GB/s; gate/up "
             f"{res16['gate_up_us']:.2f} us, {res16['gate_up_gbs']:.1f} GB/s")
+    walk_us = None
+    if not args.no_walk:
+        walk_us, walk_bytes = run_walk(torch, q4, wl, 2, 32, 1)
+        log(f"walk: {walk_us:.2f} us/walk, {walk_bytes / walk_us / 1e3:.1f} GB/s")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, wl.CFG2, args.cpu_seconds)
@@ -415,6 +452,17 @@ def main():
             "bytes_per_layer": int(res16["bytes_per_layer"]),
             "gate_up_gbs": round(res16["gate_up_gbs"], 2),
             "gate_up_us": round(res16["gate_up_us"], 3),
+        }
+    if walk_us is not None:
+        line["walk"] = {
+            "workload": "dense Q4TiledP decode walk: one layer (q, k, v, o 4096x4096, gate and up "
+                        "14336x4096, down 4096x14336) and the head 32000x4096, 5-bit log-scale "
+                        "ladder, 2 tensor replicas rotated",
+            "kernel": "k_q4tp_matvec",
+            "us_per_walk": round(walk_us, 3),
+            "bytes_per_walk": int(walk_bytes),
+            "gbs": round(walk_bytes / walk_us / 1e3, 2),
+            "frac_hbm_peak": round(walk_bytes / walk_us / 1e3 / HBM_PEAK_GBS, 4),
         }
     print(json.dumps(line), flush=True)
 

@@ -10,18 +10,23 @@
 // y[r] = sum_g scale(r,g) * (sum_j nib*x[32g+j] - 8*sum_j x[32g+j]).
 //
 // LPR lanes (a power of two >= gpr, at most 256) cover a row, one 16-byte
-// group per lane per step; x is staged in LDS with per-group sums.  The group
-// scale uses the hardware exp2 (about one ulp), as the page's kernel does.
-#include "common.hpp"
-#include "launch.hpp"
+// group per lane (two when a row has more than 256 groups); x is staged in LDS
+// with per-group sums.  The group scale uses the hardware exp2 (about one
+// ulp), as the page's kernel does.
+#include "gemv_core.hpp"
 
 namespace q4k {
 
 // Group g's 32 activations start at 36*g floats in LDS (4 pad floats per
 // group keeps the 16-byte reads of neighbouring lanes in different banks).
-__device__ __forceinline__ int gpad(int i) { return i + ((i >> 5) << 2); }
-
-template <int LPR, int ITERS>
+//
+// A workgroup takes ITERS x RPI rows.  The loads are issued in this order and
+// waited for one by one: x (a thread per 32-float group, float4), then every
+// row's (base, step) word, code bytes and 16-byte groups (branch-free, clamped
+// indices).  x is committed to LDS with its group sums (ascending, one thread
+// per group) while the weights are in flight; LDS-only barriers leave them in
+// flight.  Lane u of a row takes groups u, u + LPR, ... (NG of them).
+template <int LPR, int NG, int ITERS, bool XV>
 __global__ __launch_bounds__(256) void k_q4tp_matvec(const uint8_t *__restrict__ t,
                                                      const float *__restrict__ x,
                                                      float *__restrict__ y, int rows, int cols) {
@@ -29,87 +34,125 @@ __global__ __launch_bounds__(256) void k_q4tp_matvec(const uint8_t *__restrict__
     constexpr int RPI = 256 / LPR;
     constexpr int WL = LPR < 64 ? LPR : 64;
     constexpr int WPR = LPR / WL;
+    constexpr int XU = (LPR * NG + 255) / 256;   // staging tasks per thread
     const int gpr = cols >> 5;
-    float *xs = lds;
-    float *sx = xs + cols + (gpr << 2);
-    float *red = sx + gpr;
+    float *red = lds;           // cross-wave row sums
+    float *xs = lds + 16;       // padded activations
+    float *sx = xs + 36 * gpr;  // group sums
     const int tid = threadIdx.x;
-    for (int i = tid; i < cols; i += 256)
-        xs[gpad(i)] = x[i];
-    __syncthreads();
-    for (int g = tid; g < gpr; g += 256) {
-        const float *p = xs + 36 * g;
-        float s = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 32; i++)
-            s += p[i];
-        sx[g] = s;
-    }
-    __syncthreads();
 
+    // 1. activations, ahead of everything else
+    float4 xv[XU][8];
+#pragma unroll
+    for (int k = 0; k < XU; k++) {
+        const int f = tid + 256 * k;
+        const int fc = f < gpr ? f : gpr - 1;
+        const float *src = x + 32 * fc;
+#pragma unroll
+        for (int q = 0; q < 8; q++)
+            xv[k][q] = XV ? *(const float4 *)(src + 4 * q)
+                          : make_float4(src[4 * q], src[4 * q + 1], src[4 * q + 2], src[4 * q + 3]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. the rows' parameters, codes and groups
     const int64_t params_off = (int64_t)rows * gpr * 16;
     const int64_t codes_off = params_off + (int64_t)rows * 4;
-    const int64_t stride = (5 * gpr + 7) >> 3;
+    const int stride = (5 * gpr + 7) >> 3;
     const int u = tid % LPR;
     const int rsub = tid / LPR;
     const int row0 = blockIdx.x * (ITERS * RPI);
+    uint32_t pb[ITERS], c0[ITERS][NG], c1[ITERS][NG];
+    uint4 qv[ITERS][NG];
 #pragma unroll
     for (int it = 0; it < ITERS; it++) {
-        const int r = row0 + it * RPI + rsub;
-        const bool rok = r < rows;
-        float acc = 0.0f;
-        if (rok) {
-            const uint32_t pb = *(const uint32_t *)(t + params_off + (int64_t)r * 4);
-            const float base = lo_half(pb), step = hi_half(pb);
-            const uint8_t *cp = t + codes_off + (int64_t)r * stride;
-            for (int g = u; g < gpr; g += LPR) {
-                const uint4 q = *(const uint4 *)(t + ((int64_t)r * gpr + g) * 16);
-                const int bit = 5 * g;
-                const int cb = bit >> 3, shf = bit & 7;
-                uint32_t cw = cp[cb];
-                if (shf > 3)
-                    cw |= (uint32_t)cp[cb + 1] << 8;
-                const uint32_t code = (cw >> shf) & 31u;
-                const float scale = exp2f(__builtin_fmaf((float)code, step, base));
-                const float4 *xv = (const float4 *)(xs + 36 * g);
-                // element 8d+e of dword d: even e in the low nibbles, odd in the high
-                float lo = 0.0f, hi = 0.0f;
-                const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+        const int r0 = row0 + it * RPI + rsub;
+        const int r = r0 < rows ? r0 : rows - 1;
+        pb[it] = *(const uint32_t *)(t + params_off + (int64_t)r * 4);
+        const uint8_t *cp = t + codes_off + (int64_t)r * stride;
 #pragma unroll
-                for (int d = 0; d < 4; d++) {
-                    const uint32_t v = w4[d], s = v >> 8;
-                    const float4 x0 = xv[2 * d], x1 = xv[2 * d + 1];
-                    const uint32_t r0 = v & 0x000F000Fu, r2 = s & 0x000F000Fu;
-                    const uint32_t r1 = v & 0x00F000F0u, r3 = s & 0x00F000F0u;
-                    lo = __builtin_fmaf(lo_half(r0), x0.x, lo);   // element 0
-                    hi = __builtin_fmaf(lo_half(r1), x0.y, hi);   // element 1
-                    lo = __builtin_fmaf(lo_half(r2), x0.z, lo);   // element 2
-                    hi = __builtin_fmaf(lo_half(r3), x0.w, hi);   // element 3
-                    lo = __builtin_fmaf(hi_half(r0), x1.x, lo);   // element 4
-                    hi = __builtin_fmaf(hi_half(r1), x1.y, hi);   // element 5
-                    lo = __builtin_fmaf(hi_half(r2), x1.z, lo);   // element 6
-                    hi = __builtin_fmaf(hi_half(r3), x1.w, hi);   // element 7
-                }
-                // lo = 2^-24 * sum over even elements, hi = 2^-20 * sum over odd ones
-                const float dot = __builtin_fmaf(lo, 16777216.0f, hi * 1048576.0f);
-                acc = __builtin_fmaf(scale, __builtin_fmaf(-8.0f, sx[g], dot), acc);
+        for (int j = 0; j < NG; j++) {
+            const int g0 = u + j * LPR;
+            const int g = g0 < gpr ? g0 : gpr - 1;
+            const int cb = (5 * g) >> 3;
+            c0[it][j] = cp[cb];
+            c1[it][j] = cp[cb + 1 < stride ? cb + 1 : cb];
+            qv[it][j] = *(const uint4 *)(t + ((int64_t)r * gpr + g) * 16);
+        }
+    }
+
+    // 3. activations into LDS, with their group sums
+#pragma unroll
+    for (int k = 0; k < XU; k++) {
+        const int f = tid + 256 * k;
+        if (f < gpr) {
+            float4 *d = (float4 *)(xs + 36 * f);
+            float sum = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 8; q++) {
+                d[q] = xv[k][q];
+                sum += xv[k][q].x;
+                sum += xv[k][q].y;
+                sum += xv[k][q].z;
+                sum += xv[k][q].w;
             }
+            sx[f] = sum;
+        }
+    }
+    lds_barrier();
+
+    // 4. rows
+#pragma unroll
+    for (int it = 0; it < ITERS; it++) {
+        const float base = lo_half(pb[it]), step = hi_half(pb[it]);
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NG; j++) {
+            const int g0 = u + j * LPR;
+            const bool gok = g0 < gpr;
+            const int g = gok ? g0 : gpr - 1;
+            const uint32_t code = ((c0[it][j] | (c1[it][j] << 8)) >> ((5 * g) & 7)) & 31u;
+            const float scale = exp2f(__builtin_fmaf((float)code, step, base));
+            const float4 *xp = (const float4 *)(xs + 36 * g);
+            // element 8d+e of dword d: even e in the low nibbles, odd in the high
+            float lo = 0.0f, hi = 0.0f;
+            const uint32_t w4[4] = {qv[it][j].x, qv[it][j].y, qv[it][j].z, qv[it][j].w};
+#pragma unroll
+            for (int d = 0; d < 4; d++) {
+                const uint32_t v = w4[d], sh = v >> 8;
+                const float4 x0 = xp[2 * d], x1 = xp[2 * d + 1];
+                const uint32_t r0 = v & 0x000F000Fu, r2 = sh & 0x000F000Fu;
+                const uint32_t r1 = v & 0x00F000F0u, r3 = sh & 0x00F000F0u;
+                lo = __builtin_fmaf(lo_half(r0), x0.x, lo);   // element 0
+                hi = __builtin_fmaf(lo_half(r1), x0.y, hi);   // element 1
+                lo = __builtin_fmaf(lo_half(r2), x0.z, lo);   // element 2
+                hi = __builtin_fmaf(lo_half(r3), x0.w, hi);   // element 3
+                lo = __builtin_fmaf(hi_half(r0), x1.x, lo);   // element 4
+                hi = __builtin_fmaf(hi_half(r1), x1.y, hi);   // element 5
+                lo = __builtin_fmaf(hi_half(r2), x1.z, lo);   // element 6
+                hi = __builtin_fmaf(hi_half(r3), x1.w, hi);   // element 7
+            }
+            // lo = 2^-24 * sum over even elements, hi = 2^-20 * sum over odd ones
+            const float dot = __builtin_fmaf(lo, 16777216.0f, hi * 1048576.0f);
+            const float part = scale * __builtin_fmaf(-8.0f, sx[g], dot);
+            acc += gok ? part : 0.0f;
         }
         acc = group_sum<WL>(acc);
         if constexpr (WPR > 1) {
             const int wave = tid >> 6;
             if ((tid & 63) == 0)
                 red[wave] = acc;
-            __syncthreads();
+            lds_barrier();
             if (u == 0) {
-                float s = red[wave];
+                float sum = red[wave];
                 for (int w = 1; w < WPR; w++)
-                    s += red[wave + w];
-                acc = s;
+                    sum += red[wave + w];
+                acc = sum;
             }
-            __syncthreads();
+            lds_barrier();
         }
-        if (u == 0 && rok)
+        const int r = row0 + it * RPI + rsub;
+        if (u == 0 && r < rows)
             y[r] = acc;
     }
 }
@@ -121,33 +164,55 @@ static int tp_lanes(int gpr) {
     return l;
 }
 
-template <int LPR>
+// Rows per workgroup: the fewest row groups whose weight bytes are at least
+// twice the staged activations (4 cols bytes, read from the cache by every
+// workgroup), at most 8 (4 with two groups per lane), while the grid still
+// gives every CU a workgroup.
+template <int LPR, int NG>
 static hipError_t tp_launch(const void *t, const float *x, float *y, int rows, int cols,
                             hipStream_t st) {
     constexpr int RPI = 256 / LPR;
     const int gpr = cols >> 5;
-    const size_t lds = (size_t)(cols + 4 * gpr + gpr + 8) * sizeof(float);
-    constexpr int IT = 2;
-    auto kern = k_q4tp_matvec<LPR, IT>;
-    if (lds > 65536)
-        hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds);
-    dim3 grid((rows + IT * RPI - 1) / (IT * RPI));
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const uint8_t *)t, x, y, rows, cols);
-    return hipGetLastError();
+    const int64_t row_bytes = (int64_t)gpr * 16 + 4 + ((5 * gpr + 7) >> 3);
+    const int64_t cus = cu_count();
+    constexpr int kMaxIt = NG == 1 ? 8 : 4;
+    int it = 1;
+    while (it < kMaxIt && (int64_t)it * RPI * row_bytes < 8 * (int64_t)cols &&
+           (int64_t)((rows + 2 * it * RPI - 1) / (2 * it * RPI)) >= cus)
+        it <<= 1;
+    const size_t lds = (size_t)(16 + 36 * gpr + gpr) * sizeof(float);
+    auto go = [&](auto kern, int iters) {
+        set_lds((const void *)kern, lds);
+        dim3 grid((rows + iters * RPI - 1) / (iters * RPI));
+        hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const uint8_t *)t, x, y, rows, cols);
+        return hipGetLastError();
+    };
+    // float4 activation loads need a 16-byte aligned x
+    const bool xv = ((uintptr_t)x & 15) == 0;
+    switch (it) {
+    case 1: return xv ? go(k_q4tp_matvec<LPR, NG, 1, true>, 1) : go(k_q4tp_matvec<LPR, NG, 1, false>, 1);
+    case 2: return xv ? go(k_q4tp_matvec<LPR, NG, 2, true>, 2) : go(k_q4tp_matvec<LPR, NG, 2, false>, 2);
+    case 4: return xv ? go(k_q4tp_matvec<LPR, NG, 4, true>, 4) : go(k_q4tp_matvec<LPR, NG, 4, false>, 4);
+    default:
+        return xv ? go(k_q4tp_matvec<LPR, NG, (NG == 1 ? 8 : 4), true>, kMaxIt)
+                  : go(k_q4tp_matvec<LPR, NG, (NG == 1 ? 8 : 4), false>, kMaxIt);
+    }
 }
 
 hipError_t launch_q4tp_matvec(const void *t, const float *x, float *y, int64_t rows,
                               int64_t cols, hipStream_t st) {
     const int gpr = (int)(cols >> 5);
     switch (tp_lanes(gpr)) {
-    case 4: return tp_launch<4>(t, x, y, (int)rows, (int)cols, st);
-    case 8: return tp_launch<8>(t, x, y, (int)rows, (int)cols, st);
-    case 16: return tp_launch<16>(t, x, y, (int)rows, (int)cols, st);
-    case 32: return tp_launch<32>(t, x, y, (int)rows, (int)cols, st);
-    case 64: return tp_launch<64>(t, x, y, (int)rows, (int)cols, st);
-    case 128: return tp_launch<128>(t, x, y, (int)rows, (int)cols, st);
-    default: return tp_launch<256>(t, x, y, (int)rows, (int)cols, st);
+    case 4: return tp_launch<4, 1>(t, x, y, (int)rows, (int)cols, st);
+    case 8: return tp_launch<8, 1>(t, x, y, (int)rows, (int)cols, st);
+    case 16: return tp_launch<16, 1>(t, x, y, (int)rows, (int)cols, st);
+    case 32: return tp_launch<32, 1>(t, x, y, (int)rows, (int)cols, st);
+    case 64: return tp_launch<64, 1>(t, x, y, (int)rows, (int)cols, st);
+    case 128: return tp_launch<128, 1>(t, x, y, (int)rows, (int)cols, st);
+    default:
+        if (gpr <= 256)
+            return tp_launch<256, 1>(t, x, y, (int)rows, (int)cols, st);
+        return tp_launch<256, 2>(t, x, y, (int)rows, (int)cols, st);
     }
 }
 
