@@ -205,7 +205,9 @@ def run_walk(torch, q4, wl, replicas, walks, warmup):
     """The dense Q4TiledP decode walk (one layer's q, k, v, o, gate, up and down
     matvecs, then the head) over `replicas` device-encoded copies of its
     tensors, rotated so that consecutive walks do not find them in cache.
-    Returns microseconds per walk and its tensor bytes."""
+    Timed twice: one launch per tensor, and with q|k|v and gate|up each merged
+    into one launch.  Returns (us per walk merged, us per walk one launch per
+    tensor, tensor bytes)."""
     dev = torch.device("cuda")
     shapes = [(rows, cols) for _, rows, cols, _ in wl.walk_tensors(1, True)]
     reps = []
@@ -227,10 +229,22 @@ def run_walk(torch, q4, wl, replicas, walks, warmup):
         for (rows, cols), t, y in zip(shapes, ts, ys):
             q4.q4tp_matvec(t, x, y, rows, cols)
 
+    # q|k|v, o, gate|up, down, head
+    groups = [[0, 1, 2], [3], [4, 5], [6], [7]]
+    ym = [torch.empty(sum(shapes[j][0] for j in grp), device=dev) for grp in groups]
+
+    def walk_merged(i):
+        ts = reps[i % replicas]
+        for grp, y in zip(groups, ym):
+            q4.q4tp_matvec_multi([ts[j] for j in grp], [shapes[j][0] for j in grp], x, y,
+                                 shapes[grp[0]][1])
+
     g = capture(torch, walk, walks)
     sec, _ = time_graph(torch, g, 4, warmup)
+    gm = capture(torch, walk_merged, walks)
+    sec_m, _ = time_graph(torch, gm, 4, warmup)
     nbytes = sum(q4.q4tp_tensor_bytes(rows, cols) for rows, cols in shapes)
-    return sec / (4 * walks) * 1e6, nbytes
+    return sec_m / (4 * walks) * 1e6, sec / (4 * walks) * 1e6, nbytes
 
 
 def run_workload(torch, q4, wl, cfg, args, stacks=None):
@@ -398,8 +412,9 @@ def main():
             f"{res16['gate_up_us']:.2f} us, {res16['gate_up_gbs']:.1f} GB/s")
     walk_us = None
     if not args.no_walk:
-        walk_us, walk_bytes = run_walk(torch, q4, wl, 2, 32, 1)
-        log(f"walk: {walk_us:.2f} us/walk, {walk_bytes / walk_us / 1e3:.1f} GB/s")
+        walk_us, walk_single_us, walk_bytes = run_walk(torch, q4, wl, 2, 32, 1)
+        log(f"walk: {walk_us:.2f} us/walk merged ({walk_bytes / walk_us / 1e3:.1f} GB/s), "
+            f"{walk_single_us:.2f} us one launch per tensor")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, wl.CFG2, args.cpu_seconds)
@@ -459,7 +474,9 @@ def main():
                         "14336x4096, down 4096x14336) and the head 32000x4096, 5-bit log-scale "
                         "ladder, 2 tensor replicas rotated",
             "kernel": "k_q4tp_matvec",
+            "launches": "q|k|v, o, gate|up, down, head (merged dispatches)",
             "us_per_walk": round(walk_us, 3),
+            "us_per_walk_one_launch_per_tensor": round(walk_single_us, 3),
             "bytes_per_walk": int(walk_bytes),
             "gbs": round(walk_bytes / walk_us / 1e3, 2),
             "frac_hbm_peak": round(walk_bytes / walk_us / 1e3 / HBM_PEAK_GBS, 4),

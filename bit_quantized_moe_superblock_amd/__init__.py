@@ -11,5 +11,5 @@ from ._lib import (  # noqa: F401
     Q4K_BUCKET_ON, Q4K_BUCKET_PREBUILT, Q4KError, moe_bucket, moe_bucket_workspace_bytes, moe_combine_residual,
     moe_expert_ffn, moe_layer_forward, moe_layer_workspace_bytes, moe_layer_workspace_init, q4k_abi_version, q4k_dequantize, q4k_matrix_bytes, q4k_moe_id_gemv,
     q4k_moe_gate_up_silu,
-    q4k_quantize, q4tp_matvec, q4tp_quantize, q4tp_tensor_bytes, status_string,
+    q4k_quantize, q4tp_matvec, q4tp_matvec_multi, q4tp_quantize, q4tp_tensor_bytes, status_string,
 )

@@ -19,6 +19,7 @@ Q4K_BUCKET_AUTO, Q4K_BUCKET_OFF, Q4K_BUCKET_ON, Q4K_BUCKET_PREBUILT = 0, 1, 2, 3
 MOE_SHARED_NONE, MOE_SHARED_SIGMOID, MOE_SHARED_UNSCALED = 0, 1, 2
 Q4K_BLOCK_WEIGHTS, Q4K_BLOCK_BYTES, Q4K_MAX_TOP_K = 256, 144, 16
 Q4K_MAX_IN, Q4K_MAX_EXPERTS, Q4K_MAX_PAIRS, Q4TP_MAX_COLS = 16384, 1023, 8192, 16384
+Q4TP_MAX_TENSORS = 3
 
 # name -> (restype, argtypes); mirrors include/q4kmoe.h
 _P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -43,6 +44,7 @@ SIGNATURES = {
     "moe_combine_residual": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
     "q4tp_tensor_bytes": (_I64, [_I64, _I64]),
     "q4tp_matvec": (_I, [_P, _P, _P, _I64, _I64, _P]),
+    "q4tp_matvec_multi": (_I, [_P, _P, _I, _P, _P, _I64, _P]),
     "q4tp_quantize": (_I, [_P, _P, _I64, _I64, _P]),
 }
 
@@ -187,6 +189,18 @@ def moe_combine_residual(h_mid, expert_out, route_w, shared_out, shared_gate_log
 
 def q4tp_matvec(tensor, x, y, rows: int, cols: int, stream=None):
     _call("q4tp_matvec", _ptr(tensor), _ptr(x), _ptr(y), rows, cols, _stream(stream))
+
+
+def q4tp_matvec_multi(tensors, rows, x, y, cols: int, stream=None):
+    """Merged matvec of up to three tensors of the same width against x; y
+    holds their outputs one after another.  `tensors` and `rows` are lists."""
+    n = len(tensors)
+    if len(rows) != n:
+        raise ValueError("tensors and rows differ in length")
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[_ptr(t) for t in tensors])
+    rws = (ctypes.c_int64 * max(n, 1))(*[int(r) for r in rows])
+    _call("q4tp_matvec_multi", ctypes.cast(ptrs, ctypes.c_void_p),
+          ctypes.cast(rws, ctypes.c_void_p), n, _ptr(x), _ptr(y), cols, _stream(stream))
 
 
 def q4tp_quantize(w, tensor, rows: int, cols: int, stream=None):

@@ -437,6 +437,27 @@ int q4tp_matvec(const void *tensor, const float *x, float *y, int64_t rows, int6
     return launched(launch_q4tp_matvec(tensor, x, y, rows, cols, as_stream(stream)));
 }
 
+int q4tp_matvec_multi(const void *const *tensors, const int64_t *rows, int n_tensors,
+                      const float *x, float *y, int64_t cols, void *stream) {
+    if (n_tensors < 1 || n_tensors > Q4TP_MAX_TENSORS || cols < 32 || cols % 32 ||
+        cols > Q4TP_MAX_COLS)
+        return Q4K_ERR_SHAPE;
+    if (!tensors || !rows || !x || !y || !aligned4(x) || !aligned4(y))
+        return Q4K_ERR_NULL;
+    int64_t total = 0;
+    for (int i = 0; i < n_tensors; i++) {
+        if (rows[i] < 1 || rows[i] > (1 << 30))
+            return Q4K_ERR_SHAPE;
+        total += rows[i];
+        if (!tensors[i] || !aligned16(tensors[i]))
+            return Q4K_ERR_NULL;
+    }
+    if (total > (1 << 30))
+        return Q4K_ERR_SHAPE;
+    return launched(launch_q4tp_matvec_multi(tensors, rows, n_tensors, x, y, cols,
+                                             as_stream(stream)));
+}
+
 int q4tp_quantize(const float *w, void *tensor, int64_t rows, int64_t cols, void *stream) {
     if (rows < 1 || rows > (1 << 30) || cols < 32 || cols % 32 || cols > Q4TP_MAX_COLS)
         return Q4K_ERR_SHAPE;

@@ -18,6 +18,7 @@ constexpr int kBlockWeights = 256;
 constexpr int kBlockBytes = 144;
 constexpr int kThreads = 256;   // threads of every GEMV workgroup (4 waves)
 constexpr int kMaxTopK = 16;    // largest top_k
+constexpr int kTpMaxSegs = 3;   // Q4TiledP tensors in one merged matvec launch
 constexpr int kBucketChunk = 8; // pairs per bucketed work item
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));

@@ -36,6 +36,8 @@ hipError_t launch_moe_combine(const float *h_mid, const float *expert_out, const
                               const float *shared_out, const float *shared_gate_logit, float *out,
                               int64_t hidden, int64_t m, int64_t top_k, int shared_mode,
                               hipStream_t st);
+hipError_t launch_q4tp_matvec_multi(const void *const *ts, const int64_t *rows, int nseg,
+                                    const float *x, float *y, int64_t cols, hipStream_t st);
 hipError_t launch_q4tp_matvec(const void *t, const float *x, float *y, int64_t rows,
                               int64_t cols, hipStream_t st);
 hipError_t launch_q4tp_quant(const float *w, void *t, int64_t rows, int64_t cols,

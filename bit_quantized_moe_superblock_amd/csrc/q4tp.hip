@@ -26,11 +26,31 @@ namespace q4k {
 // indices).  x is committed to LDS with its group sums (ascending, one thread
 // per group) while the weights are in flight; LDS-only barriers leave them in
 // flight.  Lane u of a row takes groups u, u + LPR, ... (NG of them).
+// Up to three tensors of the same width read the same x in one launch (the
+// merged q|k|v and gate|up dispatch); their outputs follow one another in y.
+// Workgroup tiles never straddle two tensors.
+struct TpSegs {
+    const uint8_t *t[kTpMaxSegs];
+    int rows[kTpMaxSegs];
+    int tile_end[kTpMaxSegs];   // cumulative workgroup count
+    int yoff[kTpMaxSegs];       // first output row
+    int nseg;
+};
+
 template <int LPR, int NG, int ITERS, bool XV>
-__global__ __launch_bounds__(256) void k_q4tp_matvec(const uint8_t *__restrict__ t,
-                                                     const float *__restrict__ x,
-                                                     float *__restrict__ y, int rows, int cols) {
+__global__ __launch_bounds__(256) void k_q4tp_matvec(TpSegs sg, const float *__restrict__ x,
+                                                     float *__restrict__ yall, int cols) {
     extern __shared__ float lds[];
+    // this workgroup's tensor (uniform scalar compares)
+    int seg = 0;
+#pragma unroll
+    for (int i = 1; i < kTpMaxSegs; i++)
+        if (i < sg.nseg && (int)blockIdx.x >= sg.tile_end[i - 1])
+            seg = i;
+    const uint8_t *__restrict__ t = sg.t[seg];
+    const int rows = sg.rows[seg];
+    float *__restrict__ y = yall + sg.yoff[seg];
+    const int tile = (int)blockIdx.x - (seg ? sg.tile_end[seg - 1] : 0);
     constexpr int RPI = 256 / LPR;
     constexpr int WL = LPR < 64 ? LPR : 64;
     constexpr int WPR = LPR / WL;
@@ -61,7 +81,7 @@ __global__ __launch_bounds__(256) void k_q4tp_matvec(const uint8_t *__restrict__
     const int stride = (5 * gpr + 7) >> 3;
     const int u = tid % LPR;
     const int rsub = tid / LPR;
-    const int row0 = blockIdx.x * (ITERS * RPI);
+    const int row0 = tile * (ITERS * RPI);
     uint32_t pb[ITERS], c0[ITERS][NG], c1[ITERS][NG];
     uint4 qv[ITERS][NG];
 #pragma unroll
@@ -169,22 +189,35 @@ static int tp_lanes(int gpr) {
 // workgroup), at most 8 (4 with two groups per lane), while the grid still
 // gives every CU a workgroup.
 template <int LPR, int NG>
-static hipError_t tp_launch(const void *t, const float *x, float *y, int rows, int cols,
-                            hipStream_t st) {
+static hipError_t tp_launch(const void *const *ts, const int64_t *rows, int nseg, const float *x,
+                            float *y, int cols, hipStream_t st) {
     constexpr int RPI = 256 / LPR;
     const int gpr = cols >> 5;
     const int64_t row_bytes = (int64_t)gpr * 16 + 4 + ((5 * gpr + 7) >> 3);
     const int64_t cus = cu_count();
+    int64_t total_rows = 0;
+    for (int i = 0; i < nseg; i++)
+        total_rows += rows[i];
     constexpr int kMaxIt = NG == 1 ? 8 : 4;
     int it = 1;
     while (it < kMaxIt && (int64_t)it * RPI * row_bytes < 8 * (int64_t)cols &&
-           (int64_t)((rows + 2 * it * RPI - 1) / (2 * it * RPI)) >= cus)
+           (total_rows + 2 * it * RPI - 1) / (2 * it * RPI) >= cus)
         it <<= 1;
     const size_t lds = (size_t)(16 + 36 * gpr + gpr) * sizeof(float);
     auto go = [&](auto kern, int iters) {
+        TpSegs sg{};
+        int tiles = 0, yoff = 0;
+        for (int i = 0; i < nseg; i++) {
+            sg.t[i] = (const uint8_t *)ts[i];
+            sg.rows[i] = (int)rows[i];
+            tiles += (int)((rows[i] + iters * RPI - 1) / (iters * RPI));
+            sg.tile_end[i] = tiles;
+            sg.yoff[i] = yoff;
+            yoff += (int)rows[i];
+        }
+        sg.nseg = nseg;
         set_lds((const void *)kern, lds);
-        dim3 grid((rows + iters * RPI - 1) / (iters * RPI));
-        hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const uint8_t *)t, x, y, rows, cols);
+        hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), lds, st, sg, x, y, cols);
         return hipGetLastError();
     };
     // float4 activation loads need a 16-byte aligned x
@@ -199,21 +232,27 @@ static hipError_t tp_launch(const void *t, const float *x, float *y, int rows, i
     }
 }
 
-hipError_t launch_q4tp_matvec(const void *t, const float *x, float *y, int64_t rows,
-                              int64_t cols, hipStream_t st) {
+hipError_t launch_q4tp_matvec_multi(const void *const *ts, const int64_t *rows, int nseg,
+                                    const float *x, float *y, int64_t cols, hipStream_t st) {
     const int gpr = (int)(cols >> 5);
+    const int c = (int)cols;
     switch (tp_lanes(gpr)) {
-    case 4: return tp_launch<4, 1>(t, x, y, (int)rows, (int)cols, st);
-    case 8: return tp_launch<8, 1>(t, x, y, (int)rows, (int)cols, st);
-    case 16: return tp_launch<16, 1>(t, x, y, (int)rows, (int)cols, st);
-    case 32: return tp_launch<32, 1>(t, x, y, (int)rows, (int)cols, st);
-    case 64: return tp_launch<64, 1>(t, x, y, (int)rows, (int)cols, st);
-    case 128: return tp_launch<128, 1>(t, x, y, (int)rows, (int)cols, st);
+    case 4: return tp_launch<4, 1>(ts, rows, nseg, x, y, c, st);
+    case 8: return tp_launch<8, 1>(ts, rows, nseg, x, y, c, st);
+    case 16: return tp_launch<16, 1>(ts, rows, nseg, x, y, c, st);
+    case 32: return tp_launch<32, 1>(ts, rows, nseg, x, y, c, st);
+    case 64: return tp_launch<64, 1>(ts, rows, nseg, x, y, c, st);
+    case 128: return tp_launch<128, 1>(ts, rows, nseg, x, y, c, st);
     default:
         if (gpr <= 256)
-            return tp_launch<256, 1>(t, x, y, (int)rows, (int)cols, st);
-        return tp_launch<256, 2>(t, x, y, (int)rows, (int)cols, st);
+            return tp_launch<256, 1>(ts, rows, nseg, x, y, c, st);
+        return tp_launch<256, 2>(ts, rows, nseg, x, y, c, st);
     }
+}
+
+hipError_t launch_q4tp_matvec(const void *t, const float *x, float *y, int64_t rows,
+                              int64_t cols, hipStream_t st) {
+    return launch_q4tp_matvec_multi(&t, &rows, 1, x, y, cols, st);
 }
 
 // ------------------------------------------------------------- encoder ----

@@ -61,6 +61,7 @@ enum { MOE_SHARED_NONE = 0, MOE_SHARED_SIGMOID = 1, MOE_SHARED_UNSCALED = 2 };
 #define Q4K_MAX_EXPERTS 1023  /* bucketing keeps E+1 buckets in one block  */
 #define Q4K_MAX_PAIRS 8192    /* m*top_k handled by one bucketing launch   */
 #define Q4TP_MAX_COLS 16384   /* largest Q4TiledP row                       */
+#define Q4TP_MAX_TENSORS 3    /* [CE] merged kernel: tensors per dispatch  */
 #define Q4K_BUCKET_CHUNK 8    /* pairs per bucketed work item               */
 #define MOE_LAYER_SYNC_BYTES 4096 /* synchronisation header of a layer workspace */
 #define MOE_LAYER_SYNC_TIMEOUT_WORD 576 /* 32-bit word of that header: barrier timed out */
@@ -238,6 +239,19 @@ int64_t q4tp_tensor_bytes(int64_t rows, int64_t cols);
  * x: [cols] fp32, y: [rows] fp32.  1 <= cols <= Q4TP_MAX_COLS. */
 int q4tp_matvec(const void *tensor, const float *x, float *y, int64_t rows, int64_t cols,
                 void *stream);
+
+/* The merged dispatch ([CE] main, walk mode `m`: q|k|v and gate|up each in
+ * one dispatch; merged kernel `hlfm` over up to three tensors of the same
+ * width): n_tensors (1..Q4TP_MAX_TENSORS) Q4TiledP tensors of the same cols
+ * against the same x.  tensors[i] (device pointer, 16-byte aligned) has
+ * rows[i] rows; tensors and rows are HOST arrays of n_tensors entries, read
+ * during the call.  y receives the outputs one tensor after another: rows[0]
+ * values of tensor 0, then tensor 1, ...  Each output equals that of a
+ * separate q4tp_matvec call bit for bit.  Errors: Q4K_ERR_SHAPE (n_tensors,
+ * any rows[i] < 1, the rows summing past 2^30, or cols as in q4tp_matvec),
+ * Q4K_ERR_NULL (a null or misaligned pointer). */
+int q4tp_matvec_multi(const void *const *tensors, const int64_t *rows, int n_tensors,
+                      const float *x, float *y, int64_t cols, void *stream);
 
 /* q4tp_quantize: fp32 [rows, cols] -> Q4TiledP.  The page prints no encoder;
  * reading: t_g = max|w|/7, lt_g = log2(t_g); base = fp16(min lt),

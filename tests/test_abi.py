@@ -43,7 +43,8 @@ def test_constants_match_header(lib):
                       ("Q4K_MAX_IN", _lib.Q4K_MAX_IN), ("Q4K_MAX_EXPERTS", _lib.Q4K_MAX_EXPERTS),
                       ("Q4K_MAX_PAIRS", _lib.Q4K_MAX_PAIRS), ("Q4TP_MAX_COLS", _lib.Q4TP_MAX_COLS),
                       ("Q4K_BUCKET_CHUNK", 8), ("MOE_LAYER_SYNC_BYTES", 4096),
-                      ("MOE_LAYER_SYNC_TIMEOUT_WORD", 576)]:
+                      ("MOE_LAYER_SYNC_TIMEOUT_WORD", 576),
+                      ("Q4TP_MAX_TENSORS", _lib.Q4TP_MAX_TENSORS)]:
         assert re.search(rf"#define {name} {val}\b", src), name
     assert q4.q4k_abi_version() == 2
 
@@ -125,6 +126,15 @@ def test_ffn_combine_bucket_q4tp_validation(lib):
     assert _err(m, FAKE, FAKE, FAKE, 4, 48) == _lib.Q4K_ERR_SHAPE
     assert _err(m, FAKE, FAKE, FAKE, 4, 16384 + 32) == _lib.Q4K_ERR_SHAPE
     assert _err(m, None, FAKE, FAKE, 4, 64) == _lib.Q4K_ERR_NULL
+    mm = q4.q4tp_matvec_multi
+    assert _err(mm, [], [], FAKE, FAKE, 64) == _lib.Q4K_ERR_SHAPE
+    assert _err(mm, [FAKE] * 4, [4] * 4, FAKE, FAKE, 64) == _lib.Q4K_ERR_SHAPE
+    assert _err(mm, [FAKE, FAKE], [4, 0], FAKE, FAKE, 64) == _lib.Q4K_ERR_SHAPE
+    assert _err(mm, [FAKE, FAKE], [4, 4], FAKE, FAKE, 48) == _lib.Q4K_ERR_SHAPE
+    assert _err(mm, [FAKE, FAKE], [1 << 30, 4], FAKE, FAKE, 64) == _lib.Q4K_ERR_SHAPE
+    assert _err(mm, [FAKE, None], [4, 4], FAKE, FAKE, 64) == _lib.Q4K_ERR_NULL
+    assert _err(mm, [FAKE, FAKE + 8], [4, 4], FAKE, FAKE, 64) == _lib.Q4K_ERR_NULL
+    assert _err(mm, [FAKE], [4], FAKE + 2, FAKE, 64) == _lib.Q4K_ERR_NULL
     assert _err(q4.q4k_quantize, FAKE, FAKE, 2, 300) == _lib.Q4K_ERR_SHAPE
     assert _err(q4.q4k_dequantize, FAKE, FAKE, -1) == _lib.Q4K_ERR_SHAPE
     assert _err(q4.q4tp_quantize, FAKE, FAKE, 2, 40) == _lib.Q4K_ERR_SHAPE

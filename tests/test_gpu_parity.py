@@ -454,6 +454,38 @@ def test_q4tp_unit_probe_and_ragged(dev):
         band(sync_np(y), oracle.q4tp_matvec(t, rows, cols, x), f"{rows}x{cols}")
 
 
+def test_q4tp_merged_dispatch_and_unaligned_x(dev):
+    """The merged dispatch (cortiq-engine mv_lab.rs main, walk mode m: up to
+    three tensors of one width against one x, outputs one after another)
+    gives the bits of separate calls and the oracle's values within the band;
+    so does an x that is only 4-byte aligned (the scalar activation loads)."""
+    g = np.random.default_rng(43)
+    for cols, rows in [(4096, (257, 64, 130)), (14336, (3, 9)), (96, (11, 1, 40)), (32, (5,))]:
+        say(f"q4tp merged {cols} cols, rows {rows}")
+        ts = [oracle.q4tp_quantize((g.standard_normal((r, cols)) * 0.02).astype(np.float32))
+              for r in rows]
+        x = g.standard_normal(cols + 1).astype(np.float32)
+        d_ts = [T(t, dev) for t in ts]
+        d_x = T(x, dev)
+        y = torch.full((sum(rows),), float("nan"), device=dev)
+        q4.q4tp_matvec_multi(d_ts, list(rows), d_x[:cols], y, cols)
+        y = sync_np(y)
+        off = 0
+        for t, r in zip(d_ts, rows):
+            ys = torch.empty(r, device=dev)
+            q4.q4tp_matvec(t, d_x[:cols], ys, r, cols)
+            assert np.array_equal(bits(y[off:off + r]), bits(sync_np(ys))), f"{cols}/{r}"
+            off += r
+        want = np.concatenate([oracle.q4tp_matvec(t, r, cols, x[:cols]) for t, r in zip(ts, rows)])
+        band(y, want, f"merged {cols}")
+        # x one float into its buffer: 4-byte aligned only
+        yu = torch.empty(sum(rows), device=dev)
+        q4.q4tp_matvec_multi(d_ts, list(rows), d_x[1:cols + 1], yu, cols)
+        wu = np.concatenate([oracle.q4tp_matvec(t, r, cols, x[1:cols + 1])
+                             for t, r in zip(ts, rows)])
+        band(sync_np(yu), wu, f"merged {cols}, unaligned x")
+
+
 # ------------------------------------------------------ whole-layer entry ----
 
 def _layer_gpu(dev, cfg, d_st, sd, a, ids, flag, shared=True):
