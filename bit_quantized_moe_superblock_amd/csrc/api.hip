@@ -348,11 +348,6 @@ int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
         L.shared_mode = shared_mode;
         return launched(launch_layer_m1(L, st));
     }
-    if (bucketed) {
-        rc = launched(launch_moe_bucket(ids, P, num_experts, bws, st));
-        if (rc)
-            return rc;
-    }
     GemvLaunch G{};
     G.w0 = w_gate;
     G.w1 = w_up;
@@ -374,9 +369,6 @@ int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
     G.inner = 0;
     G.outer_sh = hidden;
     G.fused_swiglu = true;
-    rc = launched(launch_q4k_gemv(G, st));
-    if (rc)
-        return rc;
     GemvLaunch D = G;
     D.w0 = w_down;
     D.w1 = nullptr;
@@ -392,6 +384,20 @@ int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
     D.inner = inter;
     D.outer_sh = inter;
     D.fused_swiglu = false;
+    // Bucketed layers build their chunk lists inside the two matrix-core
+    // launches when the sizes allow; otherwise one bucketing launch writes
+    // the list to the layer workspace (PREBUILT is treated as ON here).
+    if (bucketed && q4k_self_bucket_ok(G) && q4k_self_bucket_ok(D)) {
+        G.bucket_ws = D.bucket_ws = nullptr;
+        G.self_bucket = D.self_bucket = true;
+    } else if (bucketed) {
+        rc = launched(launch_moe_bucket(ids, P, num_experts, bws, st));
+        if (rc)
+            return rc;
+    }
+    rc = launched(launch_q4k_gemv(G, st));
+    if (rc)
+        return rc;
     if (!bucketed)
         return launched(launch_q4k_down_combine(D, h_mid, route_w, shared_gate_logit, out,
                                                 nullptr, shared_mode, st));

@@ -20,9 +20,17 @@ struct GemvLaunch {
     int64_t n, k, top_k, num_experts, n_pairs, m_sh;
     int64_t outer, inner, outer_sh;
     bool fused_swiglu;
+    bool self_bucket;          // bucketed mode with the chunks built in-kernel from ids
 };
 
+// Largest pair count and bucket count (num_experts + 1) of self-bucketing.
+constexpr int64_t kSelfBucketMaxPairs = 1024;
+constexpr int64_t kSelfBucketMaxBuckets = 1024;
+
 hipError_t launch_q4k_gemv(const GemvLaunch &L, hipStream_t st);
+// Whether L may run bucketed with self_bucket set: the matrix-core kernel
+// (enabled, 16-byte aligned activation rows) and the size limits above.
+bool q4k_self_bucket_ok(const GemvLaunch &L);
 // Down projection fused with the weighted residual combine, one workgroup row
 // of tiles per token (few tokens).  expert_out may be null.
 hipError_t launch_q4k_down_combine(const GemvLaunch &L, const float *h_mid, const float *route_w,

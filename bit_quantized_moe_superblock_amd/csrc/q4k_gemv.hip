@@ -727,13 +727,32 @@ static GemvArgs make_args(const GemvLaunch &L) {
     return a;
 }
 
+static bool mfma_enabled() {
+    static const bool mfma = env_int("Q4KMOE_MFMA", 1) != 0;
+    return mfma;
+}
+
+bool q4k_self_bucket_ok(const GemvLaunch &L) {
+    // Q4KMOE_SELF_BUCKET=0 keeps the separate bucketing launch (read per call)
+    const char *env = getenv("Q4KMOE_SELF_BUCKET");
+    if (env != nullptr && atoi(env) == 0)
+        return false;
+    return mfma_enabled() && make_args(L).vec && L.n_pairs <= kSelfBucketMaxPairs &&
+           L.num_experts + 1 <= kSelfBucketMaxBuckets;
+}
+
 hipError_t launch_q4k_gemv(const GemvLaunch &L, hipStream_t st) {
     const GemvArgs a = make_args(L);
+    if (L.self_bucket) {   // chunks built in-kernel: the matrix-core kernel only
+        if (!q4k_self_bucket_ok(L))
+            return hipErrorInvalidValue;
+        return launch_q4k_gemv_mfma(a, L.fused_swiglu, st);
+    }
     const bool bucketed = L.bucket_ws != nullptr;
     // Bucketed mode runs on the matrix cores unless Q4KMOE_MFMA=0 selects the
     // vector-unit kernels; the matrix-core kernel reads activations as float4,
     // so rows and strides must be 16-byte aligned.
-    static const bool mfma = env_int("Q4KMOE_MFMA", 1) != 0;
+    const bool mfma = mfma_enabled();
     if (bucketed && mfma && a.vec)
         return launch_q4k_gemv_mfma(a, L.fused_swiglu, st);
     if (L.fused_swiglu)

@@ -260,40 +260,20 @@ __device__ __forceinline__ void mfma_superblock(const MfmaTile (&t)[NT], const u
     }
 }
 
-// Grid (row tiles of 64, chunk slots + shared chunks).  Slot y < n_slots is
-// chunk y of the bucketing kernel's list (at most 8 pairs of one bucket);
-// slot n_slots + s is the shared expert's tokens 8 s .. 8 s + 7.
+// ------------------------------------------------------------ one item ---
+// Item = (chunk of at most kMP pairs of one bucket, 64-row tile).  pairs[i]
+// is the i-th pair of a routed chunk (ascending pair order); a shared chunk
+// is the shared expert's tokens first .. first + cnt - 1.  The first slab
+// starts with a barrier, so consecutive items of one workgroup may reuse the
+// LDS.
 template <int NT, int EPI, int SB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SB <= 4 ? 3 : 2)))
-void k_bucket_mfma(GemvArgs a, int n_slots) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds_b[];
-    fetch_args(a);
+__device__ __forceinline__ void mfma_item(const GemvArgs &a, bool shared, int bkt, int cnt,
+                                          const int32_t *pairs, int first, int row0,
+                                          uint8_t *lds_b) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int rl = lane & 15, g = lane >> 4;
     const int E = a.num_experts, P = a.n_pairs;
-    const int y = blockIdx.y;
-    const int32_t *ws = a.bucket;
-    const BucketView bv(ws, E, P);
-    const int32_t *pairs = bv.pairs;
-    int cnt, first, bkt;
-    bool shared;
-    if (y < n_slots) {
-        if (y >= *bv.n_chunks)
-            return;
-        bkt = bv.chunks[2 * y];
-        const int packed = bv.chunks[2 * y + 1];
-        first = packed & 0xFFFFFF;
-        cnt = packed >> 24;
-        shared = false;
-    } else {
-        const int s = y - n_slots;
-        first = s * kMP;
-        cnt = a.m_sh - first < kMP ? a.m_sh - first : kMP;
-        bkt = 0;
-        shared = true;
-    }
-    const int row0 = blockIdx.x * kMRows;
-    auto pair_q = [&](int i) { return shared ? P + first + i : pairs[first + i]; };
+    auto pair_q = [&](int i) { return shared ? P + first + i : pairs[i]; };
     if (!shared && bkt == E) {   // ids outside [0, E): zero rows
         for (int i = 0; i < cnt; i++) {
             float *out = a.dst + (int64_t)pair_q(i) * a.n;
@@ -314,74 +294,220 @@ void k_bucket_mfma(GemvArgs a, int n_slots) {
         wrow[NT - 1] = (shared ? a.s1 : a.w1 + (int64_t)bkt * mat) + (int64_t)r * rowb;
     const uint8_t *sxa = lds_b + (size_t)SB * 8 * kSubB;
     const int nsub_total = a.k >> 5;
+    const int gc = cnt;
+    auto x_of = [&](int i) { return pair_x_known(a, shared, pair_q(i)); };
+    // activation rows of this thread's staging tasks (pair = task / (8 SB),
+    // clamped to the chunk), looked up once
+    const float *xrow[XRegs<SB>::U];
+#pragma unroll
+    for (int u = 0; u < XRegs<SB>::U; u++) {
+        const int p = (tid + u * kThreads) / (SB * 8);
+        xrow[u] = x_of(p < gc ? p : gc - 1);
+    }
+    float yv[NT][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            yv[nt][i] = 0.0f;
+    for (int sb0 = 0; sb0 < nb; sb0 += SB) {
+        __syncthreads();   // the previous slab's (or item's) LDS is consumed
+        // weights of the slab's first superblocks in flight while staging
+        // (kDepth superblocks in flight; indices are constants once the
+        // loop is unrolled, so the tiles stay in registers)
+        MfmaTile tt[kDepth][NT];
+        auto issue = [&](int i) {
+            const int sb = sb0 + i < nb ? sb0 + i : nb - 1;   // clamped
+#pragma unroll
+            for (int nt = 0; nt < NT; nt++)
+                mfma_load(wrow[nt], sb, g, tt[i % kDepth][nt]);
+        };
+        XRegs<SB> xr;
+        mfma_x_issue<SB>(xrow, gc, sb0 * 8, nsub_total, xr);
+        // the activations ahead of the weights: staging waits on them alone
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < (SB < kDepth ? SB : kDepth); i++)
+            issue(i);
+        mfma_x_commit<SB>(xr, gc, sb0 * 8, nsub_total, lds_b);
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < SB; i++) {
+            if (sb0 + i < nb)   // uniform
+                mfma_superblock<NT>(tt[i % kDepth], lds_b, sxa, i, yv);
+            if (i + kDepth < SB)
+                issue(i + kDepth);
+        }
+    }
+    // hi half (D rows 0..7, lanes 0..31) plus lo half (rows 8..15, lanes
+    // 32..63)
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            yv[nt][j] += __shfl_xor(yv[nt][j], 32);
+    // D rows 4g .. 4g+3 (g < 2) are pairs 4g + j of the chunk; this lane's
+    // column is row r0
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int i = 4 * g + j;
+        if (g < 2 && i < gc && r0 < a.n) {
+            const int q = pair_q(i);
+            float *out = q < P ? a.dst + (int64_t)q * a.n : a.dst_sh + (int64_t)(q - P) * a.n;
+            float part[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; nt++)
+                part[nt] = yv[nt][j];
+            out[r0] = epilogue<EPI, NT>(part);
+        }
+    }
+}
 
-    {   // one chunk: at most kMP pairs
-        const int g0 = 0, gc = cnt;
-        auto x_of = [&](int i) { return pair_x_known(a, shared, pair_q(g0 + i)); };
-        // activation rows of this thread's staging tasks (pair = task / (8 SB),
-        // clamped to the chunk), looked up once
-        const float *xrow[XRegs<SB>::U];
+// Grid (row tiles of 64, chunk slots + shared chunks).  Slot y < n_slots is
+// chunk y of the bucketing kernel's list (at most 8 pairs of one bucket);
+// slot n_slots + s is the shared expert's tokens 8 s .. 8 s + 7.
+template <int NT, int EPI, int SB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SB <= 4 ? 3 : 2)))
+void k_bucket_mfma(GemvArgs a, int n_slots) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_b[];
+    fetch_args(a);
+    const int y = blockIdx.y;
+    if (y < n_slots) {
+        const BucketView bv(a.bucket, a.num_experts, a.n_pairs);
+        if (y >= *bv.n_chunks)
+            return;
+        const int bkt = bv.chunks[2 * y];
+        const int packed = bv.chunks[2 * y + 1];
+        mfma_item<NT, EPI, SB>(a, false, bkt, packed >> 24, bv.pairs + (packed & 0xFFFFFF), 0,
+                               blockIdx.x * kMRows, lds_b);
+    } else {
+        const int first = (y - n_slots) * kMP;
+        const int cnt = a.m_sh - first < kMP ? a.m_sh - first : kMP;
+        mfma_item<NT, EPI, SB>(a, true, 0, cnt, nullptr, first, blockIdx.x * kMRows, lds_b);
+    }
+}
+
+// ------------------------------------------------------- self-bucketing ---
+// The bucketing of the ids (moeflux expert_forward.rs, encode_moe_gather_id_fuse
+// step 1) done by every workgroup in LDS, so that a layer needs no separate
+// bucketing launch: histogram of the ids over E + 1 buckets (bucket E takes
+// ids outside [0, E)), chunks of at most kMP pairs per bucket in bucket order,
+// the pairs of a bucket in ascending pair order.  This is the chunk list the
+// bucketing kernel writes, in the same order, so an item computes exactly what
+// it computes from that list.  The grid is persistent: it holds only as many
+// workgroups as fit on the device at once (never more than there can be
+// items), and workgroup w takes items w, w + G, ... of the list, so no
+// workgroup is launched only to find that its slot is past the end of it.
+constexpr int kSelfMaxPairs = 4 * kThreads;    // pairs 4 tid .. 4 tid + 3 per thread
+constexpr int kSelfMaxBuckets = 4 * kThreads;  // buckets 4 tid .. 4 tid + 3 per thread
+// chunks: at most one partial chunk per non-empty bucket plus P / kMP full ones
+constexpr int kSelfMaxChunks = kSelfMaxBuckets + kSelfMaxPairs / kMP;
+static_assert(kSelfMaxPairs == kSelfBucketMaxPairs && kSelfMaxBuckets == kSelfBucketMaxBuckets,
+              "self-bucketing limits");
+static_assert(kSelfMaxBuckets * 4 <= mfma_lds_bytes(1), "self-bucketing scratch");
+
+// Exclusive sum over the workgroup of v (in thread order); wsum is 4 words of
+// LDS that no thread reads until this returns.
+__device__ __forceinline__ int block_exclusive_sum(int v, int *wsum) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int inc = v;
 #pragma unroll
-        for (int u = 0; u < XRegs<SB>::U; u++) {
-            const int p = (tid + u * kThreads) / (SB * 8);
-            xrow[u] = x_of(p < gc ? p : gc - 1);
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(inc, off, 64);
+        if (lane >= off)
+            inc += t;
+    }
+    if (lane == 63)
+        wsum[wave] = inc;
+    lds_barrier();
+    int base = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; w++)
+        base += w < wave ? wsum[w] : 0;
+    return base + inc - v;
+}
+
+// Chunk list entry: bucket (11 bits), chunk index within the bucket (13 bits),
+// pair count (<= kMP).
+__device__ __forceinline__ int chunk_pack(int b, int i, int c) { return b | (i << 11) | (c << 24); }
+
+template <int NT, int EPI, int SB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SB <= 4 ? 3 : 2)))
+void k_bucket_mfma_self(GemvArgs a, int tiles) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_b[];
+    __shared__ int chunk_list[kSelfMaxChunks];
+    __shared__ int chunk_pairs[kMP];
+    __shared__ int wsum[8];
+    __shared__ int n_chunks_lds;
+    fetch_args(a);
+    const int tid = threadIdx.x;
+    const int E = a.num_experts, P = a.n_pairs;
+    // 1. the bucket of each of this thread's pairs 4 tid .. 4 tid + 3 (-1 past
+    //    P), from clamped unconditional loads
+    int b[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int p = 4 * tid + j;
+        const int e = a.ids[p < P ? p : P - 1];
+        b[j] = p < P ? ((unsigned)e < (unsigned)E ? e : E) : -1;
+    }
+    // 2. histogram (scratch in the staging LDS, free until the first item)
+    int *counts = (int *)lds_b;
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+        counts[4 * tid + j] = 0;
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+        if (b[j] >= 0)
+            atomicAdd(&counts[b[j]], 1);
+    lds_barrier();
+    // 3. chunk list: buckets 4 tid .. 4 tid + 3, ceil(count / kMP) chunks each
+    int c[4], hs = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int bb = 4 * tid + j;
+        c[j] = bb <= E ? counts[bb] : 0;
+        hs += (c[j] + kMP - 1) / kMP;
+    }
+    int run = block_exclusive_sum(hs, wsum);
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+        for (int i = 0; i * kMP < c[j]; i++) {
+            const int n = c[j] - i * kMP < kMP ? c[j] - i * kMP : kMP;
+            chunk_list[run++] = chunk_pack(4 * tid + j, i, n);
         }
-        float yv[NT][4];
-#pragma unroll
-        for (int nt = 0; nt < NT; nt++)
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                yv[nt][i] = 0.0f;
-        for (int sb0 = 0; sb0 < nb; sb0 += SB) {
-            __syncthreads();   // the previous slab's LDS is consumed
-            // weights of the slab's first superblocks in flight while staging
-            // (kDepth superblocks in flight; indices are constants once the
-            // loop is unrolled, so the tiles stay in registers)
-            MfmaTile tt[kDepth][NT];
-            auto issue = [&](int i) {
-                const int sb = sb0 + i < nb ? sb0 + i : nb - 1;   // clamped
-#pragma unroll
-                for (int nt = 0; nt < NT; nt++)
-                    mfma_load(wrow[nt], sb, g, tt[i % kDepth][nt]);
-            };
-            XRegs<SB> xr;
-            mfma_x_issue<SB>(xrow, gc, sb0 * 8, nsub_total, xr);
-            // the activations ahead of the weights: staging waits on them alone
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < (SB < kDepth ? SB : kDepth); i++)
-                issue(i);
-            mfma_x_commit<SB>(xr, gc, sb0 * 8, nsub_total, lds_b);
-            lds_barrier();
-#pragma unroll
-            for (int i = 0; i < SB; i++) {
-                if (sb0 + i < nb)   // uniform
-                    mfma_superblock<NT>(tt[i % kDepth], lds_b, sxa, i, yv);
-                if (i + kDepth < SB)
-                    issue(i + kDepth);
-            }
-        }
-        // hi half (D rows 0..7, lanes 0..31) plus lo half (rows 8..15, lanes
-        // 32..63)
-#pragma unroll
-        for (int nt = 0; nt < NT; nt++)
+    if (tid == kThreads - 1)
+        n_chunks_lds = run;
+    lds_barrier();
+    const int n_chunks = n_chunks_lds;
+    const int n_items = (n_chunks + (a.m_sh + kMP - 1) / kMP) * tiles;
+    // 4. the items of this workgroup
+    for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+        const int y = it / tiles, x = it - y * tiles;
+        if (y < n_chunks) {
+            const int e = chunk_list[y];
+            const int bkt = e & 0x7FF, i0 = ((e >> 11) & 0x1FFF) * kMP, cnt = e >> 24;
+            // ranks of the bucket's pairs (ascending pair order); the
+            // previous item has read chunk_pairs before the scan's barrier
+            int f = 0;
 #pragma unroll
             for (int j = 0; j < 4; j++)
-                yv[nt][j] += __shfl_xor(yv[nt][j], 32);
-        // D rows 4g .. 4g+3 (g < 2) are pairs g0 + 4g + j; this lane's column
-        // is row r0
+                f += b[j] == bkt ? 1 : 0;
+            int rank = block_exclusive_sum(f, wsum + 4);
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int i = 4 * g + j;
-            if (g < 2 && i < gc && r0 < a.n) {
-                const int q = pair_q(g0 + i);
-                float *out = q < P ? a.dst + (int64_t)q * a.n : a.dst_sh + (int64_t)(q - P) * a.n;
-                float part[NT];
-#pragma unroll
-                for (int nt = 0; nt < NT; nt++)
-                    part[nt] = yv[nt][j];
-                out[r0] = epilogue<EPI, NT>(part);
-            }
+            for (int j = 0; j < 4; j++)
+                if (b[j] == bkt) {
+                    if (rank >= i0 && rank < i0 + kMP)
+                        chunk_pairs[rank - i0] = 4 * tid + j;
+                    rank++;
+                }
+            lds_barrier();
+            mfma_item<NT, EPI, SB>(a, false, bkt, cnt, chunk_pairs, 0, x * kMRows, lds_b);
+        } else {
+            const int first = (y - n_chunks) * kMP;
+            const int cnt = a.m_sh - first < kMP ? a.m_sh - first : kMP;
+            mfma_item<NT, EPI, SB>(a, true, 0, cnt, nullptr, first, x * kMRows, lds_b);
         }
     }
 }
@@ -390,13 +516,27 @@ void k_bucket_mfma(GemvArgs a, int n_slots) {
 
 template <int NT, int EPI, int SB>
 static hipError_t go_mfma(const GemvArgs &a, hipStream_t st) {
-    auto kern = k_bucket_mfma<NT, EPI, SB>;
-    const size_t lds = set_lds((const void *)kern, mfma_lds_bytes(SB));
     // chunks of the list: at most one partial chunk per non-empty bucket
     const int64_t nb_max = a.n_pairs < (int64_t)a.num_experts + 1 ? a.n_pairs : a.num_experts + 1;
     const int n_slots = (int)(nb_max + a.n_pairs / kMP);
     const int sh_groups = (a.m_sh + kMP - 1) / kMP;
-    dim3 grid((a.n + kMRows - 1) / kMRows, n_slots + sh_groups);
+    const int tiles = (a.n + kMRows - 1) / kMRows;
+    if (a.bucket == nullptr) {   // self-bucketing, persistent grid
+        auto kern = k_bucket_mfma_self<NT, EPI, SB>;
+        const size_t lds = set_lds((const void *)kern, mfma_lds_bytes(SB));
+        int fit = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, (const void *)kern, kThreads,
+                                                         lds) != hipSuccess || fit < 1)
+            fit = 1;
+        const int64_t items = (int64_t)(n_slots + sh_groups) * tiles;
+        const int64_t cap = (int64_t)fit * cu_count();
+        hipLaunchKernelGGL(kern, dim3((unsigned)(items < cap ? items : cap)), dim3(kThreads),
+                           lds, st, a, tiles);
+        return hipGetLastError();
+    }
+    auto kern = k_bucket_mfma<NT, EPI, SB>;
+    const size_t lds = set_lds((const void *)kern, mfma_lds_bytes(SB));
+    dim3 grid(tiles, n_slots + sh_groups);
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a, n_slots);
     return hipGetLastError();
 }

@@ -198,9 +198,14 @@ int moe_expert_ffn(const void *w_gate, const void *w_up, const void *w_down,
  *   shared with a kernel that held its CUs); the output of that call is then
  *   not valid.  The rest is scratch.  Calls that may overlap in time must not
  *   share a workspace.
- *   bucket_flag: AUTO picks by m; OFF forces the few-token path; ON (or
- *   PREBUILT, treated as ON) forces bucketing.  Output bits do not depend on
- *   the path. */
+ *   bucket_flag: AUTO picks by m (bucketed when m > 2); OFF forces the
+ *   few-token path; ON (or PREBUILT, treated as ON) forces bucketing.  AUTO
+ *   gives the same bits as the flag that selects the same path; the other
+ *   path differs only by rounding (fp32 tolerance).  A bucketed layer with
+ *   m*top_k <= 1024 pairs builds its expert buckets inside the gate/up and
+ *   down launches (each workgroup from the ids, in LDS) rather than in a
+ *   separate bucketing launch; the chunks, and so the output bits, are the
+ *   same either way. */
 int64_t moe_layer_workspace_bytes(int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
                                   int64_t top_k);
 /* Zeroes the synchronisation header of a layer workspace (an asynchronous

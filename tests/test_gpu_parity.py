@@ -604,6 +604,96 @@ def test_layer_invalid_ids_and_token_mode_edges(dev):
 
 
 @pytest.fixture
+def no_self_bucket():
+    """Keeps the separate bucketing launch in bucketed layers for one call."""
+    def run(fn):
+        old = os.environ.get("Q4KMOE_SELF_BUCKET")
+        os.environ["Q4KMOE_SELF_BUCKET"] = "0"
+        try:
+            return fn()
+        finally:
+            if old is None:
+                del os.environ["Q4KMOE_SELF_BUCKET"]
+            else:
+                os.environ["Q4KMOE_SELF_BUCKET"] = old
+    return run
+
+
+def _layer_raw(dev, st, sh, h, hm, ids, rw, lg, H, I, E, m, K, mode, flag=q4.Q4K_BUCKET_ON):
+    wsb = q4.moe_layer_workspace_bytes(H, I, E, m, K)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    out = torch.empty(m, H, device=dev)
+    q4.moe_layer_forward(*st, *sh, h, hm, ids, rw, lg, out, H, I, E, m, K, mode, flag, ws, wsb)
+    return sync_np(out)
+
+
+def test_self_bucketed_layer_equals_bucketing_launch(dev, no_self_bucket):
+    """Bucketed layers build their chunk lists inside the matrix-core launches;
+    the result must equal, bit for bit, the same layer with the separate
+    bucketing launch (same chunks, same pairs, same order), and the oracle
+    within the band.  Cases: Zipf routing at m = 16; one hot bucket spanning
+    many chunks plus invalid ids; and the limits, 1024 pairs over 1023 experts
+    (1024 buckets)."""
+    # the decode workload at m = 16 (Zipf ids)
+    cfg = wl.CFG3
+    H, I, E, K, m = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.m
+    say(f"self-bucketed layer {cfg.name}")
+    a, ids, d_st, _ = _ffn_case(cfg, dev)
+    sd, _ = _shared_stacks(cfg, dev)
+    selfb = _layer_gpu(dev, cfg, d_st, sd, a, ids, q4.Q4K_BUCKET_ON)
+    viaws = no_self_bucket(lambda: _layer_gpu(dev, cfg, d_st, sd, a, ids, q4.Q4K_BUCKET_ON))
+    assert np.array_equal(bits(selfb), bits(viaws))
+    # one hot bucket of 90 pairs (12 chunks), two invalid ids, m = 24
+    g = np.random.default_rng(61)
+    H, I, E, K, m = 512, 256, 6, 4, 24
+    say(f"self-bucketed layer, hot bucket H={H} I={I} E={E} K={K} m={m}")
+    st = [np.concatenate(quantize_many([(g.standard_normal((r, c)) * 0.05).astype(np.float32)
+                                        for _ in range(E)]))
+          for r, c in [(I, H), (I, H), (H, I)]]
+    sh = [oracle.q4k_quantize((g.standard_normal((r, c)) * 0.05).astype(np.float32))
+          for r, c in [(I, H), (I, H), (H, I)]]
+    h = g.standard_normal((m, H)).astype(np.float32)
+    hm = g.standard_normal((m, H)).astype(np.float32)
+    ids2 = np.full(m * K, 2, np.int32)
+    ids2[g.choice(m * K, 4, replace=False)] = [0, 5, 1, 3]
+    ids2[7], ids2[50] = E + 1, -3
+    rw = g.random(m * K).astype(np.float32)
+    lg = g.standard_normal(m).astype(np.float32)
+    _, _, _, eo = oracle.moe_expert_ffn(*st, E, H, I, h, ids2, m, K)
+    _, _, _, so = oracle.moe_expert_ffn(*sh, 1, H, I, h, np.zeros(m, np.int32), m, 1)
+    want = oracle.moe_combine_residual(hm, eo, rw, so, lg, H, m, K, 1)
+    args = ([T(x, dev) for x in st], [T(x, dev) for x in sh], T(h, dev), T(hm, dev),
+            T(ids2, dev), T(rw, dev), T(lg, dev), H, I, E, m, K, 1)
+    selfb = _layer_raw(dev, *args)
+    viaws = no_self_bucket(lambda: _layer_raw(dev, *args))
+    band(selfb, want, "self-bucketed, hot bucket")
+    assert np.array_equal(bits(selfb), bits(viaws))
+    # the limits: 1024 pairs, 1023 experts (device-encoded weights; a property
+    # of the HIP path alone, so no oracle inputs come from it)
+    H, I, E, K, m = 256, 256, 1023, 8, 128
+    say(f"self-bucketed layer at its limits H={H} I={I} E={E} K={K} m={m}")
+    st = []
+    for t, (r, c, ne) in enumerate([(I, H, E), (I, H, E), (H, I, E), (I, H, 1), (I, H, 1),
+                                     (H, I, 1)]):
+        w = wl.device_normal((ne * r, c), 0.02, seed=7000 + t)
+        b = torch.empty(ne * q4.q4k_matrix_bytes(r, c), dtype=torch.uint8, device=dev)
+        q4.q4k_quantize(w, b, ne * r, c)
+        st.append(b)
+    ids3 = g.integers(0, E, m * K).astype(np.int32)
+    ids3[:40] = 17                                        # one bucket of 5 chunks
+    h = g.standard_normal((m, H)).astype(np.float32)
+    hm = g.standard_normal((m, H)).astype(np.float32)
+    rw = g.random(m * K).astype(np.float32)
+    lg = g.standard_normal(m).astype(np.float32)
+    args = (st[:3], st[3:], T(h, dev), T(hm, dev), T(ids3, dev), T(rw, dev), T(lg, dev),
+            H, I, E, m, K, 1)
+    selfb = _layer_raw(dev, *args)
+    viaws = no_self_bucket(lambda: _layer_raw(dev, *args))
+    assert np.isfinite(selfb).all()
+    assert np.array_equal(bits(selfb), bits(viaws))
+
+
+@pytest.fixture
 def one_launch_layer():
     """Selects the opt-in one-launch single-token layer for one test."""
     old = os.environ.get("Q4KMOE_FUSED_LAYER")
