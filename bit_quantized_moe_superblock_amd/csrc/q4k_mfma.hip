@@ -363,30 +363,6 @@ __device__ __forceinline__ void mfma_item(const GemvArgs &a, bool shared, int bk
     }
 }
 
-// Grid (row tiles of 64, chunk slots + shared chunks).  Slot y < n_slots is
-// chunk y of the bucketing kernel's list (at most 8 pairs of one bucket);
-// slot n_slots + s is the shared expert's tokens 8 s .. 8 s + 7.
-template <int NT, int EPI, int SB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SB <= 4 ? 3 : 2)))
-void k_bucket_mfma(GemvArgs a, int n_slots) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds_b[];
-    fetch_args(a);
-    const int y = blockIdx.y;
-    if (y < n_slots) {
-        const BucketView bv(a.bucket, a.num_experts, a.n_pairs);
-        if (y >= *bv.n_chunks)
-            return;
-        const int bkt = bv.chunks[2 * y];
-        const int packed = bv.chunks[2 * y + 1];
-        mfma_item<NT, EPI, SB>(a, false, bkt, packed >> 24, bv.pairs + (packed & 0xFFFFFF), 0,
-                               blockIdx.x * kMRows, lds_b);
-    } else {
-        const int first = (y - n_slots) * kMP;
-        const int cnt = a.m_sh - first < kMP ? a.m_sh - first : kMP;
-        mfma_item<NT, EPI, SB>(a, true, 0, cnt, nullptr, first, blockIdx.x * kMRows, lds_b);
-    }
-}
-
 // ------------------------------------------------------- self-bucketing ---
 // The bucketing of the ids (moeflux expert_forward.rs, encode_moe_gather_id_fuse
 // step 1) done by every workgroup in LDS, so that a layer needs no separate
@@ -394,10 +370,7 @@ void k_bucket_mfma(GemvArgs a, int n_slots) {
 // ids outside [0, E)), chunks of at most kMP pairs per bucket in bucket order,
 // the pairs of a bucket in ascending pair order.  This is the chunk list the
 // bucketing kernel writes, in the same order, so an item computes exactly what
-// it computes from that list.  The grid is persistent: it holds only as many
-// workgroups as fit on the device at once (never more than there can be
-// items), and workgroup w takes items w, w + G, ... of the list, so no
-// workgroup is launched only to find that its slot is past the end of it.
+// it computes from that list.
 constexpr int kSelfMaxPairs = 4 * kThreads;    // pairs 4 tid .. 4 tid + 3 per thread
 constexpr int kSelfMaxBuckets = 4 * kThreads;  // buckets 4 tid .. 4 tid + 3 per thread
 // chunks: at most one partial chunk per non-empty bucket plus P / kMP full ones
@@ -431,9 +404,17 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int *wsum) {
 // pair count (<= kMP).
 __device__ __forceinline__ int chunk_pack(int b, int i, int c) { return b | (i << 11) | (c << 24); }
 
+// Persistent grid over the items (chunk, 64-row tile), chunk-major, the shared
+// expert's chunks of 8 tokens after the routed ones.  The host cannot know the
+// length of the chunk list, so a grid with one workgroup per possible item
+// would mostly be workgroups that find their slot past its end; instead the
+// grid holds as many workgroups as are resident at once and workgroup w takes
+// items w, w + G, ...  With a bucket workspace the chunk list and pair lists
+// come from it (the bucketing kernel's output); without one the workgroup
+// builds them (self-bucketing).
 template <int NT, int EPI, int SB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SB <= 4 ? 3 : 2)))
-void k_bucket_mfma_self(GemvArgs a, int tiles) {
+void k_bucket_mfma(GemvArgs a, int tiles) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_b[];
     __shared__ int chunk_list[kSelfMaxChunks];
     __shared__ int chunk_pairs[kMP];
@@ -442,52 +423,72 @@ void k_bucket_mfma_self(GemvArgs a, int tiles) {
     fetch_args(a);
     const int tid = threadIdx.x;
     const int E = a.num_experts, P = a.n_pairs;
-    // 1. the bucket of each of this thread's pairs 4 tid .. 4 tid + 3 (-1 past
-    //    P), from clamped unconditional loads
-    int b[4];
+    const bool self = a.bucket == nullptr;
+    const BucketView bv(self ? chunk_list : a.bucket, E, P);   // workspace mode only
+    // 1. self-bucketing: the bucket of each of this thread's pairs
+    //    4 tid .. 4 tid + 3 (-1 past P), from clamped unconditional loads
+    int b[4] = {-1, -1, -1, -1};
+    int n_chunks;
+    if (self) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int p = 4 * tid + j;
-        const int e = a.ids[p < P ? p : P - 1];
-        b[j] = p < P ? ((unsigned)e < (unsigned)E ? e : E) : -1;
-    }
-    // 2. histogram (scratch in the staging LDS, free until the first item)
-    int *counts = (int *)lds_b;
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-        counts[4 * tid + j] = 0;
-    lds_barrier();
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-        if (b[j] >= 0)
-            atomicAdd(&counts[b[j]], 1);
-    lds_barrier();
-    // 3. chunk list: buckets 4 tid .. 4 tid + 3, ceil(count / kMP) chunks each
-    int c[4], hs = 0;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int bb = 4 * tid + j;
-        c[j] = bb <= E ? counts[bb] : 0;
-        hs += (c[j] + kMP - 1) / kMP;
-    }
-    int run = block_exclusive_sum(hs, wsum);
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-        for (int i = 0; i * kMP < c[j]; i++) {
-            const int n = c[j] - i * kMP < kMP ? c[j] - i * kMP : kMP;
-            chunk_list[run++] = chunk_pack(4 * tid + j, i, n);
+        for (int j = 0; j < 4; j++) {
+            const int p = 4 * tid + j;
+            const int e = a.ids[p < P ? p : P - 1];
+            b[j] = p < P ? ((unsigned)e < (unsigned)E ? e : E) : -1;
         }
-    if (tid == kThreads - 1)
-        n_chunks_lds = run;
-    lds_barrier();
-    const int n_chunks = n_chunks_lds;
+        // 2. histogram (scratch in the staging LDS, free until the first item)
+        int *counts = (int *)lds_b;
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            counts[4 * tid + j] = 0;
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            if (b[j] >= 0)
+                atomicAdd(&counts[b[j]], 1);
+        lds_barrier();
+        // 3. chunk list: buckets 4 tid .. 4 tid + 3, ceil(count / kMP) chunks each
+        int c[4], hs = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int bb = 4 * tid + j;
+            c[j] = bb <= E ? counts[bb] : 0;
+            hs += (c[j] + kMP - 1) / kMP;
+        }
+        int run = block_exclusive_sum(hs, wsum);
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            for (int i = 0; i * kMP < c[j]; i++) {
+                const int n = c[j] - i * kMP < kMP ? c[j] - i * kMP : kMP;
+                chunk_list[run++] = chunk_pack(4 * tid + j, i, n);
+            }
+        if (tid == kThreads - 1)
+            n_chunks_lds = run;
+        lds_barrier();
+        n_chunks = n_chunks_lds;
+    } else {
+        n_chunks = *bv.n_chunks;
+    }
     const int n_items = (n_chunks + (a.m_sh + kMP - 1) / kMP) * tiles;
     // 4. the items of this workgroup
     for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
         const int y = it / tiles, x = it - y * tiles;
-        if (y < n_chunks) {
+        const bool shared = y >= n_chunks;
+        int bkt = 0, cnt, first = 0;
+        const int32_t *pl = chunk_pairs;
+        if (shared) {
+            first = (y - n_chunks) * kMP;
+            cnt = a.m_sh - first < kMP ? a.m_sh - first : kMP;
+        } else if (!self) {
+            bkt = bv.chunks[2 * y];
+            const int packed = bv.chunks[2 * y + 1];
+            cnt = packed >> 24;
+            pl = bv.pairs + (packed & 0xFFFFFF);
+        } else {
             const int e = chunk_list[y];
-            const int bkt = e & 0x7FF, i0 = ((e >> 11) & 0x1FFF) * kMP, cnt = e >> 24;
+            bkt = e & 0x7FF;
+            cnt = e >> 24;
+            const int i0 = ((e >> 11) & 0x1FFF) * kMP;
             // ranks of the bucket's pairs (ascending pair order); the
             // previous item has read chunk_pairs before the scan's barrier
             int f = 0;
@@ -503,12 +504,8 @@ void k_bucket_mfma_self(GemvArgs a, int tiles) {
                     rank++;
                 }
             lds_barrier();
-            mfma_item<NT, EPI, SB>(a, false, bkt, cnt, chunk_pairs, 0, x * kMRows, lds_b);
-        } else {
-            const int first = (y - n_chunks) * kMP;
-            const int cnt = a.m_sh - first < kMP ? a.m_sh - first : kMP;
-            mfma_item<NT, EPI, SB>(a, true, 0, cnt, nullptr, first, x * kMRows, lds_b);
         }
+        mfma_item<NT, EPI, SB>(a, shared, bkt, cnt, pl, first, x * kMRows, lds_b);
     }
 }
 
@@ -521,23 +518,19 @@ static hipError_t go_mfma(const GemvArgs &a, hipStream_t st) {
     const int n_slots = (int)(nb_max + a.n_pairs / kMP);
     const int sh_groups = (a.m_sh + kMP - 1) / kMP;
     const int tiles = (a.n + kMRows - 1) / kMRows;
-    if (a.bucket == nullptr) {   // self-bucketing, persistent grid
-        auto kern = k_bucket_mfma_self<NT, EPI, SB>;
-        const size_t lds = set_lds((const void *)kern, mfma_lds_bytes(SB));
-        int fit = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, (const void *)kern, kThreads,
-                                                         lds) != hipSuccess || fit < 1)
-            fit = 1;
-        const int64_t items = (int64_t)(n_slots + sh_groups) * tiles;
-        const int64_t cap = (int64_t)fit * cu_count();
-        hipLaunchKernelGGL(kern, dim3((unsigned)(items < cap ? items : cap)), dim3(kThreads),
-                           lds, st, a, tiles);
-        return hipGetLastError();
-    }
     auto kern = k_bucket_mfma<NT, EPI, SB>;
     const size_t lds = set_lds((const void *)kern, mfma_lds_bytes(SB));
-    dim3 grid(tiles, n_slots + sh_groups);
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a, n_slots);
+    int fit = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, (const void *)kern, kThreads, lds) !=
+            hipSuccess ||
+        fit < 1)
+        fit = 1;
+    // as many workgroups as are resident at once, never more than the items
+    // the longest possible list gives
+    const int64_t items = (int64_t)(n_slots + sh_groups) * tiles;
+    const int64_t cap = (int64_t)fit * cu_count();
+    hipLaunchKernelGGL(kern, dim3((unsigned)(items < cap ? items : cap)), dim3(kThreads), lds, st,
+                       a, tiles);
     return hipGetLastError();
 }
 
