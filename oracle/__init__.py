@@ -1,4 +1,5 @@
-"""CPU oracle for the Q4_K MoE expert path and the Q4TiledP dense matvec.
+"""CPU oracle for the Q4_K MoE expert path, the Q4TiledP dense matvec and the
+MLX affine 4-bit expert codec.
 
 TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` are the only callers.  The product library
@@ -72,6 +73,13 @@ def _load():
         "orc_q4tp_matvec": (ctypes.c_int, [P, I64, I64, P, P]),
         "orc_q4tp_matvec_one": (ctypes.c_float, [P, I64, I64, P, I64]),
         "orc_q4tp_quantize": (ctypes.c_int, [P, I64, I64, P]),
+        "orc_bf16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
+        "orc_f32_to_bf16": (ctypes.c_uint16, [ctypes.c_float]),
+        "orc_mlx4_nibble": (ctypes.c_int, [P, I64]),
+        "orc_mlx4_dequantize": (None, [P, P, P, I64, I64, P]),
+        "orc_mlx4_quantize": (ctypes.c_int, [P, I64, I64, P, P, P]),
+        "orc_mlx4_moe_id_gemv": (ctypes.c_int, [P, I64, I64, I64, I64, I64, I64, I64, P, P,
+                                                I64, I64, I64, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -256,3 +264,52 @@ def q4tp_matvec(t: np.ndarray, rows: int, cols: int, x: np.ndarray) -> np.ndarra
 
 def q4tp_matvec_one(t: np.ndarray, rows: int, cols: int, x: np.ndarray, r: int) -> float:
     return float(_load().orc_q4tp_matvec_one(_ptr(t), rows, cols, _ptr(x), r))
+
+
+# ------------------------------------------------------ MLX affine 4-bit ----
+
+MLX_GROUP = 64
+
+
+def bf16_to_f32(h: int) -> float:
+    return float(_load().orc_bf16_to_f32(int(h)))
+
+
+def f32_to_bf16(x: float) -> int:
+    return int(_load().orc_f32_to_bf16(float(x)))
+
+
+def mlx4_nibble(packed_row: np.ndarray, c: int) -> int:
+    return int(_load().orc_mlx4_nibble(_ptr(_c(packed_row, np.uint8)), c))
+
+
+def mlx4_quantize(w: np.ndarray):
+    """fp32 [n, k] -> (packed uint8 [n, k/2], scales uint16 [n, k/64], biases uint16 [n, k/64])."""
+    w = _c(w, np.float32)
+    n, k = w.shape
+    packed = np.zeros((n, k // 2), np.uint8)
+    scales = np.zeros((n, k // MLX_GROUP), np.uint16)
+    biases = np.zeros((n, k // MLX_GROUP), np.uint16)
+    _check(_load().orc_mlx4_quantize(_ptr(w), n, k, _ptr(packed), _ptr(scales), _ptr(biases)),
+           "mlx4_quantize")
+    return packed, scales, biases
+
+
+def mlx4_dequantize(packed, scales, biases, n: int, k: int) -> np.ndarray:
+    packed, scales, biases = _c(packed, np.uint8), _c(scales, np.uint16), _c(biases, np.uint16)
+    out = np.zeros((n, k), np.float32)
+    _load().orc_mlx4_dequantize(_ptr(packed), _ptr(scales), _ptr(biases), n, k, _ptr(out))
+    return out
+
+
+def mlx4_moe_id_gemv(base: np.ndarray, expert_stride: int, packed_off: int, scales_off: int,
+                     biases_off: int, num_experts: int, n: int, k: int, src1: np.ndarray,
+                     ids: np.ndarray, m: int, top_k: int, outer: int, inner: int) -> np.ndarray:
+    """dst [m*top_k, n] of the id-GEMV over MLX 4-bit experts laid out in blocks of
+    expert_stride bytes at base (offsets of the sub-tensors inside a block)."""
+    base, src1, ids = _c(base, np.uint8), _c(src1, np.float32), _c(ids, np.int32)
+    out = np.zeros((m * top_k, n), np.float32)
+    _check(_load().orc_mlx4_moe_id_gemv(_ptr(base), expert_stride, packed_off, scales_off,
+                                        biases_off, num_experts, n, k, _ptr(src1), _ptr(ids), m,
+                                        top_k, outer, inner, _ptr(out)), "mlx4_moe_id_gemv")
+    return out

@@ -1,6 +1,6 @@
 /*
- * q4k_oracle.c -- plain CPU oracle for the Q4_K MoE expert path and the
- * Q4TiledP dense matvec.
+ * q4k_oracle.c -- plain CPU oracle for the Q4_K MoE expert path, the
+ * Q4TiledP dense matvec and the MLX affine 4-bit expert codec.
  *
  * TEST INFRASTRUCTURE ONLY.  The test-suite, the smoke check and the CPU
  * baseline leg of the benchmark are the only callers allowed.  The GPU library
@@ -564,5 +564,146 @@ int orc_q4tp_quantize(const float *w, int64_t rows, int64_t cols, uint8_t *out)
     }
     free(lt);
     free(has);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* MLX affine 4-bit expert codec ([MF] module doc "4-bit only";             */
+/* gpu_expert_forward and encode_matvec: GROUP_SIZE passed to the matvec;   */
+/* encode_moe_gather_id_fuse: per-row strides nb01_w = K/2 bytes of packed  */
+/* weights and nb01_s = (K/64)*2 bytes of bf16 scales, the same for the     */
+/* bf16 biases, sub-tensors at packed/scales/biases offsets inside an       */
+/* expert block of expert_stride bytes).                                    */
+/*                                                                          */
+/* Readings (the pages give the strides, not the bit-level format): the     */
+/* public MLX affine layout, group of 64 weights along a row, weight        */
+/* w = scale*q + bias with q the 4-bit code; row r's packed byte j holds    */
+/* weight 2j in its low nibble and 2j+1 in its high nibble (MLX packs eight */
+/* codes per little-endian 32-bit word, lowest code in the lowest bits).    */
+/* ------------------------------------------------------------------------ */
+
+#define ORC_MLX_GROUP 64
+
+/* bfloat16 <-> binary32 from the format definition: bf16 is the top half of */
+/* a binary32, so widening is exact; narrowing rounds to nearest, ties to   */
+/* even, NaN stays a (quiet) NaN.  Pinned against torch's bfloat16.         */
+float orc_bf16_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+uint16_t orc_f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+        return (uint16_t)((u >> 16) | 0x0040u);               /* quiet NaN */
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;                                        /* RNE       */
+    return (uint16_t)(u >> 16);
+}
+
+int orc_mlx4_nibble(const uint8_t *row, int64_t c)
+{
+    uint8_t b = row[c / 2];
+    return (c & 1) ? (b >> 4) : (b & 15);
+}
+
+/* Dequantize one [n, k] matrix.  w = scale*q + bias evaluated in float:    */
+/* scale has 8 significant bits and q 4, so scale*q is exact and the one    */
+/* rounding is that of the sum (the correctly rounded value of the exact    */
+/* scale*q + bias, whatever the evaluation order).  Parity: bit-exact.      */
+void orc_mlx4_dequantize(const uint8_t *packed, const uint16_t *scales, const uint16_t *biases,
+                         int64_t n, int64_t k, float *out)
+{
+    int64_t gpr = k / ORC_MLX_GROUP;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t c = 0; c < k; c++) {
+            float s = orc_bf16_to_f32(scales[r * gpr + c / ORC_MLX_GROUP]);
+            float b = orc_bf16_to_f32(biases[r * gpr + c / ORC_MLX_GROUP]);
+            float p = s * (float)orc_mlx4_nibble(packed + r * (k / 2), c);
+            out[r * k + c] = p + b;
+        }
+}
+
+/* Encoder (the pages print none; reading, a plain min/max affine code per  */
+/* group, decided in float with IEEE operations): lo = min w, hi = max w,   */
+/* scale = bf16((hi - lo)/15), bias = bf16(lo),                             */
+/* q = clamp(rne((w - bias)/scale), 0, 15), q = 0 where scale is 0.         */
+/* Its reconstruction quality against MLX's own quantizer is parity        */
+/* unpinned (MLX is not here); its bytes are compared with the GPU's.       */
+int orc_mlx4_quantize(const float *w, int64_t n, int64_t k, uint8_t *packed, uint16_t *scales,
+                      uint16_t *biases)
+{
+    if (n <= 0 || k <= 0 || k % ORC_MLX_GROUP)
+        return ORC_EINVAL;
+    int64_t gpr = k / ORC_MLX_GROUP;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t g = 0; g < gpr; g++) {
+            const float *x = w + r * k + g * ORC_MLX_GROUP;
+            float lo = x[0], hi = x[0];
+            for (int j = 1; j < ORC_MLX_GROUP; j++) {
+                lo = x[j] < lo ? x[j] : lo;
+                hi = x[j] > hi ? x[j] : hi;
+            }
+            float d = hi - lo;
+            uint16_t sh = orc_f32_to_bf16(d / 15.0f);
+            uint16_t bh = orc_f32_to_bf16(lo);
+            float s = orc_bf16_to_f32(sh), b = orc_bf16_to_f32(bh);
+            scales[r * gpr + g] = sh;
+            biases[r * gpr + g] = bh;
+            uint8_t *row = packed + r * (k / 2) + g * (ORC_MLX_GROUP / 2);
+            for (int j = 0; j < ORC_MLX_GROUP; j += 2) {
+                int q[2];
+                for (int h = 0; h < 2; h++) {
+                    float t = (x[j + h] - b) / s;
+                    q[h] = s == 0.0f ? 0 : clampi((int)rintf(t), 0, 15);
+                }
+                row[j / 2] = (uint8_t)(q[0] | (q[1] << 4));
+            }
+        }
+    return ORC_OK;
+}
+
+/* id-GEMV over MLX 4-bit experts ([MF] encode_moe_gather_id_fuse: src0 =  */
+/* expert base, expert e's block at e*expert_stride, its packed weights,    */
+/* scales and biases at the given offsets inside the block; [FK] module     */
+/* doc for the pair walk: pair p = token*top_k + slot, activation row at    */
+/* src1 + token*outer + slot*inner).  Ids outside [0, num_experts): zero    */
+/* rows.  Definition: dequantize the row, dot in double, ascending column.  */
+int orc_mlx4_moe_id_gemv(const uint8_t *base, int64_t expert_stride, int64_t packed_off,
+                         int64_t scales_off, int64_t biases_off, int64_t num_experts, int64_t n,
+                         int64_t k, const float *src1, const int32_t *ids, int64_t m,
+                         int64_t top_k, int64_t outer, int64_t inner, float *dst)
+{
+    if (k <= 0 || k % ORC_MLX_GROUP || n <= 0 || m < 0 || top_k <= 0 || num_experts <= 0)
+        return ORC_EINVAL;
+    float *tmp = (float *)malloc((size_t)k * sizeof(float));
+    if (!tmp)
+        return ORC_ENOMEM;
+    int64_t gpr = k / ORC_MLX_GROUP;
+    for (int64_t p = 0; p < m * top_k; p++) {
+        int64_t t = p / top_k, s = p % top_k;
+        int64_t e = ids[p];
+        const float *x = src1 + t * outer + s * inner;
+        for (int64_t r = 0; r < n; r++) {
+            if (e < 0 || e >= num_experts) {
+                dst[p * n + r] = 0.0f;
+                continue;
+            }
+            const uint8_t *blk = base + e * expert_stride;
+            orc_mlx4_dequantize(blk + packed_off + r * (k / 2),
+                                (const uint16_t *)(blk + scales_off) + r * gpr,
+                                (const uint16_t *)(blk + biases_off) + r * gpr, 1, k, tmp);
+            double acc = 0.0;
+            for (int64_t c = 0; c < k; c++)
+                acc += (double)tmp[c] * (double)x[c];
+            dst[p * n + r] = (float)acc;
+        }
+    }
+    free(tmp);
     return ORC_OK;
 }
