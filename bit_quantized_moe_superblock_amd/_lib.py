@@ -20,6 +20,7 @@ MOE_SHARED_NONE, MOE_SHARED_SIGMOID, MOE_SHARED_UNSCALED = 0, 1, 2
 Q4K_BLOCK_WEIGHTS, Q4K_BLOCK_BYTES, Q4K_MAX_TOP_K = 256, 144, 16
 Q4K_MAX_IN, Q4K_MAX_EXPERTS, Q4K_MAX_PAIRS, Q4TP_MAX_COLS = 16384, 1023, 8192, 16384
 Q4TP_MAX_TENSORS = 3
+MLX4_GROUP = 64
 
 # name -> (restype, argtypes); mirrors include/q4kmoe.h
 _P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -46,6 +47,11 @@ SIGNATURES = {
     "q4tp_matvec": (_I, [_P, _P, _P, _I64, _I64, _P]),
     "q4tp_matvec_multi": (_I, [_P, _P, _I, _P, _P, _I64, _P]),
     "q4tp_quantize": (_I, [_P, _P, _I64, _I64, _P]),
+    "mlx4_matrix_bytes": (_I64, [_I64, _I64]),
+    "mlx4_dequantize": (_I, [_P, _P, _P, _P, _I64, _I64, _P]),
+    "mlx4_quantize": (_I, [_P, _P, _P, _P, _I64, _I64, _P]),
+    "mlx4_moe_id_gemv": (_I, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _I64, _I64,
+                              _I64, _I64, _I64, _P]),
 }
 
 
@@ -205,3 +211,26 @@ def q4tp_matvec_multi(tensors, rows, x, y, cols: int, stream=None):
 
 def q4tp_quantize(w, tensor, rows: int, cols: int, stream=None):
     _call("q4tp_quantize", _ptr(w), _ptr(tensor), rows, cols, _stream(stream))
+
+
+def mlx4_matrix_bytes(n: int, k: int) -> int:
+    return load().mlx4_matrix_bytes(n, k)
+
+
+def mlx4_dequantize(packed, scales, biases, out, n: int, k: int, stream=None):
+    _call("mlx4_dequantize", _ptr(packed), _ptr(scales), _ptr(biases), _ptr(out), n, k,
+          _stream(stream))
+
+
+def mlx4_quantize(w, packed, scales, biases, n: int, k: int, stream=None):
+    _call("mlx4_quantize", _ptr(w), _ptr(packed), _ptr(scales), _ptr(biases), n, k,
+          _stream(stream))
+
+
+def mlx4_moe_id_gemv(expert_base, expert_stride: int, packed_off: int, scales_off: int,
+                     biases_off: int, src1, ids, dst, n: int, k: int, m: int, top_k: int,
+                     src1_outer_stride: int, src1_inner_stride: int, num_experts: int,
+                     stream=None):
+    _call("mlx4_moe_id_gemv", _ptr(expert_base), expert_stride, packed_off, scales_off,
+          biases_off, _ptr(src1), _ptr(ids), _ptr(dst), n, k, m, top_k, src1_outer_stride,
+          src1_inner_stride, num_experts, _stream(stream))

@@ -15,6 +15,7 @@ hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool aligned2(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
 
 int launched(hipError_t e) { return e == hipSuccess ? Q4K_OK : Q4K_ERR_LAUNCH; }
 
@@ -470,6 +471,77 @@ int q4tp_quantize(const float *w, void *tensor, int64_t rows, int64_t cols, void
     if (!w || !tensor || !aligned16(tensor) || !aligned4(w))
         return Q4K_ERR_NULL;
     return launched(launch_q4tp_quant(w, tensor, rows, cols, as_stream(stream)));
+}
+
+int64_t mlx4_matrix_bytes(int64_t n, int64_t k) {
+    if (n < 0 || k < MLX4_GROUP || k % MLX4_GROUP)
+        return -1;
+    return n * k / 2 + 2 * (n * (k / MLX4_GROUP) * 2);
+}
+
+int mlx4_dequantize(const void *packed, const void *scales, const void *biases, float *out,
+                    int64_t n, int64_t k, void *stream) {
+    if (n < 0 || n > (1 << 30) || k < MLX4_GROUP || k % MLX4_GROUP || k > Q4K_MAX_IN)
+        return Q4K_ERR_SHAPE;
+    if (n == 0)
+        return Q4K_OK;
+    if (!packed || !scales || !biases || !out || !aligned16(packed) || !aligned2(scales) ||
+        !aligned2(biases) || !aligned16(out))
+        return Q4K_ERR_NULL;
+    return launched(launch_mlx4_dequant(packed, scales, biases, out, n * (k / MLX4_GROUP),
+                                        as_stream(stream)));
+}
+
+int mlx4_quantize(const float *w, void *packed, void *scales, void *biases, int64_t n, int64_t k,
+                  void *stream) {
+    if (n < 0 || n > (1 << 30) || k < MLX4_GROUP || k % MLX4_GROUP || k > Q4K_MAX_IN)
+        return Q4K_ERR_SHAPE;
+    if (n == 0)
+        return Q4K_OK;
+    if (!w || !packed || !scales || !biases || !aligned4(w) || !aligned16(packed) ||
+        !aligned2(scales) || !aligned2(biases))
+        return Q4K_ERR_NULL;
+    return launched(launch_mlx4_quant(w, packed, scales, biases, n * (k / MLX4_GROUP),
+                                      as_stream(stream)));
+}
+
+int mlx4_moe_id_gemv(const void *expert_base, int64_t expert_stride, int64_t packed_off,
+                     int64_t scales_off, int64_t biases_off, const float *src1,
+                     const int32_t *ids, float *dst, int64_t n, int64_t k, int64_t m,
+                     int64_t top_k, int64_t src1_outer_stride, int64_t src1_inner_stride,
+                     int64_t num_experts, void *stream) {
+    if (n < 1 || n > (1 << 30) || k < MLX4_GROUP || k % MLX4_GROUP || k > Q4K_MAX_IN || m < 1 ||
+        top_k < 1 || top_k > Q4K_MAX_TOP_K || num_experts < 1 || m * top_k > 65535)
+        return Q4K_ERR_SHAPE;
+    // the three sub-tensors must lie inside one expert block
+    const int64_t pbytes = n * k / 2, sbytes = n * (k / MLX4_GROUP) * 2;
+    if (expert_stride < 0 || packed_off < 0 || scales_off < 0 || biases_off < 0 ||
+        packed_off + pbytes > expert_stride || scales_off + sbytes > expert_stride ||
+        biases_off + sbytes > expert_stride)
+        return Q4K_ERR_SHAPE;
+    if (src1_outer_stride < 0 || src1_inner_stride < 0)
+        return Q4K_ERR_STRIDE;
+    if (!expert_base || !src1 || !ids || !dst || !aligned16(expert_base) ||
+        expert_stride % 16 || packed_off % 16 || scales_off % 2 || biases_off % 2 ||
+        !aligned4(src1) || !aligned4(ids) || !aligned4(dst))
+        return Q4K_ERR_NULL;
+    Mlx4Launch L{};
+    L.base = expert_base;
+    L.expert_stride = expert_stride;
+    L.packed_off = packed_off;
+    L.scales_off = scales_off;
+    L.biases_off = biases_off;
+    L.src1 = src1;
+    L.ids = ids;
+    L.dst = dst;
+    L.n = n;
+    L.k = k;
+    L.m = m;
+    L.top_k = top_k;
+    L.num_experts = num_experts;
+    L.outer = src1_outer_stride;
+    L.inner = src1_inner_stride;
+    return launched(launch_mlx4_gemv(L, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -67,6 +67,22 @@ struct LayerLaunch {
 bool layer_m1_supported(int64_t hidden, int64_t inter, int64_t top_k, int has_shared);
 hipError_t launch_layer_m1(const LayerLaunch &L, hipStream_t st);
 
+// MLX affine 4-bit id-GEMV (mlx4.hip): expert e's block at base + e*expert_stride,
+// its packed weights, scales and biases at the offsets inside the block.
+struct Mlx4Launch {
+    const void *base;
+    int64_t expert_stride, packed_off, scales_off, biases_off;
+    const float *src1;
+    const int32_t *ids;
+    float *dst;
+    int64_t n, k, m, top_k, num_experts, outer, inner;
+};
+hipError_t launch_mlx4_gemv(const Mlx4Launch &L, hipStream_t st);
+hipError_t launch_mlx4_dequant(const void *packed, const void *scales, const void *biases,
+                               float *out, int64_t groups, hipStream_t st);
+hipError_t launch_mlx4_quant(const float *w, void *packed, void *scales, void *biases,
+                             int64_t groups, hipStream_t st);
+
 // Workspace of the bucketing kernel in int32 words (layout in q4kmoe.h).
 inline int64_t bucket_ws_words(int64_t n_pairs, int64_t num_experts) {
     return (num_experts + 1) + (num_experts + 2) + n_pairs + (num_experts + 1) + 1 + 1 +

@@ -1,0 +1,262 @@
+// MLX affine 4-bit expert codec on gfx950: dequantizer, encoder and the
+// id-GEMV over expert blocks.
+//
+// Format (moeflux expert_forward.rs, "4-bit only" and the gather dispatch's
+// strides: K/2 bytes of packed weights per row, K/64 bf16 scales and as many
+// bf16 biases per row; the bit layout is MLX's): groups of 64 weights along a
+// row, w = scale * q + bias, row byte j holding weight 2j in its low nibble
+// and 2j+1 in its high nibble.  An expert's packed weights, scales and biases
+// sit at byte offsets inside its block; expert e's block starts at
+// e * expert_stride (the gather dispatch's nb02).
+//
+// id-GEMV: one workgroup per (row tile, pair), as the Q4_K pair mode.  A lane
+// owns one group of one row: two 16-byte loads of its 32 packed bytes, its
+// scale and bias.  The activation row is staged once per workgroup in LDS
+// (64 floats per lane, padded by 4 so lanes' reads fall in different banks)
+// with its 32-float sums.  The nibbles become fp16 subnormals by masking
+// (low nibbles q 2^-24, high nibbles q 2^-20) and feed v_fma_mix_f32, so the
+// group's sum q.x costs one instruction per weight; then
+//     row value = sum over groups of scale * (q.x) + bias * (sum of x),
+// reduced across the row's lanes with DPP.
+#include "gemv_core.hpp"
+
+namespace q4k {
+
+constexpr int kMlxGroup = 64;
+
+struct Mlx4Args {
+    const uint8_t *base;                       // expert 0's block
+    int64_t stride, packed_off, scales_off, biases_off;
+    const float *src1;
+    const int32_t *ids;
+    float *dst;                                // [n_pairs, n]
+    int64_t outer, inner;
+    int n, k, top_k, num_experts;
+    int vec;                                   // activation rows 16-byte aligned
+};
+
+__device__ __forceinline__ float bf16_val(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+        return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// sum over the 64 weights of one group of q * x, from its 32 packed bytes and
+// the group's 64 staged activations
+__device__ __forceinline__ float group_qx(const uint4 qa, const uint4 qb, const float *xr) {
+    const uint32_t w[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 8; d++) {
+        // dword d = bytes 4d..4d+3 = weights 8d..8d+7
+        const float4 xa = *(const float4 *)(xr + 8 * d);
+        const float4 xb = *(const float4 *)(xr + 8 * d + 4);
+        const uint32_t v = w[d], s = v >> 8;
+        const uint32_t m0 = v & 0x000F000Fu;   // weights 8d, 8d+4
+        const uint32_t m1 = s & 0x000F000Fu;   // weights 8d+2, 8d+6
+        const uint32_t m2 = v & 0x00F000F0u;   // weights 8d+1, 8d+5 (x16)
+        const uint32_t m3 = s & 0x00F000F0u;   // weights 8d+3, 8d+7 (x16)
+        lo = __builtin_fmaf(lo_half(m0), xa.x, lo);
+        lo = __builtin_fmaf(hi_half(m0), xb.x, lo);
+        lo = __builtin_fmaf(lo_half(m1), xa.z, lo);
+        lo = __builtin_fmaf(hi_half(m1), xb.z, lo);
+        hi = __builtin_fmaf(lo_half(m2), xa.y, hi);
+        hi = __builtin_fmaf(hi_half(m2), xb.y, hi);
+        hi = __builtin_fmaf(lo_half(m3), xa.w, hi);
+        hi = __builtin_fmaf(hi_half(m3), xb.w, hi);
+    }
+    return lo * 16777216.0f + hi * 1048576.0f;
+}
+
+template <int LPR>
+__global__ __launch_bounds__(kThreads) void k_mlx4_rows(Mlx4Args a) {
+    extern __shared__ float lds[];
+    asm volatile("" ::"s"(a.base), "s"(a.stride), "s"(a.packed_off), "s"(a.scales_off),
+                 "s"(a.biases_off), "s"(a.src1), "s"(a.ids), "s"(a.dst));
+    asm volatile("" ::"s"(a.outer), "s"(a.inner), "s"(a.n), "s"(a.k), "s"(a.top_k),
+                 "s"(a.num_experts), "s"(a.vec));
+    constexpr int RPI = kThreads / LPR;
+    const int tid = threadIdx.x;
+    const int q = blockIdx.y;   // pair
+    const int t = q / a.top_k, s = q - t * a.top_k;
+    const float *x = a.src1 + t * a.outer + s * a.inner;
+    auto x_of = [&](int) { return x; };
+    const int total = a.k >> 5;   // 32-float sub-blocks of the row
+    float *red = lds + row_lds_floats(a.k);
+    // 1. the first staging batch ahead of the weights (waiting for it leaves
+    //    the weights in flight)
+    StageBatch xb;
+    stage_issue(x_of, 0, total, a.k, a.vec, xb);
+    // 2. the lane's group: clamped addresses, no branch
+    const int e = a.ids[q];
+    const bool valid = (unsigned)e < (unsigned)a.num_experts;
+    const uint8_t *blk = a.base + (valid ? (int64_t)e * a.stride : 0);
+    const int gpr = a.k / kMlxGroup;
+    const int u = tid % LPR, rsub = tid / LPR;
+    const bool active = u < gpr;
+    const int gl = active ? u : 0;
+    const int r0 = blockIdx.x * RPI + rsub;
+    const int r = r0 < a.n ? r0 : a.n - 1;
+    const uint8_t *prow = blk + a.packed_off + (int64_t)r * (a.k >> 1) + 32 * gl;
+    const uint4 qa = *(const uint4 *)prow;
+    const uint4 qb = *(const uint4 *)(prow + 16);
+    const int64_t gi = ((int64_t)r * gpr + gl) * 2;
+    const uint32_t sh = *(const uint16_t *)(blk + a.scales_off + gi);
+    const uint32_t bh = *(const uint16_t *)(blk + a.biases_off + gi);
+    // 3. the staged row (and any further batches)
+    stage_commit(xb, total, a.k, lds);
+    stage_rows(x_of, 1, a.k, a.vec, lds, kThreads);
+    lds_barrier();
+    // 4. the group's share, then the row sum
+    const float qx = group_qx(qa, qb, lds + xpad(kMlxGroup * gl));
+    const float *sx = lds + xpad_len(a.k);
+    const float gsum = sx[2 * gl] + sx[2 * gl + 1];
+    const float v = __builtin_fmaf(bf16_val(sh), qx, bf16_val(bh) * gsum);
+    const float row = row_reduce<LPR>(active ? v : 0.0f, red, 0);
+    if (u == 0 && r0 < a.n)
+        a.dst[(int64_t)q * a.n + r0] = valid ? row : 0.0f;
+}
+
+// One thread per group: w = scale * q + bias in float (scale * q is exact,
+// the sum rounds once).
+__global__ __launch_bounds__(256) void k_mlx4_dequant(const uint8_t *__restrict__ packed,
+                                                      const uint16_t *__restrict__ scales,
+                                                      const uint16_t *__restrict__ biases,
+                                                      float *__restrict__ out, int64_t groups) {
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (g >= groups)
+        return;
+    const uint4 qa = *(const uint4 *)(packed + 32 * g);
+    const uint4 qb = *(const uint4 *)(packed + 32 * g + 16);
+    const float sc = bf16_val(scales[g]), bi = bf16_val(biases[g]);
+    const uint32_t w[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+    float4 *o = (float4 *)(out + kMlxGroup * g);
+#pragma unroll
+    for (int d = 0; d < 8; d++) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const float p = sc * (float)((w[d] >> (4 * j)) & 15u);
+            v[j] = p + bi;
+        }
+        o[2 * d] = make_float4(v[0], v[1], v[2], v[3]);
+        o[2 * d + 1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+}
+
+// Encoder, one thread per group, every decision a single IEEE float
+// operation in the same order as the CPU reference encoder: lo, hi = min and
+// max; scale = bf16((hi - lo) / 15), bias = bf16(lo);
+// q = clamp(rne((w - bias) / scale), 0, 15), 0 where the scale is 0.
+__global__ __launch_bounds__(256) void k_mlx4_quant(const float *__restrict__ w,
+                                                    uint8_t *__restrict__ packed,
+                                                    uint16_t *__restrict__ scales,
+                                                    uint16_t *__restrict__ biases,
+                                                    int64_t groups) {
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (g >= groups)
+        return;
+    const float *x = w + kMlxGroup * g;
+    float lo = x[0], hi = x[0];
+    for (int j = 1; j < kMlxGroup; j++) {
+        const float v = x[j];
+        lo = v < lo ? v : lo;
+        hi = v > hi ? v : hi;
+    }
+    const float d = hi - lo;
+    const uint16_t sh = f32_to_bf16(d / 15.0f);
+    const uint16_t bh = f32_to_bf16(lo);
+    const float sc = bf16_val(sh), bi = bf16_val(bh);
+    scales[g] = sh;
+    biases[g] = bh;
+    uint32_t word[8];
+#pragma unroll
+    for (int dw = 0; dw < 8; dw++) {
+        uint32_t acc = 0;
+        for (int j = 0; j < 8; j++) {
+            const float tq = (x[8 * dw + j] - bi) / sc;
+            int qi = (int)__builtin_rintf(tq);
+            qi = qi < 0 ? 0 : (qi > 15 ? 15 : qi);
+            if (sc == 0.0f)
+                qi = 0;
+            acc |= (uint32_t)qi << (4 * j);
+        }
+        word[dw] = acc;
+    }
+    uint4 *o = (uint4 *)(packed + 32 * g);
+    o[0] = make_uint4(word[0], word[1], word[2], word[3]);
+    o[1] = make_uint4(word[4], word[5], word[6], word[7]);
+}
+
+// ------------------------------------------------------------------ host ---
+
+template <int LPR>
+static hipError_t go_mlx4(const Mlx4Args &a, int64_t n_pairs, hipStream_t st) {
+    constexpr int RPI = kThreads / LPR;
+    auto kern = k_mlx4_rows<LPR>;
+    const size_t lds = set_lds((const void *)kern, ((size_t)row_lds_floats(a.k) + 8) * sizeof(float));
+    dim3 grid((a.n + RPI - 1) / RPI, (unsigned)n_pairs);
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a);
+    return hipGetLastError();
+}
+
+static bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hipError_t launch_mlx4_gemv(const Mlx4Launch &L, hipStream_t st) {
+    Mlx4Args a{};
+    a.base = (const uint8_t *)L.base;
+    a.stride = L.expert_stride;
+    a.packed_off = L.packed_off;
+    a.scales_off = L.scales_off;
+    a.biases_off = L.biases_off;
+    a.src1 = L.src1;
+    a.ids = L.ids;
+    a.dst = L.dst;
+    a.outer = L.outer;
+    a.inner = L.inner;
+    a.n = (int)L.n;
+    a.k = (int)L.k;
+    a.top_k = (int)L.top_k;
+    a.num_experts = (int)L.num_experts;
+    a.vec = al16(L.src1) && L.outer % 4 == 0 && L.inner % 4 == 0;
+    const int64_t P = L.m * L.top_k;
+    int lpr = 4;
+    while (lpr < a.k / kMlxGroup)
+        lpr <<= 1;
+    switch (lpr) {
+    case 4: return go_mlx4<4>(a, P, st);
+    case 8: return go_mlx4<8>(a, P, st);
+    case 16: return go_mlx4<16>(a, P, st);
+    case 32: return go_mlx4<32>(a, P, st);
+    case 64: return go_mlx4<64>(a, P, st);
+    case 128: return go_mlx4<128>(a, P, st);
+    case 256: return go_mlx4<256>(a, P, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_mlx4_dequant(const void *packed, const void *scales, const void *biases,
+                               float *out, int64_t groups, hipStream_t st) {
+    if (groups == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_mlx4_dequant, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st,
+                       (const uint8_t *)packed, (const uint16_t *)scales,
+                       (const uint16_t *)biases, out, groups);
+    return hipGetLastError();
+}
+
+hipError_t launch_mlx4_quant(const float *w, void *packed, void *scales, void *biases,
+                             int64_t groups, hipStream_t st) {
+    if (groups == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_mlx4_quant, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st, w,
+                       (uint8_t *)packed, (uint16_t *)scales, (uint16_t *)biases, groups);
+    return hipGetLastError();
+}
+
+}  // namespace q4k

@@ -264,6 +264,62 @@ int q4tp_matvec_multi(const void *const *tensors, const int64_t *rows, int n_ten
  * nibble = clamp(rne(w/scale), -8, 7) + 8. */
 int q4tp_quantize(const float *w, void *tensor, int64_t rows, int64_t cols, void *stream);
 
+/* ---------------------------------------------------------------------- */
+/* MLX affine 4-bit expert codec ([MF] module doc "4-bit only";             */
+/* gpu_expert_forward / encode_matvec: GROUP_SIZE; encode_moe_gather_id_fuse */
+/* and its gather call: expert blocks of expert_stride bytes (nb02) holding  */
+/* packed weights (nb01_w = k/2 bytes per row), bf16 scales and bf16 biases  */
+/* (nb01_s = (k/64)*2 bytes per row) at packed/scales/biases offsets).      */
+/*                                                                          */
+/* Bit layout (reading: the pages give the strides; this is MLX's affine    */
+/* format): groups of MLX4_GROUP weights along a row; weight                 */
+/* w = scale*q + bias with q the 4-bit code; byte j of a row holds weight   */
+/* 2j in its low nibble and 2j+1 in its high nibble.                         */
+/* ---------------------------------------------------------------------- */
+#define MLX4_GROUP 64
+
+/* Bytes of one n x k matrix: packed n*k/2 + scales and biases 2*(n*k/64)*2.
+ * -1 when k is not a positive multiple of 64 or n < 0. */
+int64_t mlx4_matrix_bytes(int64_t n, int64_t k);
+
+/* packed [n, k/2] bytes, scales and biases [n, k/64] bf16 -> out fp32 [n, k].
+ * w = scale*q + bias in fp32: scale*q is exact (8 + 4 significant bits) and
+ * the sum rounds once, so the result is bit-identical to any correct
+ * evaluation.  64 <= k <= Q4K_MAX_IN, k % 64 == 0; packed and out 16-byte
+ * aligned, scales and biases 2-byte aligned.  Errors: Q4K_ERR_SHAPE,
+ * Q4K_ERR_NULL. */
+int mlx4_dequantize(const void *packed, const void *scales, const void *biases, float *out,
+                    int64_t n, int64_t k, void *stream);
+
+/* fp32 w [n, k] -> packed, scales, biases (layout above).  The pages print
+ * no encoder; reading, a plain min/max affine code per group whose steps are
+ * single IEEE float operations: lo = min w, hi = max w,
+ * scale = bf16_rne((hi - lo)/15), bias = bf16_rne(lo),
+ * q = clamp(rne((w - bias)/scale), 0, 15), q = 0 where scale is 0.
+ * Same shape and alignment rules as mlx4_dequantize (w 4-byte aligned). */
+int mlx4_quantize(const float *w, void *packed, void *scales, void *biases, int64_t n, int64_t k,
+                  void *stream);
+
+/* id-GEMV over MLX 4-bit experts ([MF] encode_moe_gather_id_fuse, one row of
+ * src1 per (token, slot) pair as in [FK]'s 2-D walk):
+ *   for p in [0, m*top_k): t = p / top_k, s = p % top_k, e = ids[p],
+ *     x = src1 + t*src1_outer_stride + s*src1_inner_stride   (floats),
+ *     blk = expert_base + e*expert_stride,
+ *     dst[p, r] = sum_c (scale*q + bias)[r, c] * x[c]
+ *   with the packed weights at blk + packed_off, scales at blk + scales_off,
+ *   biases at blk + biases_off.  ids outside [0, num_experts) give zero rows.
+ * dst: [m*top_k, n] fp32.  Shapes: n >= 1, 64 <= k <= Q4K_MAX_IN, k % 64 == 0,
+ * m >= 1, 1 <= top_k <= Q4K_MAX_TOP_K, num_experts >= 1, m*top_k <= 65535,
+ * each sub-tensor inside the block (offset + its bytes <= expert_stride),
+ * else Q4K_ERR_SHAPE.  Negative activation strides: Q4K_ERR_STRIDE.
+ * Alignment: expert_base, expert_stride and packed_off 16 bytes, scales_off and
+ * biases_off 2 bytes, src1, ids and dst 4 bytes, else Q4K_ERR_NULL. */
+int mlx4_moe_id_gemv(const void *expert_base, int64_t expert_stride, int64_t packed_off,
+                     int64_t scales_off, int64_t biases_off, const float *src1,
+                     const int32_t *ids, float *dst, int64_t n, int64_t k, int64_t m,
+                     int64_t top_k, int64_t src1_outer_stride, int64_t src1_inner_stride,
+                     int64_t num_experts, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,7 +44,7 @@ def test_constants_match_header(lib):
                       ("Q4K_MAX_PAIRS", _lib.Q4K_MAX_PAIRS), ("Q4TP_MAX_COLS", _lib.Q4TP_MAX_COLS),
                       ("Q4K_BUCKET_CHUNK", 8), ("MOE_LAYER_SYNC_BYTES", 4096),
                       ("MOE_LAYER_SYNC_TIMEOUT_WORD", 576),
-                      ("Q4TP_MAX_TENSORS", _lib.Q4TP_MAX_TENSORS)]:
+                      ("Q4TP_MAX_TENSORS", _lib.Q4TP_MAX_TENSORS), ("MLX4_GROUP", 64)]:
         assert re.search(rf"#define {name} {val}\b", src), name
     assert q4.q4k_abi_version() == 2
 
@@ -56,6 +56,11 @@ def test_size_helpers(lib):
     assert q4.q4tp_tensor_bytes(1, 4096) == 2132
     assert q4.q4tp_tensor_bytes(1, 14336) == 7452
     assert q4.q4tp_tensor_bytes(3, 33) == -1
+    # MLX 4-bit: k/2 packed bytes + 2 bf16 per 64 weights per row (the same
+    # 4.5 bits per weight as Q4_K at these shapes)
+    assert q4.mlx4_matrix_bytes(768, 2048) == 884_736
+    assert q4.mlx4_matrix_bytes(2048, 768) == 884_736
+    assert q4.mlx4_matrix_bytes(3, 96) == -1
     assert q4.moe_bucket_workspace_bytes(128, 128) == 4 * (129 + 130 + 128 + 129 + 1 + 1 + 256)
     # sync header | act [9, 768] | expert_out [8, 2048] | shared_out [1, 2048] | buckets
     assert q4.moe_layer_workspace_bytes(2048, 768, 128, 1, 8) == \
@@ -147,3 +152,37 @@ def test_binding_refuses_host_tensors(lib):
     import torch
     with pytest.raises(ValueError):
         q4.q4k_dequantize(torch.zeros(144, dtype=torch.uint8), FAKE, 1, stream=0)
+
+
+def test_mlx4_validation(lib):
+    g = q4.mlx4_moe_id_gemv
+    n, k = 64, 256
+    stride = q4.mlx4_matrix_bytes(n, k)
+    so, bo = n * k // 2, n * k // 2 + n * k // 32
+
+    def call(base=FAKE, st=stride, po=0, s_off=so, b_off=bo, x=FAKE, ids=FAKE, dst=FAKE, n=n,
+             k=k, m=3, top_k=2, outer=k, inner=0, E=4):
+        return _err(g, base, st, po, s_off, b_off, x, ids, dst, n, k, m, top_k, outer, inner, E)
+
+    assert call(k=96) == _lib.Q4K_ERR_SHAPE
+    assert call(k=0) == _lib.Q4K_ERR_SHAPE
+    assert call(k=16384 + 64) == _lib.Q4K_ERR_SHAPE
+    assert call(n=0) == _lib.Q4K_ERR_SHAPE
+    assert call(m=0) == _lib.Q4K_ERR_SHAPE
+    assert call(top_k=17) == _lib.Q4K_ERR_SHAPE
+    assert call(E=0) == _lib.Q4K_ERR_SHAPE
+    assert call(st=stride - 2) == _lib.Q4K_ERR_SHAPE      # biases past the block
+    assert call(po=stride - n * k // 2 + 16) == _lib.Q4K_ERR_SHAPE   # packed past the block
+    assert call(po=-16) == _lib.Q4K_ERR_SHAPE
+    assert call(outer=-1) == _lib.Q4K_ERR_STRIDE
+    assert call(base=None) == _lib.Q4K_ERR_NULL
+    assert call(base=FAKE + 8) == _lib.Q4K_ERR_NULL
+    assert call(st=stride + 8) == _lib.Q4K_ERR_NULL       # stride not 16-byte aligned
+    assert call(s_off=so + 1) == _lib.Q4K_ERR_NULL
+    assert call(dst=None) == _lib.Q4K_ERR_NULL
+    d = q4.mlx4_dequantize
+    assert _err(d, FAKE, FAKE, FAKE, FAKE, 4, 100) == _lib.Q4K_ERR_SHAPE
+    assert _err(d, FAKE, FAKE + 1, FAKE, FAKE, 4, 128) == _lib.Q4K_ERR_NULL
+    qz = q4.mlx4_quantize
+    assert _err(qz, FAKE, FAKE, FAKE, FAKE, 4, 32) == _lib.Q4K_ERR_SHAPE
+    assert _err(qz, FAKE, FAKE + 4, FAKE, FAKE, 4, 64) == _lib.Q4K_ERR_NULL
