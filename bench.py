@@ -247,6 +247,51 @@ def run_walk(torch, q4, wl, replicas, walks, warmup):
     return sec_m / (4 * walks) * 1e6, sec / (4 * walks) * 1e6, nbytes
 
 
+def run_mlx4(torch, q4, wl, replicas, launches, warmup):
+    """The MLX affine 4-bit id-GEMV (moeflux expert_forward.rs 4-bit experts,
+    bf16 scale and bias per 64 weights) at the single-token decode shapes:
+    gate-shaped (768 x 2048, activation row per token) and down-shaped
+    (2048 x 768, one row per pair), 128 experts, top_k 8, m = 1.  Each
+    replica is a full 128-expert stack in expert blocks (packed | scales |
+    biases), device-encoded; launches rotate over replicas and 64 routing
+    draws.  Returns {shape: (us per launch, unique weight bytes per launch)}."""
+    dev = torch.device("cuda")
+    cfg = wl.CFG2
+    E, H, I, K = cfg.num_experts, cfg.hidden, cfg.inter, cfg.top_k
+    sets = [wl.moe_activations(cfg, index=s) for s in range(64)]
+    ids = [torch.from_numpy(a.ids).to(dev) for a in sets]
+    uniq = [len(set(a.ids.tolist())) for a in sets]
+    res = {}
+    for name, n, k, outer, inner in [("gate", I, H, H, 0), ("down", H, I, K * I, I)]:
+        stride = q4.mlx4_matrix_bytes(n, k)
+        po, so, bo = 0, n * k // 2, n * k // 2 + n * k // 32
+        blobs = []
+        for r in range(replicas):
+            w = wl.device_normal((E * n, k), cfg.w_std, seed=70000 + 100 * r + len(res))
+            blob = torch.empty(E * stride, dtype=torch.uint8, device=dev)
+            for e in range(E):
+                b0 = e * stride
+                q4.mlx4_quantize(w[e * n:(e + 1) * n], blob[b0 + po:b0 + so],
+                                 blob[b0 + so:b0 + bo], blob[b0 + bo:b0 + stride], n, k)
+            del w
+            blobs.append(blob)
+        x = wl.device_normal((K, k), 1.0, seed=79999)   # row 0 for gate, 8 rows for down
+        out = torch.empty(K, n, device=dev)
+        torch.cuda.synchronize()
+
+        def launch(i, n=n, k=k, stride=stride, outer=outer, inner=inner, blobs=blobs, x=x,
+                   out=out, so=so, bo=bo):
+            q4.mlx4_moe_id_gemv(blobs[i % replicas], stride, 0, so, bo, x, ids[i % 64], out, n, k,
+                                1, K, outer, inner, E)
+
+        g = capture(torch, launch, launches)
+        sec, _ = time_graph(torch, g, 4, warmup)
+        nbytes = sum(uniq[i % 64] for i in range(launches)) / launches * stride
+        res[name] = (sec / (4 * launches) * 1e6, nbytes)
+        del blobs
+    return res
+
+
 def run_workload(torch, q4, wl, cfg, args, stacks=None):
     """Times exactly args.steps layers (and, separately, args.steps launches
     of the layer's first kernel) after args.warmup untimed ones."""
@@ -386,6 +431,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-m16", action="store_true")
     ap.add_argument("--no-walk", action="store_true")
+    ap.add_argument("--no-mlx4", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: every box here has one MI355X and this path has no "
@@ -415,6 +461,11 @@ def main():
         walk_us, walk_single_us, walk_bytes = run_walk(torch, q4, wl, 2, 32, 1)
         log(f"walk: {walk_us:.2f} us/walk merged ({walk_bytes / walk_us / 1e3:.1f} GB/s), "
             f"{walk_single_us:.2f} us one launch per tensor")
+    mlx = None
+    if not args.no_mlx4:
+        mlx = run_mlx4(torch, q4, wl, 8, 64, 1)
+        log("mlx4: " + ", ".join(f"{k} {us:.2f} us ({b / us / 1e3:.1f} GB/s)"
+                                 for k, (us, b) in mlx.items()))
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, wl.CFG2, args.cpu_seconds)
@@ -468,6 +519,17 @@ def main():
             "gate_up_gbs": round(res16["gate_up_gbs"], 2),
             "gate_up_us": round(res16["gate_up_us"], 3),
         }
+    if mlx is not None:
+        line["mlx4"] = {
+            "workload": "MLX affine 4-bit id-GEMV (bf16 scale and bias per 64 weights), 128 "
+                        "experts, top_k 8, m=1: gate-shaped 768x2048 and down-shaped 2048x768, "
+                        "8 replicas rotated",
+            "kernel": "k_mlx4_rows",
+        }
+        for k, (us, b) in mlx.items():
+            line["mlx4"][k] = {"us_per_launch": round(us, 3), "bytes_per_launch": int(b),
+                               "gbs": round(b / us / 1e3, 2),
+                               "frac_hbm_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
     if walk_us is not None:
         line["walk"] = {
             "workload": "dense Q4TiledP decode walk: one layer (q, k, v, o 4096x4096, gate and up "
