@@ -248,13 +248,14 @@ def run_walk(torch, q4, wl, replicas, walks, warmup):
 
 
 def run_mlx4(torch, q4, wl, replicas, launches, warmup):
-    """The MLX affine 4-bit id-GEMV (moeflux expert_forward.rs 4-bit experts,
-    bf16 scale and bias per 64 weights) at the single-token decode shapes:
-    gate-shaped (768 x 2048, activation row per token) and down-shaped
-    (2048 x 768, one row per pair), 128 experts, top_k 8, m = 1.  Each
-    replica is a full 128-expert stack in expert blocks (packed | scales |
-    biases), device-encoded; launches rotate over replicas and 64 routing
-    draws.  Returns {shape: (us per launch, unique weight bytes per launch)}."""
+    """The MLX affine 4-bit expert path (moeflux expert_forward.rs 4-bit
+    experts, bf16 scale and bias per 64 weights) at the single-token decode
+    shapes, 128 experts, top_k 8, m = 1: the fused gate/up + SiLU launch over
+    expert blocks holding the gate and up matrices (768 x 2048 each, one
+    activation row per token), and the down-shaped id-GEMV (2048 x 768, one
+    row per pair).  Each replica is a full 128-expert stack, device-encoded;
+    launches rotate over replicas and 64 routing draws.  Returns
+    {name: (us per launch, unique weight bytes per launch)}."""
     dev = torch.device("cuda")
     cfg = wl.CFG2
     E, H, I, K = cfg.num_experts, cfg.hidden, cfg.inter, cfg.top_k
@@ -262,27 +263,38 @@ def run_mlx4(torch, q4, wl, replicas, launches, warmup):
     ids = [torch.from_numpy(a.ids).to(dev) for a in sets]
     uniq = [len(set(a.ids.tolist())) for a in sets]
     res = {}
-    for name, n, k, outer, inner in [("gate", I, H, H, 0), ("down", H, I, K * I, I)]:
-        stride = q4.mlx4_matrix_bytes(n, k)
-        po, so, bo = 0, n * k // 2, n * k // 2 + n * k // 32
+    for name, n, k, outer, inner, nmat in [("gate_up_silu", I, H, H, 0, 2),
+                                           ("down", H, I, K * I, I, 1)]:
+        mat = q4.mlx4_matrix_bytes(n, k)
+        stride = nmat * mat
+        # matrix j of a block: packed | scales | biases at j * mat
+        offs = [(j * mat, j * mat + n * k // 2, j * mat + n * k // 2 + n * k // 32)
+                for j in range(nmat)]
         blobs = []
         for r in range(replicas):
-            w = wl.device_normal((E * n, k), cfg.w_std, seed=70000 + 100 * r + len(res))
             blob = torch.empty(E * stride, dtype=torch.uint8, device=dev)
-            for e in range(E):
-                b0 = e * stride
-                q4.mlx4_quantize(w[e * n:(e + 1) * n], blob[b0 + po:b0 + so],
-                                 blob[b0 + so:b0 + bo], blob[b0 + bo:b0 + stride], n, k)
-            del w
+            for j in range(nmat):
+                w = wl.device_normal((E * n, k), cfg.w_std, seed=70000 + 100 * r + 10 * j + nmat)
+                po, so, bo = offs[j]
+                for e in range(E):
+                    b0 = e * stride
+                    q4.mlx4_quantize(w[e * n:(e + 1) * n], blob[b0 + po:b0 + so],
+                                     blob[b0 + so:b0 + bo], blob[b0 + bo:b0 + po + mat], n, k)
+                del w
             blobs.append(blob)
-        x = wl.device_normal((K, k), 1.0, seed=79999)   # row 0 for gate, 8 rows for down
+        x = wl.device_normal((K, k), 1.0, seed=79999)   # row 0 for gate/up, 8 rows for down
         out = torch.empty(K, n, device=dev)
         torch.cuda.synchronize()
 
         def launch(i, n=n, k=k, stride=stride, outer=outer, inner=inner, blobs=blobs, x=x,
-                   out=out, so=so, bo=bo):
-            q4.mlx4_moe_id_gemv(blobs[i % replicas], stride, 0, so, bo, x, ids[i % 64], out, n, k,
-                                1, K, outer, inner, E)
+                   out=out, offs=offs, nmat=nmat):
+            blob, d_ids = blobs[i % replicas], ids[i % 64]
+            if nmat == 2:
+                q4.mlx4_moe_gate_up_silu(blob, stride, offs[0], offs[1], x, d_ids, out, n, k, 1,
+                                         K, outer, inner, E)
+            else:
+                q4.mlx4_moe_id_gemv(blob, stride, *offs[0], x, d_ids, out, n, k, 1, K, outer,
+                                    inner, E)
 
         g = capture(torch, launch, launches)
         sec, _ = time_graph(torch, g, 4, warmup)
@@ -521,9 +533,9 @@ def main():
         }
     if mlx is not None:
         line["mlx4"] = {
-            "workload": "MLX affine 4-bit id-GEMV (bf16 scale and bias per 64 weights), 128 "
-                        "experts, top_k 8, m=1: gate-shaped 768x2048 and down-shaped 2048x768, "
-                        "8 replicas rotated",
+            "workload": "MLX affine 4-bit experts (bf16 scale and bias per 64 weights), 128 "
+                        "experts, top_k 8, m=1: fused gate/up + SiLU over 768x2048 gate and up "
+                        "matrices, and the down-shaped 2048x768 id-GEMV; 8 replicas rotated",
             "kernel": "k_mlx4_rows",
         }
         for k, (us, b) in mlx.items():

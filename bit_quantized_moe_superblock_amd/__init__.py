@@ -12,5 +12,6 @@ from ._lib import (  # noqa: F401
     moe_expert_ffn, moe_layer_forward, moe_layer_workspace_bytes, moe_layer_workspace_init, q4k_abi_version, q4k_dequantize, q4k_matrix_bytes, q4k_moe_id_gemv,
     q4k_moe_gate_up_silu,
     q4k_quantize, q4tp_matvec, q4tp_matvec_multi, q4tp_quantize, q4tp_tensor_bytes, status_string,
-    MLX4_GROUP, mlx4_dequantize, mlx4_matrix_bytes, mlx4_moe_id_gemv, mlx4_quantize,
+    MLX4_GROUP, mlx4_dequantize, mlx4_matrix_bytes, mlx4_moe_gate_up_silu, mlx4_moe_id_gemv,
+    mlx4_quantize,
 )

@@ -52,6 +52,8 @@ SIGNATURES = {
     "mlx4_quantize": (_I, [_P, _P, _P, _P, _I64, _I64, _P]),
     "mlx4_moe_id_gemv": (_I, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _I64, _I64,
                               _I64, _I64, _I64, _P]),
+    "mlx4_moe_gate_up_silu": (_I, [_P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P,
+                                   _I64, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
 }
 
 
@@ -234,3 +236,12 @@ def mlx4_moe_id_gemv(expert_base, expert_stride: int, packed_off: int, scales_of
     _call("mlx4_moe_id_gemv", _ptr(expert_base), expert_stride, packed_off, scales_off,
           biases_off, _ptr(src1), _ptr(ids), _ptr(dst), n, k, m, top_k, src1_outer_stride,
           src1_inner_stride, num_experts, _stream(stream))
+
+
+def mlx4_moe_gate_up_silu(expert_base, expert_stride: int, gate_offs, up_offs, src1, ids, dst,
+                          n: int, k: int, m: int, top_k: int, src1_outer_stride: int,
+                          src1_inner_stride: int, num_experts: int, stream=None):
+    """gate_offs and up_offs are (packed, scales, biases) byte offsets inside an expert block."""
+    _call("mlx4_moe_gate_up_silu", _ptr(expert_base), expert_stride, *[int(o) for o in gate_offs],
+          *[int(o) for o in up_offs], _ptr(src1), _ptr(ids), _ptr(dst), n, k, m, top_k,
+          src1_outer_stride, src1_inner_stride, num_experts, _stream(stream))

@@ -505,32 +505,94 @@ int mlx4_quantize(const float *w, void *packed, void *scales, void *biases, int6
                                       as_stream(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shape, block and alignment checks shared by the MLX 4-bit id-GEMV entry
+// points; offs holds (packed, scales, biases) offsets of n_mats matrices.
+int mlx4_check(const void *expert_base, int64_t expert_stride, const int64_t *offs, int n_mats,
+               const float *src1, const int32_t *ids, const float *dst, int64_t n, int64_t k,
+               int64_t m, int64_t top_k, int64_t outer, int64_t inner, int64_t num_experts) {
+    if (n < 1 || n > (1 << 30) || k < MLX4_GROUP || k % MLX4_GROUP || k > Q4K_MAX_IN || m < 1 ||
+        top_k < 1 || top_k > Q4K_MAX_TOP_K || num_experts < 1 || m * top_k > 65535)
+        return Q4K_ERR_SHAPE;
+    // every sub-tensor inside one expert block
+    const int64_t pbytes = n * k / 2, sbytes = n * (k / MLX4_GROUP) * 2;
+    if (expert_stride < 0)
+        return Q4K_ERR_SHAPE;
+    for (int i = 0; i < n_mats; i++) {
+        const int64_t po = offs[3 * i], so = offs[3 * i + 1], bo = offs[3 * i + 2];
+        if (po < 0 || so < 0 || bo < 0 || po + pbytes > expert_stride ||
+            so + sbytes > expert_stride || bo + sbytes > expert_stride)
+            return Q4K_ERR_SHAPE;
+    }
+    if (outer < 0 || inner < 0)
+        return Q4K_ERR_STRIDE;
+    if (!expert_base || !src1 || !ids || !dst || !aligned16(expert_base) || expert_stride % 16 ||
+        !aligned4(src1) || !aligned4(ids) || !aligned4(dst))
+        return Q4K_ERR_NULL;
+    for (int i = 0; i < n_mats; i++)
+        if (offs[3 * i] % 16 || offs[3 * i + 1] % 2 || offs[3 * i + 2] % 2)
+            return Q4K_ERR_NULL;
+    return Q4K_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int mlx4_moe_id_gemv(const void *expert_base, int64_t expert_stride, int64_t packed_off,
                      int64_t scales_off, int64_t biases_off, const float *src1,
                      const int32_t *ids, float *dst, int64_t n, int64_t k, int64_t m,
                      int64_t top_k, int64_t src1_outer_stride, int64_t src1_inner_stride,
                      int64_t num_experts, void *stream) {
-    if (n < 1 || n > (1 << 30) || k < MLX4_GROUP || k % MLX4_GROUP || k > Q4K_MAX_IN || m < 1 ||
-        top_k < 1 || top_k > Q4K_MAX_TOP_K || num_experts < 1 || m * top_k > 65535)
-        return Q4K_ERR_SHAPE;
-    // the three sub-tensors must lie inside one expert block
-    const int64_t pbytes = n * k / 2, sbytes = n * (k / MLX4_GROUP) * 2;
-    if (expert_stride < 0 || packed_off < 0 || scales_off < 0 || biases_off < 0 ||
-        packed_off + pbytes > expert_stride || scales_off + sbytes > expert_stride ||
-        biases_off + sbytes > expert_stride)
-        return Q4K_ERR_SHAPE;
-    if (src1_outer_stride < 0 || src1_inner_stride < 0)
-        return Q4K_ERR_STRIDE;
-    if (!expert_base || !src1 || !ids || !dst || !aligned16(expert_base) ||
-        expert_stride % 16 || packed_off % 16 || scales_off % 2 || biases_off % 2 ||
-        !aligned4(src1) || !aligned4(ids) || !aligned4(dst))
-        return Q4K_ERR_NULL;
+    const int64_t offs[3] = {packed_off, scales_off, biases_off};
+    const int rc = mlx4_check(expert_base, expert_stride, offs, 1, src1, ids, dst, n, k, m, top_k,
+                              src1_outer_stride, src1_inner_stride, num_experts);
+    if (rc)
+        return rc;
     Mlx4Launch L{};
     L.base = expert_base;
     L.expert_stride = expert_stride;
     L.packed_off = packed_off;
     L.scales_off = scales_off;
     L.biases_off = biases_off;
+    L.src1 = src1;
+    L.ids = ids;
+    L.dst = dst;
+    L.n = n;
+    L.k = k;
+    L.m = m;
+    L.top_k = top_k;
+    L.num_experts = num_experts;
+    L.outer = src1_outer_stride;
+    L.inner = src1_inner_stride;
+    return launched(launch_mlx4_gemv(L, as_stream(stream)));
+}
+
+int mlx4_moe_gate_up_silu(const void *expert_base, int64_t expert_stride, int64_t gate_packed_off,
+                          int64_t gate_scales_off, int64_t gate_biases_off, int64_t up_packed_off,
+                          int64_t up_scales_off, int64_t up_biases_off, const float *src1,
+                          const int32_t *ids, float *dst, int64_t n, int64_t k, int64_t m,
+                          int64_t top_k, int64_t src1_outer_stride, int64_t src1_inner_stride,
+                          int64_t num_experts, void *stream) {
+    const int64_t offs[6] = {gate_packed_off, gate_scales_off, gate_biases_off,
+                             up_packed_off,   up_scales_off,   up_biases_off};
+    const int rc = mlx4_check(expert_base, expert_stride, offs, 2, src1, ids, dst, n, k, m, top_k,
+                              src1_outer_stride, src1_inner_stride, num_experts);
+    if (rc)
+        return rc;
+    Mlx4Launch L{};
+    L.base = expert_base;
+    L.expert_stride = expert_stride;
+    L.packed_off = gate_packed_off;
+    L.scales_off = gate_scales_off;
+    L.biases_off = gate_biases_off;
+    L.packed_off1 = up_packed_off;
+    L.scales_off1 = up_scales_off;
+    L.biases_off1 = up_biases_off;
+    L.fused_swiglu = true;
     L.src1 = src1;
     L.ids = ids;
     L.dst = dst;

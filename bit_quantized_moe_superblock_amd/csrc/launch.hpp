@@ -68,10 +68,13 @@ bool layer_m1_supported(int64_t hidden, int64_t inter, int64_t top_k, int has_sh
 hipError_t launch_layer_m1(const LayerLaunch &L, hipStream_t st);
 
 // MLX affine 4-bit id-GEMV (mlx4.hip): expert e's block at base + e*expert_stride,
-// its packed weights, scales and biases at the offsets inside the block.
+// its packed weights, scales and biases at the offsets inside the block (a
+// second set, the up matrix, for the fused gate/up + SiLU launch).
 struct Mlx4Launch {
     const void *base;
     int64_t expert_stride, packed_off, scales_off, biases_off;
+    int64_t packed_off1, scales_off1, biases_off1;   // up matrix (fused_swiglu)
+    bool fused_swiglu;
     const float *src1;
     const int32_t *ids;
     float *dst;

@@ -9,9 +9,10 @@
 // sit at byte offsets inside its block; expert e's block starts at
 // e * expert_stride (the gather dispatch's nb02).
 //
-// id-GEMV: one workgroup per (row tile, pair), as the Q4_K pair mode.  A lane
-// owns one group of one row: two 16-byte loads of its 32 packed bytes, its
-// scale and bias.  The activation row is staged once per workgroup in LDS
+// id-GEMV: one workgroup per (row tile, pair), as the Q4_K pair mode; the
+// fused variant reads the gate and up matrices of the block in the same lanes
+// and stores silu(gate) * up.  A lane owns one group of one row: two 16-byte
+// loads of its 32 packed bytes, its scale and bias.  The activation row is staged once per workgroup in LDS
 // (64 floats per lane, padded by 4 so lanes' reads fall in different banks)
 // with its 32-float sums.  The nibbles become fp16 subnormals by masking
 // (low nibbles q 2^-24, high nibbles q 2^-20) and feed v_fma_mix_f32, so the
@@ -26,7 +27,9 @@ constexpr int kMlxGroup = 64;
 
 struct Mlx4Args {
     const uint8_t *base;                       // expert 0's block
-    int64_t stride, packed_off, scales_off, biases_off;
+    int64_t stride;
+    int64_t packed_off, scales_off, biases_off;        // first matrix (gate when fused)
+    int64_t packed_off1, scales_off1, biases_off1;     // up matrix of the fused launch
     const float *src1;
     const int32_t *ids;
     float *dst;                                // [n_pairs, n]
@@ -73,13 +76,17 @@ __device__ __forceinline__ float group_qx(const uint4 qa, const uint4 qb, const 
     return lo * 16777216.0f + hi * 1048576.0f;
 }
 
-template <int LPR>
+// NT = 1: dst[p, r] = row r of the pair's matrix times x.  NT = 2: the gate
+// and up matrices of the same expert block against the same x, the lane
+// loading both groups, and dst[p, r] = silu(gate) * up.
+template <int LPR, int NT>
 __global__ __launch_bounds__(kThreads) void k_mlx4_rows(Mlx4Args a) {
     extern __shared__ float lds[];
     asm volatile("" ::"s"(a.base), "s"(a.stride), "s"(a.packed_off), "s"(a.scales_off),
                  "s"(a.biases_off), "s"(a.src1), "s"(a.ids), "s"(a.dst));
     asm volatile("" ::"s"(a.outer), "s"(a.inner), "s"(a.n), "s"(a.k), "s"(a.top_k),
-                 "s"(a.num_experts), "s"(a.vec));
+                 "s"(a.num_experts), "s"(a.vec), "s"(a.packed_off1), "s"(a.scales_off1),
+                 "s"(a.biases_off1));
     constexpr int RPI = kThreads / LPR;
     const int tid = threadIdx.x;
     const int q = blockIdx.y;   // pair
@@ -102,24 +109,35 @@ __global__ __launch_bounds__(kThreads) void k_mlx4_rows(Mlx4Args a) {
     const int gl = active ? u : 0;
     const int r0 = blockIdx.x * RPI + rsub;
     const int r = r0 < a.n ? r0 : a.n - 1;
-    const uint8_t *prow = blk + a.packed_off + (int64_t)r * (a.k >> 1) + 32 * gl;
-    const uint4 qa = *(const uint4 *)prow;
-    const uint4 qb = *(const uint4 *)(prow + 16);
+    const int64_t prel = (int64_t)r * (a.k >> 1) + 32 * gl;
     const int64_t gi = ((int64_t)r * gpr + gl) * 2;
-    const uint32_t sh = *(const uint16_t *)(blk + a.scales_off + gi);
-    const uint32_t bh = *(const uint16_t *)(blk + a.biases_off + gi);
+    uint4 qa[NT], qb[NT];
+    uint32_t sh[NT], bh[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++) {
+        const uint8_t *prow = blk + (nt ? a.packed_off1 : a.packed_off) + prel;
+        qa[nt] = *(const uint4 *)prow;
+        qb[nt] = *(const uint4 *)(prow + 16);
+        sh[nt] = *(const uint16_t *)(blk + (nt ? a.scales_off1 : a.scales_off) + gi);
+        bh[nt] = *(const uint16_t *)(blk + (nt ? a.biases_off1 : a.biases_off) + gi);
+    }
     // 3. the staged row (and any further batches)
     stage_commit(xb, total, a.k, lds);
     stage_rows(x_of, 1, a.k, a.vec, lds, kThreads);
     lds_barrier();
-    // 4. the group's share, then the row sum
-    const float qx = group_qx(qa, qb, lds + xpad(kMlxGroup * gl));
+    // 4. the group's share, then the row sums
     const float *sx = lds + xpad_len(a.k);
     const float gsum = sx[2 * gl] + sx[2 * gl + 1];
-    const float v = __builtin_fmaf(bf16_val(sh), qx, bf16_val(bh) * gsum);
-    const float row = row_reduce<LPR>(active ? v : 0.0f, red, 0);
+    float part[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++) {
+        const float qx = group_qx(qa[nt], qb[nt], lds + xpad(kMlxGroup * gl));
+        const float v = __builtin_fmaf(bf16_val(sh[nt]), qx, bf16_val(bh[nt]) * gsum);
+        part[nt] = row_reduce<LPR>(active ? v : 0.0f, red, nt);
+    }
     if (u == 0 && r0 < a.n)
-        a.dst[(int64_t)q * a.n + r0] = valid ? row : 0.0f;
+        a.dst[(int64_t)q * a.n + r0] = valid ? (NT == 2 ? silu_mul(part[0], part[1]) : part[0])
+                                             : 0.0f;
 }
 
 // One thread per group: w = scale * q + bias in float (scale * q is exact,
@@ -195,10 +213,10 @@ __global__ __launch_bounds__(256) void k_mlx4_quant(const float *__restrict__ w,
 
 // ------------------------------------------------------------------ host ---
 
-template <int LPR>
+template <int LPR, int NT>
 static hipError_t go_mlx4(const Mlx4Args &a, int64_t n_pairs, hipStream_t st) {
     constexpr int RPI = kThreads / LPR;
-    auto kern = k_mlx4_rows<LPR>;
+    auto kern = k_mlx4_rows<LPR, NT>;
     const size_t lds = set_lds((const void *)kern, ((size_t)row_lds_floats(a.k) + 8) * sizeof(float));
     dim3 grid((a.n + RPI - 1) / RPI, (unsigned)n_pairs);
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a);
@@ -214,6 +232,9 @@ hipError_t launch_mlx4_gemv(const Mlx4Launch &L, hipStream_t st) {
     a.packed_off = L.packed_off;
     a.scales_off = L.scales_off;
     a.biases_off = L.biases_off;
+    a.packed_off1 = L.packed_off1;
+    a.scales_off1 = L.scales_off1;
+    a.biases_off1 = L.biases_off1;
     a.src1 = L.src1;
     a.ids = L.ids;
     a.dst = L.dst;
@@ -228,14 +249,26 @@ hipError_t launch_mlx4_gemv(const Mlx4Launch &L, hipStream_t st) {
     int lpr = 4;
     while (lpr < a.k / kMlxGroup)
         lpr <<= 1;
+    if (L.fused_swiglu) {
+        switch (lpr) {
+        case 4: return go_mlx4<4, 2>(a, P, st);
+        case 8: return go_mlx4<8, 2>(a, P, st);
+        case 16: return go_mlx4<16, 2>(a, P, st);
+        case 32: return go_mlx4<32, 2>(a, P, st);
+        case 64: return go_mlx4<64, 2>(a, P, st);
+        case 128: return go_mlx4<128, 2>(a, P, st);
+        case 256: return go_mlx4<256, 2>(a, P, st);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (lpr) {
-    case 4: return go_mlx4<4>(a, P, st);
-    case 8: return go_mlx4<8>(a, P, st);
-    case 16: return go_mlx4<16>(a, P, st);
-    case 32: return go_mlx4<32>(a, P, st);
-    case 64: return go_mlx4<64>(a, P, st);
-    case 128: return go_mlx4<128>(a, P, st);
-    case 256: return go_mlx4<256>(a, P, st);
+    case 4: return go_mlx4<4, 1>(a, P, st);
+    case 8: return go_mlx4<8, 1>(a, P, st);
+    case 16: return go_mlx4<16, 1>(a, P, st);
+    case 32: return go_mlx4<32, 1>(a, P, st);
+    case 64: return go_mlx4<64, 1>(a, P, st);
+    case 128: return go_mlx4<128, 1>(a, P, st);
+    case 256: return go_mlx4<256, 1>(a, P, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -320,6 +320,21 @@ int mlx4_moe_id_gemv(const void *expert_base, int64_t expert_stride, int64_t pac
                      int64_t top_k, int64_t src1_outer_stride, int64_t src1_inner_stride,
                      int64_t num_experts, void *stream);
 
+/* Fused gate/up + SiLU over MLX 4-bit experts ([MF] module doc: gate and up
+ * matvecs then SwiGLU, and encode_moe_gather_id_fuse's gate and up gathers
+ * over the same expert block): the gate matrix at the gate_* offsets and the
+ * up matrix at the up_* offsets of each expert's block, both [n, k], against
+ * the same activation row;
+ *   dst[p, r] = silu(gate[p, r]) * up[p, r],  silu(z) = z / (1 + e^-z).
+ * Arguments, walk, limits and errors as mlx4_moe_id_gemv, for both sets of
+ * offsets. */
+int mlx4_moe_gate_up_silu(const void *expert_base, int64_t expert_stride, int64_t gate_packed_off,
+                          int64_t gate_scales_off, int64_t gate_biases_off, int64_t up_packed_off,
+                          int64_t up_scales_off, int64_t up_biases_off, const float *src1,
+                          const int32_t *ids, float *dst, int64_t n, int64_t k, int64_t m,
+                          int64_t top_k, int64_t src1_outer_stride, int64_t src1_inner_stride,
+                          int64_t num_experts, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

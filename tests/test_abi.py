@@ -180,6 +180,17 @@ def test_mlx4_validation(lib):
     assert call(st=stride + 8) == _lib.Q4K_ERR_NULL       # stride not 16-byte aligned
     assert call(s_off=so + 1) == _lib.Q4K_ERR_NULL
     assert call(dst=None) == _lib.Q4K_ERR_NULL
+    f = q4.mlx4_moe_gate_up_silu
+    goffs, uoffs = (0, so, bo), (0, so, bo)
+    past = stride - n * k // 2 + 16
+    assert _err(f, FAKE, stride, goffs, (past, so, bo), FAKE, FAKE, FAKE, n, k, 1, 2, k, 0, 4) == \
+        _lib.Q4K_ERR_SHAPE                                 # up's packed runs past the block
+    assert _err(f, FAKE, stride, goffs, (0, so, bo + 1), FAKE, FAKE, FAKE, n, k, 1, 2, k, 0, 4) == \
+        _lib.Q4K_ERR_SHAPE                                 # up's biases run past the block
+    assert _err(f, FAKE, stride, goffs, uoffs, FAKE, FAKE, None, n, k, 1, 2, k, 0, 4) == \
+        _lib.Q4K_ERR_NULL
+    assert _err(f, FAKE, stride, goffs, uoffs, FAKE, FAKE, FAKE, n, k, 1, 2, -k, 0, 4) == \
+        _lib.Q4K_ERR_STRIDE
     d = q4.mlx4_dequantize
     assert _err(d, FAKE, FAKE, FAKE, FAKE, 4, 100) == _lib.Q4K_ERR_SHAPE
     assert _err(d, FAKE, FAKE + 1, FAKE, FAKE, 4, 128) == _lib.Q4K_ERR_NULL

@@ -162,3 +162,43 @@ def test_mlx4_invalid_ids_and_unit_vector_probe(dev):
                 assert np.array_equal(bits(got[p]), bits(col))
             else:
                 assert np.all(got[p] == 0.0)
+
+
+@pytest.mark.parametrize("shape", [(768, 2048, 1), (768, 2048, 16), (96, 448, 3)],
+                         ids=["decode m=1", "decode m=16", "ragged"])
+def test_mlx4_gate_up_silu_matches_oracle(dev, shape):
+    """Fused gate/up + SiLU over one expert block holding the gate and up
+    matrices: against silu(oracle gate) * oracle up, and bit for bit against
+    per-token calls."""
+    n, k, m = shape
+    E, K = 128 if n == 768 else 9, 8
+    say(f"gate/up + SiLU n={n} k={k} m={m}")
+    g = np.random.default_rng(90 + m)
+    ids = np.stack([g.choice(E, K, replace=False) for _ in range(m)]).reshape(-1).astype(np.int32)
+    gate = _experts(g, E, n, k, touched=ids)
+    up = _experts(g, E, n, k, touched=ids)
+    # one block per expert: gate's packed | scales | biases, then up's
+    gb, gstride, goffs = _blob(gate)
+    ub, ustride, uoffs = _blob(up)
+    stride = gstride + ustride
+    blob = np.zeros(E * stride, np.uint8)
+    for e in range(E):
+        blob[e * stride:e * stride + gstride] = gb[e * gstride:(e + 1) * gstride]
+        blob[e * stride + gstride:(e + 1) * stride] = ub[e * ustride:(e + 1) * ustride]
+    uoffs = tuple(o + gstride for o in uoffs)
+    x = g.standard_normal((m, k)).astype(np.float32)
+    go = oracle.mlx4_moe_id_gemv(blob, stride, *goffs, E, n, k, x, ids, m, K, k, 0)
+    uo = oracle.mlx4_moe_id_gemv(blob, stride, *uoffs, E, n, k, x, ids, m, K, k, 0)
+    want = np.array([oracle.silu(float(a)) * float(b) for a, b in zip(go.reshape(-1),
+                                                                       uo.reshape(-1))])
+    d_blob, d_x, d_ids = T(blob, dev), T(x, dev), T(ids, dev)
+    out = torch.empty(m * K, n, device=dev)
+    q4.mlx4_moe_gate_up_silu(d_blob, stride, goffs, uoffs, d_x, d_ids, out, n, k, m, K, k, 0, E)
+    got = sync_np(out)
+    r = band(got, want.reshape(m * K, n), "gate/up + SiLU")
+    say(f"  rel {r[0]:.3g} cos {r[1]:.9f}")
+    for t in range(min(m, 4)):
+        one = torch.empty(K, n, device=dev)
+        q4.mlx4_moe_gate_up_silu(d_blob, stride, goffs, uoffs, d_x[t:t + 1], d_ids[t * K:(t + 1) * K],
+                                 one, n, k, 1, K, k, 0, E)
+        assert np.array_equal(bits(sync_np(one)), bits(got[t * K:(t + 1) * K]))
