@@ -64,7 +64,7 @@ const char *q4k_status_string(int status) {
     }
 }
 
-int q4k_abi_version(void) { return 2; }
+int q4k_abi_version(void) { return 3; }
 
 int64_t q4k_matrix_bytes(int64_t n, int64_t k) {
     if (n < 0 || k <= 0 || k % Q4K_BLOCK_WEIGHTS)

@@ -67,6 +67,7 @@ enum { MOE_SHARED_NONE = 0, MOE_SHARED_SIGMOID = 1, MOE_SHARED_UNSCALED = 2 };
 #define MOE_LAYER_SYNC_TIMEOUT_WORD 576 /* 32-bit word of that header: barrier timed out */
 
 const char *q4k_status_string(int status);
+/* 3: adds the MLX 4-bit entry points (mlx4_*) to version 2's set. */
 int q4k_abi_version(void);
 
 /* Bytes of an n x k Q4_K matrix: n*(k/256)*144 ([FK]

@@ -46,7 +46,7 @@ def test_constants_match_header(lib):
                       ("MOE_LAYER_SYNC_TIMEOUT_WORD", 576),
                       ("Q4TP_MAX_TENSORS", _lib.Q4TP_MAX_TENSORS), ("MLX4_GROUP", 64)]:
         assert re.search(rf"#define {name} {val}\b", src), name
-    assert q4.q4k_abi_version() == 2
+    assert q4.q4k_abi_version() == 3
 
 
 def test_size_helpers(lib):
