@@ -13,6 +13,8 @@
 // group per lane (two when a row has more than 256 groups); x is staged in LDS
 // with per-group sums.  The group scale uses the hardware exp2 (about one
 // ulp), as the page's kernel does.
+#include <type_traits>
+
 #include "gemv_core.hpp"
 
 namespace q4k {
@@ -20,10 +22,10 @@ namespace q4k {
 // Group g's 32 activations start at 36*g floats in LDS (4 pad floats per
 // group keeps the 16-byte reads of neighbouring lanes in different banks).
 //
-// A workgroup takes ITERS x RPI rows.  The loads are issued in this order and
-// waited for one by one: x (a thread per 32-float group, float4), then every
-// row's (base, step) word, code bytes and 16-byte groups (branch-free, clamped
-// indices).  x is committed to LDS with its group sums (ascending, one thread
+// A workgroup of TPB threads takes ITERS x RPI rows (RPI = TPB / LPR).  The
+// loads are issued in this order and waited for one by one: x (a thread per
+// 32-float group, float4), then every row's (base, step) word, code bytes and
+// 16-byte groups (branch-free, clamped indices).  x is committed to LDS with its group sums (ascending, one thread
 // per group) while the weights are in flight; LDS-only barriers leave them in
 // flight.  Lane u of a row takes groups u, u + LPR, ... (NG of them).
 // Up to three tensors of the same width read the same x in one launch (the
@@ -37,8 +39,8 @@ struct TpSegs {
     int nseg;
 };
 
-template <int LPR, int NG, int ITERS, bool XV>
-__global__ __launch_bounds__(256) void k_q4tp_matvec(TpSegs sg, const float *__restrict__ x,
+template <int LPR, int NG, int ITERS, bool XV, int TPB>
+__global__ __launch_bounds__(TPB) void k_q4tp_matvec(TpSegs sg, const float *__restrict__ x,
                                                      float *__restrict__ yall, int cols) {
     extern __shared__ float lds[];
     // this workgroup's tensor (uniform scalar compares)
@@ -51,12 +53,12 @@ __global__ __launch_bounds__(256) void k_q4tp_matvec(TpSegs sg, const float *__r
     const int rows = sg.rows[seg];
     float *__restrict__ y = yall + sg.yoff[seg];
     const int tile = (int)blockIdx.x - (seg ? sg.tile_end[seg - 1] : 0);
-    constexpr int RPI = 256 / LPR;
+    constexpr int RPI = TPB / LPR;
     constexpr int WL = LPR < 64 ? LPR : 64;
     constexpr int WPR = LPR / WL;
-    constexpr int XU = (LPR * NG + 255) / 256;   // staging tasks per thread
+    constexpr int XU = (LPR * NG + TPB - 1) / TPB;   // staging tasks per thread
     const int gpr = cols >> 5;
-    float *red = lds;           // cross-wave row sums
+    float *red = lds;           // cross-wave row sums (one per wave, at most 16)
     float *xs = lds + 16;       // padded activations
     float *sx = xs + 36 * gpr;  // group sums
     const int tid = threadIdx.x;
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(256) void k_q4tp_matvec(TpSegs sg, const float *__r
     float4 xv[XU][8];
 #pragma unroll
     for (int k = 0; k < XU; k++) {
-        const int f = tid + 256 * k;
+        const int f = tid + TPB * k;
         const int fc = f < gpr ? f : gpr - 1;
         const float *src = x + 32 * fc;
 #pragma unroll
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(256) void k_q4tp_matvec(TpSegs sg, const float *__r
     // 3. activations into LDS, with their group sums
 #pragma unroll
     for (int k = 0; k < XU; k++) {
-        const int f = tid + 256 * k;
+        const int f = tid + TPB * k;
         if (f < gpr) {
             float4 *d = (float4 *)(xs + 36 * f);
             float sum = 0.0f;
@@ -184,14 +186,30 @@ static int tp_lanes(int gpr) {
     return l;
 }
 
-// Rows per workgroup: the fewest row groups whose weight bytes are at least
-// twice the staged activations (4 cols bytes, read from the cache by every
-// workgroup), at most 8 (4 with two groups per lane), while the grid still
-// gives every CU a workgroup.
+// Row groups per workgroup (tpb / LPR rows each): the fewest whose weight
+// bytes are at least twice the staged activations (4 cols bytes, read from the
+// cache by every workgroup), at most 8 (4 with two groups per lane), while the
+// grid still gives every CU a workgroup.
+static int tp_iters(int tpb, int lpr, int max_it, int64_t row_bytes, int cols, int64_t total_rows,
+                    int64_t cus) {
+    const int rpi = tpb / lpr;
+    int it = 1;
+    while (it < max_it && (int64_t)it * rpi * row_bytes < 8 * (int64_t)cols &&
+           (total_rows + 2 * it * rpi - 1) / (2 * it * rpi) >= cus)
+        it <<= 1;
+    return it;
+}
+
+// Workgroup size: every workgroup stages the whole activation row in LDS, so
+// bigger workgroups (more rows per staged row) cut the activation traffic
+// from the cache, which at 256 threads was about 0.7x the weight bytes of a
+// decode walk.  512 threads in general; 1024 when rows are at most 4096
+// columns and the grid then holds at most one workgroup per CU (a small
+// tensor, where more waves per CU hide more latency).  Q4TP_THREADS (256,
+// 512 or 1024) overrides.
 template <int LPR, int NG>
 static hipError_t tp_launch(const void *const *ts, const int64_t *rows, int nseg, const float *x,
                             float *y, int cols, hipStream_t st) {
-    constexpr int RPI = 256 / LPR;
     const int gpr = cols >> 5;
     const int64_t row_bytes = (int64_t)gpr * 16 + 4 + ((5 * gpr + 7) >> 3);
     const int64_t cus = cu_count();
@@ -199,10 +217,18 @@ static hipError_t tp_launch(const void *const *ts, const int64_t *rows, int nseg
     for (int i = 0; i < nseg; i++)
         total_rows += rows[i];
     constexpr int kMaxIt = NG == 1 ? 8 : 4;
-    int it = 1;
-    while (it < kMaxIt && (int64_t)it * RPI * row_bytes < 8 * (int64_t)cols &&
-           (total_rows + 2 * it * RPI - 1) / (2 * it * RPI) >= cus)
-        it <<= 1;
+    static const int tpb_env = env_int("Q4TP_THREADS", 0);
+    int tpb = 512;
+    if (tpb_env == 256 || tpb_env == 512 || tpb_env == 1024) {
+        tpb = tpb_env;
+    } else if (NG == 1 && gpr <= 128) {
+        const int it1k = tp_iters(1024, LPR, kMaxIt, row_bytes, cols, total_rows, cus);
+        const int64_t rows1k = (int64_t)it1k * (1024 / LPR);
+        if ((total_rows + rows1k - 1) / rows1k <= cus)
+            tpb = 1024;
+    }
+    const int RPI = tpb / LPR;
+    const int it = tp_iters(tpb, LPR, kMaxIt, row_bytes, cols, total_rows, cus);
     const size_t lds = (size_t)(16 + 36 * gpr + gpr) * sizeof(float);
     auto go = [&](auto kern, int iters) {
         TpSegs sg{};
@@ -217,19 +243,27 @@ static hipError_t tp_launch(const void *const *ts, const int64_t *rows, int nseg
         }
         sg.nseg = nseg;
         set_lds((const void *)kern, lds);
-        hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), lds, st, sg, x, y, cols);
+        hipLaunchKernelGGL(kern, dim3(tiles), dim3(tpb), lds, st, sg, x, y, cols);
         return hipGetLastError();
     };
     // float4 activation loads need a 16-byte aligned x
     const bool xv = ((uintptr_t)x & 15) == 0;
-    switch (it) {
-    case 1: return xv ? go(k_q4tp_matvec<LPR, NG, 1, true>, 1) : go(k_q4tp_matvec<LPR, NG, 1, false>, 1);
-    case 2: return xv ? go(k_q4tp_matvec<LPR, NG, 2, true>, 2) : go(k_q4tp_matvec<LPR, NG, 2, false>, 2);
-    case 4: return xv ? go(k_q4tp_matvec<LPR, NG, 4, true>, 4) : go(k_q4tp_matvec<LPR, NG, 4, false>, 4);
-    default:
-        return xv ? go(k_q4tp_matvec<LPR, NG, (NG == 1 ? 8 : 4), true>, kMaxIt)
-                  : go(k_q4tp_matvec<LPR, NG, (NG == 1 ? 8 : 4), false>, kMaxIt);
-    }
+    auto pick = [&](auto tpbc) -> hipError_t {
+        constexpr int T = decltype(tpbc)::value;
+        switch (it) {
+        case 1: return xv ? go(k_q4tp_matvec<LPR, NG, 1, true, T>, 1) : go(k_q4tp_matvec<LPR, NG, 1, false, T>, 1);
+        case 2: return xv ? go(k_q4tp_matvec<LPR, NG, 2, true, T>, 2) : go(k_q4tp_matvec<LPR, NG, 2, false, T>, 2);
+        case 4: return xv ? go(k_q4tp_matvec<LPR, NG, 4, true, T>, 4) : go(k_q4tp_matvec<LPR, NG, 4, false, T>, 4);
+        default:
+            return xv ? go(k_q4tp_matvec<LPR, NG, (NG == 1 ? 8 : 4), true, T>, kMaxIt)
+                      : go(k_q4tp_matvec<LPR, NG, (NG == 1 ? 8 : 4), false, T>, kMaxIt);
+        }
+    };
+    if (tpb == 1024)
+        return pick(std::integral_constant<int, 1024>{});
+    if (tpb == 512)
+        return pick(std::integral_constant<int, 512>{});
+    return pick(std::integral_constant<int, 256>{});
 }
 
 hipError_t launch_q4tp_matvec_multi(const void *const *ts, const int64_t *rows, int nseg,
