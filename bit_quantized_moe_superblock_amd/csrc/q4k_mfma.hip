@@ -520,11 +520,16 @@ static hipError_t go_mfma(const GemvArgs &a, hipStream_t st) {
     const int tiles = (a.n + kMRows - 1) / kMRows;
     auto kern = k_bucket_mfma<NT, EPI, SB>;
     const size_t lds = set_lds((const void *)kern, mfma_lds_bytes(SB));
-    int fit = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, (const void *)kern, kThreads, lds) !=
-            hipSuccess ||
-        fit < 1)
-        fit = 1;
+    // resident workgroups per CU: a property of the kernel and its fixed LDS
+    // size, asked once per instantiation
+    static const int fit = [&] {
+        int f = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&f, (const void *)kern, kThreads, lds) !=
+                hipSuccess ||
+            f < 1)
+            f = 1;
+        return f;
+    }();
     // as many workgroups as are resident at once, never more than the items
     // the longest possible list gives
     const int64_t items = (int64_t)(n_slots + sh_groups) * tiles;
