@@ -80,6 +80,7 @@ def _load():
         "orc_mlx4_quantize": (ctypes.c_int, [P, I64, I64, P, P, P]),
         "orc_mlx4_moe_id_gemv": (ctypes.c_int, [P, I64, I64, I64, I64, I64, I64, I64, P, P,
                                                 I64, I64, I64, I64, P]),
+        "orc_rmsnorm_bf16": (ctypes.c_int, [P, P, ctypes.c_float, I64, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -312,4 +313,16 @@ def mlx4_moe_id_gemv(base: np.ndarray, expert_stride: int, packed_off: int, scal
     _check(_load().orc_mlx4_moe_id_gemv(_ptr(base), expert_stride, packed_off, scales_off,
                                         biases_off, num_experts, n, k, _ptr(src1), _ptr(ids), m,
                                         top_k, outer, inner, _ptr(out)), "mlx4_moe_id_gemv")
+    return out
+
+
+# ------------------------------------------------------ chained RMSNorm ----
+
+def rmsnorm_bf16(x: np.ndarray, w_bf16: np.ndarray, eps: float) -> np.ndarray:
+    """x [m, H] fp32, w [H] bf16 bit patterns (uint16) -> x / rms(x) * w, fp32."""
+    x = _c(np.atleast_2d(x), np.float32)
+    w = _c(w_bf16, np.uint16)
+    m, H = x.shape
+    out = np.zeros((m, H), np.float32)
+    _check(_load().orc_rmsnorm_bf16(_ptr(x), _ptr(w), float(eps), m, H, _ptr(out)), "rmsnorm_bf16")
     return out

@@ -707,3 +707,29 @@ int orc_mlx4_moe_id_gemv(const uint8_t *base, int64_t expert_stride, int64_t pac
     free(tmp);
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Chained RMSNorm of the combine output ([MF] ChainToNormed and the chain  */
+/* appendix after the combine: rms_norm_sum_sq, then rms_norm_apply_bf16    */
+/* with the next layer's input-norm weight, bf16, and eps):                 */
+/*   normed[t,i] = x[t,i] / sqrt(sum_j x[t,j]^2 / H + eps) * w[i].           */
+/* The pages name the two kernels and their inputs, not the formula; this   */
+/* is the textbook RMSNorm.  Sum of squares and the scaling in double,      */
+/* stored as float.                                                          */
+/* ------------------------------------------------------------------------ */
+int orc_rmsnorm_bf16(const float *x, const uint16_t *w, float eps, int64_t m, int64_t hidden,
+                     float *out)
+{
+    if (m < 0 || hidden <= 0)
+        return ORC_EINVAL;
+    for (int64_t t = 0; t < m; t++) {
+        const float *row = x + t * hidden;
+        double ss = 0.0;
+        for (int64_t i = 0; i < hidden; i++)
+            ss += (double)row[i] * (double)row[i];
+        double inv = 1.0 / sqrt(ss / (double)hidden + (double)eps);
+        for (int64_t i = 0; i < hidden; i++)
+            out[t * hidden + i] = (float)((double)row[i] * inv * (double)orc_bf16_to_f32(w[i]));
+    }
+    return ORC_OK;
+}

@@ -267,3 +267,43 @@ def test_bucket_zipf_config_shape():
     assert 30 <= used <= 80
     for t in range(cfg.m):
         assert len(set(ids[t * cfg.top_k:(t + 1) * cfg.top_k])) == cfg.top_k
+
+
+# ------------------------------------------------------- chained RMSNorm ----
+
+def _bf16(vals):
+    return np.array([oracle.f32_to_bf16(float(v)) for v in vals], np.uint16)
+
+
+def test_rmsnorm_hand_values_and_closed_forms():
+    # [1, 7]: mean square 25, rms 5 -> [0.2, 1.4] (by hand); weights 1 and 2
+    got = oracle.rmsnorm_bf16(np.array([[1.0, 7.0]], np.float32), _bf16([1.0, 2.0]), 0.0)
+    assert got[0].tolist() == [np.float32(0.2), np.float32(2.8)]
+    # a constant row c with eps = 0 normalises to sign(c) * w
+    w = _bf16(np.linspace(-3, 3, 64))
+    wf = np.array([oracle.bf16_to_f32(int(h)) for h in w], np.float32)
+    for c in (-2.5, 0.125, 7.0):
+        got = oracle.rmsnorm_bf16(np.full((1, 64), c, np.float32), w, 0.0)
+        assert np.array_equal(got[0], np.sign(c) * wf)
+    # zero row with eps > 0 stays zero; eps enters under the root: x = 0.5
+    # everywhere, eps = 0.75 -> rms 1 -> 0.5 * w
+    assert np.all(oracle.rmsnorm_bf16(np.zeros((2, 8), np.float32), _bf16([1.0] * 8), 1e-6) == 0)
+    got = oracle.rmsnorm_bf16(np.full((1, 8), 0.5, np.float32), _bf16([3.0] * 8), 0.75)
+    assert np.all(got == 1.5)
+
+
+def test_rmsnorm_scale_invariance_and_rows_independent():
+    g = np.random.default_rng(11)
+    x = g.standard_normal((3, 2048)).astype(np.float32)
+    w = _bf16(g.standard_normal(2048))
+    base = oracle.rmsnorm_bf16(x, w, 0.0)
+    for a in (0.5, 4.0, 1024.0):   # powers of two scale exactly
+        assert np.array_equal(oracle.rmsnorm_bf16(x * np.float32(a), w, 0.0), base)
+    # each row normalises on its own: the batch equals row-by-row calls
+    for t in range(3):
+        assert np.array_equal(oracle.rmsnorm_bf16(x[t:t + 1], w, 0.0)[0], base[t])
+    # unit mean square: the output is x * w (to float rounding)
+    xs = x[0] / np.sqrt(np.mean(x[0].astype(np.float64) ** 2))
+    wf = np.array([oracle.bf16_to_f32(int(h)) for h in w])
+    np.testing.assert_allclose(oracle.rmsnorm_bf16(xs[None].astype(np.float32), w, 0.0)[0],
+                               xs * wf, rtol=1e-6, atol=1e-7)
