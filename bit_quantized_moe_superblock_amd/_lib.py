@@ -43,6 +43,11 @@ SIGNATURES = {
     "moe_layer_forward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64,
                                _I64, _I64, _I, _I, _P, _I64, _P]),
     "moe_combine_residual": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
+    "moe_layer_forward_rmsnorm": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       ctypes.c_float, _P, _I64, _I64, _I64, _I64, _I64, _I,
+                                       _I, _P, _I64, _P]),
+    "moe_combine_residual_rmsnorm": (_I, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _I64,
+                                          _I64, _I64, _I, _P]),
     "q4tp_tensor_bytes": (_I64, [_I64, _I64]),
     "q4tp_matvec": (_I, [_P, _P, _P, _I64, _I64, _P]),
     "q4tp_matvec_multi": (_I, [_P, _P, _I, _P, _P, _I64, _P]),
@@ -245,3 +250,23 @@ def mlx4_moe_gate_up_silu(expert_base, expert_stride: int, gate_offs, up_offs, s
     _call("mlx4_moe_gate_up_silu", _ptr(expert_base), expert_stride, *[int(o) for o in gate_offs],
           *[int(o) for o in up_offs], _ptr(src1), _ptr(ids), _ptr(dst), n, k, m, top_k,
           src1_outer_stride, src1_inner_stride, num_experts, _stream(stream))
+
+
+def moe_layer_forward_rmsnorm(w_gate, w_up, w_down, sh_gate, sh_up, sh_down, h_post, h_mid, ids,
+                              route_w, shared_gate_logit, out, norm_weight, eps: float, normed,
+                              hidden: int, inter: int, num_experts: int, m: int, top_k: int,
+                              shared_mode: int, bucket_flag: int = Q4K_BUCKET_AUTO, ws=None,
+                              ws_bytes: int = 0, stream=None):
+    _call("moe_layer_forward_rmsnorm", _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(sh_gate),
+          _ptr(sh_up), _ptr(sh_down), _ptr(h_post), _ptr(h_mid), _ptr(ids), _ptr(route_w),
+          _ptr(shared_gate_logit), _ptr(out), _ptr(norm_weight), float(eps), _ptr(normed),
+          hidden, inter, num_experts, m, top_k, shared_mode, bucket_flag, _ptr(ws), ws_bytes,
+          _stream(stream))
+
+
+def moe_combine_residual_rmsnorm(h_mid, expert_out, route_w, shared_out, shared_gate_logit,
+                                 norm_weight, eps: float, out, normed, hidden: int, m: int,
+                                 top_k: int, shared_mode: int, stream=None):
+    _call("moe_combine_residual_rmsnorm", _ptr(h_mid), _ptr(expert_out), _ptr(route_w),
+          _ptr(shared_out), _ptr(shared_gate_logit), _ptr(norm_weight), float(eps), _ptr(out),
+          _ptr(normed), hidden, m, top_k, shared_mode, _stream(stream))

@@ -275,13 +275,18 @@ int moe_layer_workspace_init(void *ws, int64_t ws_bytes, void *stream) {
     return launched(hipMemsetAsync(ws, 0, MOE_LAYER_SYNC_BYTES, as_stream(stream)));
 }
 
-int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
-                      const void *sh_gate, const void *sh_up, const void *sh_down,
-                      const float *h_post, const float *h_mid, const int32_t *ids,
-                      const float *route_w, const float *shared_gate_logit, float *out,
-                      int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
-                      int64_t top_k, int shared_mode, int bucket_flag, void *ws,
-                      int64_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int layer_forward_impl(const void *w_gate, const void *w_up, const void *w_down,
+                              const void *sh_gate, const void *sh_up, const void *sh_down,
+                              const float *h_post, const float *h_mid, const int32_t *ids,
+                              const float *route_w, const float *shared_gate_logit, float *out,
+                              int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
+                              int64_t top_k, int shared_mode, int bucket_flag, void *ws,
+                              int64_t ws_bytes, void *stream, const void *norm_weight, float eps,
+                              float *normed) {
     int rc = check_gemv_shape(inter, hidden, m, top_k, num_experts);
     if (rc)
         return rc;
@@ -347,7 +352,12 @@ int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
         L.num_experts = num_experts;
         L.top_k = top_k;
         L.shared_mode = shared_mode;
-        return launched(launch_layer_m1(L, st));
+        rc = launched(launch_layer_m1(L, st));
+        if (rc || !norm_weight)
+            return rc;
+        return launched(launch_combine_norm(nullptr, nullptr, nullptr, nullptr, nullptr,
+                                            norm_weight, eps, out, normed, hidden, m, top_k,
+                                            shared_mode, false, st));
     }
     GemvLaunch G{};
     G.w0 = w_gate;
@@ -399,14 +409,59 @@ int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
     rc = launched(launch_q4k_gemv(G, st));
     if (rc)
         return rc;
-    if (!bucketed)
-        return launched(launch_q4k_down_combine(D, h_mid, route_w, shared_gate_logit, out,
-                                                nullptr, shared_mode, st));
+    if (!bucketed) {
+        rc = launched(launch_q4k_down_combine(D, h_mid, route_w, shared_gate_logit, out, nullptr,
+                                              shared_mode, st));
+        if (rc || !norm_weight)
+            return rc;
+        return launched(launch_combine_norm(nullptr, nullptr, nullptr, nullptr, nullptr,
+                                            norm_weight, eps, out, normed, hidden, m, top_k,
+                                            shared_mode, false, st));
+    }
     rc = launched(launch_q4k_gemv(D, st));
     if (rc)
         return rc;
+    if (norm_weight)   // the combine and the norm in one launch, a workgroup per token
+        return launched(launch_combine_norm(h_mid, eo, route_w, has_sh ? s_out : nullptr,
+                                            shared_gate_logit, norm_weight, eps, out, normed,
+                                            hidden, m, top_k, shared_mode, true, st));
     return launched(launch_moe_combine(h_mid, eo, route_w, has_sh ? s_out : nullptr,
                                        shared_gate_logit, out, hidden, m, top_k, shared_mode, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
+                      const void *sh_gate, const void *sh_up, const void *sh_down,
+                      const float *h_post, const float *h_mid, const int32_t *ids,
+                      const float *route_w, const float *shared_gate_logit, float *out,
+                      int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
+                      int64_t top_k, int shared_mode, int bucket_flag, void *ws,
+                      int64_t ws_bytes, void *stream) {
+    return layer_forward_impl(w_gate, w_up, w_down, sh_gate, sh_up, sh_down, h_post, h_mid, ids,
+                              route_w, shared_gate_logit, out, hidden, inter, num_experts, m,
+                              top_k, shared_mode, bucket_flag, ws, ws_bytes, stream, nullptr,
+                              0.0f, nullptr);
+}
+
+int moe_layer_forward_rmsnorm(const void *w_gate, const void *w_up, const void *w_down,
+                              const void *sh_gate, const void *sh_up, const void *sh_down,
+                              const float *h_post, const float *h_mid, const int32_t *ids,
+                              const float *route_w, const float *shared_gate_logit, float *out,
+                              const void *norm_weight, float eps, float *normed, int64_t hidden,
+                              int64_t inter, int64_t num_experts, int64_t m, int64_t top_k,
+                              int shared_mode, int bucket_flag, void *ws, int64_t ws_bytes,
+                              void *stream) {
+    if (!norm_weight || !normed || !aligned2(norm_weight) || !aligned4(normed) || normed == out)
+        return Q4K_ERR_NULL;
+    if (!(eps >= 0.0f) || eps > 3.0e38f)
+        return Q4K_ERR_ARG;
+    return layer_forward_impl(w_gate, w_up, w_down, sh_gate, sh_up, sh_down, h_post, h_mid, ids,
+                              route_w, shared_gate_logit, out, hidden, inter, num_experts, m,
+                              top_k, shared_mode, bucket_flag, ws, ws_bytes, stream, norm_weight,
+                              eps, normed);
 }
 
 int moe_combine_residual(const float *h_mid, const float *expert_out, const float *route_w,
@@ -426,6 +481,30 @@ int moe_combine_residual(const float *h_mid, const float *expert_out, const floa
         return Q4K_ERR_NULL;
     return launched(launch_moe_combine(h_mid, expert_out, route_w, shared_out, shared_gate_logit,
                                        out, hidden, m, top_k, shared_mode, as_stream(stream)));
+}
+
+int moe_combine_residual_rmsnorm(const float *h_mid, const float *expert_out,
+                                 const float *route_w, const float *shared_out,
+                                 const float *shared_gate_logit, const void *norm_weight, float eps,
+                                 float *out, float *normed, int64_t hidden, int64_t m,
+                                 int64_t top_k, int shared_mode, void *stream) {
+    if (hidden < 1 || m < 1 || m > 65535 || top_k < 1 || top_k > Q4K_MAX_TOP_K)
+        return Q4K_ERR_SHAPE;
+    if (shared_mode != MOE_SHARED_NONE && shared_mode != MOE_SHARED_SIGMOID &&
+        shared_mode != MOE_SHARED_UNSCALED)
+        return Q4K_ERR_ARG;
+    if (!(eps >= 0.0f) || eps > 3.0e38f)
+        return Q4K_ERR_ARG;
+    if (!h_mid || !expert_out || !route_w || !out || !normed || !norm_weight ||
+        !aligned2(norm_weight) || normed == out)
+        return Q4K_ERR_NULL;
+    if (shared_mode != MOE_SHARED_NONE && !shared_out)
+        return Q4K_ERR_NULL;
+    if (shared_mode == MOE_SHARED_SIGMOID && !shared_gate_logit)
+        return Q4K_ERR_NULL;
+    return launched(launch_combine_norm(h_mid, expert_out, route_w, shared_out, shared_gate_logit,
+                                        norm_weight, eps, out, normed, hidden, m, top_k,
+                                        shared_mode, true, as_stream(stream)));
 }
 
 int64_t q4tp_tensor_bytes(int64_t rows, int64_t cols) {

@@ -44,6 +44,13 @@ hipError_t launch_moe_combine(const float *h_mid, const float *expert_out, const
                               const float *shared_out, const float *shared_gate_logit, float *out,
                               int64_t hidden, int64_t m, int64_t top_k, int shared_mode,
                               hipStream_t st);
+// RMSNorm of the rows of `out` into `normed` with a bf16 weight; with
+// `combine` the rows are first computed by the combine and written to `out`.
+hipError_t launch_combine_norm(const float *h_mid, const float *expert_out, const float *route_w,
+                               const float *shared_out, const float *shared_gate_logit,
+                               const void *norm_weight, float eps, float *out, float *normed,
+                               int64_t hidden, int64_t m, int64_t top_k, int shared_mode,
+                               bool combine, hipStream_t st);
 hipError_t launch_q4tp_matvec_multi(const void *const *ts, const int64_t *rows, int nseg,
                                     const float *x, float *y, int64_t cols, hipStream_t st);
 hipError_t launch_q4tp_matvec(const void *t, const float *x, float *y, int64_t rows,

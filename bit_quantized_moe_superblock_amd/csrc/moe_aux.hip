@@ -134,22 +134,18 @@ hipError_t launch_moe_bucket(const int32_t *ids, int64_t n_pairs, int64_t num_ex
     return hipGetLastError();
 }
 
-// One thread per output element.  The top_k expert rows and weights are all
+// Combined value of output (t, i).  The top_k expert rows and weights are all
 // loaded before the first use (slots past top_k re-load the last one, clamped,
 // and are skipped), so the loads are in flight together; the sum then runs in
 // slot order, one fma per slot, as the pages' combine does.
 template <int KMAX>
-__global__ __launch_bounds__(256) void k_moe_combine(const float *__restrict__ h_mid,
-                                                     const float *__restrict__ eo,
-                                                     const float *__restrict__ w,
-                                                     const float *__restrict__ shared,
-                                                     const float *__restrict__ logit,
-                                                     float *out, int64_t H, int64_t m, int K,
-                                                     int mode) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= H * m)
-        return;
-    const int64_t t = idx / H, i = idx - t * H;
+__device__ __forceinline__ float combine_one(const float *__restrict__ h_mid,
+                                             const float *__restrict__ eo,
+                                             const float *__restrict__ w,
+                                             const float *__restrict__ shared,
+                                             const float *__restrict__ logit, int64_t H,
+                                             int64_t t, int64_t i, int K, int mode) {
+    const int64_t idx = t * H + i;
     float e[KMAX], wv[KMAX];
 #pragma unroll
     for (int s = 0; s < KMAX; s++) {
@@ -170,7 +166,90 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float *__restrict__ h
     } else if (mode == 2) {
         acc += sh;
     }
-    out[idx] = acc;
+    return acc;
+}
+
+// One thread per output element.
+template <int KMAX>
+__global__ __launch_bounds__(256) void k_moe_combine(const float *__restrict__ h_mid,
+                                                     const float *__restrict__ eo,
+                                                     const float *__restrict__ w,
+                                                     const float *__restrict__ shared,
+                                                     const float *__restrict__ logit,
+                                                     float *out, int64_t H, int64_t m, int K,
+                                                     int mode) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= H * m)
+        return;
+    const int64_t t = idx / H, i = idx - t * H;
+    out[idx] = combine_one<KMAX>(h_mid, eo, w, shared, logit, H, t, i, K, mode);
+}
+
+// RMSNorm of each row of `out` into `normed` (moeflux's chain appendix after
+// the combine: sum of squares, then the bf16-weighted apply), one workgroup
+// per token; with COMBINE the row is first computed by the combine (same
+// arithmetic as k_moe_combine) and written to `out`.
+//   normed[t, i] = out[t, i] / sqrt(sum_j out[t, j]^2 / H + eps) * w[i]
+// Each thread re-reads only the outputs it wrote itself.
+template <int KMAX, bool COMBINE>
+__global__ __launch_bounds__(256) void k_combine_norm(const float *__restrict__ h_mid,
+                                                      const float *__restrict__ eo,
+                                                      const float *__restrict__ w,
+                                                      const float *__restrict__ shared,
+                                                      const float *__restrict__ logit,
+                                                      const uint16_t *__restrict__ nw, float eps,
+                                                      float *out, float *__restrict__ normed,
+                                                      int64_t H, int K, int mode) {
+    __shared__ float part[4];
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    float ss = 0.0f;
+    for (int64_t i = tid; i < H; i += 256) {
+        float v;
+        if constexpr (COMBINE) {
+            v = combine_one<KMAX>(h_mid, eo, w, shared, logit, H, t, i, K, mode);
+            out[t * H + i] = v;
+        } else {
+            v = out[t * H + i];
+        }
+        ss = __builtin_fmaf(v, v, ss);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        ss += __shfl_xor(ss, off, 64);
+    if ((tid & 63) == 0)
+        part[tid >> 6] = ss;
+    __syncthreads();
+    const float total = (part[0] + part[1]) + (part[2] + part[3]);
+    const float inv = 1.0f / sqrtf(total / (float)H + eps);
+    for (int64_t i = tid; i < H; i += 256) {
+        const float wi = __uint_as_float((uint32_t)nw[i] << 16);
+        normed[t * H + i] = out[t * H + i] * inv * wi;
+    }
+}
+
+hipError_t launch_combine_norm(const float *h_mid, const float *expert_out, const float *route_w,
+                               const float *shared_out, const float *shared_gate_logit,
+                               const void *norm_weight, float eps, float *out, float *normed,
+                               int64_t hidden, int64_t m, int64_t top_k, int shared_mode,
+                               bool combine, hipStream_t st) {
+    if (m == 0)
+        return hipSuccess;
+    const uint16_t *nw = (const uint16_t *)norm_weight;
+    const dim3 grid((unsigned)m);
+    if (!combine)
+        hipLaunchKernelGGL((k_combine_norm<1, false>), grid, dim3(256), 0, st, h_mid, expert_out,
+                           route_w, shared_out, shared_gate_logit, nw, eps, out, normed, hidden,
+                           (int)top_k, shared_mode);
+    else if (top_k <= 8)
+        hipLaunchKernelGGL((k_combine_norm<8, true>), grid, dim3(256), 0, st, h_mid, expert_out,
+                           route_w, shared_out, shared_gate_logit, nw, eps, out, normed, hidden,
+                           (int)top_k, shared_mode);
+    else
+        hipLaunchKernelGGL((k_combine_norm<kMaxTopK, true>), grid, dim3(256), 0, st, h_mid,
+                           expert_out, route_w, shared_out, shared_gate_logit, nw, eps, out,
+                           normed, hidden, (int)top_k, shared_mode);
+    return hipGetLastError();
 }
 
 hipError_t launch_moe_combine(const float *h_mid, const float *expert_out, const float *route_w,

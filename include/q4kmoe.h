@@ -67,7 +67,9 @@ enum { MOE_SHARED_NONE = 0, MOE_SHARED_SIGMOID = 1, MOE_SHARED_UNSCALED = 2 };
 #define MOE_LAYER_SYNC_TIMEOUT_WORD 576 /* 32-bit word of that header: barrier timed out */
 
 const char *q4k_status_string(int status);
-/* 3: adds the MLX 4-bit entry points (mlx4_*) to version 2's set. */
+/* 3: adds the MLX 4-bit entry points (mlx4_*) and the chained RMSNorm
+ * (moe_layer_forward_rmsnorm, moe_combine_residual_rmsnorm) to version 2's
+ * set. */
 int q4k_abi_version(void);
 
 /* Bytes of an n x k Q4_K matrix: n*(k/256)*144 ([FK]
@@ -220,6 +222,26 @@ int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
                       int64_t top_k, int shared_mode, int bucket_flag, void *ws,
                       int64_t ws_bytes, void *stream);
 
+/* The same layer with the next layer's input RMSNorm chained on ([MF]
+ * ChainToNormed: after the combine, rms_norm_sum_sq and rms_norm_apply_bf16
+ * with the next layer's input-norm weight and eps):
+ *   out    as moe_layer_forward (bit for bit: the same launches),
+ *   normed[t, i] = out[t, i] / sqrt(sum_j out[t, j]^2 / hidden + eps) * w[i],
+ * norm_weight: [hidden] bf16, 2-byte aligned; normed: [m, hidden] fp32, not
+ * `out`.  The few-token path adds one launch (a workgroup per token) after
+ * down + combine; the bucketed path computes the combine and the norm in one
+ * launch.  Errors as moe_layer_forward, plus Q4K_ERR_NULL (norm_weight or
+ * normed missing or misaligned, normed == out) and Q4K_ERR_ARG (eps negative,
+ * infinite or NaN). */
+int moe_layer_forward_rmsnorm(const void *w_gate, const void *w_up, const void *w_down,
+                              const void *sh_gate, const void *sh_up, const void *sh_down,
+                              const float *h_post, const float *h_mid, const int32_t *ids,
+                              const float *route_w, const float *shared_gate_logit, float *out,
+                              const void *norm_weight, float eps, float *normed, int64_t hidden,
+                              int64_t inter, int64_t num_experts, int64_t m, int64_t top_k,
+                              int shared_mode, int bucket_flag, void *ws, int64_t ws_bytes,
+                              void *stream);
+
 /* Weighted combine with residual ([MF] module doc and
  * encode_moe_combine_residual_n_tokens):
  *   out[t,i] = h_mid[t,i] + sum_{s<top_k} route_w[t*top_k+s]*expert_out[t*top_k+s,i]
@@ -232,6 +254,19 @@ int moe_combine_residual(const float *h_mid, const float *expert_out, const floa
                          const float *shared_out, const float *shared_gate_logit, float *out,
                          int64_t hidden, int64_t m, int64_t top_k, int shared_mode,
                          void *stream);
+
+/* moe_combine_residual followed by the chained RMSNorm of its rows, in one
+ * launch of a workgroup per token: `out` is moe_combine_residual's result
+ * bit for bit, normed[t, i] = out[t, i] / sqrt(sum_j out[t, j]^2 / hidden + eps)
+ * * w[i] with norm_weight [hidden] bf16 (2-byte aligned).  normed must not be
+ * `out` (out may alias h_mid).  1 <= m <= 65535.  Errors as
+ * moe_combine_residual plus Q4K_ERR_NULL (norm_weight, normed) and
+ * Q4K_ERR_ARG (eps negative, infinite or NaN). */
+int moe_combine_residual_rmsnorm(const float *h_mid, const float *expert_out,
+                                 const float *route_w, const float *shared_out,
+                                 const float *shared_gate_logit, const void *norm_weight, float eps,
+                                 float *out, float *normed, int64_t hidden, int64_t m,
+                                 int64_t top_k, int shared_mode, void *stream);
 
 /* Q4TiledP dense tensor ([CE] kernel `cur`): rows x cols, cols % 32 == 0,
  * gpr = cols/32 groups of 32 signed nibbles (value = nibble - 8, byte i of a

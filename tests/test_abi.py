@@ -197,3 +197,30 @@ def test_mlx4_validation(lib):
     qz = q4.mlx4_quantize
     assert _err(qz, FAKE, FAKE, FAKE, FAKE, 4, 32) == _lib.Q4K_ERR_SHAPE
     assert _err(qz, FAKE, FAKE + 4, FAKE, FAKE, 4, 64) == _lib.Q4K_ERR_NULL
+
+
+def test_rmsnorm_chain_validation(lib):
+    c = q4.moe_combine_residual_rmsnorm
+    ok = [FAKE, FAKE, FAKE, None, None, FAKE, 1e-6, FAKE, FAKE + 4096, 64, 2, 2, 0]
+
+    def call(i=None, v=None):
+        args = list(ok)
+        if i is not None:
+            args[i] = v
+        return _err(c, *args)
+
+    assert call(9, 0) == _lib.Q4K_ERR_SHAPE          # hidden
+    assert call(10, 0) == _lib.Q4K_ERR_SHAPE         # m
+    assert call(11, 17) == _lib.Q4K_ERR_SHAPE        # top_k
+    assert call(12, 5) == _lib.Q4K_ERR_ARG           # shared mode
+    assert call(6, -1.0) == _lib.Q4K_ERR_ARG         # eps
+    assert call(6, float("nan")) == _lib.Q4K_ERR_ARG
+    assert call(5, None) == _lib.Q4K_ERR_NULL        # norm weight
+    assert call(5, FAKE + 1) == _lib.Q4K_ERR_NULL
+    assert call(8, FAKE) == _lib.Q4K_ERR_NULL        # normed == out
+    assert call(12, 1) == _lib.Q4K_ERR_NULL          # sigmoid mode needs shared and logit
+    f = q4.moe_layer_forward_rmsnorm
+    base = [FAKE] * 12
+    assert _err(f, *base, None, 1e-6, FAKE, 512, 256, 4, 1, 2, 0) == _lib.Q4K_ERR_NULL
+    assert _err(f, *base, FAKE, -1.0, FAKE + 4096, 512, 256, 4, 1, 2, 0) == _lib.Q4K_ERR_ARG
+    assert _err(f, *base, FAKE, 1e-6, FAKE, 512, 256, 4, 1, 2, 0) == _lib.Q4K_ERR_NULL

@@ -603,6 +603,68 @@ def test_layer_invalid_ids_and_token_mode_edges(dev):
         band(res[1], want, "bucketed")
 
 
+def _bf16w(g, H):
+    return np.array([oracle.f32_to_bf16(float(v)) for v in 1.0 + 0.1 * g.standard_normal(H)],
+                    np.uint16)
+
+
+@pytest.mark.parametrize("m,K,mode", [(1, 8, 1), (16, 8, 1), (3, 4, 2), (5, 16, 0)])
+def test_combine_rmsnorm_matches_oracle_and_combine(dev, m, K, mode):
+    """The fused combine + chained RMSNorm: out bit for bit the combine's,
+    normed against the oracle's RMSNorm of the oracle's combine."""
+    say(f"combine + RMSNorm m={m} K={K} mode={mode}")
+    g = np.random.default_rng(400 + m)
+    H = 2048
+    hm = g.standard_normal((m, H)).astype(np.float32)
+    eo = g.standard_normal((m * K, H)).astype(np.float32)
+    rw = g.random(m * K).astype(np.float32)
+    so = g.standard_normal((m, H)).astype(np.float32) if mode else None
+    lg = g.standard_normal(m).astype(np.float32) if mode == 1 else None
+    w = _bf16w(g, H)
+    eps = 1e-6
+    want_out = oracle.moe_combine_residual(hm, eo, rw, so, lg, H, m, K, mode)
+    want = oracle.rmsnorm_bf16(want_out, w, eps)
+    d = lambda a: None if a is None else T(a, dev)
+    out = torch.empty(m, H, device=dev)
+    normed = torch.empty(m, H, device=dev)
+    q4.moe_combine_residual_rmsnorm(T(hm, dev), T(eo, dev), T(rw, dev), d(so), d(lg),
+                                    T(w.view(np.int16), dev), eps, out, normed, H, m, K, mode)
+    ref = torch.empty(m, H, device=dev)
+    q4.moe_combine_residual(T(hm, dev), T(eo, dev), T(rw, dev), d(so), d(lg), ref, H, m, K, mode)
+    assert np.array_equal(bits(sync_np(out)), bits(sync_np(ref)))
+    band(sync_np(out), want_out, "combine")
+    r = band(sync_np(normed), want, "normed")
+    say(f"  normed rel {r[0]:.3g} cos {r[1]:.9f}")
+
+
+@pytest.mark.parametrize("cfg", [wl.CFG2, wl.CFG3], ids=lambda c: c.name)
+def test_layer_forward_rmsnorm(dev, cfg):
+    """The layer with the next layer's input RMSNorm chained on: `out` bit for
+    bit moe_layer_forward's, `normed` against the oracle's RMSNorm of the
+    oracle's layer output."""
+    say(f"moe_layer_forward_rmsnorm {cfg.name}")
+    H, I, E, K, m = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.m
+    a, ids, d_st, h_st = _ffn_case(cfg, dev)
+    sd, sh = _shared_stacks(cfg, dev)
+    g = np.random.default_rng(500 + m)
+    w = _bf16w(g, H)
+    eps = 1e-5
+    plain = _layer_gpu(dev, cfg, d_st, sd, a, ids, q4.Q4K_BUCKET_AUTO)
+    wsb = q4.moe_layer_workspace_bytes(H, I, E, m, K)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    out = torch.empty(m, H, device=dev)
+    normed = torch.empty(m, H, device=dev)
+    q4.moe_layer_forward_rmsnorm(*d_st, *sd, T(a.h_post, dev), T(a.h_mid, dev), T(ids, dev),
+                                 T(a.route_w, dev), T(a.shared_logit, dev), out,
+                                 T(w.view(np.int16), dev), eps, normed, H, I, E, m, K,
+                                 cfg.shared_mode, q4.Q4K_BUCKET_AUTO, ws, wsb)
+    got_out = sync_np(out)
+    assert np.array_equal(bits(got_out), bits(plain))
+    want = oracle.rmsnorm_bf16(_layer_oracle(cfg, h_st, sh, a, ids), w, eps)
+    r = band(sync_np(normed), want, "layer normed")
+    say(f"  normed rel {r[0]:.3g} cos {r[1]:.9f}")
+
+
 @pytest.fixture
 def no_self_bucket():
     """Keeps the separate bucketing launch in bucketed layers for one call."""
