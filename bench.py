@@ -95,6 +95,8 @@ class Layer:
         self.s_act = torch.empty(m, I, device=dev)
         self.s_out = torch.empty(m, H, device=dev)
         self.out = torch.empty(m, H, device=dev)
+        self.normed = torch.empty(m, H, device=dev)
+        self.norm_w = torch.ones(H, device=dev).to(torch.bfloat16)   # next layer's norm weight
         self.lwsb = self.q4.moe_layer_workspace_bytes(H, I, cfg.num_experts, m, K)
         self.lws = torch.zeros(self.lwsb, dtype=torch.uint8, device=dev)   # barrier words zero
         self.wsb = self.q4.moe_bucket_workspace_bytes(P, cfg.num_experts)
@@ -134,6 +136,17 @@ class Layer:
                              x["ids"], x["route_w"], x["logit"], self.out, cfg.hidden, cfg.inter,
                              cfg.num_experts, cfg.m, cfg.top_k, cfg.shared_mode,
                              q4.Q4K_BUCKET_AUTO, self.lws, self.lwsb)
+
+    def layer_norm(self, i):
+        """The layer with the next layer's input RMSNorm chained on."""
+        q4, cfg = self.q4, self.cfg
+        r, s = self.step_of(i)
+        st, x = self.stacks[r], self.sets[s]
+        q4.moe_layer_forward_rmsnorm(st[0], st[1], st[2], st[3], st[4], st[5], x["h_post"],
+                                     x["h_mid"], x["ids"], x["route_w"], x["logit"], self.out,
+                                     self.norm_w, 1e-6, self.normed, cfg.hidden, cfg.inter,
+                                     cfg.num_experts, cfg.m, cfg.top_k, cfg.shared_mode,
+                                     q4.Q4K_BUCKET_AUTO, self.lws, self.lwsb)
 
     def layer_bytes(self, i):
         r, s = self.step_of(i)
@@ -314,6 +327,7 @@ def run_workload(torch, q4, wl, cfg, args, stacks=None):
         log(f"{cfg.name}: {steps} eager layers timed")
         gpu_s, wall_s = time_eager(torch, layer.layer, steps, args.warmup)
         gu_s, _ = time_eager(torch, layer.gate_up, steps, args.warmup)
+        norm_s, _ = time_eager(torch, layer.layer_norm, steps, args.warmup)
         G, warm = 1, args.warmup
         idx = range(steps)
         mode = "eager launches"
@@ -327,7 +341,9 @@ def run_workload(torch, q4, wl, cfg, args, stacks=None):
         gpu_s, wall_s = time_graph(torch, g_layer, replays, warm_replays)
         g_gu = capture(torch, layer.gate_up, G)
         gu_s, _ = time_graph(torch, g_gu, replays, warm_replays)
-        del g_layer, g_gu
+        g_norm = capture(torch, layer.layer_norm, G)
+        norm_s, _ = time_graph(torch, g_norm, replays, warm_replays)
+        del g_layer, g_gu, g_norm
         idx = [i % G for i in range(steps)]
         mode = f"HIP graphs of {G} layers"
     total_bytes = sum(layer.layer_bytes(i) for i in idx)
@@ -335,7 +351,8 @@ def run_workload(torch, q4, wl, cfg, args, stacks=None):
     res = dict(steps=steps, warmup=warm, gpu_s=gpu_s, wall_s=wall_s, mode=mode, group=G,
                us_per_layer=gpu_s / steps * 1e6, gbs=total_bytes / gpu_s / 1e9,
                bytes_per_layer=total_bytes / steps, gate_up_us=gu_s / steps * 1e6,
-               gate_up_gbs=gu_bytes / gu_s / 1e9, gate_up_bytes=gu_bytes / steps)
+               gate_up_gbs=gu_bytes / gu_s / 1e9, gate_up_bytes=gu_bytes / steps,
+               us_per_layer_rmsnorm=norm_s / steps * 1e6)
     return res, layer.stacks
 
 
@@ -462,12 +479,14 @@ def main():
 
     res1, stacks = run_workload(torch, q4, wl, wl.CFG2, args)
     log(f"m=1: {res1['us_per_layer']:.2f} us/layer, {res1['gbs']:.1f} GB/s; gate/up "
-        f"{res1['gate_up_us']:.2f} us, {res1['gate_up_gbs']:.1f} GB/s")
+        f"{res1['gate_up_us']:.2f} us, {res1['gate_up_gbs']:.1f} GB/s; with the next "
+        f"layer's RMSNorm {res1['us_per_layer_rmsnorm']:.2f} us")
     res16 = None
     if not args.no_m16:
         res16, _ = run_workload(torch, q4, wl, wl.CFG3, args, stacks)
         log(f"m=16: {res16['us_per_layer']:.2f} us/layer, {res16['gbs']:.1f} GB/s; gate/up "
-            f"{res16['gate_up_us']:.2f} us, {res16['gate_up_gbs']:.1f} GB/s")
+            f"{res16['gate_up_us']:.2f} us, {res16['gate_up_gbs']:.1f} GB/s; with the next "
+            f"layer's RMSNorm {res16['us_per_layer_rmsnorm']:.2f} us")
     walk_us = None
     if not args.no_walk:
         walk_us, walk_single_us, walk_bytes = run_walk(torch, q4, wl, 2, 32, 1)
@@ -507,6 +526,7 @@ def main():
             "bytes_per_layer": int(res1["bytes_per_layer"]),
         },
         "us_per_layer": round(res1["us_per_layer"], 3),
+        "us_per_layer_with_next_rmsnorm": round(res1["us_per_layer_rmsnorm"], 3),
         "frac_hbm_peak": round(res1["gbs"] / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm",
@@ -526,6 +546,7 @@ def main():
             "workload": "same layer, m=16 tokens, Zipf(1.1) routing, bucketed",
             "value": round(res16["gbs"], 2), "unit": "GB/s",
             "us_per_layer": round(res16["us_per_layer"], 3),
+            "us_per_layer_with_next_rmsnorm": round(res16["us_per_layer_rmsnorm"], 3),
             "frac_hbm_peak": round(res16["gbs"] / HBM_PEAK_GBS, 4),
             "bytes_per_layer": int(res16["bytes_per_layer"]),
             "gate_up_gbs": round(res16["gate_up_gbs"], 2),

@@ -187,12 +187,15 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float *__restrict__ h
 
 // RMSNorm of each row of `out` into `normed` (moeflux's chain appendix after
 // the combine: sum of squares, then the bf16-weighted apply), one workgroup
-// per token; with COMBINE the row is first computed by the combine (same
-// arithmetic as k_moe_combine) and written to `out`.
+// per token of kNormThreads threads (a few outputs per thread, so a token's
+// loads are in flight together); with COMBINE the row is first computed by
+// the combine (same arithmetic as k_moe_combine) and written to `out`.
 //   normed[t, i] = out[t, i] / sqrt(sum_j out[t, j]^2 / H + eps) * w[i]
 // Each thread re-reads only the outputs it wrote itself.
+constexpr int kNormThreads = 1024;
+
 template <int KMAX, bool COMBINE>
-__global__ __launch_bounds__(256) void k_combine_norm(const float *__restrict__ h_mid,
+__global__ __launch_bounds__(kNormThreads) void k_combine_norm(const float *__restrict__ h_mid,
                                                       const float *__restrict__ eo,
                                                       const float *__restrict__ w,
                                                       const float *__restrict__ shared,
@@ -200,11 +203,11 @@ __global__ __launch_bounds__(256) void k_combine_norm(const float *__restrict__ 
                                                       const uint16_t *__restrict__ nw, float eps,
                                                       float *out, float *__restrict__ normed,
                                                       int64_t H, int K, int mode) {
-    __shared__ float part[4];
+    __shared__ float part[kNormThreads / 64];
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
     float ss = 0.0f;
-    for (int64_t i = tid; i < H; i += 256) {
+    for (int64_t i = tid; i < H; i += kNormThreads) {
         float v;
         if constexpr (COMBINE) {
             v = combine_one<KMAX>(h_mid, eo, w, shared, logit, H, t, i, K, mode);
@@ -220,9 +223,12 @@ __global__ __launch_bounds__(256) void k_combine_norm(const float *__restrict__ 
     if ((tid & 63) == 0)
         part[tid >> 6] = ss;
     __syncthreads();
-    const float total = (part[0] + part[1]) + (part[2] + part[3]);
+    float total = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kNormThreads / 64; w++)
+        total += part[w];
     const float inv = 1.0f / sqrtf(total / (float)H + eps);
-    for (int64_t i = tid; i < H; i += 256) {
+    for (int64_t i = tid; i < H; i += kNormThreads) {
         const float wi = __uint_as_float((uint32_t)nw[i] << 16);
         normed[t * H + i] = out[t * H + i] * inv * wi;
     }
@@ -238,15 +244,15 @@ hipError_t launch_combine_norm(const float *h_mid, const float *expert_out, cons
     const uint16_t *nw = (const uint16_t *)norm_weight;
     const dim3 grid((unsigned)m);
     if (!combine)
-        hipLaunchKernelGGL((k_combine_norm<1, false>), grid, dim3(256), 0, st, h_mid, expert_out,
+        hipLaunchKernelGGL((k_combine_norm<1, false>), grid, dim3(kNormThreads), 0, st, h_mid, expert_out,
                            route_w, shared_out, shared_gate_logit, nw, eps, out, normed, hidden,
                            (int)top_k, shared_mode);
     else if (top_k <= 8)
-        hipLaunchKernelGGL((k_combine_norm<8, true>), grid, dim3(256), 0, st, h_mid, expert_out,
+        hipLaunchKernelGGL((k_combine_norm<8, true>), grid, dim3(kNormThreads), 0, st, h_mid, expert_out,
                            route_w, shared_out, shared_gate_logit, nw, eps, out, normed, hidden,
                            (int)top_k, shared_mode);
     else
-        hipLaunchKernelGGL((k_combine_norm<kMaxTopK, true>), grid, dim3(256), 0, st, h_mid,
+        hipLaunchKernelGGL((k_combine_norm<kMaxTopK, true>), grid, dim3(kNormThreads), 0, st, h_mid,
                            expert_out, route_w, shared_out, shared_gate_logit, nw, eps, out,
                            normed, hidden, (int)top_k, shared_mode);
     return hipGetLastError();
