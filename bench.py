@@ -252,12 +252,34 @@ def run_walk(torch, q4, wl, replicas, walks, warmup):
             q4.q4tp_matvec_multi([ts[j] for j in grp], [shapes[j][0] for j in grp], x, y,
                                  shapes[grp[0]][1])
 
+    # concurrent mode (cortiq-engine mv_lab.rs, mode 'c'): the tensors of a
+    # group run on parallel graph branches, joined before the next group
+    side = [torch.cuda.Stream() for _ in range(3)]   # default priority
+
+    def walk_concurrent(i):
+        ts = reps[i % replicas]
+        main = torch.cuda.current_stream()
+        for grp in groups:
+            if len(grp) == 1:
+                j = grp[0]
+                q4.q4tp_matvec(ts[j], x, ys[j], *shapes[j])
+                continue
+            for b, j in enumerate(grp):
+                side[b].wait_stream(main)
+                with torch.cuda.stream(side[b]):
+                    q4.q4tp_matvec(ts[j], x, ys[j], *shapes[j], stream=side[b])
+            for b in range(len(grp)):
+                main.wait_stream(side[b])
+
     g = capture(torch, walk, walks)
     sec, _ = time_graph(torch, g, 4, warmup)
     gm = capture(torch, walk_merged, walks)
     sec_m, _ = time_graph(torch, gm, 4, warmup)
+    gc = capture(torch, walk_concurrent, walks)
+    sec_c, _ = time_graph(torch, gc, 4, warmup)
     nbytes = sum(q4.q4tp_tensor_bytes(rows, cols) for rows, cols in shapes)
-    return sec_m / (4 * walks) * 1e6, sec / (4 * walks) * 1e6, nbytes
+    return (sec_m / (4 * walks) * 1e6, sec / (4 * walks) * 1e6, nbytes,
+            sec_c / (4 * walks) * 1e6)
 
 
 def run_mlx4(torch, q4, wl, replicas, launches, warmup):
@@ -489,9 +511,10 @@ def main():
             f"layer's RMSNorm {res16['us_per_layer_rmsnorm']:.2f} us")
     walk_us = None
     if not args.no_walk:
-        walk_us, walk_single_us, walk_bytes = run_walk(torch, q4, wl, 2, 32, 1)
+        walk_us, walk_single_us, walk_bytes, walk_conc_us = run_walk(torch, q4, wl, 2, 32, 1)
         log(f"walk: {walk_us:.2f} us/walk merged ({walk_bytes / walk_us / 1e3:.1f} GB/s), "
-            f"{walk_single_us:.2f} us one launch per tensor")
+            f"{walk_single_us:.2f} us one launch per tensor, {walk_conc_us:.2f} us concurrent "
+            f"groups")
     mlx = None
     if not args.no_mlx4:
         mlx = run_mlx4(torch, q4, wl, 8, 64, 1)
@@ -572,6 +595,7 @@ def main():
             "launches": "q|k|v, o, gate|up, down, head (merged dispatches)",
             "us_per_walk": round(walk_us, 3),
             "us_per_walk_one_launch_per_tensor": round(walk_single_us, 3),
+            "us_per_walk_concurrent_groups": round(walk_conc_us, 3),
             "bytes_per_walk": int(walk_bytes),
             "gbs": round(walk_bytes / walk_us / 1e3, 2),
             "frac_hbm_peak": round(walk_bytes / walk_us / 1e3 / HBM_PEAK_GBS, 4),

@@ -432,6 +432,51 @@ def test_q4tp_walk_one_layer_and_head(dev):
             band(y[rs], want, name)
 
 
+def test_q4tp_concurrent_groups_graph_replays(dev):
+    """The walk's concurrent mode (cortiq-engine mv_lab.rs, mode c: a group's
+    tensors dispatched concurrently, barriers between groups) as a HIP graph
+    with parallel branches: every replay, with eager work in between, gives
+    the bits of eager one-at-a-time launches."""
+    say("q4tp concurrent groups in a graph")
+    g = np.random.default_rng(44)
+    shapes = [(96, 4096), (64, 4096), (64, 4096), (128, 4096), (40, 14336)]
+    groups = [[0, 1, 2], [3], [4]]
+    ts = [T(oracle.q4tp_quantize((g.standard_normal(s) * 0.02).astype(np.float32)), dev)
+          for s in shapes]
+    x = T(g.standard_normal(14336).astype(np.float32), dev)
+    ys = [torch.empty(r, device=dev) for r, _ in shapes]
+    ref = []
+    for t, (r, c) in zip(ts, shapes):
+        y = torch.empty(r, device=dev)
+        q4.q4tp_matvec(t, x, y, r, c)
+        ref.append(sync_np(y))
+    side = [torch.cuda.Stream() for _ in range(3)]
+
+    def walk():
+        main = torch.cuda.current_stream()
+        for grp in groups:
+            for b, j in enumerate(grp):
+                side[b].wait_stream(main)
+                with torch.cuda.stream(side[b]):
+                    q4.q4tp_matvec(ts[j], x, ys[j], *shapes[j], stream=side[b])
+            for b in range(len(grp)):
+                main.wait_stream(side[b])
+
+    walk()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        walk()
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        gr.replay()
+        torch.cuda.synchronize()
+        for j, y in enumerate(ys):
+            assert np.array_equal(bits(sync_np(y)), bits(ref[j])), (rep, j)
+        torch.empty(1 << 20, device=dev).normal_()   # eager work between replays
+
+
 def test_q4tp_unit_probe_and_ragged(dev):
     say("q4tp unit probe")
     g = np.random.default_rng(42)
