@@ -81,6 +81,11 @@ def _load():
         "orc_mlx4_moe_id_gemv": (ctypes.c_int, [P, I64, I64, I64, I64, I64, I64, I64, P, P,
                                                 I64, I64, I64, I64, P]),
         "orc_rmsnorm_bf16": (ctypes.c_int, [P, P, ctypes.c_float, I64, I64, P]),
+        "orc_mlx2_code": (ctypes.c_int, [P, I64]),
+        "orc_mlx2_dequantize": (None, [P, P, P, I64, I64, P]),
+        "orc_mlx2_quantize": (ctypes.c_int, [P, I64, I64, P, P, P]),
+        "orc_mlx2_moe_id_gemv": (ctypes.c_int, [P, I64, I64, I64, I64, I64, I64, I64, P, P,
+                                                I64, I64, I64, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -325,4 +330,40 @@ def rmsnorm_bf16(x: np.ndarray, w_bf16: np.ndarray, eps: float) -> np.ndarray:
     m, H = x.shape
     out = np.zeros((m, H), np.float32)
     _check(_load().orc_rmsnorm_bf16(_ptr(x), _ptr(w), float(eps), m, H, _ptr(out)), "rmsnorm_bf16")
+    return out
+
+
+# ------------------------------------------------------ MLX affine 2-bit ----
+
+def mlx2_code(packed_row: np.ndarray, c: int) -> int:
+    return int(_load().orc_mlx2_code(_ptr(_c(packed_row, np.uint8)), c))
+
+
+def mlx2_quantize(w: np.ndarray):
+    """fp32 [n, k] -> (packed uint8 [n, k/4], scales uint16 [n, k/64], biases uint16 [n, k/64])."""
+    w = _c(w, np.float32)
+    n, k = w.shape
+    packed = np.zeros((n, k // 4), np.uint8)
+    scales = np.zeros((n, k // MLX_GROUP), np.uint16)
+    biases = np.zeros((n, k // MLX_GROUP), np.uint16)
+    _check(_load().orc_mlx2_quantize(_ptr(w), n, k, _ptr(packed), _ptr(scales), _ptr(biases)),
+           "mlx2_quantize")
+    return packed, scales, biases
+
+
+def mlx2_dequantize(packed, scales, biases, n: int, k: int) -> np.ndarray:
+    packed, scales, biases = _c(packed, np.uint8), _c(scales, np.uint16), _c(biases, np.uint16)
+    out = np.zeros((n, k), np.float32)
+    _load().orc_mlx2_dequantize(_ptr(packed), _ptr(scales), _ptr(biases), n, k, _ptr(out))
+    return out
+
+
+def mlx2_moe_id_gemv(base, expert_stride: int, packed_off: int, scales_off: int, biases_off: int,
+                     num_experts: int, n: int, k: int, src1, ids, m: int, top_k: int, outer: int,
+                     inner: int) -> np.ndarray:
+    base, src1, ids = _c(base, np.uint8), _c(src1, np.float32), _c(ids, np.int32)
+    out = np.zeros((m * top_k, n), np.float32)
+    _check(_load().orc_mlx2_moe_id_gemv(_ptr(base), expert_stride, packed_off, scales_off,
+                                        biases_off, num_experts, n, k, _ptr(src1), _ptr(ids), m,
+                                        top_k, outer, inner, _ptr(out)), "mlx2_moe_id_gemv")
     return out

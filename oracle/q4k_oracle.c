@@ -1,6 +1,7 @@
 /*
  * q4k_oracle.c -- plain CPU oracle for the Q4_K MoE expert path, the
- * Q4TiledP dense matvec and the MLX affine 4-bit expert codec.
+ * Q4TiledP dense matvec, the MLX affine 4-bit and 2-bit expert codecs and the
+ * chained RMSNorm.
  *
  * TEST INFRASTRUCTURE ONLY.  The test-suite, the smoke check and the CPU
  * baseline leg of the benchmark are the only callers allowed.  The GPU library
@@ -696,6 +697,110 @@ int orc_mlx4_moe_id_gemv(const uint8_t *base, int64_t expert_stride, int64_t pac
             }
             const uint8_t *blk = base + e * expert_stride;
             orc_mlx4_dequantize(blk + packed_off + r * (k / 2),
+                                (const uint16_t *)(blk + scales_off) + r * gpr,
+                                (const uint16_t *)(blk + biases_off) + r * gpr, 1, k, tmp);
+            double acc = 0.0;
+            for (int64_t c = 0; c < k; c++)
+                acc += (double)tmp[c] * (double)x[c];
+            dst[p * n + r] = (float)acc;
+        }
+    }
+    free(tmp);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* MLX affine 2-bit expert codec ([MF] module doc: g_use_2bit selects the    */
+/* 2-bit matvec and expert-block layout).  Reading: MLX's 2-bit affine       */
+/* format, the 4-bit one with 2-bit codes: groups of 64 along a row, bf16   */
+/* scale and bias per group, w = scale*q + bias with q in 0..3, row byte j  */
+/* holding weights 4j..4j+3 at bits 0-1, 2-3, 4-5, 6-7 (16 codes per        */
+/* little-endian 32-bit word, lowest code in the lowest bits).  Packed rows */
+/* take k/4 bytes.                                                           */
+/* ------------------------------------------------------------------------ */
+
+int orc_mlx2_code(const uint8_t *row, int64_t c)
+{
+    return (row[c / 4] >> (2 * (c & 3))) & 3;
+}
+
+/* Dequantize: scale*q is exact (8 + 2 significant bits), the sum rounds    */
+/* once.  Parity: bit-exact.                                                 */
+void orc_mlx2_dequantize(const uint8_t *packed, const uint16_t *scales, const uint16_t *biases,
+                         int64_t n, int64_t k, float *out)
+{
+    int64_t gpr = k / ORC_MLX_GROUP;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t c = 0; c < k; c++) {
+            float s = orc_bf16_to_f32(scales[r * gpr + c / ORC_MLX_GROUP]);
+            float b = orc_bf16_to_f32(biases[r * gpr + c / ORC_MLX_GROUP]);
+            float p = s * (float)orc_mlx2_code(packed + r * (k / 4), c);
+            out[r * k + c] = p + b;
+        }
+}
+
+/* Encoder (reading, as the 4-bit one with 3 steps): lo = min w, hi = max w, */
+/* scale = bf16((hi - lo)/3), bias = bf16(lo),                              */
+/* q = clamp(rne((w - bias)/scale), 0, 3), 0 where the scale is 0.  Parity   */
+/* on bytes; quality against MLX's quantizer unpinned.                       */
+int orc_mlx2_quantize(const float *w, int64_t n, int64_t k, uint8_t *packed, uint16_t *scales,
+                      uint16_t *biases)
+{
+    if (n <= 0 || k <= 0 || k % ORC_MLX_GROUP)
+        return ORC_EINVAL;
+    int64_t gpr = k / ORC_MLX_GROUP;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t g = 0; g < gpr; g++) {
+            const float *x = w + r * k + g * ORC_MLX_GROUP;
+            float lo = x[0], hi = x[0];
+            for (int j = 1; j < ORC_MLX_GROUP; j++) {
+                lo = x[j] < lo ? x[j] : lo;
+                hi = x[j] > hi ? x[j] : hi;
+            }
+            float d = hi - lo;
+            uint16_t sh = orc_f32_to_bf16(d / 3.0f);
+            uint16_t bh = orc_f32_to_bf16(lo);
+            float s = orc_bf16_to_f32(sh), b = orc_bf16_to_f32(bh);
+            scales[r * gpr + g] = sh;
+            biases[r * gpr + g] = bh;
+            uint8_t *row = packed + r * (k / 4) + g * (ORC_MLX_GROUP / 4);
+            for (int j = 0; j < ORC_MLX_GROUP; j += 4) {
+                int byte = 0;
+                for (int h = 0; h < 4; h++) {
+                    float t = (x[j + h] - b) / s;
+                    int q = s == 0.0f ? 0 : clampi((int)rintf(t), 0, 3);
+                    byte |= q << (2 * h);
+                }
+                row[j / 4] = (uint8_t)byte;
+            }
+        }
+    return ORC_OK;
+}
+
+/* id-GEMV over MLX 2-bit experts: as orc_mlx4_moe_id_gemv with the 2-bit   */
+/* rows (k/4 packed bytes).                                                   */
+int orc_mlx2_moe_id_gemv(const uint8_t *base, int64_t expert_stride, int64_t packed_off,
+                         int64_t scales_off, int64_t biases_off, int64_t num_experts, int64_t n,
+                         int64_t k, const float *src1, const int32_t *ids, int64_t m,
+                         int64_t top_k, int64_t outer, int64_t inner, float *dst)
+{
+    if (k <= 0 || k % ORC_MLX_GROUP || n <= 0 || m < 0 || top_k <= 0 || num_experts <= 0)
+        return ORC_EINVAL;
+    float *tmp = (float *)malloc((size_t)k * sizeof(float));
+    if (!tmp)
+        return ORC_ENOMEM;
+    int64_t gpr = k / ORC_MLX_GROUP;
+    for (int64_t p = 0; p < m * top_k; p++) {
+        int64_t t = p / top_k, s = p % top_k;
+        int64_t e = ids[p];
+        const float *x = src1 + t * outer + s * inner;
+        for (int64_t r = 0; r < n; r++) {
+            if (e < 0 || e >= num_experts) {
+                dst[p * n + r] = 0.0f;
+                continue;
+            }
+            const uint8_t *blk = base + e * expert_stride;
+            orc_mlx2_dequantize(blk + packed_off + r * (k / 4),
                                 (const uint16_t *)(blk + scales_off) + r * gpr,
                                 (const uint16_t *)(blk + biases_off) + r * gpr, 1, k, tmp);
             double acc = 0.0;

@@ -187,3 +187,52 @@ def test_id_gemv_unit_vector_probe_and_invalid_ids():
         assert np.array_equal(got[0], oracle.mlx4_dequantize(*mats[2][0], n, k)[:, c])
         assert np.array_equal(got[1], oracle.mlx4_dequantize(*mats[0][0], n, k)[:, c])
         assert np.all(got[2:] == 0.0)
+
+
+# ------------------------------------------------------------- 2-bit ----
+
+def test_mlx2_code_order_and_hand_group():
+    # byte j holds weights 4j..4j+3 at bits 0-1, 2-3, 4-5, 6-7
+    packed = np.array([[0b11100100, 0b00011011] + [0] * 14], np.uint8)
+    assert [oracle.mlx2_code(packed[0], c) for c in range(8)] == [0, 1, 2, 3, 3, 2, 1, 0]
+    s = np.array([[oracle.f32_to_bf16(0.5)]], np.uint16)
+    b = np.array([[oracle.f32_to_bf16(-1.0)]], np.uint16)
+    out = oracle.mlx2_dequantize(packed, s, b, 1, G)
+    assert out[0, :8].tolist() == [-1.0, -0.5, 0.0, 0.5, 0.5, 0.0, -0.5, -1.0]
+    assert np.all(out[0, 8:] == -1.0)
+
+
+def test_mlx2_quantizer_grid_and_bound():
+    g = np.random.default_rng(6)
+    q = g.integers(0, 4, (6, 2 * G))
+    q[:, 0], q[:, G], q[:, 1], q[:, G + 1] = 0, 0, 3, 3
+    w = (np.float32(0.75) + np.float32(0.125) * q).astype(np.float32)
+    packed, s, b = oracle.mlx2_quantize(w)
+    assert np.array_equal(oracle.mlx2_dequantize(packed, s, b, 6, 2 * G), w)
+    w = (g.standard_normal((16, 4 * G)) * 0.3).astype(np.float32)
+    packed, s, b = oracle.mlx2_quantize(w)
+    d = oracle.mlx2_dequantize(packed, s, b, 16, 4 * G)
+    wg = w.reshape(16, 4, G).astype(np.float64)
+    lo, hi = wg.min(-1), wg.max(-1)
+    sf = np.array([[oracle.bf16_to_f32(int(v)) for v in row] for row in s])
+    bf = np.array([[oracle.bf16_to_f32(int(v)) for v in row] for row in b])
+    bound = 0.5 * sf + 3 * np.abs(sf - (hi - lo) / 3) + np.abs(bf - lo) + 1e-6
+    assert np.all(np.abs(d.reshape(16, 4, G) - wg).max(-1) <= bound)
+
+
+def test_mlx2_id_gemv_equals_dense_matmul():
+    g = np.random.default_rng(7)
+    E, n, k, m, K = 4, 24, 3 * G, 2, 2
+    mats = [oracle.mlx2_quantize((g.standard_normal((n, k)) * 0.3).astype(np.float32))
+            for _ in range(E)]
+    stride = n * k // 4 + 2 * (n * k // 32)
+    blob = np.concatenate([np.concatenate([p.reshape(-1), s.reshape(-1).view(np.uint8),
+                                           b.reshape(-1).view(np.uint8)]) for p, s, b in mats])
+    offs = (0, n * k // 4, n * k // 4 + n * k // 32)
+    W = np.stack([oracle.mlx2_dequantize(*mats[e], n, k) for e in range(E)]).astype(np.float64)
+    x = g.standard_normal((m * K, k)).astype(np.float32)
+    ids = np.array([3, 0, 9, 2], np.int32)
+    got = oracle.mlx2_moe_id_gemv(blob, stride, *offs, E, n, k, x, ids, m, K, K * k, k)
+    want = _dense_id_gemv(W, x.reshape(-1), ids, m, K, K * k, k, k)
+    np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-6)
+    assert np.all(got[2] == 0.0)
