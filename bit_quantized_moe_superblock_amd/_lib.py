@@ -59,6 +59,11 @@ SIGNATURES = {
                               _I64, _I64, _I64, _P]),
     "mlx4_moe_gate_up_silu": (_I, [_P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P,
                                    _I64, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
+    "mlx2_matrix_bytes": (_I64, [_I64, _I64]),
+    "mlx2_dequantize": (_I, [_P, _P, _P, _P, _I64, _I64, _P]),
+    "mlx2_quantize": (_I, [_P, _P, _P, _P, _I64, _I64, _P]),
+    "mlx2_moe_id_gemv": (_I, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _I64, _I64,
+                              _I64, _I64, _I64, _P]),
 }
 
 
@@ -270,3 +275,26 @@ def moe_combine_residual_rmsnorm(h_mid, expert_out, route_w, shared_out, shared_
     _call("moe_combine_residual_rmsnorm", _ptr(h_mid), _ptr(expert_out), _ptr(route_w),
           _ptr(shared_out), _ptr(shared_gate_logit), _ptr(norm_weight), float(eps), _ptr(out),
           _ptr(normed), hidden, m, top_k, shared_mode, _stream(stream))
+
+
+def mlx2_matrix_bytes(n: int, k: int) -> int:
+    return load().mlx2_matrix_bytes(n, k)
+
+
+def mlx2_dequantize(packed, scales, biases, out, n: int, k: int, stream=None):
+    _call("mlx2_dequantize", _ptr(packed), _ptr(scales), _ptr(biases), _ptr(out), n, k,
+          _stream(stream))
+
+
+def mlx2_quantize(w, packed, scales, biases, n: int, k: int, stream=None):
+    _call("mlx2_quantize", _ptr(w), _ptr(packed), _ptr(scales), _ptr(biases), n, k,
+          _stream(stream))
+
+
+def mlx2_moe_id_gemv(expert_base, expert_stride: int, packed_off: int, scales_off: int,
+                     biases_off: int, src1, ids, dst, n: int, k: int, m: int, top_k: int,
+                     src1_outer_stride: int, src1_inner_stride: int, num_experts: int,
+                     stream=None):
+    _call("mlx2_moe_id_gemv", _ptr(expert_base), expert_stride, packed_off, scales_off,
+          biases_off, _ptr(src1), _ptr(ids), _ptr(dst), n, k, m, top_k, src1_outer_stride,
+          src1_inner_stride, num_experts, _stream(stream))

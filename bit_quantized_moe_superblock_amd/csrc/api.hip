@@ -567,7 +567,7 @@ int mlx4_dequantize(const void *packed, const void *scales, const void *biases, 
     if (!packed || !scales || !biases || !out || !aligned16(packed) || !aligned2(scales) ||
         !aligned2(biases) || !aligned16(out))
         return Q4K_ERR_NULL;
-    return launched(launch_mlx4_dequant(packed, scales, biases, out, n * (k / MLX4_GROUP),
+    return launched(launch_mlx4_dequant(packed, scales, biases, out, n * (k / MLX4_GROUP), 4,
                                         as_stream(stream)));
 }
 
@@ -580,7 +580,7 @@ int mlx4_quantize(const float *w, void *packed, void *scales, void *biases, int6
     if (!w || !packed || !scales || !biases || !aligned4(w) || !aligned16(packed) ||
         !aligned2(scales) || !aligned2(biases))
         return Q4K_ERR_NULL;
-    return launched(launch_mlx4_quant(w, packed, scales, biases, n * (k / MLX4_GROUP),
+    return launched(launch_mlx4_quant(w, packed, scales, biases, n * (k / MLX4_GROUP), 4,
                                       as_stream(stream)));
 }
 
@@ -592,12 +592,13 @@ namespace {
 // points; offs holds (packed, scales, biases) offsets of n_mats matrices.
 int mlx4_check(const void *expert_base, int64_t expert_stride, const int64_t *offs, int n_mats,
                const float *src1, const int32_t *ids, const float *dst, int64_t n, int64_t k,
-               int64_t m, int64_t top_k, int64_t outer, int64_t inner, int64_t num_experts) {
+               int64_t m, int64_t top_k, int64_t outer, int64_t inner, int64_t num_experts,
+               int bits = 4) {
     if (n < 1 || n > (1 << 30) || k < MLX4_GROUP || k % MLX4_GROUP || k > Q4K_MAX_IN || m < 1 ||
         top_k < 1 || top_k > Q4K_MAX_TOP_K || num_experts < 1 || m * top_k > 65535)
         return Q4K_ERR_SHAPE;
     // every sub-tensor inside one expert block
-    const int64_t pbytes = n * k / 2, sbytes = n * (k / MLX4_GROUP) * 2;
+    const int64_t pbytes = n * k * bits / 8, sbytes = n * (k / MLX4_GROUP) * 2;
     if (expert_stride < 0)
         return Q4K_ERR_SHAPE;
     for (int i = 0; i < n_mats; i++) {
@@ -672,6 +673,68 @@ int mlx4_moe_gate_up_silu(const void *expert_base, int64_t expert_stride, int64_
     L.scales_off1 = up_scales_off;
     L.biases_off1 = up_biases_off;
     L.fused_swiglu = true;
+    L.src1 = src1;
+    L.ids = ids;
+    L.dst = dst;
+    L.n = n;
+    L.k = k;
+    L.m = m;
+    L.top_k = top_k;
+    L.num_experts = num_experts;
+    L.outer = src1_outer_stride;
+    L.inner = src1_inner_stride;
+    return launched(launch_mlx4_gemv(L, as_stream(stream)));
+}
+
+int64_t mlx2_matrix_bytes(int64_t n, int64_t k) {
+    if (n < 0 || k < MLX4_GROUP || k % MLX4_GROUP)
+        return -1;
+    return n * k / 4 + 2 * (n * (k / MLX4_GROUP) * 2);
+}
+
+int mlx2_dequantize(const void *packed, const void *scales, const void *biases, float *out,
+                    int64_t n, int64_t k, void *stream) {
+    if (n < 0 || n > (1 << 30) || k < MLX4_GROUP || k % MLX4_GROUP || k > Q4K_MAX_IN)
+        return Q4K_ERR_SHAPE;
+    if (n == 0)
+        return Q4K_OK;
+    if (!packed || !scales || !biases || !out || !aligned16(packed) || !aligned2(scales) ||
+        !aligned2(biases) || !aligned16(out))
+        return Q4K_ERR_NULL;
+    return launched(launch_mlx4_dequant(packed, scales, biases, out, n * (k / MLX4_GROUP), 2,
+                                        as_stream(stream)));
+}
+
+int mlx2_quantize(const float *w, void *packed, void *scales, void *biases, int64_t n, int64_t k,
+                  void *stream) {
+    if (n < 0 || n > (1 << 30) || k < MLX4_GROUP || k % MLX4_GROUP || k > Q4K_MAX_IN)
+        return Q4K_ERR_SHAPE;
+    if (n == 0)
+        return Q4K_OK;
+    if (!w || !packed || !scales || !biases || !aligned4(w) || !aligned16(packed) ||
+        !aligned2(scales) || !aligned2(biases))
+        return Q4K_ERR_NULL;
+    return launched(launch_mlx4_quant(w, packed, scales, biases, n * (k / MLX4_GROUP), 2,
+                                      as_stream(stream)));
+}
+
+int mlx2_moe_id_gemv(const void *expert_base, int64_t expert_stride, int64_t packed_off,
+                     int64_t scales_off, int64_t biases_off, const float *src1,
+                     const int32_t *ids, float *dst, int64_t n, int64_t k, int64_t m,
+                     int64_t top_k, int64_t src1_outer_stride, int64_t src1_inner_stride,
+                     int64_t num_experts, void *stream) {
+    const int64_t offs[3] = {packed_off, scales_off, biases_off};
+    const int rc = mlx4_check(expert_base, expert_stride, offs, 1, src1, ids, dst, n, k, m, top_k,
+                              src1_outer_stride, src1_inner_stride, num_experts, 2);
+    if (rc)
+        return rc;
+    Mlx4Launch L{};
+    L.base = expert_base;
+    L.expert_stride = expert_stride;
+    L.packed_off = packed_off;
+    L.scales_off = scales_off;
+    L.biases_off = biases_off;
+    L.bits = 2;
     L.src1 = src1;
     L.ids = ids;
     L.dst = dst;

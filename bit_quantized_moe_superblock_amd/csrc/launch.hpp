@@ -82,6 +82,7 @@ struct Mlx4Launch {
     int64_t expert_stride, packed_off, scales_off, biases_off;
     int64_t packed_off1, scales_off1, biases_off1;   // up matrix (fused_swiglu)
     bool fused_swiglu;
+    int bits;                                        // 4 (default when 0) or 2
     const float *src1;
     const int32_t *ids;
     float *dst;
@@ -89,9 +90,9 @@ struct Mlx4Launch {
 };
 hipError_t launch_mlx4_gemv(const Mlx4Launch &L, hipStream_t st);
 hipError_t launch_mlx4_dequant(const void *packed, const void *scales, const void *biases,
-                               float *out, int64_t groups, hipStream_t st);
+                               float *out, int64_t groups, int bits, hipStream_t st);
 hipError_t launch_mlx4_quant(const float *w, void *packed, void *scales, void *biases,
-                             int64_t groups, hipStream_t st);
+                             int64_t groups, int bits, hipStream_t st);
 
 // Workspace of the bucketing kernel in int32 words (layout in q4kmoe.h).
 inline int64_t bucket_ws_words(int64_t n_pairs, int64_t num_experts) {

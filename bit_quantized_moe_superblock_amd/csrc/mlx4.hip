@@ -1,5 +1,5 @@
-// MLX affine 4-bit expert codec on gfx950: dequantizer, encoder and the
-// id-GEMV over expert blocks.
+// MLX affine 4-bit and 2-bit expert codecs on gfx950: dequantizers, encoders
+// and the id-GEMV over expert blocks.
 //
 // Format (moeflux expert_forward.rs, "4-bit only" and the gather dispatch's
 // strides: K/2 bytes of packed weights per row, K/64 bf16 scales and as many
@@ -19,6 +19,13 @@
 // group's sum q.x costs one instruction per weight; then
 //     row value = sum over groups of scale * (q.x) + bias * (sum of x),
 // reduced across the row's lanes with DPP.
+//
+// The 2-bit variant (moeflux's g_use_2bit layout; MLX's 2-bit format): the
+// same groups, scales and biases with four 2-bit codes per byte, lowest
+// first, so a group is 16 packed bytes and one 16-byte load; its fields are
+// masked out at four shifts, all as fp16 subnormals q 2^-24.
+#include <type_traits>
+
 #include "gemv_core.hpp"
 
 namespace q4k {
@@ -79,7 +86,34 @@ __device__ __forceinline__ float group_qx(const uint4 qa, const uint4 qb, const 
 // NT = 1: dst[p, r] = row r of the pair's matrix times x.  NT = 2: the gate
 // and up matrices of the same expert block against the same x, the lane
 // loading both groups, and dst[p, r] = silu(gate) * up.
-template <int LPR, int NT>
+// sum over the 64 weights of a 2-bit group of q * x, from its 16 packed bytes
+__device__ __forceinline__ float group_qx2(const uint4 qa, const float *xr) {
+    const uint32_t w[4] = {qa.x, qa.y, qa.z, qa.w};
+    float acc = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+        // dword d = bytes 4d..4d+3 = weights 16d..16d+15
+        const float4 xa = *(const float4 *)(xr + 16 * d);        // byte 0's weights
+        const float4 xb = *(const float4 *)(xr + 16 * d + 4);    // byte 1's
+        const float4 xc = *(const float4 *)(xr + 16 * d + 8);    // byte 2's
+        const float4 xd = *(const float4 *)(xr + 16 * d + 12);   // byte 3's
+        const float ea[4] = {xa.x, xa.y, xa.z, xa.w}, eb[4] = {xb.x, xb.y, xb.z, xb.w};
+        const float ec[4] = {xc.x, xc.y, xc.z, xc.w}, ed[4] = {xd.x, xd.y, xd.z, xd.w};
+        const uint32_t v = w[d];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint32_t me = (v >> (2 * i)) & 0x00030003u;       // bytes 0 and 2, code i
+            const uint32_t mo = (v >> (8 + 2 * i)) & 0x00030003u;   // bytes 1 and 3, code i
+            acc = __builtin_fmaf(lo_half(me), ea[i], acc);
+            acc = __builtin_fmaf(hi_half(me), ec[i], acc);
+            acc = __builtin_fmaf(lo_half(mo), eb[i], acc);
+            acc = __builtin_fmaf(hi_half(mo), ed[i], acc);
+        }
+    }
+    return acc * 16777216.0f;
+}
+
+template <int LPR, int NT, int BITS>
 __global__ __launch_bounds__(kThreads) void k_mlx4_rows(Mlx4Args a) {
     extern __shared__ float lds[];
     asm volatile("" ::"s"(a.base), "s"(a.stride), "s"(a.packed_off), "s"(a.scales_off),
@@ -109,7 +143,8 @@ __global__ __launch_bounds__(kThreads) void k_mlx4_rows(Mlx4Args a) {
     const int gl = active ? u : 0;
     const int r0 = blockIdx.x * RPI + rsub;
     const int r = r0 < a.n ? r0 : a.n - 1;
-    const int64_t prel = (int64_t)r * (a.k >> 1) + 32 * gl;
+    constexpr int GB = kMlxGroup * BITS / 8;   // packed bytes of a group
+    const int64_t prel = (int64_t)r * (a.k * BITS / 8) + GB * gl;
     const int64_t gi = ((int64_t)r * gpr + gl) * 2;
     uint4 qa[NT], qb[NT];
     uint32_t sh[NT], bh[NT];
@@ -117,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void k_mlx4_rows(Mlx4Args a) {
     for (int nt = 0; nt < NT; nt++) {
         const uint8_t *prow = blk + (nt ? a.packed_off1 : a.packed_off) + prel;
         qa[nt] = *(const uint4 *)prow;
-        qb[nt] = *(const uint4 *)(prow + 16);
+        qb[nt] = BITS == 4 ? *(const uint4 *)(prow + 16) : make_uint4(0, 0, 0, 0);
         sh[nt] = *(const uint16_t *)(blk + (nt ? a.scales_off1 : a.scales_off) + gi);
         bh[nt] = *(const uint16_t *)(blk + (nt ? a.biases_off1 : a.biases_off) + gi);
     }
@@ -131,7 +166,8 @@ __global__ __launch_bounds__(kThreads) void k_mlx4_rows(Mlx4Args a) {
     float part[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; nt++) {
-        const float qx = group_qx(qa[nt], qb[nt], lds + xpad(kMlxGroup * gl));
+        const float qx = BITS == 4 ? group_qx(qa[nt], qb[nt], lds + xpad(kMlxGroup * gl))
+                                   : group_qx2(qa[nt], lds + xpad(kMlxGroup * gl));
         const float v = __builtin_fmaf(bf16_val(sh[nt]), qx, bf16_val(bh[nt]) * gsum);
         part[nt] = row_reduce<LPR>(active ? v : 0.0f, red, nt);
     }
@@ -142,6 +178,7 @@ __global__ __launch_bounds__(kThreads) void k_mlx4_rows(Mlx4Args a) {
 
 // One thread per group: w = scale * q + bias in float (scale * q is exact,
 // the sum rounds once).
+template <int BITS>
 __global__ __launch_bounds__(256) void k_mlx4_dequant(const uint8_t *__restrict__ packed,
                                                       const uint16_t *__restrict__ scales,
                                                       const uint16_t *__restrict__ biases,
@@ -149,21 +186,25 @@ __global__ __launch_bounds__(256) void k_mlx4_dequant(const uint8_t *__restrict_
     const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (g >= groups)
         return;
-    const uint4 qa = *(const uint4 *)(packed + 32 * g);
-    const uint4 qb = *(const uint4 *)(packed + 32 * g + 16);
+    constexpr int GB = kMlxGroup * BITS / 8;   // packed bytes of a group
+    constexpr int PW = 32 / BITS;              // codes per 32-bit word
+    const uint4 qa = *(const uint4 *)(packed + GB * g);
+    const uint4 qb = BITS == 4 ? *(const uint4 *)(packed + GB * g + 16) : make_uint4(0, 0, 0, 0);
     const float sc = bf16_val(scales[g]), bi = bf16_val(biases[g]);
     const uint32_t w[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
     float4 *o = (float4 *)(out + kMlxGroup * g);
 #pragma unroll
-    for (int d = 0; d < 8; d++) {
-        float v[8];
+    for (int d = 0; d < kMlxGroup / PW; d++) {
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const float p = sc * (float)((w[d] >> (4 * j)) & 15u);
-            v[j] = p + bi;
+        for (int j4 = 0; j4 < PW; j4 += 4) {
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const float p = sc * (float)((w[d] >> (BITS * (j4 + j))) & ((1u << BITS) - 1u));
+                v[j] = p + bi;
+            }
+            o[(PW * d + j4) / 4] = make_float4(v[0], v[1], v[2], v[3]);
         }
-        o[2 * d] = make_float4(v[0], v[1], v[2], v[3]);
-        o[2 * d + 1] = make_float4(v[4], v[5], v[6], v[7]);
     }
 }
 
@@ -171,6 +212,7 @@ __global__ __launch_bounds__(256) void k_mlx4_dequant(const uint8_t *__restrict_
 // operation in the same order as the CPU reference encoder: lo, hi = min and
 // max; scale = bf16((hi - lo) / 15), bias = bf16(lo);
 // q = clamp(rne((w - bias) / scale), 0, 15), 0 where the scale is 0.
+template <int BITS>
 __global__ __launch_bounds__(256) void k_mlx4_quant(const float *__restrict__ w,
                                                     uint8_t *__restrict__ packed,
                                                     uint16_t *__restrict__ scales,
@@ -187,36 +229,39 @@ __global__ __launch_bounds__(256) void k_mlx4_quant(const float *__restrict__ w,
         hi = v > hi ? v : hi;
     }
     const float d = hi - lo;
-    const uint16_t sh = f32_to_bf16(d / 15.0f);
+    constexpr int QMAX = (1 << BITS) - 1;
+    const uint16_t sh = f32_to_bf16(d / (float)QMAX);
     const uint16_t bh = f32_to_bf16(lo);
     const float sc = bf16_val(sh), bi = bf16_val(bh);
     scales[g] = sh;
     biases[g] = bh;
-    uint32_t word[8];
+    constexpr int PW = 32 / BITS;   // codes per 32-bit word
+    uint32_t word[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int dw = 0; dw < 8; dw++) {
+    for (int dw = 0; dw < kMlxGroup / PW; dw++) {
         uint32_t acc = 0;
-        for (int j = 0; j < 8; j++) {
-            const float tq = (x[8 * dw + j] - bi) / sc;
+        for (int j = 0; j < PW; j++) {
+            const float tq = (x[PW * dw + j] - bi) / sc;
             int qi = (int)__builtin_rintf(tq);
-            qi = qi < 0 ? 0 : (qi > 15 ? 15 : qi);
+            qi = qi < 0 ? 0 : (qi > QMAX ? QMAX : qi);
             if (sc == 0.0f)
                 qi = 0;
-            acc |= (uint32_t)qi << (4 * j);
+            acc |= (uint32_t)qi << (BITS * j);
         }
         word[dw] = acc;
     }
-    uint4 *o = (uint4 *)(packed + 32 * g);
+    uint4 *o = (uint4 *)(packed + kMlxGroup * BITS / 8 * g);
     o[0] = make_uint4(word[0], word[1], word[2], word[3]);
-    o[1] = make_uint4(word[4], word[5], word[6], word[7]);
+    if (BITS == 4)
+        o[1] = make_uint4(word[4], word[5], word[6], word[7]);
 }
 
 // ------------------------------------------------------------------ host ---
 
-template <int LPR, int NT>
+template <int LPR, int NT, int BITS>
 static hipError_t go_mlx4(const Mlx4Args &a, int64_t n_pairs, hipStream_t st) {
     constexpr int RPI = kThreads / LPR;
-    auto kern = k_mlx4_rows<LPR, NT>;
+    auto kern = k_mlx4_rows<LPR, NT, BITS>;
     const size_t lds = set_lds((const void *)kern, ((size_t)row_lds_floats(a.k) + 8) * sizeof(float));
     dim3 grid((a.n + RPI - 1) / RPI, (unsigned)n_pairs);
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a);
@@ -249,46 +294,52 @@ hipError_t launch_mlx4_gemv(const Mlx4Launch &L, hipStream_t st) {
     int lpr = 4;
     while (lpr < a.k / kMlxGroup)
         lpr <<= 1;
-    if (L.fused_swiglu) {
+    auto pick = [&](auto nt, auto bits) -> hipError_t {
+        constexpr int N = decltype(nt)::value, B = decltype(bits)::value;
         switch (lpr) {
-        case 4: return go_mlx4<4, 2>(a, P, st);
-        case 8: return go_mlx4<8, 2>(a, P, st);
-        case 16: return go_mlx4<16, 2>(a, P, st);
-        case 32: return go_mlx4<32, 2>(a, P, st);
-        case 64: return go_mlx4<64, 2>(a, P, st);
-        case 128: return go_mlx4<128, 2>(a, P, st);
-        case 256: return go_mlx4<256, 2>(a, P, st);
+        case 4: return go_mlx4<4, N, B>(a, P, st);
+        case 8: return go_mlx4<8, N, B>(a, P, st);
+        case 16: return go_mlx4<16, N, B>(a, P, st);
+        case 32: return go_mlx4<32, N, B>(a, P, st);
+        case 64: return go_mlx4<64, N, B>(a, P, st);
+        case 128: return go_mlx4<128, N, B>(a, P, st);
+        case 256: return go_mlx4<256, N, B>(a, P, st);
         default: return hipErrorInvalidValue;
         }
-    }
-    switch (lpr) {
-    case 4: return go_mlx4<4, 1>(a, P, st);
-    case 8: return go_mlx4<8, 1>(a, P, st);
-    case 16: return go_mlx4<16, 1>(a, P, st);
-    case 32: return go_mlx4<32, 1>(a, P, st);
-    case 64: return go_mlx4<64, 1>(a, P, st);
-    case 128: return go_mlx4<128, 1>(a, P, st);
-    case 256: return go_mlx4<256, 1>(a, P, st);
-    default: return hipErrorInvalidValue;
-    }
+    };
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I4 = std::integral_constant<int, 4>;
+    if (L.bits == 2)
+        return L.fused_swiglu ? pick(I2{}, I2{}) : pick(I1{}, I2{});
+    return L.fused_swiglu ? pick(I2{}, I4{}) : pick(I1{}, I4{});
 }
 
 hipError_t launch_mlx4_dequant(const void *packed, const void *scales, const void *biases,
-                               float *out, int64_t groups, hipStream_t st) {
+                               float *out, int64_t groups, int bits, hipStream_t st) {
     if (groups == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(k_mlx4_dequant, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st,
-                       (const uint8_t *)packed, (const uint16_t *)scales,
-                       (const uint16_t *)biases, out, groups);
+    const dim3 grid((unsigned)((groups + 255) / 256));
+    if (bits == 2)
+        hipLaunchKernelGGL(k_mlx4_dequant<2>, grid, dim3(256), 0, st, (const uint8_t *)packed,
+                           (const uint16_t *)scales, (const uint16_t *)biases, out, groups);
+    else
+        hipLaunchKernelGGL(k_mlx4_dequant<4>, grid, dim3(256), 0, st, (const uint8_t *)packed,
+                           (const uint16_t *)scales, (const uint16_t *)biases, out, groups);
     return hipGetLastError();
 }
 
 hipError_t launch_mlx4_quant(const float *w, void *packed, void *scales, void *biases,
-                             int64_t groups, hipStream_t st) {
+                             int64_t groups, int bits, hipStream_t st) {
     if (groups == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(k_mlx4_quant, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st, w,
-                       (uint8_t *)packed, (uint16_t *)scales, (uint16_t *)biases, groups);
+    const dim3 grid((unsigned)((groups + 255) / 256));
+    if (bits == 2)
+        hipLaunchKernelGGL(k_mlx4_quant<2>, grid, dim3(256), 0, st, w, (uint8_t *)packed,
+                           (uint16_t *)scales, (uint16_t *)biases, groups);
+    else
+        hipLaunchKernelGGL(k_mlx4_quant<4>, grid, dim3(256), 0, st, w, (uint8_t *)packed,
+                           (uint16_t *)scales, (uint16_t *)biases, groups);
     return hipGetLastError();
 }
 

@@ -67,7 +67,7 @@ enum { MOE_SHARED_NONE = 0, MOE_SHARED_SIGMOID = 1, MOE_SHARED_UNSCALED = 2 };
 #define MOE_LAYER_SYNC_TIMEOUT_WORD 576 /* 32-bit word of that header: barrier timed out */
 
 const char *q4k_status_string(int status);
-/* 3: adds the MLX 4-bit entry points (mlx4_*) and the chained RMSNorm
+/* 3: adds the MLX 4-bit and 2-bit entry points (mlx4_*, mlx2_*) and the chained RMSNorm
  * (moe_layer_forward_rmsnorm, moe_combine_residual_rmsnorm) to version 2's
  * set. */
 int q4k_abi_version(void);
@@ -370,6 +370,25 @@ int mlx4_moe_gate_up_silu(const void *expert_base, int64_t expert_stride, int64_
                           const int32_t *ids, float *dst, int64_t n, int64_t k, int64_t m,
                           int64_t top_k, int64_t src1_outer_stride, int64_t src1_inner_stride,
                           int64_t num_experts, void *stream);
+
+/* MLX affine 2-bit expert codec ([MF] module doc: g_use_2bit selects the
+ * 2-bit matvec and expert layout).  Reading: MLX's 2-bit affine format, the
+ * 4-bit layout above with 2-bit codes: groups of 64 weights, bf16 scale and
+ * bias per group, w = scale*q + bias with q in 0..3, byte j of a row holding
+ * weights 4j..4j+3 at bits 0-1, 2-3, 4-5 and 6-7; packed rows take k/4
+ * bytes.  The encoder is the 4-bit one with scale = bf16_rne((hi - lo)/3)
+ * and q clamped to 0..3.  Arguments, limits, alignment and errors as the
+ * mlx4_* entry points (mlx2_matrix_bytes: n*k/4 + 2*(n*k/64)*2). */
+int64_t mlx2_matrix_bytes(int64_t n, int64_t k);
+int mlx2_dequantize(const void *packed, const void *scales, const void *biases, float *out,
+                    int64_t n, int64_t k, void *stream);
+int mlx2_quantize(const float *w, void *packed, void *scales, void *biases, int64_t n, int64_t k,
+                  void *stream);
+int mlx2_moe_id_gemv(const void *expert_base, int64_t expert_stride, int64_t packed_off,
+                     int64_t scales_off, int64_t biases_off, const float *src1,
+                     const int32_t *ids, float *dst, int64_t n, int64_t k, int64_t m,
+                     int64_t top_k, int64_t src1_outer_stride, int64_t src1_inner_stride,
+                     int64_t num_experts, void *stream);
 
 #ifdef __cplusplus
 }

@@ -61,6 +61,8 @@ def test_size_helpers(lib):
     assert q4.mlx4_matrix_bytes(768, 2048) == 884_736
     assert q4.mlx4_matrix_bytes(2048, 768) == 884_736
     assert q4.mlx4_matrix_bytes(3, 96) == -1
+    assert q4.mlx2_matrix_bytes(768, 2048) == 768 * 512 + 768 * 32 * 4
+    assert q4.mlx2_matrix_bytes(3, 96) == -1
     assert q4.moe_bucket_workspace_bytes(128, 128) == 4 * (129 + 130 + 128 + 129 + 1 + 1 + 256)
     # sync header | act [9, 768] | expert_out [8, 2048] | shared_out [1, 2048] | buckets
     assert q4.moe_layer_workspace_bytes(2048, 768, 128, 1, 8) == \
@@ -224,3 +226,18 @@ def test_rmsnorm_chain_validation(lib):
     assert _err(f, *base, None, 1e-6, FAKE, 512, 256, 4, 1, 2, 0) == _lib.Q4K_ERR_NULL
     assert _err(f, *base, FAKE, -1.0, FAKE + 4096, 512, 256, 4, 1, 2, 0) == _lib.Q4K_ERR_ARG
     assert _err(f, *base, FAKE, 1e-6, FAKE, 512, 256, 4, 1, 2, 0) == _lib.Q4K_ERR_NULL
+
+
+def test_mlx2_validation(lib):
+    g = q4.mlx2_moe_id_gemv
+    n, k = 64, 256
+    stride = q4.mlx2_matrix_bytes(n, k)
+    so, bo = n * k // 4, n * k // 4 + n * k // 32
+    assert _err(g, FAKE, stride, 0, so, bo, FAKE, FAKE, FAKE, n, 96, 1, 2, k, 0, 4) == \
+        _lib.Q4K_ERR_SHAPE
+    assert _err(g, FAKE, stride - 2, 0, so, bo, FAKE, FAKE, FAKE, n, k, 1, 2, k, 0, 4) == \
+        _lib.Q4K_ERR_SHAPE                              # biases run past the block
+    assert _err(g, FAKE, stride, 8, so, bo, FAKE, FAKE, FAKE, n, k, 1, 2, k, 0, 4) == \
+        _lib.Q4K_ERR_NULL                               # packed offset not 16-byte aligned
+    assert _err(q4.mlx2_dequantize, FAKE, FAKE, FAKE, FAKE, 4, 100) == _lib.Q4K_ERR_SHAPE
+    assert _err(q4.mlx2_quantize, FAKE, FAKE + 8, FAKE, FAKE, 4, 64) == _lib.Q4K_ERR_NULL

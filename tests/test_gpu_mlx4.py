@@ -202,3 +202,68 @@ def test_mlx4_gate_up_silu_matches_oracle(dev, shape):
         q4.mlx4_moe_gate_up_silu(d_blob, stride, goffs, uoffs, d_x[t:t + 1], d_ids[t * K:(t + 1) * K],
                                  one, n, k, 1, K, k, 0, E)
         assert np.array_equal(bits(sync_np(one)), bits(got[t * K:(t + 1) * K]))
+
+
+# ------------------------------------------------------------------ 2-bit ----
+
+def _experts2(g, E, n, k, touched):
+    zero = (np.zeros((n, k // 4), np.uint8), np.zeros((n, k // G), np.uint16),
+            np.zeros((n, k // G), np.uint16))
+    touched = set(int(e) for e in touched)
+    return [oracle.mlx2_quantize((g.standard_normal((n, k)) * 0.02).astype(np.float32))
+            if e in touched else zero for e in range(E)]
+
+
+def test_mlx2_dequant_and_quantize_bit_exact(dev):
+    g = np.random.default_rng(95)
+    for n, k in [(37, 320), (3, 64), (2, 16384)]:
+        say(f"2-bit dequant/quantize n={n} k={k}")
+        packed = g.integers(0, 256, (n, k // 4), dtype=np.uint8)
+        s = np.array([oracle.f32_to_bf16(float(v)) for v in g.standard_normal(n * k // G)],
+                     np.uint16)
+        b = np.array([oracle.f32_to_bf16(float(v)) for v in g.standard_normal(n * k // G)],
+                     np.uint16)
+        want = oracle.mlx2_dequantize(packed, s, b, n, k)
+        out = torch.empty(n, k, device=dev)
+        q4.mlx2_dequantize(T(packed, dev), T(s.view(np.int16), dev), T(b.view(np.int16), dev),
+                           out, n, k)
+        assert np.array_equal(bits(sync_np(out)), bits(want))
+        w = (g.standard_normal((n, k)) * 0.02 + 0.01).astype(np.float32)
+        p_o, s_o, b_o = oracle.mlx2_quantize(w)
+        p = torch.empty(n, k // 4, dtype=torch.uint8, device=dev)
+        sd = torch.empty(n, k // G, dtype=torch.int16, device=dev)
+        bd = torch.empty(n, k // G, dtype=torch.int16, device=dev)
+        q4.mlx2_quantize(T(w, dev), p, sd, bd, n, k)
+        assert np.array_equal(sync_np(p), p_o)
+        assert np.array_equal(sync_np(sd).view(np.uint16), s_o)
+        assert np.array_equal(sync_np(bd).view(np.uint16), b_o)
+
+
+CASES2 = [("decode gate, m=1", 128, 768, 2048, 1, 8, "gate_up", 0),
+          ("decode down, m=4", 128, 2048, 768, 4, 8, "down", 32),
+          ("ragged, one group", 5, 100, 64, 3, 3, "down", 16),
+          ("widest row", 2, 8, 16384, 1, 2, "gate_up", 0)]
+
+
+@pytest.mark.parametrize("case", CASES2, ids=[c[0] for c in CASES2])
+def test_mlx2_id_gemv_matches_oracle(dev, case):
+    name, E, n, k, m, K, mode, extra = case
+    say(f"2-bit id-GEMV {name}")
+    g = np.random.default_rng(96 + CASES2.index(case))
+    ids = np.stack([g.choice(E, K, replace=False) for _ in range(m)]).reshape(-1).astype(np.int32)
+    ids[-1] = E + 2   # an invalid id: zero row
+    blob, stride, offs = _blob(_experts2(g, E, n, k, ids[:-1]), extra)
+    if mode == "gate_up":
+        x = g.standard_normal((m, k)).astype(np.float32)
+        outer, inner = k, 0
+    else:
+        x = g.standard_normal((m * K, k)).astype(np.float32)
+        outer, inner = K * k, k
+    want = oracle.mlx2_moe_id_gemv(blob, stride, *offs, E, n, k, x, ids, m, K, outer, inner)
+    out = torch.empty(m * K, n, device=dev)
+    q4.mlx2_moe_id_gemv(T(blob, dev), stride, *offs, T(x, dev), T(ids, dev), out, n, k, m, K,
+                        outer, inner, E)
+    got = sync_np(out)
+    assert np.all(got[-1] == 0.0)
+    r = band(got, want, name)
+    say(f"  rel {r[0]:.3g} cos {r[1]:.9f}")
