@@ -288,7 +288,8 @@ def run_mlx4(torch, q4, wl, replicas, launches, warmup):
     shapes, 128 experts, top_k 8, m = 1: the fused gate/up + SiLU launch over
     expert blocks holding the gate and up matrices (768 x 2048 each, one
     activation row per token), and the down-shaped id-GEMV (2048 x 768, one
-    row per pair).  Each replica is a full 128-expert stack, device-encoded;
+    row per pair), that one also in the 2-bit variant (moeflux's g_use_2bit
+    layout).  Each replica is a full 128-expert stack, device-encoded;
     launches rotate over replicas and 64 routing draws.  Returns
     {name: (us per launch, unique weight bytes per launch)}."""
     dev = torch.device("cuda")
@@ -298,23 +299,26 @@ def run_mlx4(torch, q4, wl, replicas, launches, warmup):
     ids = [torch.from_numpy(a.ids).to(dev) for a in sets]
     uniq = [len(set(a.ids.tolist())) for a in sets]
     res = {}
-    for name, n, k, outer, inner, nmat in [("gate_up_silu", I, H, H, 0, 2),
-                                           ("down", H, I, K * I, I, 1)]:
-        mat = q4.mlx4_matrix_bytes(n, k)
+    for name, n, k, outer, inner, nmat, bits in [("gate_up_silu", I, H, H, 0, 2, 4),
+                                                 ("down", H, I, K * I, I, 1, 4),
+                                                 ("down_2bit", H, I, K * I, I, 1, 2)]:
+        mat = q4.mlx4_matrix_bytes(n, k) if bits == 4 else q4.mlx2_matrix_bytes(n, k)
+        pb = n * k * bits // 8                   # packed bytes of a matrix
         stride = nmat * mat
         # matrix j of a block: packed | scales | biases at j * mat
-        offs = [(j * mat, j * mat + n * k // 2, j * mat + n * k // 2 + n * k // 32)
-                for j in range(nmat)]
+        offs = [(j * mat, j * mat + pb, j * mat + pb + n * k // 32) for j in range(nmat)]
+        quantize = q4.mlx4_quantize if bits == 4 else q4.mlx2_quantize
         blobs = []
         for r in range(replicas):
             blob = torch.empty(E * stride, dtype=torch.uint8, device=dev)
             for j in range(nmat):
-                w = wl.device_normal((E * n, k), cfg.w_std, seed=70000 + 100 * r + 10 * j + nmat)
+                w = wl.device_normal((E * n, k), cfg.w_std,
+                                     seed=70000 + 100 * r + 10 * j + nmat + 3 * bits)
                 po, so, bo = offs[j]
                 for e in range(E):
                     b0 = e * stride
-                    q4.mlx4_quantize(w[e * n:(e + 1) * n], blob[b0 + po:b0 + so],
-                                     blob[b0 + so:b0 + bo], blob[b0 + bo:b0 + po + mat], n, k)
+                    quantize(w[e * n:(e + 1) * n], blob[b0 + po:b0 + so],
+                             blob[b0 + so:b0 + bo], blob[b0 + bo:b0 + po + mat], n, k)
                 del w
             blobs.append(blob)
         x = wl.device_normal((K, k), 1.0, seed=79999)   # row 0 for gate/up, 8 rows for down
@@ -322,9 +326,12 @@ def run_mlx4(torch, q4, wl, replicas, launches, warmup):
         torch.cuda.synchronize()
 
         def launch(i, n=n, k=k, stride=stride, outer=outer, inner=inner, blobs=blobs, x=x,
-                   out=out, offs=offs, nmat=nmat):
+                   out=out, offs=offs, nmat=nmat, bits=bits):
             blob, d_ids = blobs[i % replicas], ids[i % 64]
-            if nmat == 2:
+            if bits == 2:
+                q4.mlx2_moe_id_gemv(blob, stride, *offs[0], x, d_ids, out, n, k, 1, K, outer,
+                                    inner, E)
+            elif nmat == 2:
                 q4.mlx4_moe_gate_up_silu(blob, stride, offs[0], offs[1], x, d_ids, out, n, k, 1,
                                          K, outer, inner, E)
             else:
@@ -579,7 +586,8 @@ def main():
         line["mlx4"] = {
             "workload": "MLX affine 4-bit experts (bf16 scale and bias per 64 weights), 128 "
                         "experts, top_k 8, m=1: fused gate/up + SiLU over 768x2048 gate and up "
-                        "matrices, and the down-shaped 2048x768 id-GEMV; 8 replicas rotated",
+                        "matrices, the down-shaped 2048x768 id-GEMV, and the same in the 2-bit "
+                        "variant; 8 replicas rotated",
             "kernel": "k_mlx4_rows",
         }
         for k, (us, b) in mlx.items():
