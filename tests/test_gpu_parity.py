@@ -800,6 +800,45 @@ def test_self_bucketed_layer_equals_bucketing_launch(dev, no_self_bucket):
     assert np.array_equal(bits(selfb), bits(viaws))
 
 
+def test_self_bucketed_layer_edges(dev, no_self_bucket):
+    """In-kernel bucketing at its edges: a single expert (one bucket of every
+    pair, several chunks), no shared expert, every id invalid, and m = 3, the
+    smallest bucketed batch; each equal bit for bit to the bucketing launch."""
+    g = np.random.default_rng(62)
+    H, I = 512, 256
+    for E, K, m, ids_kind, mode in [(1, 4, 5, "all0", 0), (7, 2, 3, "random", 2),
+                                    (5, 3, 4, "invalid", 1)]:
+        say(f"self-bucketing edge E={E} K={K} m={m} ids={ids_kind} shared_mode={mode}")
+        st = [np.concatenate(quantize_many([(g.standard_normal((r, c)) * 0.05).astype(np.float32)
+                                            for _ in range(E)]))
+              for r, c in [(I, H), (I, H), (H, I)]]
+        sh = [oracle.q4k_quantize((g.standard_normal((r, c)) * 0.05).astype(np.float32))
+              for r, c in [(I, H), (I, H), (H, I)]]
+        h = g.standard_normal((m, H)).astype(np.float32)
+        hm = g.standard_normal((m, H)).astype(np.float32)
+        if ids_kind == "all0":
+            ids = np.zeros(m * K, np.int32)
+        elif ids_kind == "invalid":
+            ids = np.full(m * K, E + 3, np.int32)
+        else:
+            ids = g.integers(0, E, m * K).astype(np.int32)
+        rw = g.random(m * K).astype(np.float32)
+        lg = g.standard_normal(m).astype(np.float32)
+        _, _, _, eo = oracle.moe_expert_ffn(*st, E, H, I, h, ids, m, K)
+        so = None
+        if mode:
+            _, _, _, so = oracle.moe_expert_ffn(*sh, 1, H, I, h, np.zeros(m, np.int32), m, 1)
+        want = oracle.moe_combine_residual(hm, eo, rw, so, lg if mode == 1 else None, H, m, K,
+                                           mode)
+        shd = [T(x, dev) for x in sh] if mode else [None, None, None]
+        args = ([T(x, dev) for x in st], shd, T(h, dev), T(hm, dev), T(ids, dev), T(rw, dev),
+                T(lg, dev), H, I, E, m, K, mode)
+        selfb = _layer_raw(dev, *args)
+        viaws = no_self_bucket(lambda: _layer_raw(dev, *args))
+        band(selfb, want, "self-bucketing edge")
+        assert np.array_equal(bits(selfb), bits(viaws))
+
+
 @pytest.fixture
 def one_launch_layer():
     """Selects the opt-in one-launch single-token layer for one test."""
