@@ -466,7 +466,13 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineAr
     //    load in flight when it is waited for.  A per-lane select over the
     //    ids held in registers would become an indexed array in scratch.
     __shared__ int ex_lds[kMaxTopK];
+    __shared__ float rw_lds[kMaxTopK];
     const int e_own = a.ids[tok * K + (tid < K ? tid : K - 1)];
+    // The combine's routing weights and shared-expert gate logit are loaded
+    // here, with the ids, so that the combine at the end waits on no memory.
+    const float rw_own = cb.route_w[tok * K + (tid < K ? tid : K - 1)];
+    const bool gated = a.m_sh > 0 && cb.shared_mode == 1;   // uniform
+    const float logit = gated ? cb.shared_logit[tok] : 0.0f;
     // The first staging batch of the token's activation rows (routed rows,
     // then the shared row; both bases are uniform, lanes pick between the two
     // values) is issued next, ahead of the weights, as float4 loads with a
@@ -489,8 +495,10 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineAr
         for (int q = 0; q < 8; q++)
             xb.v[q] = *(const float4 *)(src + 4 * q);
     }
-    if (tid < K)
+    if (tid < K) {
         ex_lds[tid] = (unsigned)e_own < (unsigned)a.num_experts ? e_own : -1;
+        rw_lds[tid] = rw_own;
+    }
     lds_barrier();
     // 2. slot it*RPI + rsub -> (row row0 + slot/np, pair slot%np); weight
     //    loads, branch-free (clamped addresses; the shared pair selects its
@@ -546,14 +554,14 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineAr
         float acc = hm;
         for (int s = 0; s < K; s++) {
             const float yv = ybuf[ri * np + s];
-            acc = __builtin_fmaf(cb.route_w[tok * K + s], yv, acc);
+            acc = __builtin_fmaf(rw_lds[s], yv, acc);
             if (cb.expert_out)
                 cb.expert_out[(int64_t)(tok * K + s) * a.n + r] = yv;
         }
         if (a.m_sh > 0) {
             const float ysh = ybuf[ri * np + K];
             if (cb.shared_mode == 1) {
-                const float g = 1.0f / (1.0f + expf(-cb.shared_logit[tok]));
+                const float g = 1.0f / (1.0f + expf(-logit));
                 acc = __builtin_fmaf(g, ysh, acc);
             } else if (cb.shared_mode == 2) {
                 acc += ysh;

@@ -206,7 +206,7 @@ static int tp_iters(int tpb, int lpr, int max_it, int64_t row_bytes, int cols, i
 // decode walk.  512 threads in general; 1024 when rows are at most 4096
 // columns and the grid then holds at most one workgroup per CU (a small
 // tensor, where more waves per CU hide more latency).  Q4TP_THREADS (256,
-// 512 or 1024) overrides.
+// 512 or 1024) and Q4TP_ITERS (row groups: 1, 2, 4 or 8) override.
 template <int LPR, int NG>
 static hipError_t tp_launch(const void *const *ts, const int64_t *rows, int nseg, const float *x,
                             float *y, int cols, hipStream_t st) {
@@ -228,7 +228,10 @@ static hipError_t tp_launch(const void *const *ts, const int64_t *rows, int nseg
             tpb = 1024;
     }
     const int RPI = tpb / LPR;
-    const int it = tp_iters(tpb, LPR, kMaxIt, row_bytes, cols, total_rows, cus);
+    static const int it_env = env_int("Q4TP_ITERS", 0);
+    int it = tp_iters(tpb, LPR, kMaxIt, row_bytes, cols, total_rows, cus);
+    if (it_env == 1 || it_env == 2 || it_env == 4 || it_env == 8)
+        it = it_env < kMaxIt ? it_env : kMaxIt;
     const size_t lds = (size_t)(16 + 36 * gpr + gpr) * sizeof(float);
     auto go = [&](auto kern, int iters) {
         TpSegs sg{};
