@@ -51,7 +51,7 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 constexpr int kMP = kBucketChunk;   // pairs per workgroup (A rows: 8 hi parts, 8 lo parts)
 constexpr int kMRows = 64;          // weight rows per workgroup (4 waves x 16)
 #ifndef Q4K_MFMA_DEPTH
-#define Q4K_MFMA_DEPTH 3
+#define Q4K_MFMA_DEPTH 2
 #endif
 constexpr int kDepth = Q4K_MFMA_DEPTH;   // superblocks of weights in flight per wave
 constexpr int kSubB = 2 * 4 * kMP * 16;   // LDS bytes per staged sub-block: parts x groups x pairs x 16 B
