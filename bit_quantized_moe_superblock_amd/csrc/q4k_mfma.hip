@@ -539,9 +539,12 @@ static hipError_t go_mfma(const GemvArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Superblocks per staged activation slab: 4 by default (three workgroups per
+// CU fit beside a 33 KB slab; with two superblocks of weights in flight this
+// beat whole-row slabs of 8 at two per CU), Q4KMOE_MFMA_SLAB (1..8) overrides.
 template <int NT, int EPI>
 static hipError_t mfma_sb(const GemvArgs &a, hipStream_t st) {
-    static const int slab = env_int("Q4KMOE_MFMA_SLAB", 8);
+    static const int slab = env_int("Q4KMOE_MFMA_SLAB", 4);
     const int sb_max = slab < 1 ? 1 : slab > 8 ? 8 : slab;
     switch (a.k >> 8 < sb_max ? a.k >> 8 : sb_max) {
     case 1: return go_mfma<NT, EPI, 1>(a, st);
