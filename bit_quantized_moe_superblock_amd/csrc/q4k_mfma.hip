@@ -49,7 +49,13 @@ typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr int kMP = kBucketChunk;   // pairs per workgroup (A rows: 8 hi parts, 8 lo parts)
-constexpr int kMRows = 64;          // weight rows per workgroup (4 waves x 16)
+constexpr int kMRows = 64;          // weight rows per row group (4 waves x 16)
+// Epilogue of a single-matrix launch whose two register tiles are two row
+// groups of the same matrix (rows r and r + kMRows), so that an item covers
+// 2 kMRows rows against one staged activation slab.
+constexpr int kEpiRowPair = 2;
+static_assert(kEpiRowPair != EPI_STORE && kEpiRowPair != EPI_SWIGLU, "epilogue ids");
+__host__ __device__ constexpr int item_rows(int epi) { return epi == kEpiRowPair ? 2 * kMRows : kMRows; }
 #ifndef Q4K_MFMA_DEPTH
 #define Q4K_MFMA_DEPTH 2
 #endif
@@ -277,7 +283,7 @@ __device__ __forceinline__ void mfma_item(const GemvArgs &a, bool shared, int bk
     if (!shared && bkt == E) {   // ids outside [0, E): zero rows
         for (int i = 0; i < cnt; i++) {
             float *out = a.dst + (int64_t)pair_q(i) * a.n;
-            for (int r = tid; r < kMRows; r += kThreads)
+            for (int r = tid; r < item_rows(EPI); r += kThreads)
                 if (row0 + r < a.n)
                     out[row0 + r] = 0.0f;
         }
@@ -290,8 +296,12 @@ __device__ __forceinline__ void mfma_item(const GemvArgs &a, bool shared, int bk
     const int r = r0 < a.n ? r0 : a.n - 1;
     const uint8_t *wrow[NT];
     wrow[0] = (shared ? a.s0 : a.w0 + (int64_t)bkt * mat) + (int64_t)r * rowb;
-    if (NT == 2)
+    if constexpr (EPI == kEpiRowPair) {   // the second row group of the same matrix
+        const int r2 = r0 + kMRows < a.n ? r0 + kMRows : a.n - 1;
+        wrow[NT - 1] = (shared ? a.s0 : a.w0 + (int64_t)bkt * mat) + (int64_t)r2 * rowb;
+    } else if (NT == 2) {
         wrow[NT - 1] = (shared ? a.s1 : a.w1 + (int64_t)bkt * mat) + (int64_t)r * rowb;
+    }
     const uint8_t *sxa = lds_b + (size_t)SB * 8 * kSubB;
     const int nsub_total = a.k >> 5;
     const int gc = cnt;
@@ -354,11 +364,17 @@ __device__ __forceinline__ void mfma_item(const GemvArgs &a, bool shared, int bk
         if (g < 2 && i < gc && r0 < a.n) {
             const int q = pair_q(i);
             float *out = q < P ? a.dst + (int64_t)q * a.n : a.dst_sh + (int64_t)(q - P) * a.n;
-            float part[NT];
+            if constexpr (EPI == kEpiRowPair) {
+                out[r0] = yv[0][j];
+                if (r0 + kMRows < a.n)
+                    out[r0 + kMRows] = yv[NT - 1][j];
+            } else {
+                float part[NT];
 #pragma unroll
-            for (int nt = 0; nt < NT; nt++)
-                part[nt] = yv[nt][j];
-            out[r0] = epilogue<EPI, NT>(part);
+                for (int nt = 0; nt < NT; nt++)
+                    part[nt] = yv[nt][j];
+                out[r0] = epilogue<EPI, NT>(part);
+            }
         }
     }
 }
@@ -505,7 +521,7 @@ void k_bucket_mfma(GemvArgs a, int tiles) {
                 }
             lds_barrier();
         }
-        mfma_item<NT, EPI, SB>(a, shared, bkt, cnt, pl, first, x * kMRows, lds_b);
+        mfma_item<NT, EPI, SB>(a, shared, bkt, cnt, pl, first, x * item_rows(EPI), lds_b);
     }
 }
 
@@ -517,7 +533,7 @@ static hipError_t go_mfma(const GemvArgs &a, hipStream_t st) {
     const int64_t nb_max = a.n_pairs < (int64_t)a.num_experts + 1 ? a.n_pairs : a.num_experts + 1;
     const int n_slots = (int)(nb_max + a.n_pairs / kMP);
     const int sh_groups = (a.m_sh + kMP - 1) / kMP;
-    const int tiles = (a.n + kMRows - 1) / kMRows;
+    const int tiles = (a.n + item_rows(EPI) - 1) / item_rows(EPI);
     auto kern = k_bucket_mfma<NT, EPI, SB>;
     const size_t lds = set_lds((const void *)kern, mfma_lds_bytes(SB));
     // resident workgroups per CU: a property of the kernel and its fixed LDS
@@ -561,6 +577,9 @@ static hipError_t mfma_sb(const GemvArgs &a, hipStream_t st) {
 hipError_t launch_q4k_gemv_mfma(const GemvArgs &a, bool fused_swiglu, hipStream_t st) {
     if (fused_swiglu)
         return mfma_sb<2, EPI_SWIGLU>(a, st);
+    static const bool row_pair = env_int("Q4KMOE_MFMA_ROW_PAIR", 1) != 0;
+    if (row_pair)
+        return mfma_sb<2, kEpiRowPair>(a, st);
     return mfma_sb<1, EPI_STORE>(a, st);
 }
 
