@@ -267,7 +267,8 @@ __device__ __forceinline__ void mfma_superblock(const MfmaTile (&t)[NT], const u
 }
 
 // ------------------------------------------------------------ one item ---
-// Item = (chunk of at most kMP pairs of one bucket, 64-row tile).  pairs[i]
+// Item = (chunk of at most kMP pairs of one bucket, row tile of item_rows(EPI)
+// rows: 64, or 128 as a row pair).  pairs[i]
 // is the i-th pair of a routed chunk (ascending pair order); a shared chunk
 // is the shared expert's tokens first .. first + cnt - 1.  The first slab
 // starts with a barrier, so consecutive items of one workgroup may reuse the
@@ -420,7 +421,7 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int *wsum) {
 // pair count (<= kMP).
 __device__ __forceinline__ int chunk_pack(int b, int i, int c) { return b | (i << 11) | (c << 24); }
 
-// Persistent grid over the items (chunk, 64-row tile), chunk-major, the shared
+// Persistent grid over the items (chunk, row tile), chunk-major, the shared
 // expert's chunks of 8 tokens after the routed ones.  The host cannot know the
 // length of the chunk list, so a grid with one workgroup per possible item
 // would mostly be workgroups that find their slot past its end; instead the
