@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libq4kmoe.so")
 Q4K_OK, Q4K_ERR_SHAPE, Q4K_ERR_NULL, Q4K_ERR_STRIDE, Q4K_ERR_WORKSPACE, Q4K_ERR_LAUNCH, \
     Q4K_ERR_ARG = range(7)
 Q4K_BUCKET_AUTO, Q4K_BUCKET_OFF, Q4K_BUCKET_ON, Q4K_BUCKET_PREBUILT = 0, 1, 2, 3
+Q4K_BUCKET_MODE_MASK, Q4K_SCHED_VECTOR, Q4K_SCHED_BUCKET_LAUNCH = 0xFF, 0x100, 0x200
+Q4K_AUTO_BUCKET_MIN_TOKENS = 5
 MOE_SHARED_NONE, MOE_SHARED_SIGMOID, MOE_SHARED_UNSCALED = 0, 1, 2
 Q4K_BLOCK_WEIGHTS, Q4K_BLOCK_BYTES, Q4K_MAX_TOP_K = 256, 144, 16
 Q4K_MAX_IN, Q4K_MAX_EXPERTS, Q4K_MAX_PAIRS, Q4TP_MAX_COLS = 16384, 1023, 8192, 16384
@@ -39,7 +41,6 @@ SIGNATURES = {
     "moe_expert_ffn": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P,
                             _I64, _P]),
     "moe_layer_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64]),
-    "moe_layer_workspace_init": (_I, [_P, _I64, _P]),
     "moe_layer_forward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64,
                                _I64, _I64, _I, _I, _P, _I64, _P]),
     "moe_combine_residual": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
@@ -183,10 +184,6 @@ def moe_expert_ffn(w_gate, w_up, w_down, h_post, ids, act, expert_out, hidden: i
 def moe_layer_workspace_bytes(hidden: int, inter: int, num_experts: int, m: int,
                               top_k: int) -> int:
     return load().moe_layer_workspace_bytes(hidden, inter, num_experts, m, top_k)
-
-
-def moe_layer_workspace_init(ws, ws_bytes: int, stream=None):
-    _call("moe_layer_workspace_init", _ptr(ws), ws_bytes, _stream(stream))
 
 
 def moe_layer_forward(w_gate, w_up, w_down, sh_gate, sh_up, sh_down, h_post, h_mid, ids, route_w,

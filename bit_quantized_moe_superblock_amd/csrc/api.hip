@@ -30,14 +30,35 @@ int check_gemv_shape(int64_t n, int64_t k, int64_t m, int64_t top_k, int64_t E) 
     return Q4K_OK;
 }
 
-// Bucketed mode decision and workspace check; *use set on success.
-int bucket_mode(int flag, int64_t m, int64_t P, int64_t E, void *ws, int64_t ws_bytes,
-                bool *use) {
-    if (flag != Q4K_BUCKET_AUTO && flag != Q4K_BUCKET_OFF && flag != Q4K_BUCKET_ON &&
-        flag != Q4K_BUCKET_PREBUILT)
+// Splits a bucket_flag into its mode and schedule bits; Q4K_ERR_ARG for an
+// unknown mode or bit.
+int parse_flag(int flag, int *mode, bool *vector_units, bool *bucket_launch) {
+    *mode = flag & Q4K_BUCKET_MODE_MASK;
+    const int extra = flag & ~Q4K_BUCKET_MODE_MASK;
+    if (*mode != Q4K_BUCKET_AUTO && *mode != Q4K_BUCKET_OFF && *mode != Q4K_BUCKET_ON &&
+        *mode != Q4K_BUCKET_PREBUILT)
         return Q4K_ERR_ARG;
-    *use = flag == Q4K_BUCKET_ON || flag == Q4K_BUCKET_PREBUILT ||
-           (flag == Q4K_BUCKET_AUTO && m > 1);
+    if (extra & ~(Q4K_SCHED_VECTOR | Q4K_SCHED_BUCKET_LAUNCH))
+        return Q4K_ERR_ARG;
+    *vector_units = (extra & Q4K_SCHED_VECTOR) != 0;
+    *bucket_launch = (extra & Q4K_SCHED_BUCKET_LAUNCH) != 0;
+    return Q4K_OK;
+}
+
+bool bucketed_for(int mode, int64_t m) {
+    return mode == Q4K_BUCKET_ON || mode == Q4K_BUCKET_PREBUILT ||
+           (mode == Q4K_BUCKET_AUTO && m >= Q4K_AUTO_BUCKET_MIN_TOKENS);
+}
+
+// Bucketed mode decision and workspace check of the id-GEMV entry points;
+// *use and *vec set on success.
+int bucket_mode(int flag, int64_t m, int64_t P, int64_t E, void *ws, int64_t ws_bytes,
+                bool *use, bool *vec, int *mode) {
+    bool launch_bit = false;
+    int rc = parse_flag(flag, mode, vec, &launch_bit);
+    if (rc)
+        return rc;
+    *use = bucketed_for(*mode, m);
     if (!*use)
         return Q4K_OK;
     if (P > Q4K_MAX_PAIRS)
@@ -64,7 +85,7 @@ const char *q4k_status_string(int status) {
     }
 }
 
-int q4k_abi_version(void) { return 3; }
+int q4k_abi_version(void) { return 4; }
 
 int64_t q4k_matrix_bytes(int64_t n, int64_t k) {
     if (n < 0 || k <= 0 || k % Q4K_BLOCK_WEIGHTS)
@@ -137,17 +158,19 @@ int id_gemv_entry(const void *w0, const void *w1, const float *src1, const int32
     if (src1_outer_stride < 0 || src1_inner_stride < 0)
         return Q4K_ERR_STRIDE;
     const int64_t P = m * top_k;
-    bool use = false;
-    rc = bucket_mode(bucket_flag, m, P, num_experts, ws, ws_bytes, &use);
+    bool use = false, vec_units = false;
+    int mode = 0;
+    rc = bucket_mode(bucket_flag, m, P, num_experts, ws, ws_bytes, &use, &vec_units, &mode);
     if (rc)
         return rc;
     hipStream_t st = as_stream(stream);
-    if (use && bucket_flag != Q4K_BUCKET_PREBUILT) {
+    if (use && mode != Q4K_BUCKET_PREBUILT) {
         rc = launched(launch_moe_bucket(ids, P, num_experts, (int32_t *)ws, st));
         if (rc)
             return rc;
     }
     GemvLaunch L{};
+    L.vector_units = vec_units;
     L.w0 = w_stacked;
     L.w1 = w1;
     L.src1 = src1;
@@ -215,17 +238,19 @@ int moe_expert_ffn(const void *w_gate, const void *w_up, const void *w_down,
         !aligned4(ids) || !aligned4(act) || !aligned4(expert_out))
         return Q4K_ERR_NULL;
     const int64_t P = m * top_k;
-    bool use = false;
-    rc = bucket_mode(bucket_flag, m, P, num_experts, ws, ws_bytes, &use);
+    bool use = false, vec_units = false;
+    int mode = 0;
+    rc = bucket_mode(bucket_flag, m, P, num_experts, ws, ws_bytes, &use, &vec_units, &mode);
     if (rc)
         return rc;
     hipStream_t st = as_stream(stream);
-    if (use && bucket_flag != Q4K_BUCKET_PREBUILT) {
+    if (use && mode != Q4K_BUCKET_PREBUILT) {
         rc = launched(launch_moe_bucket(ids, P, num_experts, (int32_t *)ws, st));
         if (rc)
             return rc;
     }
     GemvLaunch L{};
+    L.vector_units = vec_units;
     L.w0 = w_gate;
     L.w1 = w_up;
     L.src1 = h_post;
@@ -261,18 +286,10 @@ int64_t moe_layer_workspace_bytes(int64_t hidden, int64_t inter, int64_t num_exp
     if (hidden < 1 || inter < 1 || num_experts < 1 || m < 1 || top_k < 1)
         return -1;
     const int64_t P = m * top_k;
-    auto up16 = [](int64_t b) { return (b + 255) / 256 * 256; };
-    // sync words | act [P+m, inter] | expert_out [P, hidden] | shared_out [m, hidden] | buckets
-    return MOE_LAYER_SYNC_BYTES + up16((P + m) * inter * 4) + up16(P * hidden * 4) +
-           up16(m * hidden * 4) + up16(moe_bucket_workspace_bytes(P, num_experts));
-}
-
-int moe_layer_workspace_init(void *ws, int64_t ws_bytes, void *stream) {
-    if (!ws || !aligned16(ws))
-        return Q4K_ERR_NULL;
-    if (ws_bytes < MOE_LAYER_SYNC_BYTES)
-        return Q4K_ERR_WORKSPACE;
-    return launched(hipMemsetAsync(ws, 0, MOE_LAYER_SYNC_BYTES, as_stream(stream)));
+    auto up256 = [](int64_t b) { return (b + 255) / 256 * 256; };
+    // act [P+m, inter] | expert_out [P, hidden] | shared_out [m, hidden] | buckets
+    return up256((P + m) * inter * 4) + up256(P * hidden * 4) + up256(m * hidden * 4) +
+           up256(moe_bucket_workspace_bytes(P, num_experts));
 }
 
 }  // extern "C"
@@ -280,13 +297,13 @@ int moe_layer_workspace_init(void *ws, int64_t ws_bytes, void *stream) {
 namespace {
 
 int layer_forward_impl(const void *w_gate, const void *w_up, const void *w_down,
-                              const void *sh_gate, const void *sh_up, const void *sh_down,
-                              const float *h_post, const float *h_mid, const int32_t *ids,
-                              const float *route_w, const float *shared_gate_logit, float *out,
-                              int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
-                              int64_t top_k, int shared_mode, int bucket_flag, void *ws,
-                              int64_t ws_bytes, void *stream, const void *norm_weight, float eps,
-                              float *normed) {
+                       const void *sh_gate, const void *sh_up, const void *sh_down,
+                       const float *h_post, const float *h_mid, const int32_t *ids,
+                       const float *route_w, const float *shared_gate_logit, float *out,
+                       int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
+                       int64_t top_k, int shared_mode, int bucket_flag, void *ws,
+                       int64_t ws_bytes, void *stream, const void *norm_weight, float eps,
+                       float *normed) {
     int rc = check_gemv_shape(inter, hidden, m, top_k, num_experts);
     if (rc)
         return rc;
@@ -296,9 +313,11 @@ int layer_forward_impl(const void *w_gate, const void *w_up, const void *w_down,
     if (shared_mode != MOE_SHARED_NONE && shared_mode != MOE_SHARED_SIGMOID &&
         shared_mode != MOE_SHARED_UNSCALED)
         return Q4K_ERR_ARG;
-    if (bucket_flag != Q4K_BUCKET_AUTO && bucket_flag != Q4K_BUCKET_OFF &&
-        bucket_flag != Q4K_BUCKET_ON && bucket_flag != Q4K_BUCKET_PREBUILT)
-        return Q4K_ERR_ARG;
+    int mode = 0;
+    bool vec_units = false, bucket_launch = false;
+    rc = parse_flag(bucket_flag, &mode, &vec_units, &bucket_launch);
+    if (rc)
+        return rc;
     if (!w_gate || !w_up || !w_down || !h_post || !h_mid || !ids || !route_w || !out ||
         !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned4(h_post) ||
         !aligned4(h_mid) || !aligned4(ids) || !aligned4(route_w) || !aligned4(out))
@@ -315,50 +334,15 @@ int layer_forward_impl(const void *w_gate, const void *w_up, const void *w_down,
     const int64_t need = moe_layer_workspace_bytes(hidden, inter, num_experts, m, top_k);
     if (!ws || !aligned16(ws) || ws_bytes < need)
         return Q4K_ERR_WORKSPACE;
-    auto up16 = [](int64_t b) { return (b + 255) / 256 * 256; };
-    uint32_t *sync = (uint32_t *)ws;
-    char *base = (char *)ws + MOE_LAYER_SYNC_BYTES;
+    auto up256 = [](int64_t b) { return (b + 255) / 256 * 256; };
+    char *base = (char *)ws;
     float *act = (float *)base;
-    float *eo = (float *)(base + up16((P + m) * inter * 4));
-    float *s_out = (float *)((char *)eo + up16(P * hidden * 4));
-    int32_t *bws = (int32_t *)((char *)s_out + up16(m * hidden * 4));
+    float *eo = (float *)(base + up256((P + m) * inter * 4));
+    float *s_out = (float *)((char *)eo + up256(P * hidden * 4));
+    int32_t *bws = (int32_t *)((char *)s_out + up256(m * hidden * 4));
     const int64_t m_sh = has_sh ? m : 0;
-    const bool bucketed = bucket_flag == Q4K_BUCKET_ON || bucket_flag == Q4K_BUCKET_PREBUILT ||
-                          (bucket_flag == Q4K_BUCKET_AUTO && m > 2);
+    const bool bucketed = bucketed_for(mode, m);
     hipStream_t st = as_stream(stream);
-    // The one-launch single-token layer is opt-in (Q4KMOE_FUSED_LAYER=1): on
-    // MI355X its device-wide barrier and one-workgroup-per-CU phases cost more
-    // than the second launch they save.
-    const char *fused_env = getenv("Q4KMOE_FUSED_LAYER");
-    const bool fused_ok = fused_env != nullptr && atoi(fused_env) != 0;
-    if (m == 1 && !bucketed && fused_ok && layer_m1_supported(hidden, inter, top_k, has_sh)) {
-        LayerLaunch L{};
-        L.w_gate = w_gate;
-        L.w_up = w_up;
-        L.w_down = w_down;
-        L.sh_gate = has_sh ? sh_gate : nullptr;
-        L.sh_up = has_sh ? sh_up : nullptr;
-        L.sh_down = has_sh ? sh_down : nullptr;
-        L.h_post = h_post;
-        L.h_mid = h_mid;
-        L.ids = ids;
-        L.route_w = route_w;
-        L.shared_logit = shared_gate_logit;
-        L.out = out;
-        L.act = act;
-        L.sync = sync;
-        L.hidden = hidden;
-        L.inter = inter;
-        L.num_experts = num_experts;
-        L.top_k = top_k;
-        L.shared_mode = shared_mode;
-        rc = launched(launch_layer_m1(L, st));
-        if (rc || !norm_weight)
-            return rc;
-        return launched(launch_combine_norm(nullptr, nullptr, nullptr, nullptr, nullptr,
-                                            norm_weight, eps, out, normed, hidden, m, top_k,
-                                            shared_mode, false, st));
-    }
     GemvLaunch G{};
     G.w0 = w_gate;
     G.w1 = w_up;
@@ -380,6 +364,7 @@ int layer_forward_impl(const void *w_gate, const void *w_up, const void *w_down,
     G.inner = 0;
     G.outer_sh = hidden;
     G.fused_swiglu = true;
+    G.vector_units = vec_units;
     GemvLaunch D = G;
     D.w0 = w_down;
     D.w1 = nullptr;
@@ -395,10 +380,12 @@ int layer_forward_impl(const void *w_gate, const void *w_up, const void *w_down,
     D.inner = inter;
     D.outer_sh = inter;
     D.fused_swiglu = false;
-    // Bucketed layers build their chunk lists inside the two matrix-core
-    // launches when the sizes allow; otherwise one bucketing launch writes
-    // the list to the layer workspace (PREBUILT is treated as ON here).
-    if (bucketed && q4k_self_bucket_ok(G) && q4k_self_bucket_ok(D)) {
+    // Bucketed layers on the matrix cores build their chunk lists inside the
+    // two launches when the sizes allow; otherwise (or when asked) one
+    // bucketing launch writes the list to the layer workspace (PREBUILT is
+    // treated as ON here).
+    if (bucketed && !vec_units && !bucket_launch && q4k_self_bucket_ok(G) &&
+        q4k_self_bucket_ok(D)) {
         G.bucket_ws = D.bucket_ws = nullptr;
         G.self_bucket = D.self_bucket = true;
     } else if (bucketed) {
@@ -409,7 +396,8 @@ int layer_forward_impl(const void *w_gate, const void *w_up, const void *w_down,
     rc = launched(launch_q4k_gemv(G, st));
     if (rc)
         return rc;
-    if (!bucketed) {
+    if (!bucketed && q4k_down_combine_ok(inter, top_k, has_sh)) {
+        // few tokens: down fused with the combine, expert_out never written
         rc = launched(launch_q4k_down_combine(D, h_mid, route_w, shared_gate_logit, out, nullptr,
                                               shared_mode, st));
         if (rc || !norm_weight)

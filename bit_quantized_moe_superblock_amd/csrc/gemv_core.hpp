@@ -1,7 +1,6 @@
-// Device core shared by the Q4_K GEMV kernels (q4k_gemv.hip) and the fused
-// single-token layer kernel (q4k_layer.hip): kernel arguments, activation
-// staging, the per-unit Q4_K arithmetic, row tiles and row reductions, plus a
-// few host-side launch helpers.
+// Device core shared by the Q4_K GEMV kernels (q4k_gemv.hip, q4k_mfma.hip):
+// kernel arguments, activation staging, the per-unit Q4_K arithmetic, row
+// tiles and row reductions, plus a few host-side launch helpers.
 //
 // Layout conventions (ferrum-kernels q4_k_moe_id_gemv_batched.rs, module doc:
 // expert stacks [E, n, k/256] of 144-byte Q4_K blocks, pair p = token*top_k +
@@ -10,12 +9,10 @@
 //     lane u owning unit u = (superblock u/4, 32-byte nibble chunk u%4), i.e.
 //     64 weights: sub-block 2c in the low nibbles and 2c+1 in the high ones;
 //   - activation rows are staged in LDS (padded so a row's lanes hit different
-//     banks) with their 32-element sums, or held per lane in registers; either
-//     way each sub-block sum is taken in ascending order from 0, so every mode
-//     rounds alike and gives identical bits.
+//     banks) with their 32-element sums, each taken in ascending order from 0
+//     by one thread, so every vector-unit mode rounds alike and gives
+//     identical bits.
 #pragma once
-
-#include <stdlib.h>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -305,68 +302,6 @@ __device__ __forceinline__ void load_rows(const uint8_t *w0, const uint8_t *w1, 
     }
 }
 
-// One lane's 64 activations (sub-blocks 2c and 2c+1 of its unit) held in
-// registers, with their sub-block sums.  The sums are taken in ascending order
-// from 0, exactly as stage_commit takes them, so every mode rounds alike.
-struct LaneX {
-    float4 xa[8], xb[8];
-    float sa, sb;
-};
-
-__device__ __forceinline__ void lane_x_issue(const float *x, int u, bool vec, LaneX &l) {
-    const float *p = x + 64 * u;
-    if (vec) {   // uniform
-#pragma unroll
-        for (int d = 0; d < 8; d++) {
-            l.xa[d] = *(const float4 *)(p + 4 * d);
-            l.xb[d] = *(const float4 *)(p + 32 + 4 * d);
-        }
-    } else {
-#pragma unroll
-        for (int d = 0; d < 8; d++) {
-            l.xa[d] = make_float4(p[4 * d], p[4 * d + 1], p[4 * d + 2], p[4 * d + 3]);
-            l.xb[d] = make_float4(p[32 + 4 * d], p[33 + 4 * d], p[34 + 4 * d], p[35 + 4 * d]);
-        }
-    }
-}
-
-__device__ __forceinline__ void lane_x_sums(LaneX &l) {
-    float sa = 0.0f, sb = 0.0f;
-#pragma unroll
-    for (int d = 0; d < 8; d++) {
-        sa += l.xa[d].x;
-        sa += l.xa[d].y;
-        sa += l.xa[d].z;
-        sa += l.xa[d].w;
-    }
-#pragma unroll
-    for (int d = 0; d < 8; d++) {
-        sb += l.xb[d].x;
-        sb += l.xb[d].y;
-        sb += l.xb[d].z;
-        sb += l.xb[d].w;
-    }
-    l.sa = sa;
-    l.sb = sb;
-}
-
-// Unit value of tensor (nt, it) of the tile against the lane's activations.
-template <int NT, int ITERS>
-__device__ __forceinline__ float unit_from_regs(const Tile<NT, ITERS> &t, int nt, int it,
-                                                const LaneX &l, int c) {
-    UnitAcc acc{0.0f, 0.0f};
-    const uint32_t w[8] = {t.qa[nt][it].x, t.qa[nt][it].y, t.qa[nt][it].z, t.qa[nt][it].w,
-                           t.qb[nt][it].x, t.qb[nt][it].y, t.qb[nt][it].z, t.qb[nt][it].w};
-#pragma unroll
-    for (int d = 0; d < 8; d++) {
-        const uint32_t v = w[d], s = v >> 8;
-        const uint32_t r[4] = {v & 0x000F000Fu, s & 0x000F000Fu, v & 0x00F000F0u,
-                               s & 0x00F000F0u};
-        masked_fma(r, l.xa[d], l.xb[d], acc);
-    }
-    return unit_value(unit_scale(t.hdr[nt][it], c), acc, l.sa, l.sb);
-}
-
 // Gate and up units (tile tensors 0 and 1) of row group `it` against the
 // staged row at xrow, reading the activations once for both.  Same per-unit
 // arithmetic and order as unit_from_tile.
@@ -450,11 +385,6 @@ static inline int lanes_per_row(int k) {
     while (l < units)
         l <<= 1;
     return l;
-}
-
-static inline int env_int(const char *name, int dflt) {
-    const char *s = getenv(name);
-    return s ? atoi(s) : dflt;
 }
 
 // Compute units of the current device (256 on MI355X), cached per device.

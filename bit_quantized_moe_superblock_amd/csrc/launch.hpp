@@ -21,6 +21,7 @@ struct GemvLaunch {
     int64_t outer, inner, outer_sh;
     bool fused_swiglu;
     bool self_bucket;          // bucketed mode with the chunks built in-kernel from ids
+    bool vector_units;         // bucketed mode on the vector units, not the matrix cores
 };
 
 // Largest pair count and bucket count (num_experts + 1) of self-bucketing.
@@ -28,9 +29,11 @@ constexpr int64_t kSelfBucketMaxPairs = 1024;
 constexpr int64_t kSelfBucketMaxBuckets = 1024;
 
 hipError_t launch_q4k_gemv(const GemvLaunch &L, hipStream_t st);
-// Whether L may run bucketed with self_bucket set: the matrix-core kernel
-// (enabled, 16-byte aligned activation rows) and the size limits above.
+// Whether L may run bucketed with self_bucket set (the size limits above).
 bool q4k_self_bucket_ok(const GemvLaunch &L);
+// Whether the down projection fused with the combine fits one workgroup's
+// LDS: the token's top_k (+ shared) activation rows of k floats are staged.
+bool q4k_down_combine_ok(int64_t k, int64_t top_k, bool shared);
 // Down projection fused with the weighted residual combine, one workgroup row
 // of tiles per token (few tokens).  expert_out may be null.
 hipError_t launch_q4k_down_combine(const GemvLaunch &L, const float *h_mid, const float *route_w,
@@ -57,22 +60,6 @@ hipError_t launch_q4tp_matvec(const void *t, const float *x, float *y, int64_t r
                               int64_t cols, hipStream_t st);
 hipError_t launch_q4tp_quant(const float *w, void *t, int64_t rows, int64_t cols,
                              hipStream_t st);
-
-// One whole single-token layer in one launch (q4k_layer.hip).
-struct LayerLaunch {
-    const void *w_gate, *w_up, *w_down;
-    const void *sh_gate, *sh_up, *sh_down;   // null when there is no shared expert
-    const float *h_post, *h_mid;
-    const int32_t *ids;
-    const float *route_w, *shared_logit;
-    float *out;
-    float *act;        // [top_k (+1), inter] scratch
-    uint32_t *sync;    // barrier words (zero before first use, left zero)
-    int64_t hidden, inter, num_experts, top_k;
-    int shared_mode;
-};
-bool layer_m1_supported(int64_t hidden, int64_t inter, int64_t top_k, int has_shared);
-hipError_t launch_layer_m1(const LayerLaunch &L, hipStream_t st);
 
 // MLX affine 4-bit id-GEMV (mlx4.hip): expert e's block at base + e*expert_stride,
 // its packed weights, scales and biases at the offsets inside the block (a

@@ -23,17 +23,21 @@
 // Kernels:
 //   k_rows    pair mode: grid (row tiles, pairs [+ shared pairs]); a workgroup
 //             loads ITERS row groups of one pair up front, then computes.
-//   k_bucket  bucketed mode: grid (row groups, bucket slots [+ shared bucket]);
-//             a workgroup holds one row group of one expert with its nibbles
-//             already masked, and runs every pair of the expert's bucket
-//             against it, PC pairs per LDS chunk, so each expert's weights are
-//             read from HBM once per call (moeflux encode_moe_batched_permute_fuse).
+//   k_bucket  bucketed mode on the vector units: grid (row groups, chunk
+//             slots [+ shared chunks]); a workgroup holds one row group of one
+//             expert in registers and runs every pair of its chunk against it,
+//             PC pairs per LDS batch, so each expert's weights are read from
+//             HBM once per chunk (moeflux encode_moe_batched_permute_fuse).
+//             The matrix-core kernels (q4k_mfma.hip) are the default bucketed
+//             schedule; this one is selected explicitly.
 //   k_down_combine  token mode for few tokens: a workgroup computes a row tile
 //             of the down projection for all top_k (+ shared) pairs of one
 //             token and applies the weighted residual combine in slot order
 //             (moeflux moe_combine_residual).
-// Every kernel runs the same per-unit arithmetic in the same order, so pair,
-// bucketed and token modes give identical bits.
+// Every kernel here runs the same per-unit arithmetic in the same order, so
+// pair, vector-unit bucketed and token modes give identical bits.  Activation
+// rows need only be 4-byte aligned: staging uses float4 loads when rows and
+// strides are 16-byte aligned, 4-byte loads otherwise, with the same sums.
 #include <stdint.h>
 
 #include "gemv_core.hpp"
@@ -42,19 +46,17 @@ namespace q4k {
 
 // ------------------------------------------------------------ pair mode ----
 
-// XLDS: the pair's activation row is staged once per workgroup in LDS (a
-// thread per 32-float sub-block, float4 loads issued ahead of the weights,
-// committed with its sub-block sum) and every lane reads its unit's 64
-// activations from there; otherwise (rows not 16-byte aligned) each lane loads
-// them into registers itself.  Both give the same bits: the sub-block sums are
-// taken in ascending order from 0 either way.
-template <int LPR, int NT, int ITERS, int EPI, bool XLDS>
+// The pair's activation row is staged once per workgroup in LDS (a thread
+// per 32-float sub-block, loads issued ahead of the weights, committed with
+// its sub-block sum) and every lane reads its unit's 64 activations from
+// there.
+template <int LPR, int NT, int ITERS, int EPI>
 __global__ __launch_bounds__(kThreads) void k_rows(GemvArgs a) {
     extern __shared__ float lds[];
     fetch_args(a);
     constexpr int RPI = kThreads / LPR;
     float *red = lds;        // cross-wave row sums (rows wider than a wave)
-    float *xs = lds + 16;    // staged activation row (XLDS)
+    float *xs = lds + 16;    // staged activation row
     const int q = blockIdx.y;
     const int row0 = blockIdx.x * (ITERS * RPI);
     const PairRef pr = pair_ref(a, q);
@@ -68,63 +70,34 @@ __global__ __launch_bounds__(kThreads) void k_rows(GemvArgs a) {
     const int u = tid % LPR, rsub = tid / LPR;
     const bool active = u < 4 * (a.k >> 8);
     const int ul = active ? u : 0, cl = ul & 3;   // clamped unit (see load_rows)
-    if constexpr (XLDS) {
-        const int nsub = a.k >> 5;
-        StageBatch xb;
-        xb.f = tid;
-        {
-            const int f = tid < nsub ? tid : nsub - 1;   // clamped, no branch
+    const int nsub = a.k >> 5;
+    auto x_of = [&](int) { return pr.x; };
+    StageBatch xb;
+    stage_issue(x_of, 0, nsub, a.k, a.vec != 0, xb);
+    __builtin_amdgcn_sched_barrier(0);   // keep them ahead of the weights
+    Tile<NT, ITERS> t;
+    load_rows<LPR, NT, ITERS>(pr.w0, pr.w1, a.n, a.k, row0, true, t);
+    stage_commit(xb, nsub, a.k, xs);
+    stage_rows(x_of, 1, a.k, a.vec != 0, xs, kThreads);   // k > 8192
+    lds_barrier();
 #pragma unroll
-            for (int q = 0; q < 8; q++)
-                xb.v[q] = *(const float4 *)(pr.x + 32 * f + 4 * q);
+    for (int it = 0; it < ITERS; it++) {
+        // Computed on every lane (inactive lanes hold a clamped, valid unit)
+        // and then selected: under a branch the compiler sinks part of the
+        // weight loads into it, and their wait drains the queue.
+        float part[NT];
+        if constexpr (NT == 2) {
+            float v0, v1;
+            unit_pair_from_tile<ITERS>(t, it, xs, ul, cl, a.k, v0, v1);
+            part[0] = row_reduce<LPR>(active ? v0 : 0.0f, red, 0);
+            part[1] = row_reduce<LPR>(active ? v1 : 0.0f, red, 1);
+        } else {
+            const float uv = unit_from_tile<NT, ITERS>(t, 0, it, xs, ul, cl, a.k);
+            part[0] = row_reduce<LPR>(active ? uv : 0.0f, red, 0);
         }
-        __builtin_amdgcn_sched_barrier(0);   // keep them ahead of the weights
-        Tile<NT, ITERS> t;
-        load_rows<LPR, NT, ITERS>(pr.w0, pr.w1, a.n, a.k, row0, true, t);
-        stage_commit(xb, nsub, a.k, xs);
-        stage_rows([&](int) { return pr.x; }, 1, a.k, true, xs, kThreads);   // k > 8192
-        lds_barrier();
-#pragma unroll
-        for (int it = 0; it < ITERS; it++) {
-            // Computed on every lane (inactive lanes hold a clamped, valid
-            // unit) and then selected: under a branch the compiler sinks part
-            // of the weight loads into it, and their wait drains the queue.
-            float part[NT];
-            if constexpr (NT == 2) {
-                float v0, v1;
-                unit_pair_from_tile<ITERS>(t, it, xs, ul, cl, a.k, v0, v1);
-                part[0] = row_reduce<LPR>(active ? v0 : 0.0f, red, 0);
-                part[1] = row_reduce<LPR>(active ? v1 : 0.0f, red, 1);
-            } else {
-                const float uv = unit_from_tile<NT, ITERS>(t, 0, it, xs, ul, cl, a.k);
-                part[0] = row_reduce<LPR>(active ? uv : 0.0f, red, 0);
-            }
-            const int r = row0 + it * RPI + rsub;
-            if (u == 0 && r < a.n)
-                pr.out[r] = epilogue<EPI, NT>(part);
-        }
-    } else {
-        // each lane reads its unit's 64 activations straight into registers
-        // (the rows of a workgroup share them through the cache), then its
-        // weights
-        const int c = u & 3;
-        LaneX lx;
-        lane_x_issue(pr.x, ul, a.vec, lx);
-        Tile<NT, ITERS> t;
-        load_rows<LPR, NT, ITERS>(pr.w0, pr.w1, a.n, a.k, row0, true, t);
-        lane_x_sums(lx);
-#pragma unroll
-        for (int it = 0; it < ITERS; it++) {
-            float part[NT];
-#pragma unroll
-            for (int nt = 0; nt < NT; nt++) {
-                const float uv = unit_from_regs<NT, ITERS>(t, nt, it, lx, c);
-                part[nt] = row_reduce<LPR>(active ? uv : 0.0f, red, nt);
-            }
-            const int r = row0 + it * RPI + rsub;
-            if (u == 0 && r < a.n)
-                pr.out[r] = epilogue<EPI, NT>(part);
-        }
+        const int r = row0 + it * RPI + rsub;
+        if (u == 0 && r < a.n)
+            pr.out[r] = epilogue<EPI, NT>(part);
     }
 }
 
@@ -254,184 +227,6 @@ __global__ __launch_bounds__(kThreads) void k_bucket(GemvArgs a) {
     }
 }
 
-// ------------------------------------------------ persistent bucketed ----
-// A fixed grid of workgroups (CUs x resident workgroups) walks the work items
-// (chunk, row tile) round-robin.  The chunk and pair lists are read into LDS
-// once; each item's weights and activation loads are issued while the
-// previous item computes, so HBM and L2 latency overlap with the arithmetic.
-// One staging batch (256 sub-blocks of 32 floats) holds pc = 8192/k pairs;
-// items with more pairs than that stage the rest synchronously.
-
-constexpr int kPersistMaxPairs = 1024;
-
-template <int NT, int ITERS>
-struct Item {
-    Tile<NT, ITERS> t;
-    StageBatch xb;
-    int chunk, tile;   // chunk < 0: no item
-};
-
-template <int LPR, int NT, int ITERS, int EPI>
-__global__ __launch_bounds__(kThreads) void k_bucket_persist(GemvArgs a, int n_tiles) {
-    extern __shared__ float lds[];
-    fetch_args(a);
-    constexpr int RPI = kThreads / LPR;
-    const int tid = threadIdx.x;
-    const int P = a.n_pairs, E = a.num_experts;
-    int *meta = (int *)lds;                      // chunks[2P] | pairs[P]
-    float *xs = lds + 3 * P;
-    const int rl = row_lds_floats(a.k);
-    float *red = xs + a.pc * rl;
-    // chunk list and pair list into LDS in one round of loads
-    const int32_t *ws = a.bucket;
-    const int32_t *pairs_g = ws + (E + 1) + (E + 2);
-    const int32_t *nch_g = pairs_g + P + (E + 1) + 1;
-    const int32_t *chunks_g = nch_g + 1;
-    for (int i = tid; i < 2 * P; i += kThreads)
-        meta[i] = chunks_g[i];
-    for (int i = tid; i < P; i += kThreads)
-        meta[2 * P + i] = pairs_g[i];
-    const int nch = *nch_g;
-    __syncthreads();
-    const int n_chunks = nch + (a.m_sh + kBucketChunk - 1) / kBucketChunk;
-    const int n_items = n_chunks * n_tiles;
-    const int u = tid % LPR, rsub = tid / LPR, c = u & 3;
-    const bool active = u < 4 * (a.k >> 8);
-    const int64_t mat = (int64_t)a.n * (int64_t)(a.k >> 8) * kBlockBytes;
-
-    // (chunk) -> bucket, first pair position, pair count, weights
-    auto chunk_info = [&](int ch, int &bkt, int &first, int &cnt, bool &shared) {
-        if (ch < nch) {
-            bkt = meta[2 * ch];
-            const int pk = meta[2 * ch + 1];
-            first = pk & 0xFFFFFF;
-            cnt = pk >> 24;
-            shared = false;
-        } else {
-            bkt = -1;
-            first = (ch - nch) * kBucketChunk;
-            cnt = a.m_sh - first < kBucketChunk ? a.m_sh - first : kBucketChunk;
-            shared = true;
-        }
-    };
-    auto pair_at = [&](bool shared, int first, int i) {
-        return shared ? P + first + i : meta[2 * P + first + i];
-    };
-    auto issue = [&](int item, Item<NT, ITERS> &it) {
-        if (item >= n_items) {
-            it.chunk = -1;
-            return;
-        }
-        it.chunk = item / n_tiles;
-        it.tile = item - it.chunk * n_tiles;
-        int bkt, first, cnt;
-        bool shared;
-        chunk_info(it.chunk, bkt, first, cnt, shared);
-        const bool zero = !shared && bkt == E;
-        const uint8_t *w0 = shared ? a.s0 : a.w0 + (zero ? 0 : (int64_t)bkt * mat);
-        const uint8_t *w1 = shared ? a.s1 : (a.w1 ? a.w1 + (zero ? 0 : (int64_t)bkt * mat) : nullptr);
-        load_rows<LPR, NT, ITERS>(w0, w1, a.n, a.k, it.tile * ITERS * RPI, !zero, it.t);
-        const int cl = cnt < a.pc ? cnt : a.pc;
-        stage_issue([&](int i) { return pair_x_known(a, shared, pair_at(shared, first, i)); }, 0,
-                    zero ? 0 : cl * (a.k >> 5), a.k, a.vec, it.xb);
-    };
-
-    // Two item buffers in ping-pong: the next item loads into the buffer the
-    // current one does not use (copying it over would wait for its loads).
-    auto step = [&](int item, Item<NT, ITERS> &cur, Item<NT, ITERS> &nxt) {
-        int bkt, first, cnt;
-        bool shared;
-        chunk_info(cur.chunk, bkt, first, cnt, shared);
-        const bool zero = !shared && bkt == E;
-        const int row0 = cur.tile * ITERS * RPI;
-        const int cl0 = cnt < a.pc ? cnt : a.pc;
-        __syncthreads();   // LDS of the previous item is consumed
-        stage_commit(cur.xb, zero ? 0 : cl0 * (a.k >> 5), a.k, xs);
-        issue(item + gridDim.x, nxt);   // next item's loads fly during this item
-        if (zero) {
-            for (int i = 0; i < cnt; i++) {
-                float *out = a.dst + (int64_t)pair_at(false, first, i) * a.n;
-                for (int r = tid; r < ITERS * RPI; r += kThreads)
-                    if (row0 + r < a.n)
-                        out[row0 + r] = 0.0f;
-            }
-        } else {
-            UnitScale sc[ITERS][NT];
-#pragma unroll
-            for (int it = 0; it < ITERS; it++)
-#pragma unroll
-                for (int nt = 0; nt < NT; nt++)
-                    sc[it][nt] = unit_scale(cur.t.hdr[nt][it], c);
-            for (int c0 = 0; c0 < cnt; c0 += a.pc) {
-                const int cl = cnt - c0 < a.pc ? cnt - c0 : a.pc;
-                if (c0 > 0) {
-                    __syncthreads();
-                    stage_rows([&](int i) {
-                        return pair_x_known(a, shared, pair_at(shared, first, c0 + i));
-                    }, cl, a.k, a.vec, xs);
-                }
-                __syncthreads();
-                for (int i = 0; i < cl; i++) {
-                    const float *xrow = xs + i * rl;
-                    opaque(cur.t);
-                    UnitAcc acc[ITERS][NT];
-#pragma unroll
-                    for (int it = 0; it < ITERS; it++)
-#pragma unroll
-                        for (int nt = 0; nt < NT; nt++)
-                            acc[it][nt].a = acc[it][nt].b = 0.0f;
-                    if (active) {
-                        const float4 *xa = (const float4 *)(xrow + 68 * u);
-                        const float4 *xb = xa + 8;
-#pragma unroll
-                        for (int d = 0; d < 8; d++) {
-                            const float4 va = xa[d], vb = xb[d];
-#pragma unroll
-                            for (int it = 0; it < ITERS; it++)
-#pragma unroll
-                                for (int nt = 0; nt < NT; nt++) {
-                                    const uint4 &q = d < 4 ? cur.t.qa[nt][it] : cur.t.qb[nt][it];
-                                    const uint32_t v = (d & 3) == 0 ? q.x : (d & 3) == 1 ? q.y
-                                                     : (d & 3) == 2 ? q.z : q.w;
-                                    const uint32_t sh = v >> 8;
-                                    const uint32_t r[4] = {v & 0x000F000Fu, sh & 0x000F000Fu,
-                                                           v & 0x00F000F0u, sh & 0x00F000F0u};
-                                    masked_fma(r, va, vb, acc[it][nt]);
-                                }
-                        }
-                    }
-                    const float *sx = xrow + xpad_len(a.k);
-                    const float sxA = active ? sx[2 * u] : 0.0f;
-                    const float sxB = active ? sx[2 * u + 1] : 0.0f;
-                    const int q = pair_at(shared, first, c0 + i);
-                    float *out = q < P ? a.dst + (int64_t)q * a.n
-                                       : a.dst_sh + (int64_t)(q - P) * a.n;
-#pragma unroll
-                    for (int it = 0; it < ITERS; it++) {
-                        float part[NT];
-#pragma unroll
-                        for (int nt = 0; nt < NT; nt++) {
-                            const float v =
-                                active ? unit_value(sc[it][nt], acc[it][nt], sxA, sxB) : 0.0f;
-                            part[nt] = row_reduce<LPR>(v, red, nt);
-                        }
-                        const int r = row0 + it * RPI + rsub;
-                        if (u == 0 && r < a.n)
-                            out[r] = epilogue<EPI, NT>(part);
-                    }
-                }
-            }
-        }
-            };
-    Item<NT, ITERS> A, B;
-    issue(blockIdx.x, A);
-    for (int item = blockIdx.x; item < n_items; item += 2 * gridDim.x) {
-        step(item, A, B);
-        if (item + gridDim.x < n_items)
-            step(item + gridDim.x, B, A);
-    }
-}
-
 // ---------------------------------------------------- down + combine mode ----
 // Workgroup = (token t, TRT rows).  Slots enumerate (row, pair) with the pair
 // fastest: pairs 0..top_k-1 are the token's routed pairs, pair top_k the shared
@@ -475,10 +270,9 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineAr
     const float logit = gated ? cb.shared_logit[tok] : 0.0f;
     // The first staging batch of the token's activation rows (routed rows,
     // then the shared row; both bases are uniform, lanes pick between the two
-    // values) is issued next, ahead of the weights, as float4 loads with a
-    // clamped index and no branch: waiting for the ids above leaves it in
-    // flight, and committing it below waits for it alone.  The host launches
-    // this kernel only on 16-byte aligned rows.
+    // values) is issued next, ahead of the weights, with a clamped index and
+    // no branch: waiting for the ids above leaves it in flight, and
+    // committing it below waits for it alone.
     const float *xr = a.src1 + tok * a.outer;
     const float *xsh = a.m_sh > 0 ? a.src1_sh + tok * a.outer_sh : xr;
     const int64_t inner = a.inner;
@@ -486,15 +280,7 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineAr
     const int nsub = a.k >> 5;
     const int total = np * nsub;
     StageBatch xb;
-    {
-        xb.f = tid;
-        const int f = tid < total ? tid : total - 1;
-        const int xrow = f / nsub, j = f - xrow * nsub;
-        const float *src = x_of(xrow) + 32 * j;
-#pragma unroll
-        for (int q = 0; q < 8; q++)
-            xb.v[q] = *(const float4 *)(src + 4 * q);
-    }
+    stage_issue(x_of, 0, total, a.k, a.vec != 0, xb);
     if (tid < K) {
         ex_lds[tid] = (unsigned)e_own < (unsigned)a.num_experts ? e_own : -1;
         rw_lds[tid] = rw_own;
@@ -537,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineAr
     // 4. activation rows of the token's pairs into LDS (first batch, then any
     //    further ones)
     stage_commit(xb, total, a.k, lds);
-    stage_rows(x_of, np, a.k, true, lds, kThreads);
+    stage_rows(x_of, np, a.k, a.vec != 0, lds, kThreads);
     lds_barrier();
 #pragma unroll
     for (int it = 0; it < ITERS; it++) {
@@ -578,9 +364,6 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineAr
 // Row groups per workgroup in pair mode: as tall as possible while the grid
 // still gives every CU a workgroup (256 CUs on MI355X).
 static int pick_iters(int64_t pairs, int n, int rpi, int max_it) {
-    static const int forced = env_int("Q4KMOE_ITERS", 0);
-    if (forced == 1 || forced == 2 || forced == 3 || forced == 4 || forced == 6 || forced == 8)
-        return forced;
     // Smallest (waves of workgroups over the CUs) x (row groups per
     // workgroup): a grid just past a multiple of the CU count leaves some CUs
     // with twice the work of the rest.  Ties go to a grid that gives every CU
@@ -606,15 +389,12 @@ static int pick_iters(int64_t pairs, int n, int rpi, int max_it) {
     return best;
 }
 
-// Row groups per workgroup when the activation row is staged in LDS: the
+// Row groups per workgroup with the activation row staged in LDS: the
 // shortest tile whose staged row (4k bytes, read from the cache) is at most
 // half of its weight bytes and whose grid still gives every CU a workgroup
 // (more, smaller workgroups hide each other's latency); otherwise the rule
 // above.
 static int pick_iters_staged(int64_t pairs, int n, int rpi, int max_it, int k, int nt) {
-    static const int forced = env_int("Q4KMOE_ITERS", 0);
-    if (forced == 1 || forced == 2 || forced == 3 || forced == 4 || forced == 6 || forced == 8)
-        return forced;
     const int64_t cus = cu_count();
     const int64_t rowb = (int64_t)(k >> 8) * kBlockBytes;
     const int cand[] = {1, 2, 3, 4, 6, 8};
@@ -632,45 +412,23 @@ template <int LPR, int NT, int EPI, int IT>
 static hipError_t go_rows(const GemvArgs &a, hipStream_t st) {
     constexpr int RPI = kThreads / LPR;
     dim3 grid((a.n + IT * RPI - 1) / (IT * RPI), a.n_pairs + a.m_sh);
-    if (a.vec) {
-        auto kern = k_rows<LPR, NT, IT, EPI, true>;
-        const size_t lds = set_lds((const void *)kern, (16 + (size_t)row_lds_floats(a.k)) * sizeof(float));
-        hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a);
-    } else {
-        auto kern = k_rows<LPR, NT, IT, EPI, false>;
-        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 8 * sizeof(float), st, a);
-    }
+    auto kern = k_rows<LPR, NT, IT, EPI>;
+    const size_t lds =
+        set_lds((const void *)kern, (16 + (size_t)row_lds_floats(a.k)) * sizeof(float));
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a);
     return hipGetLastError();
 }
+
+// LDS budget of the vector-unit bucketed kernel's staged activation rows.
+constexpr int kBucketLdsBytes = 40 * 1024;
 
 template <int LPR, int NT, int EPI>
 static hipError_t launch_lpr(GemvArgs a, bool bucketed, hipStream_t st) {
     constexpr int RPI = kThreads / LPR;
-    if (bucketed && a.k <= 8192 && a.n_pairs <= kPersistMaxPairs &&
-        env_int("Q4KMOE_PERSIST", 1) != 0) {
-        constexpr int IT = NT == 2 ? 2 : 4;
-        const int rl = row_lds_floats(a.k);
-        a.pc = 8192 / a.k < kBucketChunk ? 8192 / a.k : kBucketChunk;
-        auto kern = k_bucket_persist<LPR, NT, IT, EPI>;
-        const size_t lds = set_lds((const void *)kern,
-                                   ((size_t)3 * a.n_pairs + (size_t)a.pc * rl + 8) * sizeof(float));
-        const int n_tiles = (a.n + IT * RPI - 1) / (IT * RPI);
-        // every workgroup of a persistent grid must be resident at once
-        int fit = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, (const void *)kern, kThreads,
-                                                         lds) != hipSuccess || fit < 1)
-            fit = 1;
-        static const int per_cu = env_int("Q4KMOE_PERSIST_WG", 2);
-        const int wg = per_cu < fit ? per_cu : fit;
-        hipLaunchKernelGGL(kern, dim3(cu_count() * (wg < 1 ? 1 : wg)), dim3(kThreads), lds, st,
-                           a, n_tiles);
-        return hipGetLastError();
-    }
     if (bucketed) {
         constexpr int IT = NT == 2 ? 2 : 4;
         const int rl = row_lds_floats(a.k);
-        static const int budget = env_int("Q4KMOE_CHUNK_LDS", 40 * 1024);
-        int pc = (int)((budget / 4 - 8) / rl);
+        int pc = (int)((kBucketLdsBytes / 4 - 8) / rl);
         pc = pc < 1 ? 1 : (pc > kBucketChunk ? kBucketChunk : pc);
         a.pc = pc;
         auto kern = k_bucket<LPR, NT, IT, EPI>;
@@ -681,9 +439,7 @@ static hipError_t launch_lpr(GemvArgs a, bool bucketed, hipStream_t st) {
         return hipGetLastError();
     }
     const int max_it = NT == 2 ? 4 : 8;
-    const int it = a.vec ? pick_iters_staged(a.n_pairs + a.m_sh, a.n, RPI, max_it, a.k, NT)
-                         : pick_iters(a.n_pairs + a.m_sh, a.n, RPI, max_it);
-    switch (it) {
+    switch (pick_iters_staged(a.n_pairs + a.m_sh, a.n, RPI, max_it, a.k, NT)) {
     case 8: return go_rows<LPR, NT, EPI, (NT == 2 ? 4 : 8)>(a, st);
     case 6: return go_rows<LPR, NT, EPI, (NT == 2 ? 4 : 6)>(a, st);
     case 4: return go_rows<LPR, NT, EPI, 4>(a, st);
@@ -693,6 +449,8 @@ static hipError_t launch_lpr(GemvArgs a, bool bucketed, hipStream_t st) {
     }
 }
 
+// k in [256, Q4K_MAX_IN] and a multiple of 256 (validated by the caller), so
+// lanes_per_row(k) is one of the cases.
 template <int NT, int EPI>
 static hipError_t launch_any(const GemvArgs &a, bool bucketed, hipStream_t st) {
     switch (lanes_per_row(a.k)) {
@@ -702,8 +460,7 @@ static hipError_t launch_any(const GemvArgs &a, bool bucketed, hipStream_t st) {
     case 32: return launch_lpr<32, NT, EPI>(a, bucketed, st);
     case 64: return launch_lpr<64, NT, EPI>(a, bucketed, st);
     case 128: return launch_lpr<128, NT, EPI>(a, bucketed, st);
-    case 256: return launch_lpr<256, NT, EPI>(a, bucketed, st);
-    default: return hipErrorInvalidValue;
+    default: return launch_lpr<256, NT, EPI>(a, bucketed, st);
     }
 }
 
@@ -735,47 +492,37 @@ static GemvArgs make_args(const GemvLaunch &L) {
     return a;
 }
 
-static bool mfma_enabled() {
-    static const bool mfma = env_int("Q4KMOE_MFMA", 1) != 0;
-    return mfma;
-}
-
 bool q4k_self_bucket_ok(const GemvLaunch &L) {
-    // Q4KMOE_SELF_BUCKET=0 keeps the separate bucketing launch (read per call)
-    const char *env = getenv("Q4KMOE_SELF_BUCKET");
-    if (env != nullptr && atoi(env) == 0)
-        return false;
-    return mfma_enabled() && make_args(L).vec && L.n_pairs <= kSelfBucketMaxPairs &&
-           L.num_experts + 1 <= kSelfBucketMaxBuckets;
+    return L.n_pairs <= kSelfBucketMaxPairs && L.num_experts + 1 <= kSelfBucketMaxBuckets;
 }
 
 hipError_t launch_q4k_gemv(const GemvLaunch &L, hipStream_t st) {
     const GemvArgs a = make_args(L);
-    if (L.self_bucket) {   // chunks built in-kernel: the matrix-core kernel only
-        if (!q4k_self_bucket_ok(L))
-            return hipErrorInvalidValue;
+    if (L.self_bucket)   // chunks built in-kernel: the matrix-core kernel only
         return launch_q4k_gemv_mfma(a, L.fused_swiglu, st);
-    }
     const bool bucketed = L.bucket_ws != nullptr;
-    // Bucketed mode runs on the matrix cores unless Q4KMOE_MFMA=0 selects the
-    // vector-unit kernels; the matrix-core kernel reads activations as float4,
-    // so rows and strides must be 16-byte aligned.
-    const bool mfma = mfma_enabled();
-    if (bucketed && mfma && a.vec)
+    if (bucketed && !L.vector_units)
         return launch_q4k_gemv_mfma(a, L.fused_swiglu, st);
     if (L.fused_swiglu)
         return launch_any<2, EPI_SWIGLU>(a, bucketed, st);
     return launch_any<1, EPI_STORE>(a, bucketed, st);
 }
 
+// LDS of k_down_combine: np staged rows, the slot results of at most 64 rows
+// and a few words; the CDNA4 limit is 160 KB per workgroup.
+static size_t dc_lds_bytes(int64_t k, int np, int trt) {
+    return ((size_t)np * row_lds_floats((int)k) + (size_t)trt * np + 8) * sizeof(float);
+}
+
+bool q4k_down_combine_ok(int64_t k, int64_t top_k, bool shared) {
+    return dc_lds_bytes(k, (int)top_k + (shared ? 1 : 0), 64) <= 160 * 1024;
+}
+
 template <int LPR, int IT>
 static hipError_t go_dc(const GemvArgs &a, const CombineArgs &cb, int trt, hipStream_t st) {
     auto kern = k_down_combine<LPR, IT>;
     const int np = a.top_k + (a.m_sh > 0 ? 1 : 0);
-    const size_t lds = set_lds((const void *)kern,
-                               ((size_t)np * row_lds_floats(a.k) + trt * np + 8) * sizeof(float));
-    if (trt > kThreads)
-        return hipErrorInvalidValue;
+    const size_t lds = set_lds((const void *)kern, dc_lds_bytes(a.k, np, trt));
     dim3 grid((a.n + trt - 1) / trt, (int)(a.n_pairs / a.top_k));
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a, cb, trt);
     return hipGetLastError();
@@ -788,8 +535,8 @@ static hipError_t dc_lpr(const GemvArgs &a, const CombineArgs &cb, hipStream_t s
     const int m = a.n_pairs / a.top_k;
     // rows per workgroup: the tallest tile that still gives every CU a
     // workgroup, with at most 8 row groups per lane (every workgroup stages
-    // all of the token's activation rows, so taller tiles stage less in all)
-    static const int forced = env_int("Q4KMOE_DC_ROWS", 0);
+    // all of the token's activation rows, so taller tiles stage less in all);
+    // at most 64 rows, so the combine's thread per row fits the workgroup
     const int64_t cus = cu_count();
     int trt = 1;
     for (int cand = 64; cand >= 1; cand >>= 1) {
@@ -799,8 +546,6 @@ static hipError_t dc_lpr(const GemvArgs &a, const CombineArgs &cb, hipStream_t s
             break;
         }
     }
-    if (forced > 0 && forced <= 64 && (forced * np + RPI - 1) / RPI <= 8)
-        trt = forced;
     const int its = (trt * np + RPI - 1) / RPI;
     switch (its) {
     case 1: return go_dc<LPR, 1>(a, cb, trt, st);
@@ -817,8 +562,6 @@ hipError_t launch_q4k_down_combine(const GemvLaunch &L, const float *h_mid, cons
                                    const float *shared_logit, float *out, float *expert_out,
                                    int shared_mode, hipStream_t st) {
     const GemvArgs a = make_args(L);
-    if (!a.vec)   // the kernel stages activations as float4
-        return hipErrorInvalidValue;
     CombineArgs cb{h_mid, route_w, shared_logit, out, expert_out, shared_mode};
     switch (lanes_per_row(a.k)) {
     case 4: return dc_lpr<4>(a, cb, st);
@@ -827,8 +570,7 @@ hipError_t launch_q4k_down_combine(const GemvLaunch &L, const float *h_mid, cons
     case 32: return dc_lpr<32>(a, cb, st);
     case 64: return dc_lpr<64>(a, cb, st);
     case 128: return dc_lpr<128>(a, cb, st);
-    case 256: return dc_lpr<256>(a, cb, st);
-    default: return hipErrorInvalidValue;
+    default: return dc_lpr<256>(a, cb, st);
     }
 }
 

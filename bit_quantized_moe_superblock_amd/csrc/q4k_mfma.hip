@@ -26,11 +26,16 @@
 //     so each lane loads contiguous bytes (16 of each 64-byte half of the
 //     nibbles; a row's 4 lanes read 64 contiguous bytes per load) and the
 //     activations are staged in the matching k order.
-//   - A is the activation split into two fp16 parts, x = hi + lo,
-//     hi = fp16(x), lo = fp16(x - hi), staged once per workgroup in LDS in
-//     the same k order: A rows 0..7 are the 8 pairs' hi parts, rows 8..15
-//     their lo parts, so one MFMA per sub-block covers both and the halves
-//     are added once at the end.
+//   - A is the activation split into two fp16 parts, staged once per
+//     workgroup in LDS in the same k order: A rows 0..7 are the 8 pairs' hi
+//     parts, rows 8..15 their lo parts, so one MFMA per sub-block covers both
+//     and the halves are added once at the end.  Before the split, each
+//     pair's 256 activations of a superblock are scaled by an exact power of
+//     two 2^e chosen from their largest magnitude (to [2^9, 2^10)), so
+//     x 2^e = hi + lo with hi = fp16(x 2^e), lo = fp16(x 2^e - hi) keeps about
+//     22 significant bits and the 32-element sums stay below 2^15, whatever
+//     the scale of the inputs; the superblock's D is multiplied by 2^-e
+//     (exact) before it is added in.
 //   - Each lane's D column is one weight row: the lane decodes that row's
 //     header itself (d, dmin, six-bit scales and mins), and the superblock's
 //     eight MFMAs accumulate into one D with y += d 2^24 D; the min term
@@ -39,8 +44,9 @@
 //     and the mins.
 //
 // Rounding differs from the vector-unit kernels (the matrix core's own sum
-// order, x carried as hi + lo), so this mode matches them within the fp32
-// tolerance, not bit for bit.
+// order, x carried as hi + lo), so this schedule matches them within the fp32
+// tolerance, not bit for bit; repeated calls of this schedule give identical
+// bits.
 #include "gemv_core.hpp"
 
 namespace q4k {
@@ -56,16 +62,17 @@ constexpr int kMRows = 64;          // weight rows per row group (4 waves x 16)
 constexpr int kEpiRowPair = 2;
 static_assert(kEpiRowPair != EPI_STORE && kEpiRowPair != EPI_SWIGLU, "epilogue ids");
 __host__ __device__ constexpr int item_rows(int epi) { return epi == kEpiRowPair ? 2 * kMRows : kMRows; }
-#ifndef Q4K_MFMA_DEPTH
-#define Q4K_MFMA_DEPTH 2
-#endif
-constexpr int kDepth = Q4K_MFMA_DEPTH;   // superblocks of weights in flight per wave
+constexpr int kDepth = 2;   // superblocks of weights in flight per wave
 constexpr int kSubB = 2 * 4 * kMP * 16;   // LDS bytes per staged sub-block: parts x groups x pairs x 16 B
 static_assert(kMP == 8, "A-row mapping assumes 8 pairs per workgroup");
 
 // LDS bytes of one slab of SB superblocks: the split activations, then per
-// superblock the split sub-block sums (16 rows x 8 sub-blocks of fp16).
+// superblock the split sub-block sums (16 rows x 8 sub-blocks of fp16), then
+// per superblock the 8 pairs' undo factors 2^-e (fp32).
 __host__ __device__ constexpr size_t mfma_lds_bytes(int sb) {
+    return (size_t)sb * 8 * kSubB + (size_t)sb * 256 + (size_t)sb * 32;
+}
+__host__ __device__ constexpr size_t mfma_lds_scale_off(int sb) {
     return (size_t)sb * 8 * kSubB + (size_t)sb * 256;
 }
 
@@ -86,9 +93,11 @@ struct XRegs {
     float4 v[U][8];
 };
 
+// vec: the rows and strides are 16-byte aligned (float4 loads); otherwise
+// four 4-byte loads per float4 (uniform choice).
 template <int SB>
 __device__ __forceinline__ void mfma_x_issue(const float *const (&xrow)[XRegs<SB>::U], int cnt,
-                                             int j0, int nsub_total, XRegs<SB> &xr) {
+                                             int j0, int nsub_total, bool vec, XRegs<SB> &xr) {
     constexpr int nsub = SB * 8;
 #pragma unroll
     for (int u = 0; u < XRegs<SB>::U; u++) {
@@ -96,28 +105,40 @@ __device__ __forceinline__ void mfma_x_issue(const float *const (&xrow)[XRegs<SB
         const int jl = task % nsub;
         const bool ok = task < cnt * nsub && j0 + jl < nsub_total;
         const float *src = xrow[u] + 32 * (ok ? j0 + jl : 0);   // clamped
+        if (vec) {
 #pragma unroll
-        for (int q = 0; q < 8; q++)
-            xr.v[u][q] = *(const float4 *)(src + 4 * q);
+            for (int q = 0; q < 8; q++)
+                xr.v[u][q] = *(const float4 *)(src + 4 * q);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; q++)
+                xr.v[u][q] = make_float4(src[4 * q], src[4 * q + 1], src[4 * q + 2],
+                                         src[4 * q + 3]);
+        }
     }
 }
 
-// Task (pair p, sub-block jl) sums its 32 activations in ascending order from
-// 0, splits each activation and the sum into fp16 hi + lo, and writes the
+// Task (pair p, sub-block jl) scales its 32 activations by the pair's
+// power of two for the superblock, sums them in ascending order from 0,
+// splits each scaled activation and the sum into fp16 hi + lo, and writes the
 // four k groups of both parts and the two sums.  Sub-blocks past the end of
-// the row are zeros.
+// the row are zeros.  The 8 tasks of one (pair, superblock) are 8
+// consecutive lanes of a wave (task = 8 (p SB + s) + j), which find their
+// largest magnitude with three DPP steps; the first of them stores the undo
+// factor 2^-e.  Every lane takes part in those steps (tasks past the chunk
+// contribute zeros and write nothing).
 template <int SB>
 __device__ __forceinline__ void mfma_x_commit(const XRegs<SB> &xr, int cnt, int j0,
                                               int nsub_total, uint8_t *lds) {
     constexpr int nsub = SB * 8;
     uint8_t *sxa = lds + (size_t)SB * 8 * kSubB;
+    float *sfac = (float *)(lds + mfma_lds_scale_off(SB));
 #pragma unroll
     for (int u = 0; u < XRegs<SB>::U; u++) {
         const int task = threadIdx.x + u * kThreads;
-        if (task >= cnt * nsub)
-            continue;
+        const bool ok = task < cnt * nsub;
         const int p = task / nsub, jl = task - p * nsub;
-        const bool live = j0 + jl < nsub_total;
+        const bool live = ok && j0 + jl < nsub_total;
         float v[32];
 #pragma unroll
         for (int q = 0; q < 8; q++) {
@@ -126,10 +147,28 @@ __device__ __forceinline__ void mfma_x_commit(const XRegs<SB> &xr, int cnt, int 
             v[4 * q + 2] = live ? xr.v[u][q].z : 0.0f;
             v[4 * q + 3] = live ? xr.v[u][q].w : 0.0f;
         }
+        float mx = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 32; q++)
+            mx = fmaxf(mx, fabsf(v[q]));
+        mx = fmaxf(mx, dpp_move<0xB1>(mx));    // quad_perm [1,0,3,2]
+        mx = fmaxf(mx, dpp_move<0x4E>(mx));    // quad_perm [2,3,0,1]
+        mx = fmaxf(mx, dpp_move<0x141>(mx));   // row_half_mirror: the other quad
+        // mx in [2^(E-1), 2^E) -> scaled into [2^9, 2^10); the undo factor
+        // 2^-e stays a normal fp32 number
+        int e = mx > 0.0f ? 10 - __builtin_amdgcn_frexp_expf(mx) : 0;
+        e = e < -126 ? -126 : (e > 126 ? 126 : e);
+        if (!ok)
+            continue;
+#pragma unroll
+        for (int q = 0; q < 32; q++)
+            v[q] = __builtin_ldexpf(v[q], e);
         float s = 0.0f;
 #pragma unroll
         for (int q = 0; q < 32; q++)
             s += v[q];
+        if ((jl & 7) == 0)
+            sfac[(jl >> 3) * kMP + p] = __builtin_ldexpf(1.0f, -e);
         const _Float16 sh = (_Float16)s;
         _Float16 *sx = (_Float16 *)(sxa + (size_t)(jl >> 3) * 256) + (jl & 7);
         sx[p * 8] = sh;
@@ -182,11 +221,18 @@ __device__ __forceinline__ void mfma_load(const uint8_t *row, int sb, int g, Mfm
 // where D_min is one more MFMA: its A holds the split sub-block sums in
 // k = 0..7 (lanes 0..15; zero elsewhere) and its B the six-bit mins as fp16
 // subnormals m_j 2^-24.
+//
+// Both D's are in the superblock's scaled domain: each is multiplied by its
+// pair's 2^-e (sfac, exact) before it is added in.
 template <int NT>
 __device__ __forceinline__ void mfma_superblock(const MfmaTile (&t)[NT], const uint8_t *lds,
-                                                const uint8_t *sxa, int s, float (&y)[NT][4]) {
+                                                const uint8_t *sxa, const float *sfac, int s,
+                                                float (&y)[NT][4]) {
     typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
     const int lane = threadIdx.x & 63;
+    // undo factors of this lane's D rows 4 (lane / 16) + j: pairs 4 ((lane / 16) % 2) + j
+    const float4 f = *(const float4 *)(sfac + s * kMP + 4 * ((lane >> 4) & 1));
+    const float fj[4] = {f.x, f.y, f.z, f.w};
     const int aoff = (((lane >> 3) & 1) * 4 + (lane >> 4)) * (kMP * 16) + (lane & 7) * 16;
     const h8v a_sx = *(const h8v *)(sxa + (size_t)s * 256 + (lane & 15) * 16);
     const h8v zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -222,7 +268,7 @@ __device__ __forceinline__ void mfma_superblock(const MfmaTile (&t)[NT], const u
         const float dm24 = -hi_half(t[nt].hdr.x) * 16777216.0f;
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            y[nt][i] = __builtin_fmaf(dm24, acc[nt][i], y[nt][i]);
+            y[nt][i] = __builtin_fmaf(dm24, acc[nt][i] * fj[i], y[nt][i]);
         acc[nt] = zero4;
     }
     auto scaled = [](uint32_t v, uint32_t sc) {
@@ -262,7 +308,7 @@ __device__ __forceinline__ void mfma_superblock(const MfmaTile (&t)[NT], const u
         const float d24 = lo_half(t[nt].hdr.x) * 16777216.0f;
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            y[nt][i] = __builtin_fmaf(d24, acc[nt][i], y[nt][i]);
+            y[nt][i] = __builtin_fmaf(d24, acc[nt][i] * fj[i], y[nt][i]);
     }
 }
 
@@ -304,6 +350,7 @@ __device__ __forceinline__ void mfma_item(const GemvArgs &a, bool shared, int bk
         wrow[NT - 1] = (shared ? a.s1 : a.w1 + (int64_t)bkt * mat) + (int64_t)r * rowb;
     }
     const uint8_t *sxa = lds_b + (size_t)SB * 8 * kSubB;
+    const float *sfac = (const float *)(lds_b + mfma_lds_scale_off(SB));
     const int nsub_total = a.k >> 5;
     const int gc = cnt;
     auto x_of = [&](int i) { return pair_x_known(a, shared, pair_q(i)); };
@@ -334,7 +381,7 @@ __device__ __forceinline__ void mfma_item(const GemvArgs &a, bool shared, int bk
                 mfma_load(wrow[nt], sb, g, tt[i % kDepth][nt]);
         };
         XRegs<SB> xr;
-        mfma_x_issue<SB>(xrow, gc, sb0 * 8, nsub_total, xr);
+        mfma_x_issue<SB>(xrow, gc, sb0 * 8, nsub_total, a.vec != 0, xr);
         // the activations ahead of the weights: staging waits on them alone
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -345,7 +392,7 @@ __device__ __forceinline__ void mfma_item(const GemvArgs &a, bool shared, int bk
 #pragma unroll
         for (int i = 0; i < SB; i++) {
             if (sb0 + i < nb)   // uniform
-                mfma_superblock<NT>(tt[i % kDepth], lds_b, sxa, i, yv);
+                mfma_superblock<NT>(tt[i % kDepth], lds_b, sxa, sfac, i, yv);
             if (i + kDepth < SB)
                 issue(i + kDepth);
         }
@@ -556,32 +603,25 @@ static hipError_t go_mfma(const GemvArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Superblocks per staged activation slab: 4 by default (three workgroups per
-// CU fit beside a 33 KB slab; with two superblocks of weights in flight this
-// beat whole-row slabs of 8 at two per CU), Q4KMOE_MFMA_SLAB (1..8) overrides.
+// Superblocks per staged activation slab: 4 (three workgroups per CU fit
+// beside a 33 KB slab; with two superblocks of weights in flight this beat
+// whole-row slabs of 8 at two per CU), fewer when the row is shorter.
 template <int NT, int EPI>
 static hipError_t mfma_sb(const GemvArgs &a, hipStream_t st) {
-    static const int slab = env_int("Q4KMOE_MFMA_SLAB", 4);
-    const int sb_max = slab < 1 ? 1 : slab > 8 ? 8 : slab;
-    switch (a.k >> 8 < sb_max ? a.k >> 8 : sb_max) {
+    switch (a.k >> 8) {
     case 1: return go_mfma<NT, EPI, 1>(a, st);
     case 2: return go_mfma<NT, EPI, 2>(a, st);
     case 3: return go_mfma<NT, EPI, 3>(a, st);
-    case 4: return go_mfma<NT, EPI, 4>(a, st);
-    case 5: return go_mfma<NT, EPI, 5>(a, st);
-    case 6: return go_mfma<NT, EPI, 6>(a, st);
-    case 7: return go_mfma<NT, EPI, 7>(a, st);
-    default: return go_mfma<NT, EPI, 8>(a, st);
+    default: return go_mfma<NT, EPI, 4>(a, st);
     }
 }
 
+// Gate/up: the gate and up tiles of 64 rows; a single matrix: two 64-row
+// groups of it (row pair).
 hipError_t launch_q4k_gemv_mfma(const GemvArgs &a, bool fused_swiglu, hipStream_t st) {
     if (fused_swiglu)
         return mfma_sb<2, EPI_SWIGLU>(a, st);
-    static const bool row_pair = env_int("Q4KMOE_MFMA_ROW_PAIR", 1) != 0;
-    if (row_pair)
-        return mfma_sb<2, kEpiRowPair>(a, st);
-    return mfma_sb<1, EPI_STORE>(a, st);
+    return mfma_sb<2, kEpiRowPair>(a, st);
 }
 
 }  // namespace q4k

@@ -205,8 +205,7 @@ static int tp_iters(int tpb, int lpr, int max_it, int64_t row_bytes, int cols, i
 // from the cache, which at 256 threads was about 0.7x the weight bytes of a
 // decode walk.  512 threads in general; 1024 when rows are at most 4096
 // columns and the grid then holds at most one workgroup per CU (a small
-// tensor, where more waves per CU hide more latency).  Q4TP_THREADS (256,
-// 512 or 1024) and Q4TP_ITERS (row groups: 1, 2, 4 or 8) override.
+// tensor, where more waves per CU hide more latency).
 template <int LPR, int NG>
 static hipError_t tp_launch(const void *const *ts, const int64_t *rows, int nseg, const float *x,
                             float *y, int cols, hipStream_t st) {
@@ -217,21 +216,15 @@ static hipError_t tp_launch(const void *const *ts, const int64_t *rows, int nseg
     for (int i = 0; i < nseg; i++)
         total_rows += rows[i];
     constexpr int kMaxIt = NG == 1 ? 8 : 4;
-    static const int tpb_env = env_int("Q4TP_THREADS", 0);
     int tpb = 512;
-    if (tpb_env == 256 || tpb_env == 512 || tpb_env == 1024) {
-        tpb = tpb_env;
-    } else if (NG == 1 && gpr <= 128) {
+    if (NG == 1 && gpr <= 128) {
         const int it1k = tp_iters(1024, LPR, kMaxIt, row_bytes, cols, total_rows, cus);
         const int64_t rows1k = (int64_t)it1k * (1024 / LPR);
         if ((total_rows + rows1k - 1) / rows1k <= cus)
             tpb = 1024;
     }
     const int RPI = tpb / LPR;
-    static const int it_env = env_int("Q4TP_ITERS", 0);
-    int it = tp_iters(tpb, LPR, kMaxIt, row_bytes, cols, total_rows, cus);
-    if (it_env == 1 || it_env == 2 || it_env == 4 || it_env == 8)
-        it = it_env < kMaxIt ? it_env : kMaxIt;
+    const int it = tp_iters(tpb, LPR, kMaxIt, row_bytes, cols, total_rows, cus);
     const size_t lds = (size_t)(16 + 36 * gpr + gpr) * sizeof(float);
     auto go = [&](auto kern, int iters) {
         TpSegs sg{};

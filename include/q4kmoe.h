@@ -40,14 +40,48 @@ enum {
     Q4K_ERR_ARG = 6        /* an enum argument has an unknown value             */
 };
 
-/* Bucketing flag of the id-GEMV entry points ([MF]
+/* Bucketing flag of the id-GEMV, FFN and layer entry points ([MF]
  * encode_moe_batched_permute_fuse: group (token, slot) pairs by expert so each
- * expert's weights are read once).  AUTO buckets when more than one token is
- * in the batch.  PREBUILT runs the bucketed kernels on a workspace that
- * moe_bucket (or an earlier call) already filled for the same ids, so gate/up
- * and down pay for one bucketing pass.  The output is identical bit for bit
- * in every mode. */
+ * expert's weights are read once).  A flag is one mode, optionally OR-ed with
+ * schedule bits.
+ *
+ * Modes:
+ *   OFF      pair mode (token mode in the layer): every pair reads its
+ *            expert's rows itself, on the vector units.
+ *   ON       bucketed: one work item per chunk of at most Q4K_BUCKET_CHUNK
+ *            pairs of one expert, which reads the expert's rows once for all
+ *            of them.
+ *   AUTO     ON when m >= Q4K_AUTO_BUCKET_MIN_TOKENS, else OFF.  At fewer
+ *            tokens most experts serve a single pair, so there is no dense
+ *            contraction to gain from.
+ *   PREBUILT ON, on a workspace that moe_bucket (or an earlier call) already
+ *            filled for the same ids, so gate/up and down pay for one
+ *            bucketing pass (the layer entry points treat it as ON).
+ * Schedule bits:
+ *   Q4K_SCHED_VECTOR        bucketed work runs on the vector units (the same
+ *                           per-weight arithmetic and order as pair mode)
+ *                           instead of the matrix cores.
+ *   Q4K_SCHED_BUCKET_LAUNCH layer entry points: bucket with a separate
+ *                           launch into the workspace rather than inside the
+ *                           matrix-core launches (both give the same chunk
+ *                           lists, so the same bits).  Ignored elsewhere.
+ * An unknown mode or bit returns Q4K_ERR_ARG.
+ *
+ * Numerics: the output depends only on the arguments, never on the process
+ * environment.  Pair mode, token mode and vector-unit bucketing share one
+ * per-weight arithmetic and summation order, so they agree bit for bit, and
+ * a batch equals the same pairs run one token at a time bit for bit.  The
+ * matrix-core schedule (ON and PREBUILT without Q4K_SCHED_VECTOR) sums in the
+ * matrix core's order with each activation carried as two fp16 parts after
+ * an exact power-of-two scaling per (pair, superblock); it agrees with the
+ * vector-unit schedules within the fp32 band
+ * (max_abs_diff <= 1e-3 * max|out|, cosine >= 0.9999) at any finite
+ * activation scale, and repeated calls of it give identical bits. */
 enum { Q4K_BUCKET_AUTO = 0, Q4K_BUCKET_OFF = 1, Q4K_BUCKET_ON = 2, Q4K_BUCKET_PREBUILT = 3 };
+#define Q4K_BUCKET_MODE_MASK 0xFF
+#define Q4K_SCHED_VECTOR 0x100
+#define Q4K_SCHED_BUCKET_LAUNCH 0x200
+#define Q4K_AUTO_BUCKET_MIN_TOKENS 5
 
 /* Shared-expert term of the combine ([MF] combine_kernel_name and the
  * variant comment: sigmoid-gated for Qwen3 MoE, added unscaled for
@@ -63,13 +97,13 @@ enum { MOE_SHARED_NONE = 0, MOE_SHARED_SIGMOID = 1, MOE_SHARED_UNSCALED = 2 };
 #define Q4TP_MAX_COLS 16384   /* largest Q4TiledP row                       */
 #define Q4TP_MAX_TENSORS 3    /* [CE] merged kernel: tensors per dispatch  */
 #define Q4K_BUCKET_CHUNK 8    /* pairs per bucketed work item               */
-#define MOE_LAYER_SYNC_BYTES 4096 /* synchronisation header of a layer workspace */
-#define MOE_LAYER_SYNC_TIMEOUT_WORD 576 /* 32-bit word of that header: barrier timed out */
 
 const char *q4k_status_string(int status);
-/* 3: adds the MLX 4-bit and 2-bit entry points (mlx4_*, mlx2_*) and the chained RMSNorm
- * (moe_layer_forward_rmsnorm, moe_combine_residual_rmsnorm) to version 2's
- * set. */
+/* 4: bucket_flag takes schedule bits (Q4K_SCHED_*); AUTO buckets from
+ * Q4K_AUTO_BUCKET_MIN_TOKENS tokens; the layer workspace has no
+ * synchronisation header (moe_layer_workspace_init is gone); activation rows
+ * of every entry point need only 4-byte alignment.  3 added the MLX 4-bit and
+ * 2-bit entry points and the chained RMSNorm. */
 int q4k_abi_version(void);
 
 /* Bytes of an n x k Q4_K matrix: n*(k/256)*144 ([FK]
@@ -117,21 +151,25 @@ int moe_bucket(const int32_t *ids, int64_t n_pairs, int64_t num_experts, void *w
 
 /* Batched indirect-dispatch Q4_K GEMV ([FK]
  * dispatch_gemv_q4k_moe_id_batched_on_encoder and module doc).
- *   w_stacked : [num_experts, n, k/256] superblocks; expert e starts at byte
- *               e*n*(k/256)*144.  The caller pre-offsets the pointer if the
- *               stack starts inside a larger buffer ([FK] weights_byte_offset).
- *   src1      : activations; pair p = token*top_k + slot reads the k floats at
+ *   w_stacked : [num_experts, n, k/256] superblocks, 16-byte aligned; expert
+ *               e starts at byte e*n*(k/256)*144.  The caller pre-offsets the
+ *               pointer if the stack starts inside a larger buffer ([FK]
+ *               weights_byte_offset).
+ *   src1      : activations, 4-byte aligned (any float offset and stride;
+ *               16-byte aligned rows load faster); pair p = token*top_k + slot
+ *               reads the k floats at
  *               src1 + token*src1_outer_stride + slot*src1_inner_stride.
  *               gate/up: outer = k, inner = 0; down: outer = top_k*k, inner = k.
  *   ids       : [m*top_k] int32 expert ids.  An id outside [0, num_experts)
  *               gives a zero output row (the pages leave it undefined).
  *   dst       : [m*top_k, n] fp32.
  *   Requires k % 256 == 0, 256 <= k <= Q4K_MAX_IN, n >= 1, m >= 1,
- *   1 <= top_k <= Q4K_MAX_TOP_K, 1 <= num_experts <= Q4K_MAX_EXPERTS, strides
- *   >= 0.  ([FK] asserts k%256 and n%4; n%4 is not needed here.)
- *   bucket_flag: Q4K_BUCKET_*; the bucketed mode needs
- *   ws_bytes >= moe_bucket_workspace_bytes(m*top_k, num_experts), otherwise ws
- *   may be NULL.  Output is independent of bucketing and of m bit for bit. */
+ *   1 <= top_k <= Q4K_MAX_TOP_K, 1 <= num_experts <= Q4K_MAX_EXPERTS,
+ *   m*top_k <= 65535 (Q4K_MAX_PAIRS when bucketed), strides >= 0.  ([FK]
+ *   asserts k%256 and n%4; n%4 is not needed here.)
+ *   bucket_flag: mode and schedule bits (see Q4K_BUCKET_*); a bucketed call
+ *   needs ws_bytes >= moe_bucket_workspace_bytes(m*top_k, num_experts),
+ *   otherwise ws may be NULL.  Bits: see the numerics note at Q4K_BUCKET_*. */
 int q4k_moe_id_gemv(const void *w_stacked, const float *src1, const int32_t *ids, float *dst,
                     int64_t n, int64_t k, int64_t m, int64_t top_k,
                     int64_t src1_outer_stride, int64_t src1_inner_stride,
@@ -178,42 +216,34 @@ int moe_expert_ffn(const void *w_gate, const void *w_up, const void *w_down,
  * and the weighted residual combine ([MF] gpu_batched_experts_forward and
  * emit_batched_experts: gate/up, SwiGLU, down for every selected expert and
  * the shared one, then moe_combine_residual), in the fewest launches:
- *   one token  : the whole layer in one launch (gate/up+SiLU, a device-wide
- *                barrier, down fused with the combine), for the shapes this
- *                kernel tiles (hidden 1024..4096 and inter up to 2048 at
- *                top_k <= 16 on a 256-CU device); otherwise as few tokens;
- *   few tokens : fused gate/up+SiLU over routed and shared pairs, then the
- *                down projection fused with the combine (2 launches);
- *   more tokens: bucketing, bucketed gate/up+SiLU and down (the shared expert
- *                as one more bucket holding every token), then the combine.
+ *   token mode (OFF, or AUTO below Q4K_AUTO_BUCKET_MIN_TOKENS tokens): fused
+ *                gate/up+SiLU over routed and shared pairs, then the down
+ *                projection fused with the combine (2 launches; when the
+ *                token's top_k+1 activation rows of `inter` floats do not fit
+ *                one workgroup's LDS, down and the combine are 2 launches);
+ *   bucketed (ON, PREBUILT, or AUTO from Q4K_AUTO_BUCKET_MIN_TOKENS tokens):
+ *                bucketed gate/up+SiLU and down (the shared expert as one more
+ *                bucket holding every token), then the combine.  On the
+ *                matrix cores with m*top_k <= 1024 and num_experts <= 1023
+ *                the expert buckets are built inside the gate/up and down
+ *                launches (each workgroup from the ids, in LDS); otherwise,
+ *                or with Q4K_SCHED_BUCKET_LAUNCH, one bucketing launch writes
+ *                them to the workspace.  The chunks, and so the bits, are
+ *                the same either way.
  *   w_gate, w_up, w_down : routed stacks as in moe_expert_ffn
  *   sh_gate, sh_up, sh_down : one-expert stacks of the same row shapes, or
  *                all NULL with shared_mode == MOE_SHARED_NONE
  *   h_post [m,hidden], h_mid [m,hidden], ids [m*top_k], route_w [m*top_k],
- *   shared_gate_logit [m] (MOE_SHARED_SIGMOID only), out [m,hidden] fp32.
- *   ws: at least moe_layer_workspace_bytes(...) bytes, 16-byte aligned.  Its
- *   first MOE_LAYER_SYNC_BYTES hold the one-launch path's barrier words: they
- *   must be zero before the first call with this workspace (allocate it
- *   zeroed, or call moe_layer_workspace_init once, outside graph capture).
- *   Calls advance per-workgroup generation words there.
- *   32-bit word MOE_LAYER_SYNC_TIMEOUT_WORD is set to 1 if a barrier wait
- *   ever timed out (the grid was not resident at once, e.g. the device was
- *   shared with a kernel that held its CUs); the output of that call is then
- *   not valid.  The rest is scratch.  Calls that may overlap in time must not
- *   share a workspace.
- *   bucket_flag: AUTO picks by m (bucketed when m > 2); OFF forces the
- *   few-token path; ON (or PREBUILT, treated as ON) forces bucketing.  AUTO
- *   gives the same bits as the flag that selects the same path; the other
- *   path differs only by rounding (fp32 tolerance).  A bucketed layer with
- *   m*top_k <= 1024 pairs builds its expert buckets inside the gate/up and
- *   down launches (each workgroup from the ids, in LDS) rather than in a
- *   separate bucketing launch; the chunks, and so the output bits, are the
- *   same either way. */
+ *   shared_gate_logit [m] (MOE_SHARED_SIGMOID only), out [m,hidden] fp32,
+ *   all 4-byte aligned; weight stacks 16-byte aligned.
+ *   ws: scratch of at least moe_layer_workspace_bytes(...) bytes, 16-byte
+ *   aligned, no initial contents required; calls that may overlap in time must
+ *   not share a workspace.  m*top_k <= Q4K_MAX_PAIRS.
+ *   bucket_flag: as for q4k_moe_id_gemv.  The bits of `out` depend only on
+ *   the arguments; token mode and vector-unit bucketing agree bit for bit, the
+ *   matrix-core schedule within the band. */
 int64_t moe_layer_workspace_bytes(int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
                                   int64_t top_k);
-/* Zeroes the synchronisation header of a layer workspace (an asynchronous
- * memset on `stream`).  ws_bytes < MOE_LAYER_SYNC_BYTES -> Q4K_ERR_WORKSPACE. */
-int moe_layer_workspace_init(void *ws, int64_t ws_bytes, void *stream);
 int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
                       const void *sh_gate, const void *sh_up, const void *sh_down,
                       const float *h_post, const float *h_mid, const int32_t *ids,

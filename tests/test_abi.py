@@ -42,11 +42,14 @@ def test_constants_match_header(lib):
     for name, val in [("Q4K_BLOCK_WEIGHTS", 256), ("Q4K_BLOCK_BYTES", 144), ("Q4K_MAX_TOP_K", 16),
                       ("Q4K_MAX_IN", _lib.Q4K_MAX_IN), ("Q4K_MAX_EXPERTS", _lib.Q4K_MAX_EXPERTS),
                       ("Q4K_MAX_PAIRS", _lib.Q4K_MAX_PAIRS), ("Q4TP_MAX_COLS", _lib.Q4TP_MAX_COLS),
-                      ("Q4K_BUCKET_CHUNK", 8), ("MOE_LAYER_SYNC_BYTES", 4096),
-                      ("MOE_LAYER_SYNC_TIMEOUT_WORD", 576),
+                      ("Q4K_BUCKET_CHUNK", 8), ("Q4K_BUCKET_MODE_MASK", "0xFF"),
+                      ("Q4K_SCHED_VECTOR", "0x100"), ("Q4K_SCHED_BUCKET_LAUNCH", "0x200"),
+                      ("Q4K_AUTO_BUCKET_MIN_TOKENS", _lib.Q4K_AUTO_BUCKET_MIN_TOKENS),
                       ("Q4TP_MAX_TENSORS", _lib.Q4TP_MAX_TENSORS), ("MLX4_GROUP", 64)]:
         assert re.search(rf"#define {name} {val}\b", src), name
-    assert q4.q4k_abi_version() == 3
+    assert (_lib.Q4K_BUCKET_MODE_MASK, _lib.Q4K_SCHED_VECTOR, _lib.Q4K_SCHED_BUCKET_LAUNCH) == \
+        (0xFF, 0x100, 0x200)
+    assert q4.q4k_abi_version() == 4
 
 
 def test_size_helpers(lib):
@@ -64,9 +67,8 @@ def test_size_helpers(lib):
     assert q4.mlx2_matrix_bytes(768, 2048) == 768 * 512 + 768 * 32 * 4
     assert q4.mlx2_matrix_bytes(3, 96) == -1
     assert q4.moe_bucket_workspace_bytes(128, 128) == 4 * (129 + 130 + 128 + 129 + 1 + 1 + 256)
-    # sync header | act [9, 768] | expert_out [8, 2048] | shared_out [1, 2048] | buckets
-    assert q4.moe_layer_workspace_bytes(2048, 768, 128, 1, 8) == \
-        4096 + 27648 + 65536 + 8192 + 1792
+    # act [9, 768] | expert_out [8, 2048] | shared_out [1, 2048] | buckets
+    assert q4.moe_layer_workspace_bytes(2048, 768, 128, 1, 8) == 27648 + 65536 + 8192 + 1792
 
 
 def test_status_strings(lib):
@@ -107,9 +109,16 @@ def test_id_gemv_validation(lib):
     assert call(outer=-1) == _lib.Q4K_ERR_STRIDE
     assert call(inner=-5) == _lib.Q4K_ERR_STRIDE
     assert call(flag=7) == _lib.Q4K_ERR_ARG
+    assert call(flag=q4.Q4K_BUCKET_ON | 0x400) == _lib.Q4K_ERR_ARG    # unknown schedule bit
     assert call(flag=q4.Q4K_BUCKET_ON) == _lib.Q4K_ERR_WORKSPACE
+    assert call(flag=q4.Q4K_BUCKET_ON | q4.Q4K_SCHED_VECTOR) == _lib.Q4K_ERR_WORKSPACE
     assert call(flag=q4.Q4K_BUCKET_ON, ws=FAKE, wsb=8) == _lib.Q4K_ERR_WORKSPACE
-    assert call(flag=q4.Q4K_BUCKET_AUTO) == _lib.Q4K_ERR_WORKSPACE   # m > 1 buckets
+    # AUTO buckets from Q4K_AUTO_BUCKET_MIN_TOKENS tokens on, so only then
+    # does it need a workspace
+    mt = q4.Q4K_AUTO_BUCKET_MIN_TOKENS
+    assert call(m=mt, flag=q4.Q4K_BUCKET_AUTO) == _lib.Q4K_ERR_WORKSPACE
+    assert call(m=mt - 1, flag=q4.Q4K_BUCKET_AUTO, x=None) == _lib.Q4K_ERR_NULL
+    assert call(x=FAKE + 2) == _lib.Q4K_ERR_NULL      # activations need 4-byte alignment
 
 
 def test_ffn_combine_bucket_q4tp_validation(lib):
@@ -145,9 +154,14 @@ def test_ffn_combine_bucket_q4tp_validation(lib):
     assert _err(q4.q4k_quantize, FAKE, FAKE, 2, 300) == _lib.Q4K_ERR_SHAPE
     assert _err(q4.q4k_dequantize, FAKE, FAKE, -1) == _lib.Q4K_ERR_SHAPE
     assert _err(q4.q4tp_quantize, FAKE, FAKE, 2, 40) == _lib.Q4K_ERR_SHAPE
-    w = q4.moe_layer_workspace_init
-    assert _err(w, None, 1024) == _lib.Q4K_ERR_NULL
-    assert _err(w, FAKE, 4095) == _lib.Q4K_ERR_WORKSPACE
+    lf = q4.moe_layer_forward
+    st = [FAKE] * 6
+    io = [FAKE] * 6
+    need = q4.moe_layer_workspace_bytes(512, 256, 4, 2, 2)
+    assert _err(lf, *st, *io, 512, 256, 4, 2, 2, 1, 0x7, FAKE, need) == _lib.Q4K_ERR_ARG
+    assert _err(lf, *st, *io, 512, 256, 4, 2, 2, 1, 0x802, FAKE, need) == _lib.Q4K_ERR_ARG
+    assert _err(lf, *st, *io, 512, 256, 4, 2, 2, 1, 0, FAKE, need - 4) == _lib.Q4K_ERR_WORKSPACE
+    assert _err(lf, *st, *io, 512, 256, 4, 2, 2, 1, 0, None, need) == _lib.Q4K_ERR_WORKSPACE
 
 
 def test_binding_refuses_host_tensors(lib):

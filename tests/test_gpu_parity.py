@@ -140,11 +140,15 @@ def test_id_gemv_tiny_config(dev):
             cfg.top_k, cfg.k, 0)
     outs = {f: _id_gemv(dev, *args, f) for f in (q4.Q4K_BUCKET_OFF, q4.Q4K_BUCKET_ON,
                                                   q4.Q4K_BUCKET_AUTO)}
+    outs["vector"] = _id_gemv(dev, *args, q4.Q4K_BUCKET_ON | q4.Q4K_SCHED_VECTOR)
     for f, o in outs.items():
         rel, cos = band(o, want, f"cfg1 flag {f}")
         say(f"  cfg1 flag {f}: rel err {rel:.3g} cos {cos:.9f}")
-    # AUTO buckets at m = 3: the same launch as ON (matrix cores), bit for bit
-    assert np.array_equal(bits(outs[q4.Q4K_BUCKET_AUTO]), bits(outs[q4.Q4K_BUCKET_ON]))
+    # AUTO at m = 3 is pair mode (below Q4K_AUTO_BUCKET_MIN_TOKENS), and
+    # bucketing on the vector units gives the same bits
+    assert cfg.m < q4.Q4K_AUTO_BUCKET_MIN_TOKENS
+    assert np.array_equal(bits(outs[q4.Q4K_BUCKET_AUTO]), bits(outs[q4.Q4K_BUCKET_OFF]))
+    assert np.array_equal(bits(outs["vector"]), bits(outs[q4.Q4K_BUCKET_OFF]))
 
 
 def _golden_case():
@@ -536,7 +540,7 @@ def test_q4tp_merged_dispatch_and_unaligned_x(dev):
 def _layer_gpu(dev, cfg, d_st, sd, a, ids, flag, shared=True):
     H, I, E, K, m = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.m
     wsb = q4.moe_layer_workspace_bytes(H, I, E, m, K)
-    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)   # barrier words start at zero
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     out = torch.empty(m, H, device=dev)
     mode = cfg.shared_mode if shared else q4.MOE_SHARED_NONE
     sh = sd if shared else (None, None, None)
@@ -571,8 +575,9 @@ def test_layer_forward_matches_oracle_and_unfused(dev, cfg):
     want = _layer_oracle(cfg, h_st, sh, a, ids)
     r = band(outs[q4.Q4K_BUCKET_AUTO], want, "layer")
     say(f"  layer rel {r[0]:.3g} cos {r[1]:.9f}")
-    same = q4.Q4K_BUCKET_OFF if m <= 2 else q4.Q4K_BUCKET_ON
-    other = q4.Q4K_BUCKET_ON if m <= 2 else q4.Q4K_BUCKET_OFF
+    few = m < q4.Q4K_AUTO_BUCKET_MIN_TOKENS
+    same = q4.Q4K_BUCKET_OFF if few else q4.Q4K_BUCKET_ON
+    other = q4.Q4K_BUCKET_ON if few else q4.Q4K_BUCKET_OFF
     assert np.array_equal(bits(outs[same]), bits(outs[q4.Q4K_BUCKET_AUTO]))
     band(outs[other], want, "layer, other schedule")
     # unfused composition of the same layer (the shared FFN on AUTO too: at
@@ -636,7 +641,6 @@ def test_layer_invalid_ids_and_token_mode_edges(dev):
         want = oracle.moe_combine_residual(hm, eo, rw, so, lg, H, m, K, 1)
         wsb = q4.moe_layer_workspace_bytes(H, I, E, m, K)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-        q4.moe_layer_workspace_init(ws, wsb)
         res = []
         for flag in (q4.Q4K_BUCKET_OFF, q4.Q4K_BUCKET_ON):
             out = torch.empty(m, H, device=dev)
@@ -710,20 +714,8 @@ def test_layer_forward_rmsnorm(dev, cfg):
     say(f"  normed rel {r[0]:.3g} cos {r[1]:.9f}")
 
 
-@pytest.fixture
-def no_self_bucket():
-    """Keeps the separate bucketing launch in bucketed layers for one call."""
-    def run(fn):
-        old = os.environ.get("Q4KMOE_SELF_BUCKET")
-        os.environ["Q4KMOE_SELF_BUCKET"] = "0"
-        try:
-            return fn()
-        finally:
-            if old is None:
-                del os.environ["Q4KMOE_SELF_BUCKET"]
-            else:
-                os.environ["Q4KMOE_SELF_BUCKET"] = old
-    return run
+# bucketed on the matrix cores with the separate bucketing launch
+ON_VIA_WS = q4.Q4K_BUCKET_ON | q4.Q4K_SCHED_BUCKET_LAUNCH
 
 
 def _layer_raw(dev, st, sh, h, hm, ids, rw, lg, H, I, E, m, K, mode, flag=q4.Q4K_BUCKET_ON):
@@ -734,7 +726,7 @@ def _layer_raw(dev, st, sh, h, hm, ids, rw, lg, H, I, E, m, K, mode, flag=q4.Q4K
     return sync_np(out)
 
 
-def test_self_bucketed_layer_equals_bucketing_launch(dev, no_self_bucket):
+def test_self_bucketed_layer_equals_bucketing_launch(dev):
     """Bucketed layers build their chunk lists inside the matrix-core launches;
     the result must equal, bit for bit, the same layer with the separate
     bucketing launch (same chunks, same pairs, same order), and the oracle
@@ -748,7 +740,7 @@ def test_self_bucketed_layer_equals_bucketing_launch(dev, no_self_bucket):
     a, ids, d_st, _ = _ffn_case(cfg, dev)
     sd, _ = _shared_stacks(cfg, dev)
     selfb = _layer_gpu(dev, cfg, d_st, sd, a, ids, q4.Q4K_BUCKET_ON)
-    viaws = no_self_bucket(lambda: _layer_gpu(dev, cfg, d_st, sd, a, ids, q4.Q4K_BUCKET_ON))
+    viaws = _layer_gpu(dev, cfg, d_st, sd, a, ids, ON_VIA_WS)
     assert np.array_equal(bits(selfb), bits(viaws))
     # one hot bucket of 90 pairs (12 chunks), two invalid ids, m = 24
     g = np.random.default_rng(61)
@@ -772,7 +764,7 @@ def test_self_bucketed_layer_equals_bucketing_launch(dev, no_self_bucket):
     args = ([T(x, dev) for x in st], [T(x, dev) for x in sh], T(h, dev), T(hm, dev),
             T(ids2, dev), T(rw, dev), T(lg, dev), H, I, E, m, K, 1)
     selfb = _layer_raw(dev, *args)
-    viaws = no_self_bucket(lambda: _layer_raw(dev, *args))
+    viaws = _layer_raw(dev, *args, flag=ON_VIA_WS)
     band(selfb, want, "self-bucketed, hot bucket")
     assert np.array_equal(bits(selfb), bits(viaws))
     # the limits: 1024 pairs, 1023 experts (device-encoded weights; a property
@@ -795,12 +787,12 @@ def test_self_bucketed_layer_equals_bucketing_launch(dev, no_self_bucket):
     args = (st[:3], st[3:], T(h, dev), T(hm, dev), T(ids3, dev), T(rw, dev), T(lg, dev),
             H, I, E, m, K, 1)
     selfb = _layer_raw(dev, *args)
-    viaws = no_self_bucket(lambda: _layer_raw(dev, *args))
+    viaws = _layer_raw(dev, *args, flag=ON_VIA_WS)
     assert np.isfinite(selfb).all()
     assert np.array_equal(bits(selfb), bits(viaws))
 
 
-def test_self_bucketed_layer_edges(dev, no_self_bucket):
+def test_self_bucketed_layer_edges(dev):
     """In-kernel bucketing at its edges: a single expert (one bucket of every
     pair, several chunks), no shared expert, every id invalid, and m = 3, the
     smallest bucketed batch; each equal bit for bit to the bucketing launch."""
@@ -834,134 +826,9 @@ def test_self_bucketed_layer_edges(dev, no_self_bucket):
         args = ([T(x, dev) for x in st], shd, T(h, dev), T(hm, dev), T(ids, dev), T(rw, dev),
                 T(lg, dev), H, I, E, m, K, mode)
         selfb = _layer_raw(dev, *args)
-        viaws = no_self_bucket(lambda: _layer_raw(dev, *args))
+        viaws = _layer_raw(dev, *args, flag=ON_VIA_WS)
         band(selfb, want, "self-bucketing edge")
         assert np.array_equal(bits(selfb), bits(viaws))
-
-
-@pytest.fixture
-def one_launch_layer():
-    """Selects the opt-in one-launch single-token layer for one test."""
-    old = os.environ.get("Q4KMOE_FUSED_LAYER")
-    os.environ["Q4KMOE_FUSED_LAYER"] = "1"
-    yield
-    if old is None:
-        del os.environ["Q4KMOE_FUSED_LAYER"]
-    else:
-        os.environ["Q4KMOE_FUSED_LAYER"] = old
-
-
-@pytest.mark.parametrize("cfg", [wl.CFG2], ids=lambda c: c.name)
-def test_one_launch_layer_matches_two_launch_and_oracle(dev, cfg, one_launch_layer):
-    """The opt-in one-launch layer against the oracle and bit for bit against
-    the default two-launch layer, with and without a shared expert, and with
-    an invalid id at top_k 16."""
-    say("one-launch layer vs two-launch and oracle")
-    H, I, E, K, m = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.m
-    a, ids, d_st, h_st = _ffn_case(cfg, dev)
-    sd, sh = _shared_stacks(cfg, dev)
-    for shared in (True, False):
-        one = _layer_gpu(dev, cfg, d_st, sd, a, ids, q4.Q4K_BUCKET_AUTO, shared)
-        os.environ["Q4KMOE_FUSED_LAYER"] = "0"
-        two = _layer_gpu(dev, cfg, d_st, sd, a, ids, q4.Q4K_BUCKET_AUTO, shared)
-        os.environ["Q4KMOE_FUSED_LAYER"] = "1"
-        band(one, _layer_oracle(cfg, h_st, sh, a, ids, shared), f"one launch, shared={shared}")
-        assert np.array_equal(bits(one), bits(two)), shared
-    g = np.random.default_rng(51)
-    H, I, E, K = 1280, 512, 20, 16
-    st = [np.concatenate(quantize_many([(g.standard_normal((r, c)) * 0.05).astype(np.float32)
-                                        for _ in range(E)]))
-          for r, c in [(I, H), (I, H), (H, I)]]
-    shs = [oracle.q4k_quantize((g.standard_normal((r, c)) * 0.05).astype(np.float32))
-           for r, c in [(I, H), (I, H), (H, I)]]
-    h = g.standard_normal((1, H)).astype(np.float32)
-    hm = g.standard_normal((1, H)).astype(np.float32)
-    ids2 = g.integers(0, E, K).astype(np.int32)
-    ids2[3] = -2
-    rw = g.random(K).astype(np.float32)
-    lg = g.standard_normal(1).astype(np.float32)
-    _, _, _, eo = oracle.moe_expert_ffn(*st, E, H, I, h, ids2, 1, K)
-    _, _, _, so = oracle.moe_expert_ffn(*shs, 1, H, I, h, np.zeros(1, np.int32), 1, 1)
-    want = oracle.moe_combine_residual(hm, eo, rw, so, lg, H, 1, K, 1)
-    wsb = q4.moe_layer_workspace_bytes(H, I, E, 1, K)
-    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
-    res = []
-    for fused in ("1", "0"):
-        os.environ["Q4KMOE_FUSED_LAYER"] = fused
-        out = torch.empty(1, H, device=dev)
-        q4.moe_layer_forward(*[T(x, dev) for x in st], *[T(x, dev) for x in shs], T(h, dev),
-                             T(hm, dev), T(ids2, dev), T(rw, dev), T(lg, dev), out, H, I, E, 1, K,
-                             1, q4.Q4K_BUCKET_AUTO, ws, wsb)
-        res.append(sync_np(out))
-    os.environ["Q4KMOE_FUSED_LAYER"] = "1"
-    band(res[0], want, "one launch, top_k 16, invalid id")
-    assert np.array_equal(bits(res[0]), bits(res[1]))
-
-
-def test_one_launch_layer_graph_replays_and_barrier_words(dev, one_launch_layer):
-    """The single-token layer in one launch: a HIP graph of the call replayed
-    with new inputs copied in between (each replay checked against the eager
-    result for those inputs), 40 eager calls in a row on one workspace, and
-    the workspace's barrier words as documented, with the timeout word clear."""
-    cfg = wl.CFG2
-    H, I, E, K, m = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.m
-    say("one-launch layer: graph replays and barrier words")
-    a, ids, d_st, h_st = _ffn_case(cfg, dev)
-    sd, sh = _shared_stacks(cfg, dev)
-    wsb = q4.moe_layer_workspace_bytes(H, I, E, m, K)
-    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
-    g = np.random.default_rng(77)
-    draws = []
-    for i in range(4):
-        hp = (g.standard_normal((m, H))).astype(np.float32)
-        hm = (g.standard_normal((m, H))).astype(np.float32)
-        draws.append((hp, hm))
-    d_hp, d_hm = T(draws[0][0], dev), T(draws[0][1], dev)
-    d_ids, d_rw, d_lg = T(ids, dev), T(a.route_w, dev), T(a.shared_logit, dev)
-    out = torch.empty(m, H, device=dev)
-
-    def call():
-        q4.moe_layer_forward(*d_st, *sd, d_hp, d_hm, d_ids, d_rw, d_lg, out, H, I, E, m, K,
-                             cfg.shared_mode, q4.Q4K_BUCKET_AUTO, ws, wsb)
-
-    eager = []
-    for hp, hm in draws:
-        d_hp.copy_(T(hp, dev))
-        d_hm.copy_(T(hm, dev))
-        call()
-        eager.append(sync_np(out).copy())
-    for i, (hp, hm) in enumerate(draws):
-        sub = wl.MoeActivations(hp, hm, ids, a.route_w, a.shared_logit)
-        band(eager[i], _layer_oracle(cfg, h_st, sh, sub, ids), f"draw {i}")
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        call()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        call()
-    for rep in range(3):
-        for i, (hp, hm) in enumerate(draws):
-            d_hp.copy_(T(hp, dev))
-            d_hm.copy_(T(hm, dev))
-            torch.cuda.synchronize()
-            graph.replay()
-            got = sync_np(out)
-            assert np.array_equal(bits(got), bits(eager[i])), (rep, i)
-    for _ in range(40):
-        call()
-    assert np.array_equal(bits(sync_np(out)), bits(eager[-1]))
-    words = ws[:4096].view(torch.int32).cpu().numpy()
-    grid = torch.cuda.get_device_properties(0).multi_processor_count   # one workgroup per CU
-    launches = 4 + 1 + 12 + 40
-    assert (words[:grid] == launches).all(), np.unique(words[:grid])   # per-workgroup flags
-    assert words[544] == launches                                    # release word
-    assert words[576] == 0                                           # MOE_LAYER_SYNC_TIMEOUT_WORD
-    rest = np.delete(words, list(range(grid)) + [544])
-    assert not rest.any(), np.nonzero(rest)
-    del graph
 
 
 @pytest.mark.parametrize("cfg,sample", [(wl.CFG4_M1, None), (wl.CFG4_M32, [0, 13, 31])],
@@ -980,8 +847,9 @@ def test_large_layer_deepseek_class(dev, cfg, sample):
     u_d, u_h = touched_stack(cfg, wl.T_UP, I, H, experts, dev)
     d_d, d_h = touched_stack(cfg, wl.T_DOWN, H, I, experts, dev)
     sd, sh = _shared_stacks(cfg, dev)
+    same = q4.Q4K_BUCKET_OFF if m < q4.Q4K_AUTO_BUCKET_MIN_TOKENS else q4.Q4K_BUCKET_ON
     outs = {f: _layer_gpu(dev, cfg, (g_d, u_d, d_d), sd, a, ids, f)
-            for f in (q4.Q4K_BUCKET_AUTO, q4.Q4K_BUCKET_OFF if m <= 2 else q4.Q4K_BUCKET_ON)}
+            for f in (q4.Q4K_BUCKET_AUTO, same)}
     vals = list(outs.values())
     assert np.array_equal(bits(vals[0]), bits(vals[-1]))
     for t in toks:
