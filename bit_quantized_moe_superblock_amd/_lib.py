@@ -14,7 +14,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4kmoe.so")
 
 Q4K_OK, Q4K_ERR_SHAPE, Q4K_ERR_NULL, Q4K_ERR_STRIDE, Q4K_ERR_WORKSPACE, Q4K_ERR_LAUNCH, \
-    Q4K_ERR_ARG = range(7)
+    Q4K_ERR_ARG, Q4K_ERR_SCRATCH = range(8)
+MOE_LAYER_NOALLOC_MAX_BYTES = 16 << 20
 Q4K_BUCKET_AUTO, Q4K_BUCKET_OFF, Q4K_BUCKET_ON, Q4K_BUCKET_PREBUILT = 0, 1, 2, 3
 Q4K_BUCKET_MODE_MASK, Q4K_SCHED_VECTOR, Q4K_SCHED_BUCKET_LAUNCH = 0xFF, 0x100, 0x200
 Q4K_AUTO_BUCKET_MIN_TOKENS = 5
@@ -43,6 +44,8 @@ SIGNATURES = {
     "moe_layer_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64]),
     "moe_layer_forward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64,
                                _I64, _I64, _I, _I, _P, _I64, _P]),
+    "moe_layer_forward_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64,
+                                       _I64, _I64, _I64, _I64, _I, _I, _P]),
     "moe_combine_residual": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
     "moe_layer_forward_rmsnorm": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        ctypes.c_float, _P, _I64, _I64, _I64, _I64, _I64, _I,
@@ -194,6 +197,16 @@ def moe_layer_forward(w_gate, w_up, w_down, sh_gate, sh_up, sh_down, h_post, h_m
           _ptr(sh_up), _ptr(sh_down), _ptr(h_post), _ptr(h_mid), _ptr(ids), _ptr(route_w),
           _ptr(shared_gate_logit), _ptr(out), hidden, inter, num_experts, m, top_k, shared_mode,
           bucket_flag, _ptr(ws), ws_bytes, _stream(stream))
+
+
+def moe_layer_forward_noalloc(w_gate, w_up, w_down, sh_gate, sh_up, sh_down, h_post, h_mid, ids,
+                              route_w, shared_gate_logit, out, hidden: int, inter: int,
+                              num_experts: int, m: int, top_k: int, shared_mode: int,
+                              bucket_flag: int = Q4K_BUCKET_AUTO, stream=None):
+    _call("moe_layer_forward_noalloc", _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(sh_gate),
+          _ptr(sh_up), _ptr(sh_down), _ptr(h_post), _ptr(h_mid), _ptr(ids), _ptr(route_w),
+          _ptr(shared_gate_logit), _ptr(out), hidden, inter, num_experts, m, top_k, shared_mode,
+          bucket_flag, _stream(stream))
 
 
 def moe_combine_residual(h_mid, expert_out, route_w, shared_out, shared_gate_logit, out,

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "q4kmoe.h"
 #include "launch.hpp"
 
@@ -81,6 +83,7 @@ const char *q4k_status_string(int status) {
     case Q4K_ERR_WORKSPACE: return "workspace missing or too small";
     case Q4K_ERR_LAUNCH: return "HIP launch failed";
     case Q4K_ERR_ARG: return "unknown enum argument";
+    case Q4K_ERR_SCRATCH: return "scratch needed exceeds the library's static scratch";
     default: return "unknown status";
     }
 }
@@ -432,6 +435,63 @@ int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
                               route_w, shared_gate_logit, out, hidden, inter, num_experts, m,
                               top_k, shared_mode, bucket_flag, ws, ws_bytes, stream, nullptr,
                               0.0f, nullptr);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------ no-allocation layer ----
+// Device scratch of the no-allocation layer: one array per GPU, loaded with
+// the library's code and held until the process ends.  Host code never uses
+// the name as an address (on the host it is a stand-in for the symbol);
+// kernels get the device address that hipGetSymbolAddress returns.
+static __device__ __align__(256) uint8_t scratch[MOE_LAYER_NOALLOC_MAX_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device
+
+// Address of the current device's scratch, looked up once per device with
+// that device current; nullptr when the lookup fails.
+void *device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward_noalloc(const void *w_gate, const void *w_up, const void *w_down,
+                              const void *sh_gate, const void *sh_up, const void *sh_down,
+                              const float *h_post, const float *h_mid, const int32_t *ids,
+                              const float *route_w, const float *shared_gate_logit, float *out,
+                              int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
+                              int64_t top_k, int shared_mode, int bucket_flag, void *stream) {
+    const int64_t need = moe_layer_workspace_bytes(hidden, inter, num_experts, m, top_k);
+    if (need < 0)
+        return Q4K_ERR_SHAPE;
+    if (need > MOE_LAYER_NOALLOC_MAX_BYTES)
+        return Q4K_ERR_SCRATCH;
+    void *ws = device_scratch();
+    if (!ws)
+        return Q4K_ERR_LAUNCH;
+    // the workspace needs no initial contents: every word is written before
+    // it is read within the call
+    return layer_forward_impl(w_gate, w_up, w_down, sh_gate, sh_up, sh_down, h_post, h_mid, ids,
+                              route_w, shared_gate_logit, out, hidden, inter, num_experts, m,
+                              top_k, shared_mode, bucket_flag, ws, MOE_LAYER_NOALLOC_MAX_BYTES,
+                              stream, nullptr, 0.0f, nullptr);
 }
 
 int moe_layer_forward_rmsnorm(const void *w_gate, const void *w_up, const void *w_down,

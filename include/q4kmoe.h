@@ -37,7 +37,8 @@ enum {
     Q4K_ERR_STRIDE = 3,    /* an activation stride is negative                  */
     Q4K_ERR_WORKSPACE = 4, /* workspace missing or smaller than required        */
     Q4K_ERR_LAUNCH = 5,    /* the HIP runtime rejected a launch                 */
-    Q4K_ERR_ARG = 6        /* an enum argument has an unknown value             */
+    Q4K_ERR_ARG = 6,       /* an enum argument has an unknown value             */
+    Q4K_ERR_SCRATCH = 7    /* the no-allocation layer's scratch is too small    */
 };
 
 /* Bucketing flag of the id-GEMV, FFN and layer entry points ([MF]
@@ -251,6 +252,30 @@ int moe_layer_forward(const void *w_gate, const void *w_up, const void *w_down,
                       int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
                       int64_t top_k, int shared_mode, int bucket_flag, void *ws,
                       int64_t ws_bytes, void *stream);
+
+/* moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The call allocates nothing: its scratch
+ * (what moe_layer_workspace_bytes reports) is a static device array of
+ * MOE_LAYER_NOALLOC_MAX_BYTES bytes that every GPU the library runs on holds
+ * from the library's first use on it until the process ends.  Each device's
+ * array is looked up once (on the first call with that device current); the
+ * stream must belong to the current device.  Every call on one GPU uses the
+ * same array, so calls on one GPU that may overlap in time (other streams,
+ * other host threads) race and must be serialised by the caller; the array
+ * keeps the last call's contents, and no call needs it cleared.  Arguments,
+ * schedules and output bits are those of moe_layer_forward with the same
+ * arguments.  Errors as moe_layer_forward, plus Q4K_ERR_SCRATCH when
+ * moe_layer_workspace_bytes(hidden, inter, num_experts, m, top_k) exceeds
+ * MOE_LAYER_NOALLOC_MAX_BYTES (e.g. hidden 7168, inter 2048, top_k 8 fits up
+ * to m = 48) and Q4K_ERR_LAUNCH when the array's address cannot be found. */
+#define MOE_LAYER_NOALLOC_MAX_BYTES (16 << 20)
+int moe_layer_forward_noalloc(const void *w_gate, const void *w_up, const void *w_down,
+                              const void *sh_gate, const void *sh_up, const void *sh_down,
+                              const float *h_post, const float *h_mid, const int32_t *ids,
+                              const float *route_w, const float *shared_gate_logit, float *out,
+                              int64_t hidden, int64_t inter, int64_t num_experts, int64_t m,
+                              int64_t top_k, int shared_mode, int bucket_flag, void *stream);
 
 /* The same layer with the next layer's input RMSNorm chained on ([MF]
  * ChainToNormed: after the combine, rms_norm_sum_sq and rms_norm_apply_bf16

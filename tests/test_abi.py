@@ -72,7 +72,7 @@ def test_size_helpers(lib):
 
 
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(8):
         assert q4.status_string(s) and q4.status_string(s) != "unknown status"
     assert q4.status_string(99) == "unknown status"
 
@@ -162,6 +162,14 @@ def test_ffn_combine_bucket_q4tp_validation(lib):
     assert _err(lf, *st, *io, 512, 256, 4, 2, 2, 1, 0x802, FAKE, need) == _lib.Q4K_ERR_ARG
     assert _err(lf, *st, *io, 512, 256, 4, 2, 2, 1, 0, FAKE, need - 4) == _lib.Q4K_ERR_WORKSPACE
     assert _err(lf, *st, *io, 512, 256, 4, 2, 2, 1, 0, None, need) == _lib.Q4K_ERR_WORKSPACE
+    # the no-allocation layer: sizes past its static scratch are refused
+    # before any HIP call
+    na = q4.moe_layer_forward_noalloc
+    assert q4.moe_layer_workspace_bytes(7168, 2048, 256, 48, 8) <= q4.MOE_LAYER_NOALLOC_MAX_BYTES
+    assert q4.moe_layer_workspace_bytes(7168, 2048, 256, 64, 8) > q4.MOE_LAYER_NOALLOC_MAX_BYTES
+    assert _err(na, *st, *io, 7168, 2048, 256, 64, 8, 2, 0) == _lib.Q4K_ERR_SCRATCH
+    assert _err(na, *st, *io, 7168, 2048, 256, 0, 8, 2, 0) == _lib.Q4K_ERR_SHAPE
+    assert re.search(r"#define MOE_LAYER_NOALLOC_MAX_BYTES \(16 << 20\)", open(HEADER).read())
 
 
 def test_binding_refuses_host_tensors(lib):
