@@ -1,36 +1,47 @@
 #!/usr/bin/env python3
-"""Benchmark of one Q4_K MoE decode layer on one MI355X.
+"""Benchmark of the Q4_K MoE decode layer on one MI355X.
 
-A step is one whole MoE layer on one batch of synthetic decode input:
-expert bucketing (when m > 1), the fused gate/up id-GEMV with SiLU over the
-routed experts, the down id-GEMV, the shared expert's gate/up and down, and the
-weighted residual combine -- every kernel of the hot path.
+A step is one whole MoE layer on one batch of synthetic decode input: the
+fused gate/up id-GEMV with SiLU over the routed experts and the shared expert,
+the down id-GEMV, and the weighted residual combine (with expert bucketing
+when the batch is large enough) -- every kernel of the hot path.
 
-Workload (the throughput line): hidden 2048, expert intermediate 768, 128
-experts, top_k 8, m = 1 token, sigmoid-gated shared expert of the same shape
-(a Qwen3-30B-A3B-class layer; ferrum-kernels q4_k_moe_id_gemv_batched.rs
-microbench shape, moeflux expert_forward.rs combine).  A second object reports
-m = 16 tokens with Zipf(1.1) routing, where bucketing lets tokens that share
-an expert read it once.
+Headline workload (the JSON line's `value`): hidden 2048, expert intermediate
+768, 128 experts, top_k 8, m = 1 token, sigmoid-gated shared expert of the
+same shape (a Qwen3-30B-A3B-class layer; ferrum-kernels
+q4_k_moe_id_gemv_batched.rs microbench shape, moeflux expert_forward.rs
+combine).  value = unique expert-weight bytes per layer (distinct routed
+experts plus the shared expert, three matrices each) / wall time per layer.
 
-Cold-cache protocol: the weights exist as R independent replicas (each a full
-128-expert layer, 340 MB) and G id sets; consecutive steps use different
-replicas, so a graph replay of G steps touches far more distinct bytes than the
-256 MB Infinity Cache holds.  Steps are captured into HIP graphs (one launch
-per G layers) so host overhead does not pace the GPU.
+Further objects on the same line:
+  m16      the same layer at m = 16 with Zipf(1.1) routing (bucketed), and its
+           gate/up and down launches alone;
+  sweep    m in {1, 2, 4, 8, 16}: the layer in AUTO, token mode, bucketed on
+           the matrix cores and bucketed on the vector units, with the pages'
+           batching criterion (ferrum moe_gemv_scaling_microbench: m = 16 in
+           less than 0.6 x 16 x the m = 1 time);
+  cfg4     hidden 7168, inter 2048, 256 experts, top_k 8 at m = 1 and m = 32;
+  walk     the dense Q4TiledP decode walk (cortiq-engine mv_lab.rs) over
+           several layers plus the head;
+  mlx4     the MLX affine 4-bit / 2-bit id-GEMV at the single-token shapes;
+  roofline the dominant kernel of the headline layer against HBM peak, with
+           `ceiling` = the read rate of the same bytes by a plain coalesced
+           read of the same expert matrices (q4k_ceiling_read);
+  cpu_baseline  the CPU oracle's layer on one thread and on all host cores.
 
-value = unique expert-weight bytes read per layer (distinct routed experts
-plus the shared expert, three matrices each) / wall time per layer.
-roofline = the layer's first kernel (fused gate/up + SiLU over the routed
-experts with the shared expert in the same launch), timed by a graph of only
-its launches over the same rotation (in-graph launches run back to back, so
-the per-launch time is the kernel's duration), against the 8 TB/s HBM peak.
-cpu_baseline = the CPU oracle's layer forward, single-threaded, on a bounded
-sample of the same workload.
+Protocol: weights live as R device-encoded replicas and G routing draws; step
+i uses replica i mod R and draw i mod G, so consecutive steps read different
+bytes and a graph of steps touches far more than the 256 MB Infinity Cache.
+Steps are captured into HIP graphs.  Warm-up steps use draws disjoint from
+the timed ones.  Every figure is timed in R rounds, figures round-robin (the
+pages' lab protocol, cortiq-engine mv_lab.rs `main`), and reported as the
+median with the quartiles; each headline round times exactly --steps layers
+between device synchronisations, with HIP events on the launch stream.
 """
 from __future__ import annotations
 
 import argparse
+import concurrent.futures as cf
 import json
 import os
 import sys
@@ -41,7 +52,6 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE id-GEMV effective HBM GB/s (% of peak) + µs/MoE layer at M=1,16"
 HBM_PEAK_GBS = 8000.0
-# FETCH_SIZE + WRITE_SIZE of the dominant kernel, scaled by a plain copy
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gate_up_silu_m1_hbm_traffic.md")
 
 
@@ -49,271 +59,300 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-class Layer:
-    """Device-resident weight replicas and per-step inputs of one MoE workload."""
+def quartiles(vals):
+    v = sorted(vals)
+    n = len(v)
 
-    def __init__(self, torch, q4, wl, cfg, replicas, stacks=None):
-        self.torch, self.q4, self.cfg = torch, q4, cfg
-        dev = torch.device("cuda")
-        H, I, E = cfg.hidden, cfg.inter, cfg.num_experts
-        self.mat_bytes = q4.q4k_matrix_bytes(I, H)           # one expert matrix
-        self.expert_bytes = 3 * self.mat_bytes
-        if stacks is None:
-            stacks = []
-            for r in range(replicas):
-                st = []
-                for t, (rows, cols, n_exp) in enumerate([(I, H, E), (I, H, E), (H, I, E),
-                                                          (I, H, 1), (I, H, 1), (H, I, 1)]):
-                    w = wl.device_normal((n_exp * rows, cols), cfg.w_std, seed=1000 * r + t)
-                    b = torch.empty(n_exp * q4.q4k_matrix_bytes(rows, cols), dtype=torch.uint8,
-                                    device=dev)
-                    q4.q4k_quantize(w, b, n_exp * rows, cols)
-                    del w
-                    st.append(b)
-                stacks.append(st)
-            torch.cuda.synchronize()
-        self.stacks = stacks
+    def q(p):
+        x = p * (n - 1)
+        lo = int(x)
+        hi = min(lo + 1, n - 1)
+        return v[lo] + (v[hi] - v[lo]) * (x - lo)
+    return q(0.25), q(0.5), q(0.75)
 
-    def inputs(self, wl, n_sets):
-        torch, cfg = self.torch, self.cfg
-        dev = torch.device("cuda")
-        self.sets = []
-        self.unique = []
-        for s in range(n_sets):
-            a = wl.moe_activations(cfg, index=s)
-            self.sets.append(dict(
-                h_post=torch.from_numpy(a.h_post).to(dev),
-                h_mid=torch.from_numpy(a.h_mid).to(dev),
-                ids=torch.from_numpy(a.ids).to(dev),
-                route_w=torch.from_numpy(a.route_w).to(dev),
-                logit=torch.from_numpy(a.shared_logit).to(dev)))
-            self.unique.append(len(set(a.ids.tolist())))
-        m, K, H, I = cfg.m, cfg.top_k, cfg.hidden, cfg.inter
-        P = m * K
-        self.act = torch.empty(P, I, device=dev)
-        self.eo = torch.empty(P, H, device=dev)
-        self.s_act = torch.empty(m, I, device=dev)
-        self.s_out = torch.empty(m, H, device=dev)
-        self.out = torch.empty(m, H, device=dev)
-        self.normed = torch.empty(m, H, device=dev)
-        self.norm_w = torch.ones(H, device=dev).to(torch.bfloat16)   # next layer's norm weight
-        self.lwsb = self.q4.moe_layer_workspace_bytes(H, I, cfg.num_experts, m, K)
-        self.lws = torch.zeros(self.lwsb, dtype=torch.uint8, device=dev)   # barrier words zero
-        self.wsb = self.q4.moe_bucket_workspace_bytes(P, cfg.num_experts)
-        # one bucket workspace per id set, filled here, so a graph of gate/up
-        # launches alone still reads the buckets of its own routing
-        self.ws_sets = []
-        for x in self.sets:
-            ws = torch.empty(self.wsb, dtype=torch.uint8, device=dev)
-            if m > 1:
-                self.q4.moe_bucket(x["ids"], P, cfg.num_experts, ws, self.wsb)
-            self.ws_sets.append(ws)
+
+# ------------------------------------------------------------ timing ----
+
+class Figure:
+    """A HIP graph of `n` steps and the bytes those steps read; timed once
+    per round."""
+
+    def __init__(self, torch, name, fn, idx, bytes_of, warm_idx=None):
+        self.torch, self.name, self.n = torch, name, len(idx)
+        # the graph holds raw device pointers of whatever fn launches with: keep
+        # fn (and the tensors its closure owns) alive as long as the graph
+        self.fn = fn
+        self.bytes = sum(bytes_of(i) for i in idx)
+        log(f"capturing {name} ({self.n} steps)")
+        self.graph = capture(torch, fn, idx)
+        self.warm = capture(torch, fn, warm_idx) if warm_idx else None
+        self.secs = []
+
+    def run(self):
+        torch = self.torch
         torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        self.graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        self.secs.append(e0.elapsed_time(e1) / 1e3)
 
-    def step_of(self, i):
-        return i % len(self.stacks), i % len(self.sets)
-
-    def bucketed(self):
-        return self.cfg.m > 2    # moe_layer_forward's AUTO rule
-
-    def gate_up(self, i):
-        """The layer's first kernel alone: fused gate/up + SiLU over the routed
-        pairs with the shared expert in the same launch (buckets pre-built)."""
-        q4, cfg = self.q4, self.cfg
-        r, s = self.step_of(i)
-        st, x = self.stacks[r], self.sets[s]
-        flag = q4.Q4K_BUCKET_PREBUILT if self.bucketed() else q4.Q4K_BUCKET_OFF
-        q4.q4k_moe_gate_up_silu(st[0], st[1], x["h_post"], x["ids"], self.act, cfg.inter,
-                                cfg.hidden, cfg.m, cfg.top_k, cfg.hidden, 0, cfg.num_experts,
-                                st[3], st[4], self.s_act, flag, self.ws_sets[s], self.wsb)
-
-    def layer(self, i):
-        """One whole MoE layer (every kernel of the hot path)."""
-        q4, cfg = self.q4, self.cfg
-        r, s = self.step_of(i)
-        st, x = self.stacks[r], self.sets[s]
-        q4.moe_layer_forward(st[0], st[1], st[2], st[3], st[4], st[5], x["h_post"], x["h_mid"],
-                             x["ids"], x["route_w"], x["logit"], self.out, cfg.hidden, cfg.inter,
-                             cfg.num_experts, cfg.m, cfg.top_k, cfg.shared_mode,
-                             q4.Q4K_BUCKET_AUTO, self.lws, self.lwsb)
-
-    def layer_norm(self, i):
-        """The layer with the next layer's input RMSNorm chained on."""
-        q4, cfg = self.q4, self.cfg
-        r, s = self.step_of(i)
-        st, x = self.stacks[r], self.sets[s]
-        q4.moe_layer_forward_rmsnorm(st[0], st[1], st[2], st[3], st[4], st[5], x["h_post"],
-                                     x["h_mid"], x["ids"], x["route_w"], x["logit"], self.out,
-                                     self.norm_w, 1e-6, self.normed, cfg.hidden, cfg.inter,
-                                     cfg.num_experts, cfg.m, cfg.top_k, cfg.shared_mode,
-                                     q4.Q4K_BUCKET_AUTO, self.lws, self.lwsb)
-
-    def layer_bytes(self, i):
-        r, s = self.step_of(i)
-        return (self.unique[s] + 1) * self.expert_bytes
-
-    def gate_up_bytes(self, i):
-        r, s = self.step_of(i)
-        return (self.unique[s] + 1) * 2 * self.mat_bytes
+    def summary(self):
+        q1, med, q3 = quartiles([s / self.n * 1e6 for s in self.secs])
+        return dict(us=round(med, 3), us_q1=round(q1, 3), us_q3=round(q3, 3),
+                    gbs=round(self.bytes / self.n / med / 1e3, 2),
+                    frac_hbm_peak=round(self.bytes / self.n / med / 1e3 / HBM_PEAK_GBS, 4),
+                    bytes_per_step=int(self.bytes / self.n), steps=self.n, rounds=len(self.secs))
 
 
-def capture(torch, fn, n):
-    """HIP graph of fn(0..n-1), warmed up on a side stream first."""
+def capture(torch, fn, idx):
+    """HIP graph of fn(i) for i in idx, run once on a side stream first."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for i in range(n):
+        for i in idx:
             fn(i)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for i in range(n):
+        for i in idx:
             fn(i)
     torch.cuda.synchronize()
     return g
 
 
-def time_graph(torch, g, replays, warmup):
-    for _ in range(warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(replays):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) / 1e3, wall
+def run_rounds(figs, rounds):
+    for f in figs:
+        if f.warm is not None:
+            f.warm.replay()
+    for _ in range(rounds):
+        for f in figs:
+            f.run()
 
 
-def largest_divisor_at_most(k, cap):
-    for g in range(min(k, cap), 0, -1):
-        if k % g == 0:
-            return g
-    return 1
+# ---------------------------------------------------------- workload ----
+
+class Moe:
+    """Device-resident expert replicas and per-step inputs of one MoE
+    workload (config cfg), plus the byte ranges each step reads."""
+
+    def __init__(self, torch, q4, wl, cfg, replicas, n_sets, stacks=None, shared=None,
+                 shared_replicas=None):
+        self.torch, self.q4, self.cfg = torch, q4, cfg
+        dev = torch.device("cuda")
+        H, I, E = cfg.hidden, cfg.inter, cfg.num_experts
+        self.mat = q4.q4k_matrix_bytes(I, H)          # gate/up and down matrices alike
+        if stacks is None:
+            stacks = [[self._encode(wl, E, rows, cols, cfg.w_std, 1000 * r + t)
+                       for t, (rows, cols) in enumerate([(I, H), (I, H), (H, I)])]
+                      for r in range(replicas)]
+        if shared is None:
+            shared = [[self._encode(wl, 1, rows, cols, cfg.w_std, 1000 * r + 3 + t)
+                       for t, (rows, cols) in enumerate([(I, H), (I, H), (H, I)])]
+                      for r in range(shared_replicas or len(stacks))]
+        self.stacks, self.shared = stacks, shared
+        torch.cuda.synchronize()
+        m, K = cfg.m, cfg.top_k
+        P = m * K
+        self.sets, self.unique, self.ws_sets, self.ranges = [], [], [], []
+        for s in range(n_sets):
+            a = wl.moe_activations(cfg, index=s)
+            self.sets.append(dict(h_post=torch.from_numpy(a.h_post).to(dev),
+                                  h_mid=torch.from_numpy(a.h_mid).to(dev),
+                                  ids=torch.from_numpy(a.ids).to(dev),
+                                  route_w=torch.from_numpy(a.route_w).to(dev),
+                                  logit=torch.from_numpy(a.shared_logit).to(dev)))
+            self.unique.append(sorted(set(int(e) for e in a.ids if 0 <= e < E)))
+            wsb = q4.moe_bucket_workspace_bytes(P, E)
+            ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+            q4.moe_bucket(self.sets[-1]["ids"], P, E, ws, wsb)
+            self.ws_sets.append(ws)
+        self.wsb = q4.moe_bucket_workspace_bytes(P, E)
+        self.act = torch.randn(P + m, I, device=dev)
+        self.eo = torch.empty(P, H, device=dev)
+        self.s_act = torch.empty(m, I, device=dev)
+        self.out = torch.empty(m, H, device=dev)
+        self.normed = torch.empty(m, H, device=dev)
+        self.norm_w = torch.ones(H, device=dev).to(torch.bfloat16)
+        self.lwsb = q4.moe_layer_workspace_bytes(H, I, E, m, K)
+        self.lws = torch.empty(self.lwsb, dtype=torch.uint8, device=dev)
+        self.sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        self.ceiling_offsets = []
+        torch.cuda.synchronize()
+
+    def _encode(self, wl, n_exp, rows, cols, std, seed):
+        torch, q4 = self.torch, self.q4
+        b = torch.empty(n_exp * q4.q4k_matrix_bytes(rows, cols), dtype=torch.uint8,
+                        device="cuda")
+        per = max(1, (1 << 28) // (rows * cols * 4))     # experts per encoding batch (<= 256 MB fp32)
+        mb = q4.q4k_matrix_bytes(rows, cols)
+        for e0 in range(0, n_exp, per):
+            ne = min(per, n_exp - e0)
+            w = wl.device_normal((ne * rows, cols), std, seed=seed * 4099 + e0)
+            q4.q4k_quantize(w, b[e0 * mb:(e0 + ne) * mb], ne * rows, cols)
+            del w
+        return b
+
+    def pick(self, i):
+        return self.stacks[i % len(self.stacks)], self.shared[i % len(self.shared)], \
+            i % len(self.sets)
+
+    def key(self, i):
+        return i % len(self.stacks), i % len(self.shared), i % len(self.sets)
+
+    def layer(self, i, flag=None):
+        q4, c = self.q4, self.cfg
+        st, sh, s = self.pick(i)
+        x = self.sets[s]
+        q4.moe_layer_forward(*st, *sh, x["h_post"], x["h_mid"], x["ids"], x["route_w"],
+                             x["logit"], self.out, c.hidden, c.inter, c.num_experts, c.m,
+                             c.top_k, c.shared_mode,
+                             q4.Q4K_BUCKET_AUTO if flag is None else flag, self.lws, self.lwsb)
+
+    def layer_norm(self, i):
+        q4, c = self.q4, self.cfg
+        st, sh, s = self.pick(i)
+        x = self.sets[s]
+        q4.moe_layer_forward_rmsnorm(*st, *sh, x["h_post"], x["h_mid"], x["ids"], x["route_w"],
+                                     x["logit"], self.out, self.norm_w, 1e-6, self.normed,
+                                     c.hidden, c.inter, c.num_experts, c.m, c.top_k,
+                                     c.shared_mode, q4.Q4K_BUCKET_AUTO, self.lws, self.lwsb)
+
+    def bucketed(self):
+        return self.cfg.m >= self.q4.Q4K_AUTO_BUCKET_MIN_TOKENS
+
+    def gate_up(self, i):
+        """The layer's first launch alone (buckets pre-built when bucketed)."""
+        q4, c = self.q4, self.cfg
+        st, sh, s = self.pick(i)
+        x = self.sets[s]
+        flag = q4.Q4K_BUCKET_PREBUILT if self.bucketed() else q4.Q4K_BUCKET_OFF
+        q4.q4k_moe_gate_up_silu(st[0], st[1], x["h_post"], x["ids"], self.act, c.inter,
+                                c.hidden, c.m, c.top_k, c.hidden, 0, c.num_experts, sh[0], sh[1],
+                                self.s_act, flag, self.ws_sets[s], self.wsb)
+
+    def down(self, i):
+        """The routed down projection alone (the bucketed id-GEMV on pre-built
+        buckets, one activation row per pair)."""
+        q4, c = self.q4, self.cfg
+        st, sh, s = self.pick(i)
+        x = self.sets[s]
+        q4.q4k_moe_id_gemv(st[2], self.act, x["ids"], self.eo, c.hidden, c.inter, c.m, c.top_k,
+                           c.top_k * c.inter, c.inter, c.num_experts, q4.Q4K_BUCKET_PREBUILT,
+                           self.ws_sets[s], self.wsb)
+
+    def ceiling(self, mats):
+        """fn(i): a plain read of the matrices `mats` (0 gate, 1 up, 2 down)
+        of the experts step i touches (and the shared expert's)."""
+        torch, q4 = self.torch, self.q4
+        base = self.stacks[0][0]
+        b0 = base.data_ptr()
+        offs = {}
+        for r in range(max(len(self.stacks), len(self.shared))):
+            for s in range(len(self.sets)):
+                ks = (r % len(self.stacks), r % len(self.shared), s)
+                st, sh = self.stacks[ks[0]], self.shared[ks[1]]
+                o = [st[t].data_ptr() + e * self.mat - b0 for e in self.unique[s] for t in mats]
+                o += [sh[t].data_ptr() - b0 for t in mats]
+                offs[ks] = torch.tensor(o, dtype=torch.int64, device="cuda")
+
+        # owned by the workload too: captured graphs replay with these pointers
+        self.ceiling_offsets.append(offs)
+
+        def fn(i):
+            t = offs[self.key(i)]
+            q4.q4k_ceiling_read(base, t, t.numel(), self.mat, self.sink)
+        return fn
+
+    def bytes_of(self, n_mats):
+        return lambda i: (len(self.unique[i % len(self.sets)]) + 1) * n_mats * self.mat
 
 
-def time_eager(torch, fn, steps, warmup, start=0):
-    """fn(i) launched one by one (no graph), timed with events on the launch
-    stream; used under hardware-counter profiling."""
-    for i in range(warmup):
-        fn(start + i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for i in range(steps):
-        fn(start + warmup + i)
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / 1e3, time.perf_counter() - t0
+# --------------------------------------------------------- sections ----
 
-
-def run_walk(torch, q4, wl, replicas, walks, warmup):
-    """The dense Q4TiledP decode walk (one layer's q, k, v, o, gate, up and down
-    matvecs, then the head) over `replicas` device-encoded copies of its
-    tensors, rotated so that consecutive walks do not find them in cache.
-    Timed twice: one launch per tensor, and with q|k|v and gate|up each merged
-    into one launch.  Returns (us per walk merged, us per walk one launch per
-    tensor, tensor bytes)."""
+def section_walk(torch, q4, wl, n_layers, rounds):
+    """The dense Q4TiledP decode walk: n_layers distinct layers of q, k, v, o
+    (4096x4096), gate, up (14336x4096), down (4096x14336), then the head
+    (32000x4096), merged dispatches q|k|v and gate|up (the pages' mode `m`),
+    and one launch per tensor; 2 replicas of the whole walk alternate."""
     dev = torch.device("cuda")
-    shapes = [(rows, cols) for _, rows, cols, _ in wl.walk_tensors(1, True)]
+    shapes = [(r, c) for _, r, c, _ in wl.walk_tensors(n_layers, True)]
     reps = []
-    for r in range(replicas):
+    for rep in range(2):
         ts = []
         for i, (rows, cols) in enumerate(shapes):
-            w = wl.device_normal((rows, cols), 0.02, seed=50000 + 100 * r + i)
+            w = wl.device_normal((rows, cols), 0.02, seed=50000 + 1000 * rep + i)
             t = torch.empty(q4.q4tp_tensor_bytes(rows, cols), dtype=torch.uint8, device=dev)
             q4.q4tp_quantize(w, t, rows, cols)
             del w
             ts.append(t)
         reps.append(ts)
     x = wl.device_normal((wl.WALK_X_LEN,), 1.0, seed=59999)
-    ys = [torch.empty(rows, device=dev) for rows, _ in shapes]
+    ys = [torch.empty(r, device=dev) for r, _ in shapes]
+    groups = []
+    for layer in range(n_layers):
+        b = 7 * layer
+        groups += [[b, b + 1, b + 2], [b + 3], [b + 4, b + 5], [b + 6]]
+    groups.append([7 * n_layers])
+    ym = [torch.empty(sum(shapes[j][0] for j in g), device=dev) for g in groups]
     torch.cuda.synchronize()
 
-    def walk(i):
-        ts = reps[i % replicas]
-        for (rows, cols), t, y in zip(shapes, ts, ys):
-            q4.q4tp_matvec(t, x, y, rows, cols)
+    def merged(i):
+        ts = reps[i % 2]
+        for g, y in zip(groups, ym):
+            q4.q4tp_matvec_multi([ts[j] for j in g], [shapes[j][0] for j in g], x, y,
+                                 shapes[g[0]][1])
 
-    # q|k|v, o, gate|up, down, head
-    groups = [[0, 1, 2], [3], [4, 5], [6], [7]]
-    ym = [torch.empty(sum(shapes[j][0] for j in grp), device=dev) for grp in groups]
+    def single(i):
+        ts = reps[i % 2]
+        for (r, c), t, y in zip(shapes, ts, ys):
+            q4.q4tp_matvec(t, x, y, r, c)
 
-    def walk_merged(i):
-        ts = reps[i % replicas]
-        for grp, y in zip(groups, ym):
-            q4.q4tp_matvec_multi([ts[j] for j in grp], [shapes[j][0] for j in grp], x, y,
-                                 shapes[grp[0]][1])
-
-    # concurrent mode (cortiq-engine mv_lab.rs, mode 'c'): the tensors of a
-    # group run on parallel graph branches, joined before the next group
-    side = [torch.cuda.Stream() for _ in range(3)]   # default priority
-
-    def walk_concurrent(i):
-        ts = reps[i % replicas]
-        main = torch.cuda.current_stream()
-        for grp in groups:
-            if len(grp) == 1:
-                j = grp[0]
-                q4.q4tp_matvec(ts[j], x, ys[j], *shapes[j])
-                continue
-            for b, j in enumerate(grp):
-                side[b].wait_stream(main)
-                with torch.cuda.stream(side[b]):
-                    q4.q4tp_matvec(ts[j], x, ys[j], *shapes[j], stream=side[b])
-            for b in range(len(grp)):
-                main.wait_stream(side[b])
-
-    g = capture(torch, walk, walks)
-    sec, _ = time_graph(torch, g, 4, warmup)
-    gm = capture(torch, walk_merged, walks)
-    sec_m, _ = time_graph(torch, gm, 4, warmup)
-    gc = capture(torch, walk_concurrent, walks)
-    sec_c, _ = time_graph(torch, gc, 4, warmup)
-    nbytes = sum(q4.q4tp_tensor_bytes(rows, cols) for rows, cols in shapes)
-    return (sec_m / (4 * walks) * 1e6, sec / (4 * walks) * 1e6, nbytes,
-            sec_c / (4 * walks) * 1e6)
+    nbytes = sum(q4.q4tp_tensor_bytes(r, c) for r, c in shapes)
+    figs = [Figure(torch, "walk merged", merged, range(4), lambda i: nbytes),
+            Figure(torch, "walk single", single, range(4), lambda i: nbytes)]
+    run_rounds(figs, rounds)
+    m, s = figs[0].summary(), figs[1].summary()
+    return {
+        "workload": f"dense Q4TiledP decode walk: {n_layers} layers of q, k, v, o 4096x4096, "
+                    "gate and up 14336x4096, down 4096x14336, then the head 32000x4096, "
+                    "5-bit log-scale ladder, 2 walk replicas alternating",
+        "kernel": "k_q4tp_matvec", "launches": "q|k|v, o, gate|up, down per layer, head",
+        "bytes_per_walk": int(nbytes), "us_per_walk": m["us"], "us_q1": m["us_q1"],
+        "us_q3": m["us_q3"], "gbs": m["gbs"], "frac_hbm_peak": m["frac_hbm_peak"],
+        "us_per_walk_one_launch_per_tensor": s["us"], "gbs_one_launch_per_tensor": s["gbs"],
+    }
 
 
-def run_mlx4(torch, q4, wl, replicas, launches, warmup):
-    """The MLX affine 4-bit expert path (moeflux expert_forward.rs 4-bit
-    experts, bf16 scale and bias per 64 weights) at the single-token decode
-    shapes, 128 experts, top_k 8, m = 1: the fused gate/up + SiLU launch over
-    expert blocks holding the gate and up matrices (768 x 2048 each, one
-    activation row per token), and the down-shaped id-GEMV (2048 x 768, one
-    row per pair), that one also in the 2-bit variant (moeflux's g_use_2bit
-    layout).  Each replica is a full 128-expert stack, device-encoded;
-    launches rotate over replicas and 64 routing draws.  Returns
-    {name: (us per launch, unique weight bytes per launch)}."""
+def section_mlx4(torch, q4, wl, rounds):
+    """MLX affine 4-bit expert path at the single-token decode shapes (moeflux
+    expert_forward.rs 4-bit experts, bf16 scale and bias per 64 weights), 128
+    experts, top_k 8, m = 1: the fused gate/up + SiLU over expert blocks
+    holding the 768x2048 gate and up matrices, the down-shaped 2048x768
+    id-GEMV, and the latter in the 2-bit variant; 8 replicas rotate."""
     dev = torch.device("cuda")
     cfg = wl.CFG2
     E, H, I, K = cfg.num_experts, cfg.hidden, cfg.inter, cfg.top_k
-    sets = [wl.moe_activations(cfg, index=s) for s in range(64)]
-    ids = [torch.from_numpy(a.ids).to(dev) for a in sets]
-    uniq = [len(set(a.ids.tolist())) for a in sets]
+    draws = [wl.moe_activations(cfg, index=s) for s in range(64)]
+    ids = [torch.from_numpy(a.ids).to(dev) for a in draws]
+    uniq = [len(set(a.ids.tolist())) for a in draws]
     res = {}
     for name, n, k, outer, inner, nmat, bits in [("gate_up_silu", I, H, H, 0, 2, 4),
                                                  ("down", H, I, K * I, I, 1, 4),
                                                  ("down_2bit", H, I, K * I, I, 1, 2)]:
         mat = q4.mlx4_matrix_bytes(n, k) if bits == 4 else q4.mlx2_matrix_bytes(n, k)
-        pb = n * k * bits // 8                   # packed bytes of a matrix
+        pb = n * k * bits // 8
         stride = nmat * mat
-        # matrix j of a block: packed | scales | biases at j * mat
         offs = [(j * mat, j * mat + pb, j * mat + pb + n * k // 32) for j in range(nmat)]
         quantize = q4.mlx4_quantize if bits == 4 else q4.mlx2_quantize
         blobs = []
-        for r in range(replicas):
+        for r in range(8):
             blob = torch.empty(E * stride, dtype=torch.uint8, device=dev)
             for j in range(nmat):
-                w = wl.device_normal((E * n, k), cfg.w_std,
-                                     seed=70000 + 100 * r + 10 * j + nmat + 3 * bits)
+                w = wl.device_normal((E * n, k), cfg.w_std, seed=70000 + 100 * r + 10 * j + nmat + 3 * bits)
                 po, so, bo = offs[j]
                 for e in range(E):
                     b0 = e * stride
@@ -321,13 +360,13 @@ def run_mlx4(torch, q4, wl, replicas, launches, warmup):
                              blob[b0 + so:b0 + bo], blob[b0 + bo:b0 + po + mat], n, k)
                 del w
             blobs.append(blob)
-        x = wl.device_normal((K, k), 1.0, seed=79999)   # row 0 for gate/up, 8 rows for down
+        x = wl.device_normal((K, k), 1.0, seed=79999)
         out = torch.empty(K, n, device=dev)
         torch.cuda.synchronize()
 
         def launch(i, n=n, k=k, stride=stride, outer=outer, inner=inner, blobs=blobs, x=x,
                    out=out, offs=offs, nmat=nmat, bits=bits):
-            blob, d_ids = blobs[i % replicas], ids[i % 64]
+            blob, d_ids = blobs[i % 8], ids[i % 64]
             if bits == 2:
                 q4.mlx2_moe_id_gemv(blob, stride, *offs[0], x, d_ids, out, n, k, 1, K, outer,
                                     inner, E)
@@ -338,108 +377,33 @@ def run_mlx4(torch, q4, wl, replicas, launches, warmup):
                 q4.mlx4_moe_id_gemv(blob, stride, *offs[0], x, d_ids, out, n, k, 1, K, outer,
                                     inner, E)
 
-        g = capture(torch, launch, launches)
-        sec, _ = time_graph(torch, g, 4, warmup)
-        nbytes = sum(uniq[i % 64] for i in range(launches)) / launches * stride
-        res[name] = (sec / (4 * launches) * 1e6, nbytes)
+        f = Figure(torch, name, launch, range(64), lambda i, stride=stride: uniq[i % 64] * stride)
+        run_rounds([f], rounds)
+        sm = f.summary()
+        res[name] = {"us_per_launch": sm["us"], "us_q1": sm["us_q1"], "us_q3": sm["us_q3"],
+                     "bytes_per_launch": sm["bytes_per_step"], "gbs": sm["gbs"],
+                     "frac_hbm_peak": sm["frac_hbm_peak"]}
         del blobs
+        torch.cuda.empty_cache()
     return res
 
 
-def run_workload(torch, q4, wl, cfg, args, stacks=None):
-    """Times exactly args.steps layers (and, separately, args.steps launches
-    of the layer's first kernel) after args.warmup untimed ones."""
-    steps = args.steps
-    layer = Layer(torch, q4, wl, cfg, args.replicas, stacks)
-    layer.inputs(wl, args.id_sets)
-    if args.eager:
-        log(f"{cfg.name}: {steps} eager layers timed")
-        gpu_s, wall_s = time_eager(torch, layer.layer, steps, args.warmup)
-        gu_s, _ = time_eager(torch, layer.gate_up, steps, args.warmup)
-        norm_s, _ = time_eager(torch, layer.layer_norm, steps, args.warmup)
-        G, warm = 1, args.warmup
-        idx = range(steps)
-        mode = "eager launches"
-    else:
-        G = largest_divisor_at_most(steps, args.group)
-        replays = steps // G
-        warm_replays = max(1, -(-args.warmup // G))
-        warm = warm_replays * G
-        log(f"{cfg.name}: capturing {G} layers per graph, {replays} replays timed")
-        g_layer = capture(torch, layer.layer, G)
-        gpu_s, wall_s = time_graph(torch, g_layer, replays, warm_replays)
-        g_gu = capture(torch, layer.gate_up, G)
-        gu_s, _ = time_graph(torch, g_gu, replays, warm_replays)
-        g_norm = capture(torch, layer.layer_norm, G)
-        norm_s, _ = time_graph(torch, g_norm, replays, warm_replays)
-        del g_layer, g_gu, g_norm
-        idx = [i % G for i in range(steps)]
-        mode = f"HIP graphs of {G} layers"
-    total_bytes = sum(layer.layer_bytes(i) for i in idx)
-    gu_bytes = sum(layer.gate_up_bytes(i) for i in idx)
-    res = dict(steps=steps, warmup=warm, gpu_s=gpu_s, wall_s=wall_s, mode=mode, group=G,
-               us_per_layer=gpu_s / steps * 1e6, gbs=total_bytes / gpu_s / 1e9,
-               bytes_per_layer=total_bytes / steps, gate_up_us=gu_s / steps * 1e6,
-               gate_up_gbs=gu_bytes / gu_s / 1e9, gate_up_bytes=gu_bytes / steps,
-               us_per_layer_rmsnorm=norm_s / steps * 1e6)
-    return res, layer.stacks
-
-
-def copy_calibration(torch, mib):
-    """A plain device-to-device copy of a known size, the yardstick that the
-    FETCH_SIZE / WRITE_SIZE counters are scaled by."""
-    n = mib << 20
-    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-    dst = torch.empty_like(src)
-    torch.cuda.synchronize()
-    for _ in range(10):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 10}), flush=True)
-
-
-def source_digest(files):
-    """sha256 over the named kernel sources (paths relative to the repository
-    root): a stored counter figure is reported only while the code it was
-    taken from is unchanged."""
-    import hashlib
-    h = hashlib.sha256()
-    for rel in files:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(rel.encode() + b"\0" + f.read())
-    return h.hexdigest()
-
-
-def stored_traffic(path):
-    """HBM bytes per launch of the dominant kernel from a profile summary
-    (lines `traffic_bytes_per_launch: N`, `source_files: F...` and
-    `source_sha256: H`), or None when the summary is absent or was taken on
-    other kernel sources."""
+def cpu_model():
     try:
-        with open(path) as f:
-            text = f.read()
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
     except OSError:
-        return None
-    fields = {}
-    for ln in text.splitlines():
-        if ":" in ln:
-            k, v = ln.split(":", 1)
-            fields[k.strip().strip("-* `")] = v.strip().strip("`")
-    files = fields.get("source_files", "").split()
-    try:
-        if not files or fields.get("source_sha256") != source_digest(files):
-            return None
-    except OSError:
-        return None
-    try:
-        return int(fields["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+        pass
+    return "unknown"
 
 
 def cpu_baseline(wl, cfg, seconds):
-    """The oracle's layer forward (routed FFN, shared expert, combine), one
-    thread, repeated on one id set until `seconds` of work is done."""
+    """The oracle's layer forward (routed FFN, shared expert, combine) on one
+    id set: on one host thread, and with the layer's independent expert FFNs
+    (each routed pair and the shared expert) on a pool of threads, whose
+    results are the same bits (each pair is computed alone either way)."""
     import numpy as np
 
     import oracle
@@ -454,47 +418,142 @@ def cpu_baseline(wl, cfg, seconds):
     sh = [oracle.q4k_quantize(wl.expert_weight(cfg, wl.T_SH_GATE + t, 0, rows, cols))
           for t, (rows, cols) in enumerate([(I, H), (I, H), (H, I)])]
     zeros = np.zeros(m, np.int32)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
+    layer_bytes = (len(experts) + 1) * 3 * mb
+    ids = a.ids.reshape(m, K)
+
+    def one_thread():
         _, _, _, eo = oracle.moe_expert_ffn(*stk, E, H, I, a.h_post, a.ids, m, K)
         _, _, _, so = oracle.moe_expert_ffn(*sh, 1, H, I, a.h_post, zeros, m, 1)
-        oracle.moe_combine_residual(a.h_mid, eo, a.route_w, so, a.shared_logit, H, m, K,
-                                    cfg.shared_mode)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or n >= 10000:
-            break
-    layer_bytes = (len(experts) + 1) * 3 * mb
-    return dict(value=round(layer_bytes * n / el / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                sample=f"{n} layer forwards of {cfg.name} (id set 0: {len(experts)} routed + 1 "
-                       f"shared expert, oracle-encoded weights), {el:.1f} s, one thread; "
-                       f"{el / n * 1e6:.0f} us/layer")
+        return oracle.moe_combine_residual(a.h_mid, eo, a.route_w, so, a.shared_logit, H, m, K,
+                                           cfg.shared_mode)
+
+    share = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    n_tasks = m * K + 1
+    threads = max(1, min(n_tasks, share, 16))
+    pool = cf.ThreadPoolExecutor(max_workers=threads)
+
+    def pair(p):
+        t, s = divmod(p, K)
+        if p == m * K:
+            return oracle.moe_expert_ffn(*sh, 1, H, I, a.h_post, zeros, m, 1)[3]
+        return oracle.moe_expert_ffn(*stk, E, H, I, a.h_post[t:t + 1], ids[t, s:s + 1], 1, 1)[3]
+
+    def all_cores():
+        res = list(pool.map(pair, range(n_tasks)))
+        eo = np.concatenate(res[:m * K])
+        return oracle.moe_combine_residual(a.h_mid, eo, a.route_w, res[-1], a.shared_logit, H,
+                                           m, K, cfg.shared_mode)
+
+    assert np.array_equal(one_thread().view(np.uint32), all_cores().view(np.uint32))
+    out = {}
+    for name, fn in (("one_thread", one_thread), ("all_cores", all_cores)):
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or n >= 10000:
+                break
+        out[name] = (n, el)
+    pool.shutdown()
+    n1, e1 = out["one_thread"]
+    na, ea = out["all_cores"]
+    return {
+        "value": round(layer_bytes * na / ea / 1e9, 4), "unit": "GB/s", "cores": threads,
+        "kind": "oracle",
+        "sample": f"{na} layer forwards of {cfg.name} (id set 0: {len(experts)} routed + 1 "
+                  f"shared expert, oracle-encoded weights) in {ea:.1f} s on {threads} threads "
+                  f"(one per expert FFN), {ea / na * 1e6:.0f} us/layer",
+        "one_thread": {"value": round(layer_bytes * n1 / e1 / 1e9, 4), "unit": "GB/s",
+                       "us_per_layer": round(e1 / n1 * 1e6, 1), "layers": n1},
+        "all_cores": {"value": round(layer_bytes * na / ea / 1e9, 4), "unit": "GB/s",
+                      "us_per_layer": round(ea / na * 1e6, 1), "layers": na,
+                      "threads": threads},
+        "host": {"cpu_model": cpu_model(), "nproc": os.cpu_count(), "affinity": share},
+    }
+
+
+def source_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in files:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(path):
+    """HBM bytes per launch of the dominant kernel from a profile summary
+    (lines `traffic_bytes_per_launch: N`, `source_files: F...` and
+    `source_sha256: H`), or None when absent or taken on other sources."""
+    try:
+        with open(path) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = {}
+    for ln in text.splitlines():
+        if ":" in ln:
+            k, v = ln.split(":", 1)
+            fields[k.strip().strip("-* `")] = v.strip().strip("`")
+    files = fields.get("source_files", "").split()
+    try:
+        if not files or fields.get("source_sha256") != source_digest(files):
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, mib):
+    """A plain device copy of a known size: the yardstick for HBM counters."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 10}), flush=True)
+
+
+def eager(torch, fn, steps, warmup):
+    """fn(i) launched one by one (counter passes)."""
+    for i in range(warmup):
+        fn(steps + i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1024, help="timed layers")
-    ap.add_argument("--warmup", type=int, default=128, help="untimed layers")
-    ap.add_argument("--group", type=int, default=64,
-                    help="layers captured per graph (a divisor of --steps)")
+    ap.add_argument("--steps", type=int, default=32, help="timed layers per headline round")
+    ap.add_argument("--warmup", type=int, default=16, help="untimed layers before the rounds")
+    ap.add_argument("--rounds", type=int, default=5, help="timed rounds per figure")
+    ap.add_argument("--replicas", type=int, default=16, help="weight replicas rotated")
+    ap.add_argument("--id-sets", type=int, default=128,
+                    help="routing draws rotated (warm-up draws are disjoint from the timed "
+                         "ones while steps + warmup <= id-sets)")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0, help="per CPU-baseline variant")
+    ap.add_argument("--only", default="", help="comma list of sections: m1,m16,sweep,cfg4,walk,"
+                                               "mlx4,cpu (default: all)")
     ap.add_argument("--eager", action="store_true",
-                    help="launch every kernel directly instead of through graphs")
+                    help="launch the headline and m16 kernels one by one, no graphs (counters)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter yardstick)")
-    ap.add_argument("--replicas", type=int, default=16, help="weight replicas rotated")
-    ap.add_argument("--id-sets", type=int, default=64, help="routing draws rotated")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-m16", action="store_true")
-    ap.add_argument("--no-walk", action="store_true")
-    ap.add_argument("--no-mlx4", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: every box here has one MI355X and this path has no "
-              f"multi-GPU mode (asked for --gpus {args.gpus}).", file=sys.stderr)
+        print(f"bench.py measures one GPU: this path has no multi-GPU mode and every box here "
+              f"has one MI355X (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+    want = set(s for s in args.only.split(",") if s) or \
+        {"m1", "m16", "sweep", "cfg4", "walk", "mlx4", "cpu"}
 
     import torch
 
@@ -506,108 +565,180 @@ def main():
         copy_calibration(torch, args.calibrate_copy)
         return
 
-    res1, stacks = run_workload(torch, q4, wl, wl.CFG2, args)
-    log(f"m=1: {res1['us_per_layer']:.2f} us/layer, {res1['gbs']:.1f} GB/s; gate/up "
-        f"{res1['gate_up_us']:.2f} us, {res1['gate_up_gbs']:.1f} GB/s; with the next "
-        f"layer's RMSNorm {res1['us_per_layer_rmsnorm']:.2f} us")
-    res16 = None
-    if not args.no_m16:
-        res16, _ = run_workload(torch, q4, wl, wl.CFG3, args, stacks)
-        log(f"m=16: {res16['us_per_layer']:.2f} us/layer, {res16['gbs']:.1f} GB/s; gate/up "
-            f"{res16['gate_up_us']:.2f} us, {res16['gate_up_gbs']:.1f} GB/s; with the next "
-            f"layer's RMSNorm {res16['us_per_layer_rmsnorm']:.2f} us")
-    walk_us = None
-    if not args.no_walk:
-        walk_us, walk_single_us, walk_bytes, walk_conc_us = run_walk(torch, q4, wl, 2, 32, 1)
-        log(f"walk: {walk_us:.2f} us/walk merged ({walk_bytes / walk_us / 1e3:.1f} GB/s), "
-            f"{walk_single_us:.2f} us one launch per tensor, {walk_conc_us:.2f} us concurrent "
-            f"groups")
-    mlx = None
-    if not args.no_mlx4:
-        mlx = run_mlx4(torch, q4, wl, 8, 64, 1)
-        log("mlx4: " + ", ".join(f"{k} {us:.2f} us ({b / us / 1e3:.1f} GB/s)"
-                                 for k, (us, b) in mlx.items()))
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, wl.CFG2, args.cpu_seconds)
-        log(f"cpu oracle: {cpu['value']} GB/s")
+    K, W, R = args.steps, args.warmup, args.rounds
+    t_start = time.perf_counter()
+    log(f"encoding {args.replicas} replicas of the hidden-2048 layer")
+    m1 = Moe(torch, q4, wl, wl.CFG2, args.replicas, args.id_sets)
+    line = {}
+    if args.eager:
+        for name, mo in (("m1", m1),
+                         ("m16", Moe(torch, q4, wl, wl.CFG3, 0, args.id_sets, m1.stacks,
+                                     m1.shared))):
+            for kern in (mo.layer, mo.gate_up, mo.down):
+                sec = eager(torch, kern, K, W)
+                log(f"{name} {kern.__name__}: {sec / K * 1e6:.2f} us per call (eager)")
+        return
 
-    cfg = wl.CFG2
-    line = {
+    # ---- headline: m = 1 layer, its gate/up launch, and the ceiling
+    timed = list(range(K))
+    warm = list(range(K, K + W)) if W else None
+    figs = {"m1": Figure(torch, "m1 layer", m1.layer, timed, m1.bytes_of(3), warm),
+            "m1_gu": Figure(torch, "m1 gate/up", m1.gate_up, range(64), m1.bytes_of(2)),
+            "m1_norm": Figure(torch, "m1 layer + rmsnorm", m1.layer_norm, range(64),
+                              m1.bytes_of(3)),
+            "m1_ceil": Figure(torch, "m1 ceiling", m1.ceiling([0, 1, 2]), range(64),
+                              m1.bytes_of(3)),
+            "m1_gu_ceil": Figure(torch, "m1 gate/up ceiling", m1.ceiling([0, 1]), range(64),
+                                 m1.bytes_of(2))}
+    m16 = None
+    if "m16" in want or "sweep" in want:
+        m16 = Moe(torch, q4, wl, wl.CFG3, 0, args.id_sets, m1.stacks, m1.shared)
+    if "m16" in want:
+        figs.update({
+            "m16": Figure(torch, "m16 layer", m16.layer, range(32), m16.bytes_of(3)),
+            "m16_norm": Figure(torch, "m16 layer + rmsnorm", m16.layer_norm, range(32),
+                               m16.bytes_of(3)),
+            "m16_gu": Figure(torch, "m16 gate/up", m16.gate_up, range(32), m16.bytes_of(2)),
+            "m16_down": Figure(torch, "m16 down", m16.down, range(32),
+                               lambda i: len(m16.unique[i % len(m16.sets)]) * m16.mat),
+            "m16_ceil": Figure(torch, "m16 ceiling", m16.ceiling([0, 1, 2]), range(32),
+                               m16.bytes_of(3)),
+            "m16_gu_ceil": Figure(torch, "m16 gate/up ceiling", m16.ceiling([0, 1]), range(32),
+                                  m16.bytes_of(2))})
+    sweep = {}
+    if "sweep" in want:
+        import dataclasses
+        flags = {"auto": q4.Q4K_BUCKET_AUTO, "token": q4.Q4K_BUCKET_OFF,
+                 "matrix_cores": q4.Q4K_BUCKET_ON,
+                 "vector_bucketed": q4.Q4K_BUCKET_ON | q4.Q4K_SCHED_VECTOR}
+        for m in (1, 2, 4, 8, 16):
+            cfg = wl.CFG2 if m == 1 else dataclasses.replace(
+                wl.CFG3, name=f"decode_m{m}_zipf", m=m)
+            mo = m1 if m == 1 else (m16 if m == 16 else
+                                    Moe(torch, q4, wl, cfg, 0, args.id_sets, m1.stacks, m1.shared))
+            for fname, fl in flags.items():
+                figs[f"sweep_{m}_{fname}"] = Figure(
+                    torch, f"m={m} {fname}", (lambda i, mo=mo, fl=fl: mo.layer(i, fl)),
+                    range(32), mo.bytes_of(3))
+            sweep[m] = mo
+    log(f"timing {len(figs)} figures, {R} rounds round-robin")
+    run_rounds(list(figs.values()), R)
+    S = {k: f.summary() for k, f in figs.items()}
+
+    hl = S["m1"]
+    gu, gu_ceil = S["m1_gu"], S["m1_gu_ceil"]
+    per_round = [s / K * 1e6 for s in figs["m1"].secs]
+    line.update({
         "metric": METRIC,
-        "value": round(res1["gbs"], 2),
+        "value": hl["gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": res1["steps"],
-        "warmup": res1["warmup"],
-        "ms_per_step": round(res1["us_per_layer"] / 1e3, 6),
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(hl["us"] / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "single-token MoE FFN decode layer: hidden 2048, expert intermediate 768, "
-                        "128 experts, top_k 8, m=1, Q4_K weights N(0,0.02^2), sigmoid-gated "
-                        "shared expert, weighted residual combine",
-            "hidden": cfg.hidden, "inter": cfg.inter, "experts": cfg.num_experts,
-            "top_k": cfg.top_k, "m": cfg.m, "weight_replicas": args.replicas,
-            "id_sets": args.id_sets, "launch": res1["mode"],
-            "bytes_per_layer": int(res1["bytes_per_layer"]),
+            "workload": "single-token MoE FFN decode layer: hidden 2048, expert intermediate "
+                        "768, 128 experts, top_k 8, m=1, Q4_K weights N(0,0.02^2), "
+                        "sigmoid-gated shared expert, weighted residual combine",
+            "hidden": 2048, "inter": 768, "experts": 128, "top_k": 8, "m": 1,
+            "weight_replicas": args.replicas, "id_sets": args.id_sets,
+            "launch": f"HIP graph of {K} layers per round, {R} rounds",
+            "bytes_per_layer": hl["bytes_per_step"],
         },
-        "us_per_layer": round(res1["us_per_layer"], 3),
-        "us_per_layer_with_next_rmsnorm": round(res1["us_per_layer_rmsnorm"], 3),
-        "frac_hbm_peak": round(res1["gbs"] / HBM_PEAK_GBS, 4),
+        "us_per_layer": hl["us"], "us_per_layer_q1": hl["us_q1"],
+        "us_per_layer_q3": hl["us_q3"],
+        "us_per_layer_rounds": [round(x, 3) for x in per_round],
+        "frac_hbm_peak": hl["frac_hbm_peak"],
+        "ceiling_gbs": S["m1_ceil"]["gbs"],
+        "us_per_layer_with_next_rmsnorm": S["m1_norm"]["us"],
         "roofline": {
             "bound": "hbm",
             "kernel": "fused gate/up id-GEMV + SiLU (routed + shared experts)",
-            "achieved": round(res1["gate_up_gbs"], 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(res1["gate_up_gbs"] / HBM_PEAK_GBS, 4),
+            "achieved": gu["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gu["gbs"] / HBM_PEAK_GBS, 4),
             "traffic": stored_traffic(TRAFFIC_PROFILE),
-            "us_per_launch": round(res1["gate_up_us"], 3),
-            "bytes_per_launch": int(res1["gate_up_bytes"]),
+            "us_per_launch": gu["us"], "us_q1": gu["us_q1"], "us_q3": gu["us_q3"],
+            "bytes_per_launch": gu["bytes_per_step"],
+            "ceiling": gu_ceil["gbs"],
+            "frac_of_ceiling": round(gu["gbs"] / gu_ceil["gbs"], 4),
         },
-        "cpu_baseline": cpu,
-    }
-    if res16 is not None:
+    })
+    if "m16" in want:
+        L, G, D = S["m16"], S["m16_gu"], S["m16_down"]
         line["m16"] = {
             "workload": "same layer, m=16 tokens, Zipf(1.1) routing, bucketed",
-            "value": round(res16["gbs"], 2), "unit": "GB/s",
-            "us_per_layer": round(res16["us_per_layer"], 3),
-            "us_per_layer_with_next_rmsnorm": round(res16["us_per_layer_rmsnorm"], 3),
-            "frac_hbm_peak": round(res16["gbs"] / HBM_PEAK_GBS, 4),
-            "bytes_per_layer": int(res16["bytes_per_layer"]),
-            "gate_up_gbs": round(res16["gate_up_gbs"], 2),
-            "gate_up_us": round(res16["gate_up_us"], 3),
+            "value": L["gbs"], "unit": "GB/s", "us_per_layer": L["us"],
+            "us_q1": L["us_q1"], "us_q3": L["us_q3"], "frac_hbm_peak": L["frac_hbm_peak"],
+            "bytes_per_layer": L["bytes_per_step"], "ceiling_gbs": S["m16_ceil"]["gbs"],
+            "us_per_layer_with_next_rmsnorm": S["m16_norm"]["us"],
+            "roofline": {"bound": "hbm", "kernel": "bucketed gate/up + SiLU (matrix cores, "
+                                                   "pre-built buckets)",
+                         "achieved": G["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(G["gbs"] / HBM_PEAK_GBS, 4), "us_per_launch": G["us"],
+                         "bytes_per_launch": G["bytes_per_step"],
+                         "ceiling": S["m16_gu_ceil"]["gbs"],
+                         "frac_of_ceiling": round(G["gbs"] / S["m16_gu_ceil"]["gbs"], 4)},
+            "down": {"us_per_launch": D["us"], "gbs": D["gbs"],
+                     "bytes_per_launch": D["bytes_per_step"]},
         }
-    if mlx is not None:
-        line["mlx4"] = {
-            "workload": "MLX affine 4-bit experts (bf16 scale and bias per 64 weights), 128 "
-                        "experts, top_k 8, m=1: fused gate/up + SiLU over 768x2048 gate and up "
-                        "matrices, the down-shaped 2048x768 id-GEMV, and the same in the 2-bit "
-                        "variant; 8 replicas rotated",
-            "kernel": "k_mlx4_rows",
+    if sweep:
+        t1 = S["sweep_1_auto"]["us"]
+        rows = {}
+        for m in sweep:
+            rows[str(m)] = {f: {"us": S[f"sweep_{m}_{f}"]["us"], "gbs": S[f"sweep_{m}_{f}"]["gbs"]}
+                            for f in ("auto", "token", "matrix_cores", "vector_bucketed")}
+            rows[str(m)]["scaling_vs_m1"] = round(S[f"sweep_{m}_auto"]["us"] / t1, 3)
+        t16 = S["sweep_16_auto"]["us"]
+        line["sweep"] = {
+            "workload": "the hidden-2048 layer at m tokens (m=1: uniform distinct ids; m>1: "
+                        "Zipf(1.1)), us per layer and unique-byte GB/s per schedule",
+            "m": rows, "auto_bucket_min_tokens": q4.Q4K_AUTO_BUCKET_MIN_TOKENS,
+            "batches_well": {"m16_us": t16, "bound_us": round(0.6 * 16 * t1, 3),
+                             "ok": t16 < 0.6 * 16 * t1},
         }
-        for k, (us, b) in mlx.items():
-            line["mlx4"][k] = {"us_per_launch": round(us, 3), "bytes_per_launch": int(b),
-                               "gbs": round(b / us / 1e3, 2),
-                               "frac_hbm_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
-    if walk_us is not None:
-        line["walk"] = {
-            "workload": "dense Q4TiledP decode walk: one layer (q, k, v, o 4096x4096, gate and up "
-                        "14336x4096, down 4096x14336) and the head 32000x4096, 5-bit log-scale "
-                        "ladder, 2 tensor replicas rotated",
-            "kernel": "k_q4tp_matvec",
-            "launches": "q|k|v, o, gate|up, down, head (merged dispatches)",
-            "us_per_walk": round(walk_us, 3),
-            "us_per_walk_one_launch_per_tensor": round(walk_single_us, 3),
-            "us_per_walk_concurrent_groups": round(walk_conc_us, 3),
-            "bytes_per_walk": int(walk_bytes),
-            "gbs": round(walk_bytes / walk_us / 1e3, 2),
-            "frac_hbm_peak": round(walk_bytes / walk_us / 1e3 / HBM_PEAK_GBS, 4),
-        }
+    del figs
+    torch.cuda.empty_cache()
+
+    if "cfg4" in want:
+        log("cfg4: encoding one 6.3 GB layer (256 experts, hidden 7168, inter 2048)")
+        c4 = {}
+        big = Moe(torch, q4, wl, wl.CFG4_M1, 1, 32, shared_replicas=8)
+        big32 = Moe(torch, q4, wl, wl.CFG4_M32, 0, 8, big.stacks, big.shared)
+        f4 = {"m1": Figure(torch, "cfg4 m1", big.layer, range(32), big.bytes_of(3)),
+              "m1_ceil": Figure(torch, "cfg4 m1 ceiling", big.ceiling([0, 1, 2]), range(32),
+                                big.bytes_of(3)),
+              "m32": Figure(torch, "cfg4 m32", big32.layer, range(8), big32.bytes_of(3)),
+              "m32_ceil": Figure(torch, "cfg4 m32 ceiling", big32.ceiling([0, 1, 2]), range(8),
+                                 big32.bytes_of(3))}
+        run_rounds(list(f4.values()), R)
+        for k in ("m1", "m32"):
+            s, c = f4[k].summary(), f4[k + "_ceil"].summary()
+            c4[k] = {"us_per_layer": s["us"], "us_q1": s["us_q1"], "us_q3": s["us_q3"],
+                     "gbs": s["gbs"], "frac_hbm_peak": s["frac_hbm_peak"],
+                     "bytes_per_layer": s["bytes_per_step"], "ceiling_gbs": c["gbs"]}
+        c4["workload"] = ("large-expert layer: hidden 7168, inter 2048, 256 experts, top_k 8, "
+                          "unscaled shared expert (8 replicas); m=1 over 32 uniform draws of "
+                          "distinct experts (a graph reads ~4 GB), m=32 over 8 draws")
+        line["cfg4"] = c4
+        del f4, big, big32
+        torch.cuda.empty_cache()
+    if "walk" in want:
+        log("walk: encoding 8 layers + head, 2 replicas")
+        line["walk"] = section_walk(torch, q4, wl, 8, R)
+        torch.cuda.empty_cache()
+    if "mlx4" in want:
+        line["mlx4"] = section_mlx4(torch, q4, wl, R)
+    if "cpu" in want:
+        log("cpu oracle baseline")
+        line["cpu_baseline"] = cpu_baseline(wl, wl.CFG2, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    log(f"done in {time.perf_counter() - t_start:.0f} s")
     print(json.dumps(line), flush=True)
 
 

@@ -15,5 +15,5 @@ from ._lib import (  # noqa: F401
     q4k_quantize, q4tp_matvec, q4tp_matvec_multi, q4tp_quantize, q4tp_tensor_bytes, status_string,
     MLX4_GROUP, mlx4_dequantize, mlx4_matrix_bytes, mlx4_moe_gate_up_silu, mlx4_moe_id_gemv,
     mlx4_quantize, moe_combine_residual_rmsnorm, moe_layer_forward_rmsnorm, mlx2_dequantize,
-    mlx2_matrix_bytes, mlx2_moe_id_gemv, mlx2_quantize,
+    mlx2_matrix_bytes, mlx2_moe_id_gemv, mlx2_quantize, q4k_ceiling_read,
 )

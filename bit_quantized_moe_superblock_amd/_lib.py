@@ -68,6 +68,8 @@ SIGNATURES = {
     "mlx2_quantize": (_I, [_P, _P, _P, _P, _I64, _I64, _P]),
     "mlx2_moe_id_gemv": (_I, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _I64, _I64,
                               _I64, _I64, _I64, _P]),
+    # include/q4kceil.h (measurement)
+    "q4k_ceiling_read": (_I, [_P, _P, _I64, _I64, _P, _P]),
 }
 
 
@@ -308,3 +310,12 @@ def mlx2_moe_id_gemv(expert_base, expert_stride: int, packed_off: int, scales_of
     _call("mlx2_moe_id_gemv", _ptr(expert_base), expert_stride, packed_off, scales_off,
           biases_off, _ptr(src1), _ptr(ids), _ptr(dst), n, k, m, top_k, src1_outer_stride,
           src1_inner_stride, num_experts, _stream(stream))
+
+
+def q4k_ceiling_read(base, offsets, n_ranges: int, range_bytes: int, sink, stream=None):
+    """Measurement only (include/q4kceil.h): read n_ranges ranges of
+    range_bytes bytes at base + offsets[i] (offsets: a device int64 tensor)."""
+    rc = load().q4k_ceiling_read(_ptr(base), _ptr(offsets), n_ranges, range_bytes, _ptr(sink),
+                                 _stream(stream))
+    if rc != 0:
+        raise RuntimeError(f"q4k_ceiling_read: status {rc}")

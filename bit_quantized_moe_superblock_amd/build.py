@@ -15,7 +15,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libq4kmoe.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 SOURCES = ["api.hip", "q4k_gemv.hip", "q4k_mfma.hip", "q4k_codec.hip", "moe_aux.hip",
-           "q4tp.hip", "mlx4.hip"]
+           "q4tp.hip", "mlx4.hip", "ceiling.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-mllvm", "-amdgpu-mfma-vgpr-form=1",

@@ -113,8 +113,11 @@ struct StageBatch {
     int f;
 };
 
-template <typename XOf>
-__device__ __forceinline__ void stage_issue(XOf x_of, int base, int total, int k, bool vec,
+// VEC: rows and strides are 16-byte aligned (float4 loads); otherwise 4-byte
+// loads.  A compile-time choice: with the choice made at run time the compiler
+// merges both sides into the 4-byte loads.
+template <bool VEC, typename XOf>
+__device__ __forceinline__ void stage_issue(XOf x_of, int base, int total, int k,
                                             StageBatch &b) {
     const int nsub = k >> 5;
     b.f = base + (int)threadIdx.x;
@@ -125,7 +128,7 @@ __device__ __forceinline__ void stage_issue(XOf x_of, int base, int total, int k
     const int f = b.f < total ? b.f : total - 1;
     const int row = f / nsub, j = f - row * nsub;
     const float *src = x_of(row) + 32 * j;
-    if (vec) {   // uniform
+    if constexpr (VEC) {
 #pragma unroll
         for (int q = 0; q < 8; q++)
             b.v[q] = *(const float4 *)(src + 4 * q);
@@ -157,13 +160,12 @@ __device__ __forceinline__ void stage_commit(const StageBatch &b, int total, int
 
 // Stage rows [0, cl) starting at flattened sub-block `from` (batches of 256).
 // No barrier.
-template <typename XOf>
-__device__ __forceinline__ void stage_rows(XOf x_of, int cl, int k, bool vec, float *lds,
-                                           int from = 0) {
+template <bool VEC, typename XOf>
+__device__ __forceinline__ void stage_rows(XOf x_of, int cl, int k, float *lds, int from = 0) {
     const int total = cl * (k >> 5);
     for (int base = from; base < total; base += kThreads) {
         StageBatch b;
-        stage_issue(x_of, base, total, k, vec, b);
+        stage_issue<VEC>(x_of, base, total, k, b);
         stage_commit(b, total, k, lds);
     }
 }

@@ -113,7 +113,7 @@ __device__ __forceinline__ float group_qx2(const uint4 qa, const float *xr) {
     return acc * 16777216.0f;
 }
 
-template <int LPR, int NT, int BITS>
+template <int LPR, int NT, int BITS, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_mlx4_rows(Mlx4Args a) {
     extern __shared__ float lds[];
     asm volatile("" ::"s"(a.base), "s"(a.stride), "s"(a.packed_off), "s"(a.scales_off),
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void k_mlx4_rows(Mlx4Args a) {
     // 1. the first staging batch ahead of the weights (waiting for it leaves
     //    the weights in flight)
     StageBatch xb;
-    stage_issue(x_of, 0, total, a.k, a.vec, xb);
+    stage_issue<VEC>(x_of, 0, total, a.k, xb);
     // 2. the lane's group: clamped addresses, no branch
     const int e = a.ids[q];
     const bool valid = (unsigned)e < (unsigned)a.num_experts;
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void k_mlx4_rows(Mlx4Args a) {
     }
     // 3. the staged row (and any further batches)
     stage_commit(xb, total, a.k, lds);
-    stage_rows(x_of, 1, a.k, a.vec, lds, kThreads);
+    stage_rows<VEC>(x_of, 1, a.k, lds, kThreads);
     lds_barrier();
     // 4. the group's share, then the row sums
     const float *sx = lds + xpad_len(a.k);
@@ -261,11 +261,14 @@ __global__ __launch_bounds__(256) void k_mlx4_quant(const float *__restrict__ w,
 template <int LPR, int NT, int BITS>
 static hipError_t go_mlx4(const Mlx4Args &a, int64_t n_pairs, hipStream_t st) {
     constexpr int RPI = kThreads / LPR;
-    auto kern = k_mlx4_rows<LPR, NT, BITS>;
-    const size_t lds = set_lds((const void *)kern, ((size_t)row_lds_floats(a.k) + 8) * sizeof(float));
     dim3 grid((a.n + RPI - 1) / RPI, (unsigned)n_pairs);
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a);
-    return hipGetLastError();
+    auto go = [&](auto kern) {
+        const size_t lds =
+            set_lds((const void *)kern, ((size_t)row_lds_floats(a.k) + 8) * sizeof(float));
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a);
+        return hipGetLastError();
+    };
+    return a.vec ? go(k_mlx4_rows<LPR, NT, BITS, true>) : go(k_mlx4_rows<LPR, NT, BITS, false>);
 }
 
 static bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -50,7 +50,7 @@ namespace q4k {
 // per 32-float sub-block, loads issued ahead of the weights, committed with
 // its sub-block sum) and every lane reads its unit's 64 activations from
 // there.
-template <int LPR, int NT, int ITERS, int EPI>
+template <int LPR, int NT, int ITERS, int EPI, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_rows(GemvArgs a) {
     extern __shared__ float lds[];
     fetch_args(a);
@@ -73,12 +73,12 @@ __global__ __launch_bounds__(kThreads) void k_rows(GemvArgs a) {
     const int nsub = a.k >> 5;
     auto x_of = [&](int) { return pr.x; };
     StageBatch xb;
-    stage_issue(x_of, 0, nsub, a.k, a.vec != 0, xb);
+    stage_issue<VEC>(x_of, 0, nsub, a.k, xb);
     __builtin_amdgcn_sched_barrier(0);   // keep them ahead of the weights
     Tile<NT, ITERS> t;
     load_rows<LPR, NT, ITERS>(pr.w0, pr.w1, a.n, a.k, row0, true, t);
     stage_commit(xb, nsub, a.k, xs);
-    stage_rows(x_of, 1, a.k, a.vec != 0, xs, kThreads);   // k > 8192
+    stage_rows<VEC>(x_of, 1, a.k, xs, kThreads);   // k > 8192
     lds_barrier();
 #pragma unroll
     for (int it = 0; it < ITERS; it++) {
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void k_rows(GemvArgs a) {
 // rows are staged in LDS (pc at a time); each lane keeps its ITERS x NT weight
 // units in registers and reads every activation float once per pair for all of
 // them.  Chunks past the routed ones carry the shared expert (all tokens).
-template <int LPR, int NT, int ITERS, int EPI>
+template <int LPR, int NT, int ITERS, int EPI, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_bucket(GemvArgs a) {
     extern __shared__ float lds[];
     fetch_args(a);
@@ -156,11 +156,11 @@ __global__ __launch_bounds__(kThreads) void k_bucket(GemvArgs a) {
     auto xq = [&](int i) { return pair_x_known(a, shared, pair_of(i)); };
     const int total = first * (a.k >> 5);
     StageBatch sb;
-    stage_issue(xq, 0, total, a.k, a.vec, sb);
+    stage_issue<VEC>(xq, 0, total, a.k, sb);
     Tile<NT, ITERS> t;
     load_rows<LPR, NT, ITERS>(w0, w1, a.n, a.k, row0, true, t);
     stage_commit(sb, total, a.k, lds);
-    stage_rows(xq, first, a.k, a.vec, lds, kThreads);
+    stage_rows<VEC>(xq, first, a.k, lds, kThreads);
     const int u = tid % LPR, rsub = tid / LPR, c = u & 3;
     const bool active = u < 4 * (a.k >> 8);
     UnitScale sc[ITERS][NT];
@@ -173,8 +173,8 @@ __global__ __launch_bounds__(kThreads) void k_bucket(GemvArgs a) {
         const int cl = cnt - c0 < a.pc ? cnt - c0 : a.pc;
         if (c0 > 0) {
             __syncthreads();   // the previous pass is consumed
-            stage_rows([&](int i) { return pair_x_known(a, shared, pair_of(c0 + i)); }, cl, a.k,
-                       a.vec, lds);
+            stage_rows<VEC>([&](int i) { return pair_x_known(a, shared, pair_of(c0 + i)); }, cl,
+                            a.k, lds);
         }
         __syncthreads();
         for (int i = 0; i < cl; i++) {
@@ -240,7 +240,7 @@ struct CombineArgs {
     int shared_mode;
 };
 
-template <int LPR, int ITERS>
+template <int LPR, int ITERS, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineArgs cb, int trt) {
     extern __shared__ float lds[];
     fetch_args(a);
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineAr
     const int nsub = a.k >> 5;
     const int total = np * nsub;
     StageBatch xb;
-    stage_issue(x_of, 0, total, a.k, a.vec != 0, xb);
+    stage_issue<VEC>(x_of, 0, total, a.k, xb);
     if (tid < K) {
         ex_lds[tid] = (unsigned)e_own < (unsigned)a.num_experts ? e_own : -1;
         rw_lds[tid] = rw_own;
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(GemvArgs a, CombineAr
     // 4. activation rows of the token's pairs into LDS (first batch, then any
     //    further ones)
     stage_commit(xb, total, a.k, lds);
-    stage_rows(x_of, np, a.k, a.vec != 0, lds, kThreads);
+    stage_rows<VEC>(x_of, np, a.k, lds, kThreads);
     lds_barrier();
 #pragma unroll
     for (int it = 0; it < ITERS; it++) {
@@ -412,11 +412,13 @@ template <int LPR, int NT, int EPI, int IT>
 static hipError_t go_rows(const GemvArgs &a, hipStream_t st) {
     constexpr int RPI = kThreads / LPR;
     dim3 grid((a.n + IT * RPI - 1) / (IT * RPI), a.n_pairs + a.m_sh);
-    auto kern = k_rows<LPR, NT, IT, EPI>;
-    const size_t lds =
-        set_lds((const void *)kern, (16 + (size_t)row_lds_floats(a.k)) * sizeof(float));
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a);
-    return hipGetLastError();
+    auto go = [&](auto kern) {
+        const size_t lds =
+            set_lds((const void *)kern, (16 + (size_t)row_lds_floats(a.k)) * sizeof(float));
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a);
+        return hipGetLastError();
+    };
+    return a.vec ? go(k_rows<LPR, NT, IT, EPI, true>) : go(k_rows<LPR, NT, IT, EPI, false>);
 }
 
 // LDS budget of the vector-unit bucketed kernel's staged activation rows.
@@ -431,12 +433,14 @@ static hipError_t launch_lpr(GemvArgs a, bool bucketed, hipStream_t st) {
         int pc = (int)((kBucketLdsBytes / 4 - 8) / rl);
         pc = pc < 1 ? 1 : (pc > kBucketChunk ? kBucketChunk : pc);
         a.pc = pc;
-        auto kern = k_bucket<LPR, NT, IT, EPI>;
-        const size_t lds = set_lds((const void *)kern, ((size_t)pc * rl + 8) * sizeof(float));
         const int shared_chunks = (a.m_sh + kBucketChunk - 1) / kBucketChunk;
         dim3 grid((a.n + IT * RPI - 1) / (IT * RPI), a.n_pairs + shared_chunks);
-        hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a);
-        return hipGetLastError();
+        auto go = [&](auto kern) {
+            const size_t lds = set_lds((const void *)kern, ((size_t)pc * rl + 8) * sizeof(float));
+            hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a);
+            return hipGetLastError();
+        };
+        return a.vec ? go(k_bucket<LPR, NT, IT, EPI, true>) : go(k_bucket<LPR, NT, IT, EPI, false>);
     }
     const int max_it = NT == 2 ? 4 : 8;
     switch (pick_iters_staged(a.n_pairs + a.m_sh, a.n, RPI, max_it, a.k, NT)) {
@@ -520,12 +524,14 @@ bool q4k_down_combine_ok(int64_t k, int64_t top_k, bool shared) {
 
 template <int LPR, int IT>
 static hipError_t go_dc(const GemvArgs &a, const CombineArgs &cb, int trt, hipStream_t st) {
-    auto kern = k_down_combine<LPR, IT>;
     const int np = a.top_k + (a.m_sh > 0 ? 1 : 0);
-    const size_t lds = set_lds((const void *)kern, dc_lds_bytes(a.k, np, trt));
     dim3 grid((a.n + trt - 1) / trt, (int)(a.n_pairs / a.top_k));
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a, cb, trt);
-    return hipGetLastError();
+    auto go = [&](auto kern) {
+        const size_t lds = set_lds((const void *)kern, dc_lds_bytes(a.k, np, trt));
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, a, cb, trt);
+        return hipGetLastError();
+    };
+    return a.vec ? go(k_down_combine<LPR, IT, true>) : go(k_down_combine<LPR, IT, false>);
 }
 
 template <int LPR>

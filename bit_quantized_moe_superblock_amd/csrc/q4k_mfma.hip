@@ -93,11 +93,11 @@ struct XRegs {
     float4 v[U][8];
 };
 
-// vec: the rows and strides are 16-byte aligned (float4 loads); otherwise
-// four 4-byte loads per float4 (uniform choice).
-template <int SB>
+// VEC: the rows and strides are 16-byte aligned (float4 loads); otherwise
+// four 4-byte loads per float4.
+template <int SB, bool VEC>
 __device__ __forceinline__ void mfma_x_issue(const float *const (&xrow)[XRegs<SB>::U], int cnt,
-                                             int j0, int nsub_total, bool vec, XRegs<SB> &xr) {
+                                             int j0, int nsub_total, XRegs<SB> &xr) {
     constexpr int nsub = SB * 8;
 #pragma unroll
     for (int u = 0; u < XRegs<SB>::U; u++) {
@@ -105,7 +105,7 @@ __device__ __forceinline__ void mfma_x_issue(const float *const (&xrow)[XRegs<SB
         const int jl = task % nsub;
         const bool ok = task < cnt * nsub && j0 + jl < nsub_total;
         const float *src = xrow[u] + 32 * (ok ? j0 + jl : 0);   // clamped
-        if (vec) {
+        if constexpr (VEC) {
 #pragma unroll
             for (int q = 0; q < 8; q++)
                 xr.v[u][q] = *(const float4 *)(src + 4 * q);
@@ -319,7 +319,7 @@ __device__ __forceinline__ void mfma_superblock(const MfmaTile (&t)[NT], const u
 // is the shared expert's tokens first .. first + cnt - 1.  The first slab
 // starts with a barrier, so consecutive items of one workgroup may reuse the
 // LDS.
-template <int NT, int EPI, int SB>
+template <int NT, int EPI, int SB, bool VEC>
 __device__ __forceinline__ void mfma_item(const GemvArgs &a, bool shared, int bkt, int cnt,
                                           const int32_t *pairs, int first, int row0,
                                           uint8_t *lds_b) {
@@ -381,7 +381,7 @@ __device__ __forceinline__ void mfma_item(const GemvArgs &a, bool shared, int bk
                 mfma_load(wrow[nt], sb, g, tt[i % kDepth][nt]);
         };
         XRegs<SB> xr;
-        mfma_x_issue<SB>(xrow, gc, sb0 * 8, nsub_total, a.vec != 0, xr);
+        mfma_x_issue<SB, VEC>(xrow, gc, sb0 * 8, nsub_total, xr);
         // the activations ahead of the weights: staging waits on them alone
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -476,7 +476,7 @@ __device__ __forceinline__ int chunk_pack(int b, int i, int c) { return b | (i <
 // items w, w + G, ...  With a bucket workspace the chunk list and pair lists
 // come from it (the bucketing kernel's output); without one the workgroup
 // builds them (self-bucketing).
-template <int NT, int EPI, int SB>
+template <int NT, int EPI, int SB, bool VEC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SB <= 4 ? 3 : 2)))
 void k_bucket_mfma(GemvArgs a, int tiles) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_b[];
@@ -569,20 +569,20 @@ void k_bucket_mfma(GemvArgs a, int tiles) {
                 }
             lds_barrier();
         }
-        mfma_item<NT, EPI, SB>(a, shared, bkt, cnt, pl, first, x * item_rows(EPI), lds_b);
+        mfma_item<NT, EPI, SB, VEC>(a, shared, bkt, cnt, pl, first, x * item_rows(EPI), lds_b);
     }
 }
 
 // ------------------------------------------------------------------ host ---
 
-template <int NT, int EPI, int SB>
+template <int NT, int EPI, int SB, bool VEC>
 static hipError_t go_mfma(const GemvArgs &a, hipStream_t st) {
     // chunks of the list: at most one partial chunk per non-empty bucket
     const int64_t nb_max = a.n_pairs < (int64_t)a.num_experts + 1 ? a.n_pairs : a.num_experts + 1;
     const int n_slots = (int)(nb_max + a.n_pairs / kMP);
     const int sh_groups = (a.m_sh + kMP - 1) / kMP;
     const int tiles = (a.n + item_rows(EPI) - 1) / item_rows(EPI);
-    auto kern = k_bucket_mfma<NT, EPI, SB>;
+    auto kern = k_bucket_mfma<NT, EPI, SB, VEC>;
     const size_t lds = set_lds((const void *)kern, mfma_lds_bytes(SB));
     // resident workgroups per CU: a property of the kernel and its fixed LDS
     // size, asked once per instantiation
@@ -606,13 +606,13 @@ static hipError_t go_mfma(const GemvArgs &a, hipStream_t st) {
 // Superblocks per staged activation slab: 4 (three workgroups per CU fit
 // beside a 33 KB slab; with two superblocks of weights in flight this beat
 // whole-row slabs of 8 at two per CU), fewer when the row is shorter.
-template <int NT, int EPI>
+template <int NT, int EPI, bool VEC>
 static hipError_t mfma_sb(const GemvArgs &a, hipStream_t st) {
     switch (a.k >> 8) {
-    case 1: return go_mfma<NT, EPI, 1>(a, st);
-    case 2: return go_mfma<NT, EPI, 2>(a, st);
-    case 3: return go_mfma<NT, EPI, 3>(a, st);
-    default: return go_mfma<NT, EPI, 4>(a, st);
+    case 1: return go_mfma<NT, EPI, 1, VEC>(a, st);
+    case 2: return go_mfma<NT, EPI, 2, VEC>(a, st);
+    case 3: return go_mfma<NT, EPI, 3, VEC>(a, st);
+    default: return go_mfma<NT, EPI, 4, VEC>(a, st);
     }
 }
 
@@ -620,8 +620,8 @@ static hipError_t mfma_sb(const GemvArgs &a, hipStream_t st) {
 // groups of it (row pair).
 hipError_t launch_q4k_gemv_mfma(const GemvArgs &a, bool fused_swiglu, hipStream_t st) {
     if (fused_swiglu)
-        return mfma_sb<2, EPI_SWIGLU>(a, st);
-    return mfma_sb<2, kEpiRowPair>(a, st);
+        return a.vec ? mfma_sb<2, EPI_SWIGLU, true>(a, st) : mfma_sb<2, EPI_SWIGLU, false>(a, st);
+    return a.vec ? mfma_sb<2, kEpiRowPair, true>(a, st) : mfma_sb<2, kEpiRowPair, false>(a, st);
 }
 
 }  // namespace q4k
