@@ -144,7 +144,7 @@ class Moe:
         self.torch, self.q4, self.cfg = torch, q4, cfg
         dev = torch.device("cuda")
         H, I, E = cfg.hidden, cfg.inter, cfg.num_experts
-        self.mat = q4.q4k_matrix_bytes(I, H)          # gate/up and down matrices alike
+        self.mat = q4.q4k_tiles_bytes(I, H)           # gate/up and down matrices alike
         if stacks is None:
             stacks = [[self._encode(wl, E, rows, cols, cfg.w_std, 1000 * r + t)
                        for t, (rows, cols) in enumerate([(I, H), (I, H), (H, I)])]
@@ -184,16 +184,19 @@ class Moe:
         torch.cuda.synchronize()
 
     def _encode(self, wl, n_exp, rows, cols, std, seed):
+        """n_exp experts of rows x cols: N(0, std^2) on the device, Q4_K
+        encoded, then packed into the tile layout the GEMV kernels read."""
         torch, q4 = self.torch, self.q4
-        b = torch.empty(n_exp * q4.q4k_matrix_bytes(rows, cols), dtype=torch.uint8,
-                        device="cuda")
+        mb, tb = q4.q4k_matrix_bytes(rows, cols), q4.q4k_tiles_bytes(rows, cols)
+        b = torch.empty(n_exp * tb, dtype=torch.uint8, device="cuda")
         per = max(1, (1 << 28) // (rows * cols * 4))     # experts per encoding batch (<= 256 MB fp32)
-        mb = q4.q4k_matrix_bytes(rows, cols)
         for e0 in range(0, n_exp, per):
             ne = min(per, n_exp - e0)
             w = wl.device_normal((ne * rows, cols), std, seed=seed * 4099 + e0)
-            q4.q4k_quantize(w, b[e0 * mb:(e0 + ne) * mb], ne * rows, cols)
-            del w
+            gguf = torch.empty(ne * mb, dtype=torch.uint8, device="cuda")
+            q4.q4k_quantize(w, gguf, ne * rows, cols)
+            q4.q4k_pack_tiles(gguf, b[e0 * tb:(e0 + ne) * tb], ne, rows, cols)
+            del w, gguf
         return b
 
     def pick(self, i):

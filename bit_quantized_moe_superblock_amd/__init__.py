@@ -10,7 +10,7 @@ from ._lib import (  # noqa: F401
     MOE_SHARED_NONE, MOE_SHARED_SIGMOID, MOE_SHARED_UNSCALED, Q4K_BUCKET_AUTO, Q4K_BUCKET_OFF,
     Q4K_BUCKET_ON, Q4K_BUCKET_PREBUILT, Q4K_BUCKET_MODE_MASK, Q4K_SCHED_VECTOR,
     Q4K_SCHED_BUCKET_LAUNCH, Q4K_AUTO_BUCKET_MIN_TOKENS, MOE_LAYER_NOALLOC_MAX_BYTES, Q4KError, moe_bucket, moe_bucket_workspace_bytes, moe_combine_residual,
-    moe_expert_ffn, moe_layer_forward, moe_layer_forward_noalloc, moe_layer_workspace_bytes, q4k_abi_version, q4k_dequantize, q4k_matrix_bytes, q4k_moe_id_gemv,
+    moe_expert_ffn, moe_layer_forward, moe_layer_forward_noalloc, moe_layer_workspace_bytes, q4k_abi_version, q4k_dequantize, q4k_matrix_bytes, q4k_tiles_bytes, q4k_pack_tiles, q4k_unpack_tiles, q4k_moe_id_gemv,
     q4k_moe_gate_up_silu,
     q4k_quantize, q4tp_matvec, q4tp_matvec_multi, q4tp_quantize, q4tp_tensor_bytes, status_string,
     MLX4_GROUP, mlx4_dequantize, mlx4_matrix_bytes, mlx4_moe_gate_up_silu, mlx4_moe_id_gemv,

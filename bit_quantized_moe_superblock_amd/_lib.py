@@ -33,6 +33,9 @@ SIGNATURES = {
     "q4k_matrix_bytes": (_I64, [_I64, _I64]),
     "q4k_dequantize": (_I, [_P, _P, _I64, _P]),
     "q4k_quantize": (_I, [_P, _P, _I64, _I64, _P]),
+    "q4k_tiles_bytes": (_I64, [_I64, _I64]),
+    "q4k_pack_tiles": (_I, [_P, _P, _I64, _I64, _I64, _P]),
+    "q4k_unpack_tiles": (_I, [_P, _P, _I64, _I64, _I64, _P]),
     "moe_bucket_workspace_bytes": (_I64, [_I64, _I64]),
     "moe_bucket": (_I, [_P, _I64, _I64, _P, _I64, _P]),
     "q4k_moe_id_gemv": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _I, _P,
@@ -142,6 +145,18 @@ def q4k_matrix_bytes(n: int, k: int) -> int:
 
 def q4tp_tensor_bytes(rows: int, cols: int) -> int:
     return load().q4tp_tensor_bytes(rows, cols)
+
+
+def q4k_tiles_bytes(n: int, k: int) -> int:
+    return load().q4k_tiles_bytes(n, k)
+
+
+def q4k_pack_tiles(blocks, tiles, n_mats: int, n: int, k: int, stream=None):
+    _call("q4k_pack_tiles", _ptr(blocks), _ptr(tiles), n_mats, n, k, _stream(stream))
+
+
+def q4k_unpack_tiles(tiles, blocks, n_mats: int, n: int, k: int, stream=None):
+    _call("q4k_unpack_tiles", _ptr(tiles), _ptr(blocks), n_mats, n, k, _stream(stream))
 
 
 def moe_bucket_workspace_bytes(n_pairs: int, num_experts: int) -> int:

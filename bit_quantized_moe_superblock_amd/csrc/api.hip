@@ -7,6 +7,7 @@
 #include <mutex>
 
 #include "q4kmoe.h"
+#include "common.hpp"
 #include "launch.hpp"
 
 using namespace q4k;
@@ -115,6 +116,41 @@ int q4k_quantize(const float *w, void *blocks, int64_t n_rows, int64_t k, void *
         return Q4K_ERR_NULL;
     return launched(launch_q4k_quant(w, blocks, n_rows * (k / Q4K_BLOCK_WEIGHTS),
                                      as_stream(stream)));
+}
+
+int64_t q4k_tiles_bytes(int64_t n, int64_t k) {
+    if (n < 0 || k <= 0 || k % Q4K_BLOCK_WEIGHTS)
+        return -1;
+    return tiles_matrix_bytes(n, k);
+}
+
+namespace {
+
+int pack_entry(const void *src, void *dst, int64_t n_mats, int64_t n, int64_t k, bool unpack,
+               void *stream) {
+    if (n_mats < 0 || n < 1 || n > (1 << 30) || k <= 0 || k % Q4K_BLOCK_WEIGHTS ||
+        k > (1 << 20))
+        return Q4K_ERR_SHAPE;
+    // one launch of a thread per block: the grid must fit 2^31 - 1 workgroups
+    if (n_mats > ((int64_t)1 << 38) / (tile_rows(n) * (k / Q4K_BLOCK_WEIGHTS)))
+        return Q4K_ERR_SHAPE;
+    if (n_mats == 0)
+        return Q4K_OK;
+    if (!src || !dst || !aligned16(src) || !aligned16(dst) || src == dst)
+        return Q4K_ERR_NULL;
+    return launched(launch_q4k_pack_tiles(src, dst, n_mats, n, k, unpack, as_stream(stream)));
+}
+
+}  // namespace
+
+int q4k_pack_tiles(const void *blocks, void *tiles, int64_t n_mats, int64_t n, int64_t k,
+                   void *stream) {
+    return pack_entry(blocks, tiles, n_mats, n, k, false, stream);
+}
+
+int q4k_unpack_tiles(const void *tiles, void *blocks, int64_t n_mats, int64_t n, int64_t k,
+                     void *stream) {
+    return pack_entry(tiles, blocks, n_mats, n, k, true, stream);
 }
 
 int64_t moe_bucket_workspace_bytes(int64_t n_pairs, int64_t num_experts) {

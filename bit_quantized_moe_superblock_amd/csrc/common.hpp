@@ -21,6 +21,39 @@ constexpr int kMaxTopK = 16;    // largest top_k
 constexpr int kTpMaxSegs = 3;   // Q4TiledP tensors in one merged matvec launch
 constexpr int kBucketChunk = 8; // pairs per bucketed work item
 
+// ------------------------------------------------------------ tile layout --
+// The GEMV kernels read Q4_K matrices in a tile-interleaved order of the same
+// 144-byte superblocks (q4k_pack_tiles writes it from GGUF row order).  Rows
+// go in groups of kTileRows = 8; tile (G, s) holds superblock s of rows
+// 8G .. 8G + 7 in kTileBytes = 1152 bytes at (G * nb + s) * 1152:
+//   [0, 128)     the 8 rows' 16-byte headers (d, dmin, packed scales), row r8
+//                at 16 r8;
+//   [128, 640)   first halves of the 32-byte nibble chunks: bytes 32c .. 32c+15
+//                of row r8's 128 nibble bytes at 128 + 16 (8c + r8);
+//   [640, 1152)  second halves: bytes 32c+16 .. 32c+31 at 640 + 16 (8c + r8).
+// A lane that owns chunk c of row r8 (the unit of the GEMV kernels) thus
+// reads its two 16-byte halves from places where the 32 lanes of a tile read
+// 512 contiguous bytes per load instruction, whatever the row length.  Rows
+// past n up to the next multiple of 8 are zero blocks.
+constexpr int kTileRows = 8;
+constexpr int kTileBytes = kTileRows * kBlockBytes;   // 1152
+constexpr int kTileHalf0 = 128;
+constexpr int kTileHalf1 = 640;
+
+__host__ __device__ constexpr int64_t tile_rows(int64_t n) {
+    return (n + kTileRows - 1) / kTileRows * kTileRows;
+}
+// Bytes of an n x k matrix in the tile layout (equal to the GGUF bytes when
+// n is a multiple of 8).
+__host__ __device__ constexpr int64_t tiles_matrix_bytes(int64_t n, int64_t k) {
+    return tile_rows(n) * (k >> 8) * kBlockBytes;
+}
+// Byte offset of tile (row group G, superblock s) in a matrix of nb
+// superblocks per row.
+__host__ __device__ constexpr int64_t tile_offset(int64_t G, int s, int nb) {
+    return (G * nb + s) * (int64_t)kTileBytes;
+}
+
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 // Half lanes of a packed register widened to float.  Feeding them straight into
@@ -49,23 +82,25 @@ struct UnitScale {
     float mA, mB;   // dmin*min of sub-blocks A and B
 };
 
-// Both decodings are computed and one is selected: with a branch on c the
-// compiler sinks the load of the header's last word into the c >= 2 side, and
-// waiting for that late load drains every load still in flight.
+// Branch-free: with c' = c & 1 the chunk reads the byte pairs P = s[2c'..],
+// Q = s[4+2c'..], R = s[8+2c'..] (one shift each); the low chunks take
+// P & 63, Q & 63 per byte, the high ones (R & 15 | (P >> 6) << 4) and
+// (R >> 4 | (Q >> 6) << 4); both are formed and one is selected per lane, and
+// the bytes convert to float directly.
 __device__ __forceinline__ UnitScale unit_scale(uint4 h, int c) {
-    const uint32_t sh = (c & 1) << 4;   // bytes 2c and 2c+1, modulo 4
-    const uint32_t b0 = h.y >> sh, b1 = h.z >> sh, b2 = h.w >> sh;
+    const uint32_t sh = (c & 1) << 4;
+    const uint32_t P = h.y >> sh, Q = h.z >> sh, R = h.w >> sh;
+    const uint32_t sc_lo = P & 0x3F3Fu, m_lo = Q & 0x3F3Fu;
+    const uint32_t sc_hi = (R & 0x0F0Fu) | ((P >> 2) & 0x3030u);
+    const uint32_t m_hi = ((R >> 4) & 0x0F0Fu) | ((Q >> 2) & 0x3030u);
     const bool hi = c >= 2;
-    const uint32_t scA = hi ? (b2 & 15u) | ((b0 >> 2) & 0x30u) : b0 & 63u;
-    const uint32_t scB = hi ? ((b2 >> 8) & 15u) | ((b0 >> 10) & 0x30u) : (b0 >> 8) & 63u;
-    const uint32_t mA = hi ? ((b2 >> 4) & 15u) | ((b1 >> 2) & 0x30u) : b1 & 63u;
-    const uint32_t mB = hi ? ((b2 >> 12) & 15u) | ((b1 >> 10) & 0x30u) : (b1 >> 8) & 63u;
+    const uint32_t sc = hi ? sc_hi : sc_lo, mn = hi ? m_hi : m_lo;
     const float d = lo_half(h.x), dmin = hi_half(h.x);
     UnitScale s;
-    s.kA = d * (float)scA;
-    s.kB = d * (float)scB;
-    s.mA = dmin * (float)mA;
-    s.mB = dmin * (float)mB;
+    s.kA = d * (float)(sc & 0xFFu);   // v_cvt_f32_ubyte0
+    s.kB = d * (float)((sc >> 8) & 0xFFu);
+    s.mA = dmin * (float)(mn & 0xFFu);
+    s.mB = dmin * (float)((mn >> 8) & 0xFFu);
     return s;
 }
 

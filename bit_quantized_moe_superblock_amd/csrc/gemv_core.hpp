@@ -1,17 +1,17 @@
 // Device core shared by the Q4_K GEMV kernels (q4k_gemv.hip, q4k_mfma.hip):
-// kernel arguments, activation staging, the per-unit Q4_K arithmetic, row
-// tiles and row reductions, plus a few host-side launch helpers.
+// kernel arguments, pair addressing, activation staging, the per-unit Q4_K
+// arithmetic on the tile layout, and the row sums of a wave.
 //
-// Layout conventions (ferrum-kernels q4_k_moe_id_gemv_batched.rs, module doc:
-// expert stacks [E, n, k/256] of 144-byte Q4_K blocks, pair p = token*top_k +
+// Conventions (ferrum-kernels q4_k_moe_id_gemv_batched.rs, module doc: expert
+// stacks [E, n, k/256] of 144-byte Q4_K superblocks, pair p = token*top_k +
 // slot, activation row src1 + token*outer + slot*inner):
-//   - 256 threads per workgroup; LPR consecutive lanes cover one weight row,
-//     lane u owning unit u = (superblock u/4, 32-byte nibble chunk u%4), i.e.
-//     64 weights: sub-block 2c in the low nibbles and 2c+1 in the high ones;
-//   - activation rows are staged in LDS (padded so a row's lanes hit different
-//     banks) with their 32-element sums, each taken in ascending order from 0
-//     by one thread, so every vector-unit mode rounds alike and gives
-//     identical bits.
+//   - the stacks are in the tile layout of common.hpp: expert e's matrix starts
+//     at e * tiles_matrix_bytes(n, k);
+//   - a unit is (row, superblock s, 32-byte nibble chunk c): 64 weights, sub-
+//     block 2c in the low nibbles and 2c+1 in the high ones;
+//   - activation rows are staged in LDS (padded so the lanes of a tile hit
+//     different banks) with their 32-element sums, each taken in ascending
+//     order from 0 by one thread.
 #pragma once
 
 #include "common.hpp"
@@ -31,8 +31,8 @@ struct GemvArgs {
     float *dst;               // [n_pairs, n]
     float *dst_sh;            // [m_sh, n]
     int64_t outer, inner, outer_sh;
+    int64_t mat;              // bytes of one expert matrix (tile layout)
     int n, k, top_k, num_experts, n_pairs, m_sh;
-    int pc;                   // pairs per LDS chunk (bucketed mode)
     int vec;                  // activation rows 16-byte aligned (float4 staging)
 };
 
@@ -45,8 +45,8 @@ __device__ __forceinline__ void fetch_args(const GemvArgs &a) {
     asm volatile("" ::"s"(a.w0), "s"(a.w1), "s"(a.s0), "s"(a.s1), "s"(a.src1), "s"(a.src1_sh),
                  "s"(a.ids), "s"(a.bucket));
     asm volatile("" ::"s"(a.dst), "s"(a.dst_sh), "s"(a.outer), "s"(a.inner), "s"(a.outer_sh),
-                 "s"(a.n), "s"(a.k), "s"(a.top_k), "s"(a.num_experts), "s"(a.n_pairs),
-                 "s"(a.m_sh), "s"(a.pc), "s"(a.vec));
+                 "s"(a.mat), "s"(a.n), "s"(a.k), "s"(a.top_k), "s"(a.num_experts),
+                 "s"(a.n_pairs), "s"(a.m_sh), "s"(a.vec));
 }
 
 // Where pair q (q >= n_pairs: shared pair of token q - n_pairs) reads and writes.
@@ -59,12 +59,11 @@ struct PairRef {
 
 __device__ __forceinline__ PairRef pair_ref(const GemvArgs &a, int q) {
     PairRef r;
-    const int64_t nb01 = (int64_t)(a.k >> 8) * kBlockBytes;
     if (q < a.n_pairs) {
         const int e = a.ids[q];
         const int t = q / a.top_k, s = q - t * a.top_k;
         r.valid = (unsigned)e < (unsigned)a.num_experts;
-        const int64_t off = r.valid ? (int64_t)e * a.n * nb01 : 0;
+        const int64_t off = r.valid ? (int64_t)e * a.mat : 0;
         r.w0 = a.w0 + off;
         r.w1 = a.w1 ? a.w1 + off : nullptr;
         r.x = a.src1 + t * a.outer + s * a.inner;
@@ -80,19 +79,10 @@ __device__ __forceinline__ PairRef pair_ref(const GemvArgs &a, int q) {
     return r;
 }
 
-// Activation row of pair q (no id lookup needed).
-__device__ __forceinline__ const float *pair_x(const GemvArgs &a, int q) {
-    if (q < a.n_pairs) {
-        const int t = q / a.top_k, s = q - t * a.top_k;
-        return a.src1 + t * a.outer + s * a.inner;
-    }
-    return a.src1_sh + (q - a.n_pairs) * a.outer_sh;
-}
-
-// Same, when the caller knows (uniformly across the workgroup) whether the
-// pair is a shared-expert pair.  A lane-varying choice between the two
-// argument fields compiles into a per-lane load from the argument segment,
-// whose wait would also wait for every weight load in flight.
+// Activation row of pair q, when the caller knows (uniformly across the
+// workgroup) whether the pair is a shared-expert pair.  A lane-varying choice
+// between the two argument fields compiles into a per-lane load from the
+// argument segment, whose wait would also wait for every weight load in flight.
 __device__ __forceinline__ const float *pair_x_known(const GemvArgs &a, bool shared, int q) {
     if (shared)
         return a.src1_sh + (q - a.n_pairs) * a.outer_sh;
@@ -158,12 +148,12 @@ __device__ __forceinline__ void stage_commit(const StageBatch &b, int total, int
     }
 }
 
-// Stage rows [0, cl) starting at flattened sub-block `from` (batches of 256).
-// No barrier.
-template <bool VEC, typename XOf>
+// Stage rows [0, cl) starting at flattened sub-block `from`, in batches of
+// NTHR (the workgroup's threads).  No barrier.
+template <bool VEC, int NTHR, typename XOf>
 __device__ __forceinline__ void stage_rows(XOf x_of, int cl, int k, float *lds, int from = 0) {
     const int total = cl * (k >> 5);
-    for (int base = from; base < total; base += kThreads) {
+    for (int base = from; base < total; base += NTHR) {
         StageBatch b;
         stage_issue<VEC>(x_of, base, total, k, b);
         stage_commit(b, total, k, lds);
@@ -171,25 +161,6 @@ __device__ __forceinline__ void stage_rows(XOf x_of, int cl, int k, float *lds, 
 }
 
 // ------------------------------------------------------- unit arithmetic ----
-
-// Masked nibbles of one 32-byte chunk: for each of its 8 dwords, the four
-// fp16-subnormal pairs (low nibbles of bytes 0,2 and 1,3; high nibbles of the
-// same).
-struct Masks {
-    uint32_t m[8][4];
-};
-
-__device__ __forceinline__ void make_masks(const uint4 &qa, const uint4 &qb, Masks &k) {
-    const uint32_t w[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-#pragma unroll
-    for (int d = 0; d < 8; d++) {
-        const uint32_t v = w[d], s = v >> 8;
-        k.m[d][0] = v & 0x000F000Fu;
-        k.m[d][1] = s & 0x000F000Fu;
-        k.m[d][2] = v & 0x00F000F0u;
-        k.m[d][3] = s & 0x00F000F0u;
-    }
-}
 
 // Accumulate one 8-weight step d of a unit (see nib_fma in common.hpp for the
 // element order) from precomputed masks.
@@ -205,31 +176,6 @@ __device__ __forceinline__ void masked_fma(const uint32_t (&r)[4], float4 xa, fl
     acc.b = __builtin_fmaf(hi_half(r[3]), xb.w, acc.b);
 }
 
-// Reduce a per-lane unit value over the LPR lanes of its row.  For rows wider
-// than a wave the wave sums go through `red` (2 barriers); `slot_lane0` is true
-// on the lane that receives the row total.
-template <int LPR>
-__device__ __forceinline__ float row_reduce(float v, float *red, int nt_index) {
-    constexpr int WL = LPR < 64 ? LPR : 64;
-    constexpr int WPR = LPR / WL;
-    v = group_sum<WL>(v);
-    if constexpr (WPR > 1) {
-        const int tid = threadIdx.x;
-        const int wave = tid >> 6;
-        if ((tid & 63) == 0)
-            red[nt_index * 4 + wave] = v;
-        __syncthreads();
-        if ((tid % LPR) == 0) {
-            float s = red[nt_index * 4 + wave];
-            for (int w = 1; w < WPR; w++)
-                s += red[nt_index * 4 + wave + w];
-            v = s;
-        }
-        __syncthreads();
-    }
-    return v;
-}
-
 template <int EPI, int NT>
 __device__ __forceinline__ float epilogue(const float (&part)[NT]) {
     if constexpr (EPI == EPI_SWIGLU)
@@ -238,128 +184,144 @@ __device__ __forceinline__ float epilogue(const float (&part)[NT]) {
         return part[0];
 }
 
-// Row tile of one lane: ITERS row groups, NT tensors.
-template <int NT, int ITERS>
-struct Tile {
-    uint4 hdr[NT][ITERS];
-    uint4 qa[NT][ITERS];
-    uint4 qb[NT][ITERS];
+// ------------------------------------------------------------- tile steps ----
+// A vector-unit step is one superblock s of 16 weight rows.  Lane l owns chunk
+// c = (l >> 3) & 3 of row r8 = l & 7 of its half j = l >> 5 of the step; the
+// halves are two row groups of one matrix (pair mode) or one row group of two
+// matrices (token mode, two pairs).  Per load instruction the 32 lanes of a
+// half read 512 contiguous bytes of one tile.
+//
+// The superblocks of a row fall into kClasses step classes, s = cls + 4t, so
+// that four waves can share a row.  Every vector-unit kernel forms a row
+// value in one order: per lane, the class's unit values in ascending t from
+// 0; chunk_sum over the four chunk lanes; then the four class sums as
+// ((p0 + p1) + p2) + p3 (a class without superblocks is +0).  Pair,
+// bucketed and token modes therefore agree bit for bit, however they spread
+// the classes over waves.
+constexpr int kClasses = 4;
+
+// Superblocks of class cls in a row of nb.
+__host__ __device__ constexpr int class_steps(int nb, int cls) {
+    return nb > cls ? (nb - cls + kClasses - 1) / kClasses : 0;
+}
+
+template <int NT>
+struct Step {
+    uint4 hdr[NT], qa[NT], qb[NT];
 };
 
-// Hide a tile's registers from loop-invariant code motion.  Without this the
-// compiler hoists the masked and fp32-converted weights out of a per-pair loop
-// into (accumulation) registers, which costs a register read plus an fma per
-// weight and pair instead of one v_fma_mix_f32 that decodes as it multiplies.
-template <int NT, int ITERS>
-__device__ __forceinline__ void opaque(Tile<NT, ITERS> &t) {
+// Issue the lane's unit of superblock s, row group G, for NT matrices.
+template <int NT>
+__device__ __forceinline__ void load_step(const uint8_t *const (&mat)[NT], int64_t G, int s,
+                                          int nb, Step<NT> &st) {
+    const int l32 = threadIdx.x & 31, r8 = threadIdx.x & 7;
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++) {
+        const uint8_t *t = mat[nt] + tile_offset(G, s, nb);
+        st.hdr[nt] = *(const uint4 *)(t + 16 * r8);
+        st.qa[nt] = *(const uint4 *)(t + kTileHalf0 + 16 * l32);
+        st.qb[nt] = *(const uint4 *)(t + kTileHalf1 + 16 * l32);
+    }
+}
+
+// Unit values of a step for the NT matrices, added to acc[nt]: xu holds the
+// unit's 64 activations, sums its two 32-element sums.  The activations are
+// read once for all NT matrices.
+template <int NT>
+__device__ __forceinline__ void step_units(const Step<NT> &st, const float *xu, const float *sums,
+                                           float (&acc)[NT]) {
+    const int c = (threadIdx.x >> 3) & 3;
+    const float4 *xa = (const float4 *)xu;
+    const float4 *xb = (const float4 *)(xu + 32);
+    UnitAcc ua[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; nt++)
-#pragma unroll
-        for (int it = 0; it < ITERS; it++) {
-            asm volatile("" : "+v"(t.qa[nt][it].x), "+v"(t.qa[nt][it].y), "+v"(t.qa[nt][it].z),
-                         "+v"(t.qa[nt][it].w));
-            asm volatile("" : "+v"(t.qb[nt][it].x), "+v"(t.qb[nt][it].y), "+v"(t.qb[nt][it].z),
-                         "+v"(t.qb[nt][it].w));
-        }
-}
-
-template <int LPR, int NT, int ITERS>
-__device__ __forceinline__ void load_rows(const uint8_t *w0, const uint8_t *w1, int n, int k,
-                                          int row0, bool valid, Tile<NT, ITERS> &t) {
-    constexpr int RPI = kThreads / LPR;
-    const int tid = threadIdx.x;
-    const int nb = k >> 8;
-    // Lanes past the row's units and row groups past n load a clamped, valid
-    // address instead of branching: their results never reach a reduction or
-    // a store, and a lane-divergent load makes the compiler wait for it at the
-    // join (register copies out of the loaded registers).
-    const int u0 = tid % LPR;
-    const int u = u0 < 4 * nb ? u0 : 0;
-    const int rsub = tid / LPR;
-    const int64_t nb01 = (int64_t)nb * kBlockBytes;
-    const int64_t uoff = (int64_t)(u >> 2) * kBlockBytes;
-    const int c = u & 3;
-    if (!valid) {   // uniform: nothing to load
-#pragma unroll
-        for (int it = 0; it < ITERS; it++)
-#pragma unroll
-            for (int nt = 0; nt < NT; nt++) {
-                t.hdr[nt][it] = make_uint4(0, 0, 0, 0);
-                t.qa[nt][it] = make_uint4(0, 0, 0, 0);
-                t.qb[nt][it] = make_uint4(0, 0, 0, 0);
-            }
-        return;
-    }
-#pragma unroll
-    for (int it = 0; it < ITERS; it++) {
-        const int r0 = row0 + it * RPI + rsub;
-        const int r = r0 < n ? r0 : n - 1;
-#pragma unroll
-        for (int nt = 0; nt < NT; nt++) {
-            const uint8_t *rp = (nt == 0 ? w0 : w1) + uoff + (int64_t)r * nb01;
-            t.hdr[nt][it] = *(const uint4 *)rp;
-            t.qa[nt][it] = *(const uint4 *)(rp + 16 + 32 * c);
-            t.qb[nt][it] = *(const uint4 *)(rp + 32 + 32 * c);
-        }
-    }
-}
-
-// Gate and up units (tile tensors 0 and 1) of row group `it` against the
-// staged row at xrow, reading the activations once for both.  Same per-unit
-// arithmetic and order as unit_from_tile.
-template <int ITERS>
-__device__ __forceinline__ void unit_pair_from_tile(const Tile<2, ITERS> &t, int it,
-                                                    const float *xrow, int u, int c, int k,
-                                                    float &v0, float &v1) {
-    const float *xl = xrow + 68 * u;   // xpad(64u)
-    const float4 *xa = (const float4 *)xl;
-    const float4 *xb = (const float4 *)(xl + 32);
-    UnitAcc acc0{0.0f, 0.0f}, acc1{0.0f, 0.0f};
-    const uint32_t w0[8] = {t.qa[0][it].x, t.qa[0][it].y, t.qa[0][it].z, t.qa[0][it].w,
-                            t.qb[0][it].x, t.qb[0][it].y, t.qb[0][it].z, t.qb[0][it].w};
-    const uint32_t w1[8] = {t.qa[1][it].x, t.qa[1][it].y, t.qa[1][it].z, t.qa[1][it].w,
-                            t.qb[1][it].x, t.qb[1][it].y, t.qb[1][it].z, t.qb[1][it].w};
+        ua[nt].a = ua[nt].b = 0.0f;
 #pragma unroll
     for (int d = 0; d < 8; d++) {
         const float4 va = xa[d], vb = xb[d];
-        {
-            const uint32_t v = w0[d], s = v >> 8;
-            const uint32_t r[4] = {v & 0x000F000Fu, s & 0x000F000Fu, v & 0x00F000F0u,
-                                   s & 0x00F000F0u};
-            masked_fma(r, va, vb, acc0);
-        }
-        {
-            const uint32_t v = w1[d], s = v >> 8;
-            const uint32_t r[4] = {v & 0x000F000Fu, s & 0x000F000Fu, v & 0x00F000F0u,
-                                   s & 0x00F000F0u};
-            masked_fma(r, va, vb, acc1);
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++) {
+            const uint4 &q = d < 4 ? st.qa[nt] : st.qb[nt];
+            const uint32_t v = (d & 3) == 0 ? q.x : (d & 3) == 1 ? q.y : (d & 3) == 2 ? q.z : q.w;
+            const uint32_t sh = v >> 8;
+            const uint32_t r[4] = {v & 0x000F000Fu, sh & 0x000F000Fu, v & 0x00F000F0u,
+                                   sh & 0x00F000F0u};
+            masked_fma(r, va, vb, ua[nt]);
         }
     }
-    const float *sx = xrow + xpad_len(k);
-    const float sxa = sx[2 * u], sxb = sx[2 * u + 1];
-    v0 = unit_value(unit_scale(t.hdr[0][it], c), acc0, sxa, sxb);
-    v1 = unit_value(unit_scale(t.hdr[1][it], c), acc1, sxa, sxb);
+    const float sxa = sums[0], sxb = sums[1];
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++)
+        acc[nt] += unit_value(unit_scale(st.hdr[nt], c), ua[nt], sxa, sxb);
 }
 
-// Unit value of tensor (nt, it) of the tile against the staged row at xrow.
-template <int NT, int ITERS>
-__device__ __forceinline__ float unit_from_tile(const Tile<NT, ITERS> &t, int nt, int it,
-                                                const float *xrow, int u, int c, int k) {
-    const float *xl = xrow + 68 * u;   // xpad(64u)
-    const float4 *xa = (const float4 *)xl;
-    const float4 *xb = (const float4 *)(xl + 32);
-    UnitAcc acc{0.0f, 0.0f};
-    const uint32_t w[8] = {t.qa[nt][it].x, t.qa[nt][it].y, t.qa[nt][it].z, t.qa[nt][it].w,
-                           t.qb[nt][it].x, t.qb[nt][it].y, t.qb[nt][it].z, t.qb[nt][it].w};
+// Row total of a lane's class sum over the four chunk lanes (l ^ 8, then
+// l ^ 16).  Lanes 0..7 and 32..39 hold the totals of the two halves' rows.
+__device__ __forceinline__ float chunk_sum(float v) {
+    v += dpp_move<0x128>(v);   // row_ror:8 within 16 lanes: the partner l ^ 8
+    v += __shfl_xor(v, 16);
+    return v;
+}
+
+// The row value from its four class sums (see kClasses).
+__device__ __forceinline__ float class_total(float p0, float p1, float p2, float p3) {
+    return ((p0 + p1) + p2) + p3;
+}
+
+// Per-wave activation staging of pair mode: a wave stages the superblocks of
+// its class, one step (superblock) per kStepFloats LDS floats: the four units
+// of 64 floats, each padded by 4 floats, then the 8 sub-block sums.  Lane
+// 8u + j stages sub-block j of the wave's u-th superblock (in batches of 8
+// superblocks), summing its 32 floats in ascending order from 0 as
+// stage_commit does, so both stagings give the same sums.
+constexpr int kStepFloats = 4 * 68 + 8;
+
+struct WaveStage {
+    float4 v[8];
+};
+
+template <bool VEC>
+__device__ __forceinline__ void wave_stage_issue(const float *x, int cls, int T, int t0,
+                                                 WaveStage &b) {
+    const int l = threadIdx.x & 63;
+    const int t = t0 + (l >> 3);
+    const int tc = t < T ? t : T - 1;   // clamped (T >= 1): never committed
+    const float *src = x + 256 * (cls + kClasses * tc) + 32 * (l & 7);
+    if constexpr (VEC) {
 #pragma unroll
-    for (int d = 0; d < 8; d++) {
-        const uint32_t v = w[d], s = v >> 8;
-        const uint32_t r[4] = {v & 0x000F000Fu, s & 0x000F000Fu, v & 0x00F000F0u,
-                               s & 0x00F000F0u};
-        masked_fma(r, xa[d], xb[d], acc);
+        for (int q = 0; q < 8; q++)
+            b.v[q] = *(const float4 *)(src + 4 * q);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 8; q++)
+            b.v[q] = make_float4(src[4 * q], src[4 * q + 1], src[4 * q + 2], src[4 * q + 3]);
     }
-    const float *sx = xrow + xpad_len(k);
-    return unit_value(unit_scale(t.hdr[nt][it], c), acc, sx[2 * u], sx[2 * u + 1]);
+}
+
+__device__ __forceinline__ void wave_stage_commit(const WaveStage &b, int T, int t0, float *xw) {
+    const int l = threadIdx.x & 63;
+    const int t = t0 + (l >> 3), j = l & 7;
+    if (t < T) {
+        float *step = xw + t * kStepFloats;
+        float4 *d = (float4 *)(step + 68 * (j >> 1) + 32 * (j & 1));
+        float s = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            d[q] = b.v[q];
+            s += b.v[q].x;
+            s += b.v[q].y;
+            s += b.v[q].z;
+            s += b.v[q].w;
+        }
+        step[4 * 68 + j] = s;
+    }
+}
+
+// This wave's LDS writes are complete and no LDS access moves across: the
+// wave reads what its own lanes staged (no other wave is involved).
+__device__ __forceinline__ void wave_lds_fence() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 // Bucket workspace views (layout documented with moe_bucket in q4kmoe.h).
@@ -380,14 +342,6 @@ struct BucketView {
 
 // Bucketed mode on the matrix cores (q4k_mfma.hip).
 hipError_t launch_q4k_gemv_mfma(const GemvArgs &a, bool fused_swiglu, hipStream_t st);
-
-static inline int lanes_per_row(int k) {
-    const int units = 4 * (k >> 8);
-    int l = 4;
-    while (l < units)
-        l <<= 1;
-    return l;
-}
 
 // Compute units of the current device (256 on MI355X), cached per device.
 static inline int cu_count() {

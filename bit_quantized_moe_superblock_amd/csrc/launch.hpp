@@ -40,6 +40,10 @@ hipError_t launch_q4k_down_combine(const GemvLaunch &L, const float *h_mid, cons
                                    const float *shared_logit, float *out, float *expert_out,
                                    int shared_mode, hipStream_t st);
 hipError_t launch_q4k_dequant(const void *blocks, float *out, int64_t n_blocks, hipStream_t st);
+// n_mats matrices of n x k between GGUF row order and the tile layout
+// (common.hpp); unpack reverses it.
+hipError_t launch_q4k_pack_tiles(const void *src, void *dst, int64_t n_mats, int64_t n,
+                                 int64_t k, bool unpack, hipStream_t st);
 hipError_t launch_q4k_quant(const float *w, void *blocks, int64_t n_blocks, hipStream_t st);
 hipError_t launch_moe_bucket(const int32_t *ids, int64_t n_pairs, int64_t num_experts,
                              int32_t *ws, hipStream_t st);

@@ -113,6 +113,31 @@ __device__ __forceinline__ float group_qx2(const uint4 qa, const float *xr) {
     return acc * 16777216.0f;
 }
 
+// Reduce a per-lane value over the LPR lanes of its row.  For rows wider
+// than a wave the wave sums go through `red` (2 barriers); the first lane of
+// the row receives the row total.
+template <int LPR>
+__device__ __forceinline__ float row_reduce(float v, float *red, int nt_index) {
+    constexpr int WL = LPR < 64 ? LPR : 64;
+    constexpr int WPR = LPR / WL;
+    v = group_sum<WL>(v);
+    if constexpr (WPR > 1) {
+        const int tid = threadIdx.x;
+        const int wave = tid >> 6;
+        if ((tid & 63) == 0)
+            red[nt_index * 4 + wave] = v;
+        __syncthreads();
+        if ((tid % LPR) == 0) {
+            float s = red[nt_index * 4 + wave];
+            for (int w = 1; w < WPR; w++)
+                s += red[nt_index * 4 + wave + w];
+            v = s;
+        }
+        __syncthreads();
+    }
+    return v;
+}
+
 template <int LPR, int NT, int BITS, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_mlx4_rows(Mlx4Args a) {
     extern __shared__ float lds[];
@@ -158,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void k_mlx4_rows(Mlx4Args a) {
     }
     // 3. the staged row (and any further batches)
     stage_commit(xb, total, a.k, lds);
-    stage_rows<VEC>(x_of, 1, a.k, lds, kThreads);
+    stage_rows<VEC, kThreads>(x_of, 1, a.k, lds, kThreads);
     lds_barrier();
     // 4. the group's share, then the row sums
     const float *sx = lds + xpad_len(a.k);

@@ -121,6 +121,77 @@ __global__ __launch_bounds__(256) void k_q4k_quant(const float *__restrict__ w,
     }
 }
 
+// GGUF row order <-> tile layout (common.hpp), one thread per (matrix, row,
+// superblock) block: nine 16-byte pieces moved as they are.  Rows of the last
+// row group past n are written as zero blocks (pack) or skipped (unpack).
+__global__ __launch_bounds__(256) void k_q4k_pack_tiles(const uint8_t *__restrict__ src,
+                                                        uint8_t *__restrict__ dst, int64_t n,
+                                                        int nb, int64_t per_mat,
+                                                        int64_t n_blocks) {
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= n_blocks)   // n_blocks = n_mats * tile_rows(n) * nb
+        return;
+    const int64_t mi = b / per_mat, rb = b - mi * per_mat;   // per_mat = tile_rows(n) * nb
+    const int64_t r = rb / nb;
+    const int s = (int)(rb - r * nb);
+    uint8_t *t = dst + mi * per_mat * kBlockBytes + tile_offset(r / kTileRows, s, nb);
+    const int r8 = (int)(r % kTileRows);
+    uint4 p[9];
+    if (r < n) {
+        const uint4 *g = (const uint4 *)(src + (mi * n * nb + r * nb + s) * kBlockBytes);
+#pragma unroll
+        for (int i = 0; i < 9; i++)
+            p[i] = g[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 9; i++)
+            p[i] = make_uint4(0, 0, 0, 0);
+    }
+    *(uint4 *)(t + 16 * r8) = p[0];
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        *(uint4 *)(t + kTileHalf0 + 16 * (8 * c + r8)) = p[1 + 2 * c];
+        *(uint4 *)(t + kTileHalf1 + 16 * (8 * c + r8)) = p[2 + 2 * c];
+    }
+}
+
+__global__ __launch_bounds__(256) void k_q4k_unpack_tiles(const uint8_t *__restrict__ src,
+                                                          uint8_t *__restrict__ dst, int64_t n,
+                                                          int nb, int64_t tiled_mat,
+                                                          int64_t n_blocks) {
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= n_blocks)   // n_blocks = n_mats * n * nb
+        return;
+    const int64_t per = n * nb;
+    const int64_t mi = b / per, rb = b - mi * per;
+    const int64_t r = rb / nb;
+    const int s = (int)(rb - r * nb);
+    const uint8_t *t = src + mi * tiled_mat + tile_offset(r / kTileRows, s, nb);
+    const int r8 = (int)(r % kTileRows);
+    uint4 *g = (uint4 *)(dst + b * kBlockBytes);
+    g[0] = *(const uint4 *)(t + 16 * r8);
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        g[1 + 2 * c] = *(const uint4 *)(t + kTileHalf0 + 16 * (8 * c + r8));
+        g[2 + 2 * c] = *(const uint4 *)(t + kTileHalf1 + 16 * (8 * c + r8));
+    }
+}
+
+hipError_t launch_q4k_pack_tiles(const void *src, void *dst, int64_t n_mats, int64_t n,
+                                 int64_t k, bool unpack, hipStream_t st) {
+    const int nb = (int)(k >> 8);
+    const int64_t per_tiled = tile_rows(n) * nb;
+    const int64_t blocks = n_mats * (unpack ? n * nb : per_tiled);
+    const dim3 grid((unsigned)((blocks + 255) / 256));
+    if (unpack)
+        hipLaunchKernelGGL(k_q4k_unpack_tiles, grid, dim3(256), 0, st, (const uint8_t *)src,
+                           (uint8_t *)dst, n, nb, per_tiled * kBlockBytes, blocks);
+    else
+        hipLaunchKernelGGL(k_q4k_pack_tiles, grid, dim3(256), 0, st, (const uint8_t *)src,
+                           (uint8_t *)dst, n, nb, per_tiled, blocks);
+    return hipGetLastError();
+}
+
 hipError_t launch_q4k_dequant(const void *blocks, float *out, int64_t n_blocks, hipStream_t st) {
     if (n_blocks == 0)
         return hipSuccess;

@@ -15,17 +15,19 @@
 // lane l holds A[l % 16][8 (l / 16) + i], B[8 (l / 16) + i][l % 16] for
 // i < 8, and D[4 (l / 16) + j][l % 16] for j < 4.
 //
-//   - B comes straight from the nibbles: with v the dword of bytes b0..b3,
+//   - B comes straight from the nibbles: lane group g (lanes 16g .. 16g+15,
+//     one weight row per lane) holds the row's 32-byte nibble chunk g (the
+//     tile layout puts its two 16-byte halves where the lanes of a tile read
+//     contiguous bytes), i.e. positions 0..31 of sub-block 2g (low nibbles)
+//     and 2g + 1 (high nibbles).  With v a dword of bytes b0..b3,
 //     (v & 0x000F000F) holds (q(b0), q(b2)) and ((v >> 8) & 0x000F000F)
 //     (q(b1), q(b3)) as 16-bit integers (shifts by 4 and 12 give the high
 //     nibbles).  One packed 16-bit multiply by the sub-block's six-bit scale
 //     makes them q sc <= 945, which read as fp16 are the subnormals
-//     q sc 2^-24; the matrix core takes fp16 subnormals exactly.  The k order
-//     inside each group of 8 is therefore (0,2,1,3,4,6,5,7).
-//   - With the scales inside B, one MFMA may mix sub-blocks of a superblock,
-//     so each lane loads contiguous bytes (16 of each 64-byte half of the
-//     nibbles; a row's 4 lanes read 64 contiguous bytes per load) and the
-//     activations are staged in the matching k order.
+//     q sc 2^-24; the matrix core takes fp16 subnormals exactly.  MFMA
+//     t = 4u + 2hh + e of a superblock takes from every lane group the 8
+//     positions 16u + 8e .. 16u + 8e + 7 of its sub-block 2g + hh, in the k
+//     order (0,2,1,3,4,6,5,7); the activations are staged in the same order.
 //   - A is the activation split into two fp16 parts, staged once per
 //     workgroup in LDS in the same k order: A rows 0..7 are the 8 pairs' hi
 //     parts, rows 8..15 their lo parts, so one MFMA per sub-block covers both
@@ -76,9 +78,8 @@ __host__ __device__ constexpr size_t mfma_lds_scale_off(int sb) {
     return (size_t)sb * 8 * kSubB + (size_t)sb * 256;
 }
 
-// One superblock of a lane's row: the header and 32 of the 128 nibble bytes,
-// qs[16 g, 16 g + 16) and qs[64 + 16 g, 64 + 16 g + 16) for lane group g, so
-// that the 4 lanes of a row read 64 contiguous bytes per load.
+// One superblock of a lane's row: the header and nibble chunk g (its two
+// 16-byte halves u[0], u[1]) for lane group g.
 struct MfmaTile {
     uint4 hdr;
     uint4 u[2];
@@ -173,10 +174,10 @@ __device__ __forceinline__ void mfma_x_commit(const XRegs<SB> &xr, int cnt, int 
         _Float16 *sx = (_Float16 *)(sxa + (size_t)(jl >> 3) * 256) + (jl & 7);
         sx[p * 8] = sh;
         sx[(8 + p) * 8] = (_Float16)(s - (float)sh);
-        // sub-block j = 2c + hh (c = 2hu + gg) of superblock jl / 8: its
-        // positions 8 q8 .. 8 q8 + 7 are the k group g = 2 gg + q8 / 2 of MFMA
-        // t = 4hu + 2hh + q8 % 2 (the nibbles a lane of group g holds)
-        const int j = jl & 7, c = j >> 1, hh = j & 1, hu = c >> 1, gg = c & 1;
+        // sub-block j = 2g + hh of superblock jl / 8 is held by lane group g;
+        // its positions 8 q8 .. 8 q8 + 7 (half u = q8 / 2, dword pair
+        // e = q8 % 2) feed MFMA t = 4u + 2hh + e
+        const int j = jl & 7, g = j >> 1, hh = j & 1;
         uint8_t *dst = lds + (size_t)(jl >> 3) * 8 * kSubB;
 #pragma unroll
         for (int q8 = 0; q8 < 4; q8++) {
@@ -189,7 +190,7 @@ __device__ __forceinline__ void mfma_x_commit(const XRegs<SB> &xr, int cnt, int 
                 hi[i] = h;
                 lo[i] = (_Float16)(x - (float)h);
             }
-            const int g = 2 * gg + (q8 >> 1), t = 4 * hu + 2 * hh + (q8 & 1);
+            const int t = 4 * (q8 >> 1) + 2 * hh + (q8 & 1);
             uint8_t *blk = dst + (size_t)t * kSubB;
             *(h8v *)(blk + (size_t)(0 * 4 + g) * (kMP * 16) + p * 16) = hi;
             *(h8v *)(blk + (size_t)(1 * 4 + g) * (kMP * 16) + p * 16) = lo;
@@ -197,11 +198,15 @@ __device__ __forceinline__ void mfma_x_commit(const XRegs<SB> &xr, int cnt, int 
     }
 }
 
-__device__ __forceinline__ void mfma_load(const uint8_t *row, int sb, int g, MfmaTile &t) {
-    const uint8_t *b = row + (size_t)sb * kBlockBytes;
-    t.hdr = *(const uint4 *)b;
-    t.u[0] = *(const uint4 *)(b + 16 + 16 * g);
-    t.u[1] = *(const uint4 *)(b + 80 + 16 * g);
+// Superblock sb of the lane's row: row r8 of row group G of the matrix at
+// mat (tile layout, nb superblocks per row).  The 8 lanes of a tile and
+// chunk read 128 contiguous bytes, the 32 lanes of a tile 512.
+__device__ __forceinline__ void mfma_load(const uint8_t *mat, int64_t G, int r8, int sb, int nb,
+                                          int g, MfmaTile &t) {
+    const uint8_t *b = mat + tile_offset(G, sb, nb);
+    t.hdr = *(const uint4 *)(b + 16 * r8);
+    t.u[0] = *(const uint4 *)(b + kTileHalf0 + 16 * (8 * g + r8));
+    t.u[1] = *(const uint4 *)(b + kTileHalf1 + 16 * (8 * g + r8));
 }
 
 // One superblock of the lane's row against the staged pairs.  A rows 0..7
@@ -209,12 +214,11 @@ __device__ __forceinline__ void mfma_load(const uint8_t *row, int sb, int g, Mfm
 // 32..63) accumulate the lo half, which the caller adds to the hi half once
 // at the end.
 //
-// Lane group g holds nibble bytes 16 g .. 16 g + 15 of the two 64-byte
-// halves u of the block: sub-blocks j = 4u + 2gg + hh (gg = g / 2, hh = 0
-// low nibbles, 1 high nibbles), positions 16 (g % 2) .. + 15.  Each of its
-// B values is the nibble times the sub-block's six-bit scale, an integer
-// q sc <= 945 taken as the fp16 subnormal q sc 2^-24 (exact), so the eight
-// MFMAs of the superblock accumulate into one D and
+// Lane group g holds nibble chunk g of its row: sub-blocks 2g (hh = 0, low
+// nibbles) and 2g + 1 (hh = 1, high nibbles), positions 16u .. 16u + 15 in
+// half u.  Each of its B values is the nibble times the sub-block's six-bit
+// scale, an integer q sc <= 945 taken as the fp16 subnormal q sc 2^-24
+// (exact), so the eight MFMAs of the superblock accumulate into one D and
 //
 //   y += d 2^24 D - dmin 2^24 D_min
 //
@@ -237,13 +241,15 @@ __device__ __forceinline__ void mfma_superblock(const MfmaTile (&t)[NT], const u
     const h8v a_sx = *(const h8v *)(sxa + (size_t)s * 256 + (lane & 15) * 16);
     const h8v zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
     const h8v amin = lane < 16 ? a_sx : zero8;
-    // scale byte 2gg + hh of a packed scale word, into both 16-bit halves
-    const uint32_t gg2 = (uint32_t)(lane >> 5) * 2u;
-    const uint32_t sel0 = 0x0c000c00u | gg2 | (gg2 << 16);
+    // scale of sub-block 2g + hh: byte 2 (g % 2) + hh of the packed scales of
+    // sub-blocks 0..3 (g < 2) or 4..7, into both 16-bit halves
+    const int g = lane >> 4;
+    const uint32_t gb = (uint32_t)(g & 1) * 2u;
+    const uint32_t sel0 = 0x0c000c00u | gb | (gb << 16);
     const uint32_t sel1 = sel0 + 0x00010001u;
     const f4v zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
     f4v acc[NT];
-    uint32_t scp[NT][2][2];   // [u][hh]
+    uint32_t scp[NT][2];   // [hh]
 #pragma unroll
     for (int nt = 0; nt < NT; nt++) {
         const uint4 h = t[nt].hdr;
@@ -251,10 +257,9 @@ __device__ __forceinline__ void mfma_superblock(const MfmaTile (&t)[NT], const u
         const uint32_t sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
         const uint32_t mn03 = h.z & 0x3F3F3F3Fu;
         const uint32_t mn47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
-        scp[nt][0][0] = __builtin_amdgcn_perm(0u, sc03, sel0);
-        scp[nt][0][1] = __builtin_amdgcn_perm(0u, sc03, sel1);
-        scp[nt][1][0] = __builtin_amdgcn_perm(0u, sc47, sel0);
-        scp[nt][1][1] = __builtin_amdgcn_perm(0u, sc47, sel1);
+        const uint32_t scw = g < 2 ? sc03 : sc47;
+        scp[nt][0] = __builtin_amdgcn_perm(0u, scw, sel0);
+        scp[nt][1] = __builtin_amdgcn_perm(0u, scw, sel1);
         const uint4 bm = make_uint4(__builtin_amdgcn_perm(0u, mn03, 0x0c010c00u),
                                     __builtin_amdgcn_perm(0u, mn03, 0x0c030c02u),
                                     __builtin_amdgcn_perm(0u, mn47, 0x0c010c00u),
@@ -284,7 +289,7 @@ __device__ __forceinline__ void mfma_superblock(const MfmaTile (&t)[NT], const u
             for (int nt = 0; nt < NT; nt++) {
                 const uint32_t w0 = e ? t[nt].u[u].z : t[nt].u[u].x;
                 const uint32_t w1 = e ? t[nt].u[u].w : t[nt].u[u].y;
-                const uint32_t s0 = scp[nt][u][0], s1 = scp[nt][u][1];
+                const uint32_t s0 = scp[nt][0], s1 = scp[nt][1];
                 blo[nt] = make_uint4(scaled(w0 & 0x000F000Fu, s0), scaled((w0 >> 8) & 0x000F000Fu, s0),
                                      scaled(w1 & 0x000F000Fu, s0), scaled((w1 >> 8) & 0x000F000Fu, s0));
                 bhi[nt] = make_uint4(scaled((w0 >> 4) & 0x000F000Fu, s1),
@@ -337,17 +342,25 @@ __device__ __forceinline__ void mfma_item(const GemvArgs &a, bool shared, int bk
         return;
     }
     const int nb = a.k >> 8;                                  // superblocks per row
-    const int64_t rowb = (int64_t)nb * kBlockBytes;
-    const int64_t mat = (int64_t)a.n * rowb;
     const int r0 = row0 + wave * 16 + rl;                     // this lane's weight row
-    const int r = r0 < a.n ? r0 : a.n - 1;
-    const uint8_t *wrow[NT];
-    wrow[0] = (shared ? a.s0 : a.w0 + (int64_t)bkt * mat) + (int64_t)r * rowb;
+    // its row group (clamped to the last one; rows past n up to a multiple of
+    // 8 are zero blocks in the tile layout) and row within the group
+    const int64_t n8 = (a.n + kTileRows - 1) / kTileRows;
+    const int r8 = r0 & (kTileRows - 1);
+    auto group = [&](int rr) {
+        const int64_t G = rr / kTileRows;
+        return G < n8 ? G : n8 - 1;
+    };
+    const uint8_t *wmat[NT];
+    int64_t wg[NT];
+    wmat[0] = shared ? a.s0 : a.w0 + (int64_t)bkt * a.mat;
+    wg[0] = group(r0);
     if constexpr (EPI == kEpiRowPair) {   // the second row group of the same matrix
-        const int r2 = r0 + kMRows < a.n ? r0 + kMRows : a.n - 1;
-        wrow[NT - 1] = (shared ? a.s0 : a.w0 + (int64_t)bkt * mat) + (int64_t)r2 * rowb;
+        wmat[NT - 1] = wmat[0];
+        wg[NT - 1] = group(r0 + kMRows);
     } else if (NT == 2) {
-        wrow[NT - 1] = (shared ? a.s1 : a.w1 + (int64_t)bkt * mat) + (int64_t)r * rowb;
+        wmat[NT - 1] = shared ? a.s1 : a.w1 + (int64_t)bkt * a.mat;
+        wg[NT - 1] = wg[0];
     }
     const uint8_t *sxa = lds_b + (size_t)SB * 8 * kSubB;
     const float *sfac = (const float *)(lds_b + mfma_lds_scale_off(SB));
@@ -378,7 +391,7 @@ __device__ __forceinline__ void mfma_item(const GemvArgs &a, bool shared, int bk
             const int sb = sb0 + i < nb ? sb0 + i : nb - 1;   // clamped
 #pragma unroll
             for (int nt = 0; nt < NT; nt++)
-                mfma_load(wrow[nt], sb, g, tt[i % kDepth][nt]);
+                mfma_load(wmat[nt], wg[nt], r8, sb, nb, g, tt[i % kDepth][nt]);
         };
         XRegs<SB> xr;
         mfma_x_issue<SB, VEC>(xrow, gc, sb0 * 8, nsub_total, xr);

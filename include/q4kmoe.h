@@ -100,7 +100,8 @@ enum { MOE_SHARED_NONE = 0, MOE_SHARED_SIGMOID = 1, MOE_SHARED_UNSCALED = 2 };
 #define Q4K_BUCKET_CHUNK 8    /* pairs per bucketed work item               */
 
 const char *q4k_status_string(int status);
-/* 4: bucket_flag takes schedule bits (Q4K_SCHED_*); AUTO buckets from
+/* 4: weight stacks in the tile layout (q4k_pack_tiles); bucket_flag takes
+ * schedule bits (Q4K_SCHED_*); AUTO buckets from
  * Q4K_AUTO_BUCKET_MIN_TOKENS tokens; the layer workspace has no
  * synchronisation header (moe_layer_workspace_init is gone); activation rows
  * of every entry point need only 4-byte alignment.  3 added the MLX 4-bit and
@@ -132,6 +133,37 @@ int q4k_dequantize(const void *blocks, float *out, int64_t n_blocks, void *strea
  * min = rne(b/dmin), q = rne((w + dmin*min)/(d*scale)), all clamped). */
 int q4k_quantize(const float *w, void *blocks, int64_t n_rows, int64_t k, void *stream);
 
+/* ---------------------------------------------------------------------- */
+/* Tile layout of the expert stacks.  Every GEMV, FFN and layer entry point  */
+/* reads its Q4_K weight stacks in this order, which q4k_pack_tiles writes   */
+/* once, at load time, from GGUF row order (the superblocks above, row after */
+/* row).  It holds the same 144-byte superblocks, regrouped so that the      */
+/* lanes of a GPU wave read contiguous bytes per load instruction:           */
+/*   rows go in groups of 8 (the last group padded with zero blocks); for    */
+/*   row group G and superblock s (nb = k/256 per row), tile (G, s) of 1152  */
+/*   bytes sits at (G*nb + s)*1152 and holds                                 */
+/*     bytes    0..127   the 8 rows' 16-byte headers (d, dmin, scales), row  */
+/*                       r at 16*r;                                          */
+/*     bytes  128..639   for chunk c = 0..3 and row r: nibble bytes          */
+/*                       32c .. 32c+15 of the row at 128 + 16*(8c + r);      */
+/*     bytes  640..1151  nibble bytes 32c+16 .. 32c+31 at 640 + 16*(8c + r). */
+/* An n x k matrix takes q4k_tiles_bytes(n, k) = ceil(n/8)*8*(k/256)*144    */
+/* bytes, the GGUF size when n is a multiple of 8; expert e of a stack       */
+/* starts at e*q4k_tiles_bytes(n, k).                                         */
+/* ---------------------------------------------------------------------- */
+int64_t q4k_tiles_bytes(int64_t n, int64_t k);   /* -1 on a bad shape */
+
+/* n_mats matrices of n x k: GGUF row order (n_mats * n*(k/256)*144 bytes at
+ * `blocks`) -> tile layout (n_mats * q4k_tiles_bytes(n, k) bytes at `tiles`);
+ * a pure permutation of the bytes (zero blocks fill a last partial row
+ * group).  q4k_unpack_tiles is its inverse.  n >= 1, k a positive multiple
+ * of 256, n_mats >= 0; both pointers 16-byte aligned and distinct.  Errors:
+ * Q4K_ERR_SHAPE, Q4K_ERR_NULL. */
+int q4k_pack_tiles(const void *blocks, void *tiles, int64_t n_mats, int64_t n, int64_t k,
+                   void *stream);
+int q4k_unpack_tiles(const void *tiles, void *blocks, int64_t n_mats, int64_t n, int64_t k,
+                     void *stream);
+
 /* Scratch bytes that the bucketed modes need for `n_pairs` (token, slot)
  * pairs over `num_experts` experts. */
 int64_t moe_bucket_workspace_bytes(int64_t n_pairs, int64_t num_experts);
@@ -152,9 +184,10 @@ int moe_bucket(const int32_t *ids, int64_t n_pairs, int64_t num_experts, void *w
 
 /* Batched indirect-dispatch Q4_K GEMV ([FK]
  * dispatch_gemv_q4k_moe_id_batched_on_encoder and module doc).
- *   w_stacked : [num_experts, n, k/256] superblocks, 16-byte aligned; expert
- *               e starts at byte e*n*(k/256)*144.  The caller pre-offsets the
- *               pointer if the stack starts inside a larger buffer ([FK]
+ *   w_stacked : [num_experts] n x k Q4_K matrices in the tile layout
+ *               (q4k_pack_tiles), 16-byte aligned; expert e starts at byte
+ *               e*q4k_tiles_bytes(n, k).  The caller pre-offsets the pointer
+ *               if the stack starts inside a larger buffer ([FK]
  *               weights_byte_offset).
  *   src1      : activations, 4-byte aligned (any float offset and stride;
  *               16-byte aligned rows load faster); pair p = token*top_k + slot
@@ -180,7 +213,8 @@ int q4k_moe_id_gemv(const void *w_stacked, const float *src1, const int32_t *ids
 /* Fused gate + up id-GEMV with SiLU ([FK] test module:
  * dispatch_gemv_q4k_moe_id_gate_up_silu_batched_on_encoder, which writes
  * [m*top_k, n] rows of silu(gate.x) * (up.x); [MF] swiglu_fused).
- *   w_gate, w_up : two stacks of the same shape [num_experts, n, k/256]
+ *   w_gate, w_up : two stacks of the same shape ([num_experts] n x k
+ *                  matrices, tile layout)
  *   out          : [m*top_k, n] fp32, out[p,r] = silu(g)*u with
  *                  g = W_gate[ids[p]][r].x, u = W_up[ids[p]][r].x, x the
  *                  pair's activation row (strides as in q4k_moe_id_gemv).
@@ -199,8 +233,8 @@ int q4k_moe_gate_up_silu(const void *w_gate, const void *w_up, const float *src1
 
 /* Expert FFN for all (token, slot) pairs ([MF] module doc: gate and up
  * matvecs, SwiGLU, down matvec; encode_moe_gather_id_fuse for the strides).
- *   w_gate, w_up : [num_experts, inter, hidden/256] superblocks
- *   w_down       : [num_experts, hidden, inter/256] superblocks
+ *   w_gate, w_up : [num_experts] inter x hidden matrices, tile layout
+ *   w_down       : [num_experts] hidden x inter matrices, tile layout
  *   h_post       : [m, hidden] fp32 (one row per token, shared by its slots)
  *   ids          : [m*top_k] int32
  *   act          : [m*top_k, inter] fp32 out: silu(gate.x) * (up.x)

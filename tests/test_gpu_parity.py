@@ -38,6 +38,22 @@ def T(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
+def W(stack, n, k, dev):
+    """Q4_K matrices of n x k in GGUF row order (a host array or a device
+    tensor) -> a device stack in the tile layout every GEMV entry point reads
+    (q4k_pack_tiles)."""
+    d = stack if torch.is_tensor(stack) else T(stack, dev)
+    n_mats = d.numel() // q4.q4k_matrix_bytes(n, k)
+    out = torch.empty(n_mats * q4.q4k_tiles_bytes(n, k), dtype=torch.uint8, device=dev)
+    q4.q4k_pack_tiles(d, out, n_mats, n, k)
+    return out
+
+
+def Ws(stacks, H, I, dev):
+    """gate, up, down stacks (inter x hidden, inter x hidden, hidden x inter)."""
+    return [W(s, r, c, dev) for s, (r, c) in zip(stacks, [(I, H), (I, H), (H, I)])]
+
+
 def sync_np(t):
     torch.cuda.synchronize()
     return t.cpu().numpy()
@@ -62,14 +78,12 @@ def touched_stack(cfg, tensor_id, rows, cols, experts, dev, num_experts=None):
     weights, the rest stay zero (never read by a correct kernel)."""
     E = num_experts or cfg.num_experts
     nbytes = oracle.q4k_matrix_bytes(rows, cols)
-    d = torch.zeros(E * nbytes, dtype=torch.uint8, device=dev)
     experts = sorted(set(int(e) for e in experts))
     blks = list(POOL.map(lambda e: expert_blocks(cfg, tensor_id, e, rows, cols), experts))
     host = np.zeros(E * nbytes, np.uint8)
     for e, b in zip(experts, blks):
-        d[e * nbytes:(e + 1) * nbytes] = T(b, dev)
         host[e * nbytes:(e + 1) * nbytes] = b
-    return d, host
+    return W(host, rows, cols, dev), host
 
 
 # --------------------------------------------------------------- decode ----
@@ -119,6 +133,43 @@ def test_quantize_bytes_match_oracle(dev):
     assert np.array_equal(got, want), f"{(got != want).sum()} bytes differ"
 
 
+def _tiles_ref(gguf, n_mats, n, k):
+    """The tile layout as include/q4kmoe.h defines it, written out with numpy:
+    per matrix, tile (G, s) of 1152 bytes at (G*nb + s)*1152 holding the 8
+    rows' headers, then for chunk c and row r the first and the second 16
+    nibble bytes of the chunk."""
+    nb = k // 256
+    n8 = -(-n // 8) * 8
+    blocks = gguf.reshape(n_mats, n, nb, 144)
+    out = np.zeros((n_mats, n8 // 8, nb, 1152), np.uint8)
+    for r in range(n):
+        G, r8 = divmod(r, 8)
+        b = blocks[:, r]                                   # [n_mats, nb, 144]
+        out[:, G, :, 16 * r8:16 * r8 + 16] = b[:, :, 0:16]
+        for c in range(4):
+            o0 = 128 + 16 * (8 * c + r8)
+            o1 = 640 + 16 * (8 * c + r8)
+            out[:, G, :, o0:o0 + 16] = b[:, :, 16 + 32 * c:32 + 32 * c]
+            out[:, G, :, o1:o1 + 16] = b[:, :, 32 + 32 * c:48 + 32 * c]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("n,k,n_mats", [(13, 768, 3), (64, 2048, 2), (1, 256, 1), (100, 4096, 1)])
+def test_pack_tiles_layout_and_round_trip(dev, n, k, n_mats):
+    """q4k_pack_tiles writes the documented layout byte for byte (zero blocks
+    past n), and q4k_unpack_tiles restores the GGUF bytes."""
+    say(f"pack tiles n={n} k={k} mats={n_mats}")
+    g = np.random.default_rng(n * 31 + k)
+    raw = g.integers(0, 256, n_mats * q4.q4k_matrix_bytes(n, k), dtype=np.uint8)
+    assert q4.q4k_tiles_bytes(n, k) == -(-n // 8) * 8 * (k // 256) * 144
+    packed = W(raw, n, k, dev)
+    assert packed.numel() == n_mats * q4.q4k_tiles_bytes(n, k)
+    assert np.array_equal(sync_np(packed), _tiles_ref(raw, n_mats, n, k))
+    back = torch.empty(raw.size, dtype=torch.uint8, device=dev)
+    q4.q4k_unpack_tiles(packed, back, n_mats, n, k)
+    assert np.array_equal(sync_np(back), raw)
+
+
 # -------------------------------------------------------------- id-GEMV ----
 
 def _id_gemv(dev, stack, E, n, k, x, ids, m, K, outer, inner, flag):
@@ -136,7 +187,7 @@ def test_id_gemv_tiny_config(dev):
     stack = np.concatenate([oracle.q4k_quantize(e) for e in w])
     want = oracle.q4k_moe_id_gemv(stack, cfg.num_experts, cfg.n, cfg.k, x, ids, cfg.m, cfg.top_k,
                                   cfg.k, 0)
-    args = (T(stack, dev), cfg.num_experts, cfg.n, cfg.k, T(x, dev), T(ids, dev), cfg.m,
+    args = (W(stack, cfg.n, cfg.k, dev), cfg.num_experts, cfg.n, cfg.k, T(x, dev), T(ids, dev), cfg.m,
             cfg.top_k, cfg.k, 0)
     outs = {f: _id_gemv(dev, *args, f) for f in (q4.Q4K_BUCKET_OFF, q4.Q4K_BUCKET_ON,
                                                   q4.Q4K_BUCKET_AUTO)}
@@ -175,7 +226,7 @@ def test_batched_equals_per_token_pages_case(dev, mode):
     c, E, n, k, m, K, ids, wg, wd, ag, ad = _golden_case()
     wts, act, outer, inner = (wg, ag, k, 0) if mode == "gate_up" else (wd, ad, K * k, k)
     stack = np.concatenate([oracle.q4k_quantize(w) for w in wts])
-    d_stack, d_act, d_ids = T(stack, dev), T(act, dev), T(ids, dev)
+    d_stack, d_act, d_ids = W(stack, n, k, dev), T(act, dev), T(ids, dev)
     batched = _id_gemv(dev, d_stack, E, n, k, d_act, d_ids, m, K, outer, inner,
                        q4.Q4K_BUCKET_OFF)
     per_tok = np.concatenate([
@@ -199,18 +250,18 @@ def test_unit_vector_probe_returns_dequantized_columns(dev, k):
     E, n = 3, 37
     stack = np.concatenate(quantize_many(
         [(g.standard_normal((n, k)) * 0.02).astype(np.float32) for _ in range(E)]))
-    W = oracle.q4k_dequantize(stack).reshape(E, n, k)
+    Wd = oracle.q4k_dequantize(stack).reshape(E, n, k)
     cols = sorted(set([0, 1, 31, 32, 63, 64, 255, 256 % k, k - 1, k // 2 + 5]))
     x = np.zeros((len(cols), k), np.float32)
     for i, c in enumerate(cols):
         x[i, c] = 1.0
     ids = np.array([[2, 0, 1]] * len(cols), np.int32).reshape(-1)
     for flag in (q4.Q4K_BUCKET_OFF, q4.Q4K_BUCKET_ON):
-        out = _id_gemv(dev, T(stack, dev), E, n, k, T(x, dev), T(ids, dev), len(cols), 3, k, 0,
+        out = _id_gemv(dev, W(stack, n, k, dev), E, n, k, T(x, dev), T(ids, dev), len(cols), 3, k, 0,
                        flag).reshape(len(cols), 3, n)
         for i, c in enumerate(cols):
             for s, e in enumerate([2, 0, 1]):
-                assert np.array_equal(bits(out[i, s]), bits(W[e, :, c])), (k, c, e, flag)
+                assert np.array_equal(bits(out[i, s]), bits(Wd[e, :, c])), (k, c, e, flag)
 
 
 @pytest.mark.parametrize("n,k,m,K,E", [
@@ -229,7 +280,7 @@ def test_id_gemv_ragged_shapes_and_edges(dev, n, k, m, K, E):
         ids[2] = E + 3
     for outer, inner in [(K * k, k), (K * k, 0)]:
         want = oracle.q4k_moe_id_gemv(stack, E, n, k, x.reshape(-1), ids, m, K, outer, inner)
-        d = (T(stack, dev), E, n, k, T(x.reshape(-1), dev), T(ids, dev), m, K, outer, inner)
+        d = (W(stack, n, k, dev), E, n, k, T(x.reshape(-1), dev), T(ids, dev), m, K, outer, inner)
         a = _id_gemv(dev, *d, q4.Q4K_BUCKET_OFF)
         b = _id_gemv(dev, *d, q4.Q4K_BUCKET_ON)
         band(a, want, f"n={n} k={k}")
@@ -332,7 +383,7 @@ def _shared_stacks(cfg, dev):
     H, I = cfg.hidden, cfg.inter
     hs = [expert_blocks(cfg, t, 0, r, c) for t, r, c in
           [(wl.T_SH_GATE, I, H), (wl.T_SH_UP, I, H), (wl.T_SH_DOWN, H, I)]]
-    return [T(h, dev) for h in hs], hs
+    return Ws(hs, H, I, dev), hs
 
 
 @pytest.mark.parametrize("cfg", [wl.CFG2, wl.CFG3], ids=lambda c: c.name)
@@ -644,7 +695,7 @@ def test_layer_invalid_ids_and_token_mode_edges(dev):
         res = []
         for flag in (q4.Q4K_BUCKET_OFF, q4.Q4K_BUCKET_ON):
             out = torch.empty(m, H, device=dev)
-            q4.moe_layer_forward(*[T(s, dev) for s in st], *[T(s, dev) for s in sh], T(h, dev),
+            q4.moe_layer_forward(*Ws(st, H, I, dev), *Ws(sh, H, I, dev), T(h, dev),
                                  T(hm, dev), T(ids, dev), T(rw, dev), T(lg, dev), out, H, I, E, m,
                                  K, 1, flag, ws, wsb)
             res.append(sync_np(out))
@@ -761,7 +812,7 @@ def test_self_bucketed_layer_equals_bucketing_launch(dev):
     _, _, _, eo = oracle.moe_expert_ffn(*st, E, H, I, h, ids2, m, K)
     _, _, _, so = oracle.moe_expert_ffn(*sh, 1, H, I, h, np.zeros(m, np.int32), m, 1)
     want = oracle.moe_combine_residual(hm, eo, rw, so, lg, H, m, K, 1)
-    args = ([T(x, dev) for x in st], [T(x, dev) for x in sh], T(h, dev), T(hm, dev),
+    args = (Ws(st, H, I, dev), Ws(sh, H, I, dev), T(h, dev), T(hm, dev),
             T(ids2, dev), T(rw, dev), T(lg, dev), H, I, E, m, K, 1)
     selfb = _layer_raw(dev, *args)
     viaws = _layer_raw(dev, *args, flag=ON_VIA_WS)
@@ -777,7 +828,7 @@ def test_self_bucketed_layer_equals_bucketing_launch(dev):
         w = wl.device_normal((ne * r, c), 0.02, seed=7000 + t)
         b = torch.empty(ne * q4.q4k_matrix_bytes(r, c), dtype=torch.uint8, device=dev)
         q4.q4k_quantize(w, b, ne * r, c)
-        st.append(b)
+        st.append(W(b, r, c, dev))
     ids3 = g.integers(0, E, m * K).astype(np.int32)
     ids3[:40] = 17                                        # one bucket of 5 chunks
     h = g.standard_normal((m, H)).astype(np.float32)
@@ -822,8 +873,8 @@ def test_self_bucketed_layer_edges(dev):
             _, _, _, so = oracle.moe_expert_ffn(*sh, 1, H, I, h, np.zeros(m, np.int32), m, 1)
         want = oracle.moe_combine_residual(hm, eo, rw, so, lg if mode == 1 else None, H, m, K,
                                            mode)
-        shd = [T(x, dev) for x in sh] if mode else [None, None, None]
-        args = ([T(x, dev) for x in st], shd, T(h, dev), T(hm, dev), T(ids, dev), T(rw, dev),
+        shd = Ws(sh, H, I, dev) if mode else [None, None, None]
+        args = (Ws(st, H, I, dev), shd, T(h, dev), T(hm, dev), T(ids, dev), T(rw, dev),
                 T(lg, dev), H, I, E, m, K, mode)
         selfb = _layer_raw(dev, *args)
         viaws = _layer_raw(dev, *args, flag=ON_VIA_WS)

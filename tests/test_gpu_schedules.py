@@ -22,7 +22,7 @@ import oracle
 import bit_quantized_moe_superblock_amd as q4
 from bit_quantized_moe_superblock_amd import workloads as wl
 from _util import band, bits
-from test_gpu_parity import (T, _ffn_case, _shared_stacks, quantize_many, say, sync_np)
+from test_gpu_parity import (T, Ws, _ffn_case, _shared_stacks, quantize_many, say, sync_np)
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -286,7 +286,7 @@ def test_layer_token_mode_when_down_rows_do_not_fit(dev):
     rw = g.random(m * K).astype(np.float32)
     lg = g.standard_normal(m).astype(np.float32)
     want = _oracle_layer(st, sh, h, hm, ids, rw, lg, H, I, E, m, K, 1)
-    args = ([T(x, dev) for x in st], [T(x, dev) for x in sh], T(h, dev), T(hm, dev), T(ids, dev),
+    args = (Ws(st, H, I, dev), Ws(sh, H, I, dev), T(h, dev), T(hm, dev), T(ids, dev),
             T(rw, dev), T(lg, dev), H, I, E, m, K, 1)
     off = _layer(dev, *args, OFF)
     band_rows(off, want, "token mode, unfused down")
@@ -310,7 +310,7 @@ def test_layer_past_in_kernel_bucketing_limit_unaligned(dev):
     rw = g.random(m * K).astype(np.float32)
     lg = g.standard_normal(m).astype(np.float32)
     want = _oracle_layer(st, sh, hx, hm, ids, rw, lg, H, I, E, m, K, 2)
-    args = ([T(x, dev) for x in st], [T(x, dev) for x in sh], T(hbuf, dev)[1:], T(hm, dev),
+    args = (Ws(st, H, I, dev), Ws(sh, H, I, dev), T(hbuf, dev)[1:], T(hm, dev),
             T(ids, dev), T(rw, dev), T(lg, dev), H, I, E, m, K, 2)
     outs = {f: _layer(dev, *args, f) for f in (ON, VEC, OFF)}
     for f, o in outs.items():

@@ -28,11 +28,20 @@ def _stacks(cfg, ids, dev):
             host[e * nb:(e + 1) * nb] = oracle.q4k_quantize(
                 wl.expert_weight(cfg, t, e, rows, cols))
         h.append(host)
-        d.append(torch.from_numpy(host).to("cuda"))
+        d.append(_tiles(host, rows, cols))
     sh_h = [oracle.q4k_quantize(wl.expert_weight(cfg, wl.T_SH_GATE + t, 0, rows, cols))
             for t, (rows, cols) in enumerate([(I, H), (I, H), (H, I)])]
-    sh_d = [torch.from_numpy(x).to("cuda") for x in sh_h]
+    sh_d = [_tiles(x, rows, cols) for x, (rows, cols) in zip(sh_h, [(I, H), (I, H), (H, I)])]
     return d, h, sh_d, sh_h
+
+
+def _tiles(host, n, k):
+    """GGUF-order matrices -> a device stack in the tile layout."""
+    src = torch.from_numpy(host).to("cuda")
+    n_mats = host.size // q4.q4k_matrix_bytes(n, k)
+    out = torch.empty(n_mats * q4.q4k_tiles_bytes(n, k), dtype=torch.uint8, device="cuda")
+    q4.q4k_pack_tiles(src, out, n_mats, n, k)
+    return out
 
 
 def _run(cfg, flag):
