@@ -79,6 +79,27 @@ __device__ __forceinline__ PairRef pair_ref(const GemvArgs &a, int q) {
     return r;
 }
 
+// pair_ref from an id the caller has already loaded (e_raw: ids[q] for a
+// routed pair) and the pair's activation row x.
+__device__ __forceinline__ PairRef pair_ref_id(const GemvArgs &a, int q, int e_raw,
+                                               const float *x) {
+    PairRef r;
+    r.x = x;
+    if (q < a.n_pairs) {
+        r.valid = (unsigned)e_raw < (unsigned)a.num_experts;
+        const int64_t off = r.valid ? (int64_t)e_raw * a.mat : 0;
+        r.w0 = a.w0 + off;
+        r.w1 = a.w1 ? a.w1 + off : nullptr;
+        r.out = a.dst + (int64_t)q * a.n;
+    } else {
+        r.valid = true;
+        r.w0 = a.s0;
+        r.w1 = a.s1;
+        r.out = a.dst_sh + (int64_t)(q - a.n_pairs) * a.n;
+    }
+    return r;
+}
+
 // Activation row of pair q, when the caller knows (uniformly across the
 // workgroup) whether the pair is a shared-expert pair.  A lane-varying choice
 // between the two argument fields compiles into a per-lane load from the
@@ -111,10 +132,10 @@ __device__ __forceinline__ void stage_issue(XOf x_of, int base, int total, int k
                                             StageBatch &b) {
     const int nsub = k >> 5;
     b.f = base + (int)threadIdx.x;
-    if (total <= 0)
-        return;
     // Threads past the end re-load the last sub-block (clamped, never
-    // committed) so the loads need no lane-divergent branch.
+    // committed) so the loads need no branch: a load under a branch makes
+    // the wait-count pass lose the issue order at the join, and a later
+    // wait for an earlier load then drains these too.  total >= 1.
     const int f = b.f < total ? b.f : total - 1;
     const int row = f / nsub, j = f - row * nsub;
     const float *src = x_of(row) + 32 * j;
@@ -281,13 +302,17 @@ struct WaveStage {
     float4 v[8];
 };
 
+// Lanes past the class's superblocks (or of a class without any) load a
+// clamped superblock of the row and commit nothing, so the loads need no
+// branch.
 template <bool VEC>
-__device__ __forceinline__ void wave_stage_issue(const float *x, int cls, int T, int t0,
+__device__ __forceinline__ void wave_stage_issue(const float *x, int cls, int T, int t0, int nb,
                                                  WaveStage &b) {
     const int l = threadIdx.x & 63;
     const int t = t0 + (l >> 3);
-    const int tc = t < T ? t : T - 1;   // clamped (T >= 1): never committed
-    const float *src = x + 256 * (cls + kClasses * tc) + 32 * (l & 7);
+    const int tc = t < T ? t : (T > 0 ? T - 1 : 0);
+    const int sb = cls + kClasses * tc;
+    const float *src = x + 256 * (sb < nb ? sb : nb - 1) + 32 * (l & 7);
     if constexpr (VEC) {
 #pragma unroll
         for (int q = 0; q < 8; q++)

@@ -51,7 +51,28 @@ __global__ __launch_bounds__(64 * kClasses) void k_rows(GemvArgs a) {
         const BucketView bv(a.bucket, a.num_experts, a.n_pairs);
         q = bv.pairs[q];
     }
-    const PairRef pr = pair_ref(a, q);
+    const int nb = a.k >> 8;
+    const int T = class_steps(nb, wave);   // superblocks wave + 4t, t < T
+    // The pair's id is requested first and its activations next (they do not
+    // depend on the id), so waiting for the id leaves them in flight.
+    const bool routed = q < a.n_pairs;
+    int e_raw = a.ids[routed ? q : 0];
+    __builtin_amdgcn_sched_barrier(0);
+    const float *x;
+    if (routed) {
+        const int t = q / a.top_k, s = q - t * a.top_k;
+        x = a.src1 + t * a.outer + s * a.inner;
+    } else {
+        x = a.src1_sh + (q - a.n_pairs) * a.outer_sh;
+    }
+    WaveStage xb;
+    wave_stage_issue<VEC>(x, wave, T, 0, nb, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    // first use of the id, after the activation loads: its wait leaves them
+    // in flight (left to itself the compiler moves the id into a scalar
+    // register, and so waits for it, right after its load)
+    asm volatile("" : "+v"(e_raw));
+    const PairRef pr = pair_ref_id(a, q, e_raw, x);
     constexpr int ROWS = RP * 2 * kTileRows;   // rows of the workgroup
     const int64_t row0 = (int64_t)blockIdx.x * ROWS;
     if (!pr.valid) {   // id outside [0, E): zero rows
@@ -65,8 +86,6 @@ __global__ __launch_bounds__(64 * kClasses) void k_rows(GemvArgs a) {
         const int64_t g = (int64_t)blockIdx.x * (2 * RP) + 2 * rp + (lane >> 5);
         return g < n8 ? g : (int64_t)n8 - 1;
     };
-    const int nb = a.k >> 8;
-    const int T = class_steps(nb, wave);           // superblocks wave + 4t, t < T
     float *xw = lds + wave * class_steps(nb, 0) * kStepFloats;
     const uint8_t *mat[NT];
     mat[0] = pr.w0;
@@ -87,16 +106,13 @@ __global__ __launch_bounds__(64 * kClasses) void k_rows(GemvArgs a) {
         for (int nt = 0; nt < NT; nt++)
             acc[rp][nt] = 0.0f;
     if (T > 0) {   // uniform per wave
-        WaveStage xb;
-        wave_stage_issue<VEC>(pr.x, wave, T, 0, xb);
-        __builtin_amdgcn_sched_barrier(0);   // the activation loads ahead of the weights
         Step<NT> buf[D];
 #pragma unroll
         for (int d = 0; d < D; d++)
             load_unit(d, buf[d]);
         wave_stage_commit(xb, T, 0, xw);
         for (int t0 = 8; t0 < T; t0 += 8) {   // more than 8 superblocks per class
-            wave_stage_issue<VEC>(pr.x, wave, T, t0, xb);
+            wave_stage_issue<VEC>(pr.x, wave, T, t0, nb, xb);
             wave_stage_commit(xb, T, t0, xw);
         }
         wave_lds_fence();
@@ -190,14 +206,14 @@ __global__ __launch_bounds__(64 * W) void k_down_combine(GemvArgs a, CombineArgs
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
     const int64_t G = blockIdx.x;
-    // 1. the combine's routing weights, gate logit and h_mid, loaded here so
-    //    that the combine at the end waits on no memory (one load per thread,
-    //    unconditional with a clamped index)
+    // 1. the token's ids, then the combine's routing weights, gate logit and
+    //    h_mid, loaded here so that the combine at the end waits on no memory
+    //    (one load per thread, unconditional with a clamped index)
     __shared__ float rw_lds[kMaxTopK];
-    __shared__ int dead_lds[kMaxTopK];
+    __shared__ int ex_lds[kMaxTopK];
     const int own = tok * K + (tid < K ? tid : K - 1);
+    const int e_own = a.ids[own];   // first: waiting for it leaves the rest in flight
     const float rw_own = cb.route_w[own];
-    const int e_own = a.ids[own];
     const bool gated = a.m_sh > 0 && cb.shared_mode == 1;   // uniform
     const float logit = gated ? cb.shared_logit[tok] : 0.0f;
     const int64_t orow = G * kTileRows + (tid < kTileRows ? tid : 0);
@@ -215,6 +231,13 @@ __global__ __launch_bounds__(64 * W) void k_down_combine(GemvArgs a, CombineArgs
     const int total = np * nsub;
     StageBatch xb;
     stage_issue<VEC>(x_of, 0, total, a.k, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    // the token's experts into LDS (-1 for ids outside [0, E))
+    if (tid < K) {
+        ex_lds[tid] = (unsigned)e_own < (unsigned)a.num_experts ? e_own : -1;
+        rw_lds[tid] = rw_own;
+    }
+    lds_barrier();
     // 2. this wave's tasks j = 0 .. ntask-1 (task wave + W j): pair pair pp,
     //    class c, T(c) superblocks each; S superblocks in all, walked D at a
     //    time with the loads D ahead (clamped to the last: no load under a
@@ -235,15 +258,11 @@ __global__ __launch_bounds__(64 * W) void k_down_combine(GemvArgs a, CombineArgs
         return p < np ? p : np - 1;
     };
     auto mat_of = [&](int pp) -> const uint8_t * {
-        // both pairs' experts by scalar loads, then this lane's one
-        const int p0 = 2 * pp, p1 = 2 * pp + 1 < np ? 2 * pp + 1 : np - 1;
-        const int e0 = p0 < K ? a.ids[tok * K + p0] : 0;
-        const int e1 = p1 < K ? a.ids[tok * K + p1] : 0;
-        const int p = jh ? p1 : p0;
-        const int e = jh ? e1 : e0;
+        const int p = pair_of(pp);
         if (p >= K)
             return a.s0;
-        return a.w0 + (int64_t)((unsigned)e < (unsigned)a.num_experts ? e : 0) * a.mat;
+        const int e = ex_lds[p];
+        return a.w0 + (int64_t)(e >= 0 ? e : 0) * a.mat;
     };
     int lj = 0, lt = 0, ls = 0;   // load cursor: task lj, its superblock lt
     auto load_next = [&](Step<1> &b) {
@@ -262,10 +281,6 @@ __global__ __launch_bounds__(64 * W) void k_down_combine(GemvArgs a, CombineArgs
 #pragma unroll
         for (int d = 0; d < D; d++)
             load_next(buf[d]);
-    }
-    if (tid < K) {
-        rw_lds[tid] = rw_own;
-        dead_lds[tid] = (unsigned)e_own >= (unsigned)a.num_experts;
     }
     // 3. activation rows of the token's pairs into LDS (first batch, then any
     //    further ones)
@@ -308,7 +323,7 @@ __global__ __launch_bounds__(64 * W) void k_down_combine(GemvArgs a, CombineArgs
         };
         float accr = hm;
         for (int s = 0; s < K; s++) {
-            const float yv = dead_lds[s] ? 0.0f : y_of(s);   // invalid id: no contribution
+            const float yv = ex_lds[s] < 0 ? 0.0f : y_of(s);   // invalid id: no contribution
             accr = __builtin_fmaf(rw_lds[s], yv, accr);
             if (cb.expert_out)
                 cb.expert_out[(int64_t)(tok * K + s) * a.n + orow] = yv;
