@@ -39,10 +39,10 @@ namespace q4k {
 
 // ------------------------------------------------------------ pair mode ----
 
-template <int NT, int EPI, bool VEC, int D, int RP>
+template <int NT, int EPI, bool VEC, int D>
 __global__ __launch_bounds__(64 * kClasses) void k_rows(GemvArgs a) {
     extern __shared__ float lds[];   // per wave: its class's staged superblocks
-    __shared__ float part[kClasses][RP][NT][2 * kTileRows];
+    __shared__ float part[kClasses][NT][2 * kTileRows];
     fetch_args(a);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
@@ -73,43 +73,31 @@ __global__ __launch_bounds__(64 * kClasses) void k_rows(GemvArgs a) {
     // register, and so waits for it, right after its load)
     asm volatile("" : "+v"(e_raw));
     const PairRef pr = pair_ref_id(a, q, e_raw, x);
-    constexpr int ROWS = RP * 2 * kTileRows;   // rows of the workgroup
-    const int64_t row0 = (int64_t)blockIdx.x * ROWS;
+    const int64_t row0 = (int64_t)blockIdx.x * (2 * kTileRows);
     if (!pr.valid) {   // id outside [0, E): zero rows
-        if (tid < ROWS && row0 + tid < a.n)
+        if (tid < 2 * kTileRows && row0 + tid < a.n)
             pr.out[row0 + tid] = 0.0f;
         return;
     }
     const int n8 = (a.n + kTileRows - 1) / kTileRows;
-    // row group of this lane in row pair rp (clamped; stores are guarded)
-    auto group = [&](int rp) {
-        const int64_t g = (int64_t)blockIdx.x * (2 * RP) + 2 * rp + (lane >> 5);
-        return g < n8 ? g : (int64_t)n8 - 1;
-    };
+    const int64_t Graw = 2 * (int64_t)blockIdx.x + (lane >> 5);
+    const int64_t G = Graw < n8 ? Graw : n8 - 1;   // this lane's row group (clamped;
+                                                   // stores are guarded)
     float *xw = lds + wave * class_steps(nb, 0) * kStepFloats;
     const uint8_t *mat[NT];
     mat[0] = pr.w0;
     if constexpr (NT == 2)
         mat[1] = pr.w1;
-    // unit u of the wave: row pair u / T, its superblock u % T (clamped to the
-    // last unit, u < RP T)
-    const int U = RP * T;
-    auto load_unit = [&](int u, Step<NT> &b) {
-        const int uc = u < U ? u : U - 1;
-        const int rp = uc / T, t = uc - rp * T;
-        load_step<NT>(mat, group(rp), wave + kClasses * t, nb, b);
-    };
-    float acc[RP][NT];
+    auto sb_of = [&](int t) { return wave + kClasses * (t < T ? t : T - 1); };   // clamped
+    float acc[NT];
 #pragma unroll
-    for (int rp = 0; rp < RP; rp++)
-#pragma unroll
-        for (int nt = 0; nt < NT; nt++)
-            acc[rp][nt] = 0.0f;
+    for (int nt = 0; nt < NT; nt++)
+        acc[nt] = 0.0f;
     if (T > 0) {   // uniform per wave
         Step<NT> buf[D];
 #pragma unroll
         for (int d = 0; d < D; d++)
-            load_unit(d, buf[d]);
+            load_step<NT>(mat, G, sb_of(d), nb, buf[d]);
         wave_stage_commit(xb, T, 0, xw);
         for (int t0 = 8; t0 < T; t0 += 8) {   // more than 8 superblocks per class
             wave_stage_issue<VEC>(pr.x, wave, T, t0, nb, xb);
@@ -117,58 +105,34 @@ __global__ __launch_bounds__(64 * kClasses) void k_rows(GemvArgs a) {
         }
         wave_lds_fence();
         const int c = (lane >> 3) & 3;
-        // D units per round; the refill loads the ones D ahead (clamped to
-        // the last, so that no load sits under a branch).  The row pairs run
-        // in order, each over the class's superblocks in ascending order.
-        for (int u0 = 0; u0 < U; u0 += D) {
+        // D superblocks per round; the refill loads the ones D ahead (clamped
+        // to the last, so that no load sits under a branch)
+        for (int t0 = 0; t0 < T; t0 += D) {
 #pragma unroll
             for (int d = 0; d < D; d++) {
-                const int u = u0 + d;
-                if (u < U) {
-                    const int rp = u / T, t = u - rp * T;
-                    const float *xs = xw + t * kStepFloats;
-                    float a1[NT];
-#pragma unroll
-                    for (int nt = 0; nt < NT; nt++)
-                        a1[nt] = 0.0f;
-                    // the row pair's accumulators by a uniform index: select
-                    // into and out of a temporary so they stay in registers
-#pragma unroll
-                    for (int r = 0; r < RP; r++)
-                        if (r == rp)
-#pragma unroll
-                            for (int nt = 0; nt < NT; nt++)
-                                a1[nt] = acc[r][nt];
-                    step_units<NT>(buf[d], xs + 68 * c, xs + 4 * 68 + 2 * c, a1);
-#pragma unroll
-                    for (int r = 0; r < RP; r++)
-                        if (r == rp)
-#pragma unroll
-                            for (int nt = 0; nt < NT; nt++)
-                                acc[r][nt] = a1[nt];
+                if (t0 + d < T) {
+                    const float *xs = xw + (t0 + d) * kStepFloats;
+                    step_units<NT>(buf[d], xs + 68 * c, xs + 4 * 68 + 2 * c, acc);
                 }
-                if (u0 + D < U)
-                    load_unit(u0 + D + d, buf[d]);
+                if (t0 + D < T)
+                    load_step<NT>(mat, G, sb_of(t0 + D + d), nb, buf[d]);
             }
         }
     }
 #pragma unroll
-    for (int rp = 0; rp < RP; rp++)
-#pragma unroll
-        for (int nt = 0; nt < NT; nt++) {
-            const float v = chunk_sum(acc[rp][nt]);
-            if ((lane & 24) == 0)   // lanes 0..7 and 32..39
-                part[wave][rp][nt][((lane >> 5) << 3) | (lane & 7)] = v;
-        }
+    for (int nt = 0; nt < NT; nt++) {
+        const float v = chunk_sum(acc[nt]);
+        if ((lane & 24) == 0)   // lanes 0..7 and 32..39
+            part[wave][nt][((lane >> 5) << 3) | (lane & 7)] = v;
+    }
     __syncthreads();
     const int64_t row = row0 + tid;
-    if (tid < ROWS && row < a.n) {
-        const int rp = tid >> 4, r16 = tid & 15;
+    if (tid < 2 * kTileRows && row < a.n) {
         float tot[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; nt++)
-            tot[nt] = class_total(part[0][rp][nt][r16], part[1][rp][nt][r16],
-                                  part[2][rp][nt][r16], part[3][rp][nt][r16]);
+            tot[nt] = class_total(part[0][nt][tid], part[1][nt][tid], part[2][nt][tid],
+                                  part[3][nt][tid]);
         pr.out[row] = epilogue<EPI, NT>(tot);
     }
 }
@@ -379,34 +343,24 @@ static size_t rows_lds_bytes(int64_t k) {
     return (size_t)kClasses * class_steps((int)(k >> 8), 0) * kStepFloats * sizeof(float);
 }
 
-template <int NT, int EPI, int D, int RP>
+template <int NT, int EPI, int D>
 static hipError_t go_rows(const GemvArgs &a, hipStream_t st) {
     const int n8 = (a.n + kTileRows - 1) / kTileRows;
-    dim3 grid((n8 + 2 * RP - 1) / (2 * RP), a.n_pairs + a.m_sh);
+    dim3 grid((n8 + 1) / 2, a.n_pairs + a.m_sh);
     auto go = [&](auto kern) {
         const size_t lds = set_lds((const void *)kern, rows_lds_bytes(a.k));
         hipLaunchKernelGGL(kern, grid, dim3(64 * kClasses), lds, st, a);
         return hipGetLastError();
     };
-    return a.vec ? go(k_rows<NT, EPI, true, D, RP>) : go(k_rows<NT, EPI, false, D, RP>);
+    return a.vec ? go(k_rows<NT, EPI, true, D>) : go(k_rows<NT, EPI, false, D>);
 }
 
-template <int NT, int EPI, int RP>
-static hipError_t rows_depth(const GemvArgs &a, hipStream_t st) {
-    const int u = RP * class_steps(a.k >> 8, 0);
-    return u <= 1 ? go_rows<NT, EPI, 1, RP>(a, st) : go_rows<NT, EPI, 2, RP>(a, st);
-}
-
-// Row pairs per workgroup: RP = 1 while that leaves fewer than 2 workgroups
-// per CU, else 2 (a wave then reuses its staged activations for both pairs);
-// units in flight per wave: all when a wave has one or two, two otherwise.
+// Superblocks in flight per wave: all of a class's when it has one or two,
+// two otherwise.
 template <int NT, int EPI>
 static hipError_t launch_rows(const GemvArgs &a, hipStream_t st) {
-    const int64_t n8 = (a.n + kTileRows - 1) / kTileRows;
-    const int64_t pairs = a.n_pairs + a.m_sh;
-    if ((n8 + 3) / 4 * pairs >= 2 * (int64_t)cu_count())
-        return rows_depth<NT, EPI, 2>(a, st);
-    return rows_depth<NT, EPI, 1>(a, st);
+    return class_steps(a.k >> 8, 0) <= 1 ? go_rows<NT, EPI, 1>(a, st)
+                                         : go_rows<NT, EPI, 2>(a, st);
 }
 
 bool q4k_self_bucket_ok(const GemvLaunch &L) {
@@ -431,8 +385,11 @@ static size_t dc_lds_bytes(int64_t k, int np) {
            sizeof(float);
 }
 
+// The token's rows must leave room for several workgroups per CU: with one
+// (e.g. top_k 8 at k = 2048: 80 KB) the launch runs in latency-bound rounds
+// of one workgroup per CU, slower than pair mode plus the combine.
 bool q4k_down_combine_ok(int64_t k, int64_t top_k, bool shared) {
-    return dc_lds_bytes(k, (int)top_k + (shared ? 1 : 0)) <= 160 * 1024;
+    return dc_lds_bytes(k, (int)top_k + (shared ? 1 : 0)) <= 48 * 1024;
 }
 
 template <int D, int W>

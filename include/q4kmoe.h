@@ -254,8 +254,9 @@ int moe_expert_ffn(const void *w_gate, const void *w_up, const void *w_down,
  *   token mode (OFF, or AUTO below Q4K_AUTO_BUCKET_MIN_TOKENS tokens): fused
  *                gate/up+SiLU over routed and shared pairs, then the down
  *                projection fused with the combine (2 launches; when the
- *                token's top_k+1 activation rows of `inter` floats do not fit
- *                one workgroup's LDS, down and the combine are 2 launches);
+ *                token's top_k+1 activation rows of `inter` floats take more
+ *                than 48 KB of a workgroup's LDS, down and the combine are 2
+ *                launches -- the same bits either way);
  *   bucketed (ON, PREBUILT, or AUTO from Q4K_AUTO_BUCKET_MIN_TOKENS tokens):
  *                bucketed gate/up+SiLU and down (the shared expert as one more
  *                bucket holding every token), then the combine.  On the
