@@ -382,7 +382,7 @@ __device__ __forceinline__ void mfma_item(const GemvArgs &a, bool shared, int bk
         for (int i = 0; i < 4; i++)
             yv[nt][i] = 0.0f;
     for (int sb0 = 0; sb0 < nb; sb0 += SB) {
-        __syncthreads();   // the previous slab's (or item's) LDS is consumed
+        lds_barrier();   // the previous slab's (or item's) LDS is consumed
         // weights of the slab's first superblocks in flight while staging
         // (kDepth superblocks in flight; indices are constants once the
         // loop is unrolled, so the tiles stay in registers)
