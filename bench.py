@@ -718,12 +718,27 @@ def main():
               "m32": Figure(torch, "cfg4 m32", big32.layer, range(8), big32.bytes_of(3)),
               "m32_ceil": Figure(torch, "cfg4 m32 ceiling", big32.ceiling([0, 1, 2]), range(8),
                                  big32.bytes_of(3))}
+        # the dominant launch of each (gate/up + SiLU) and the plain read of its bytes
+        for k, mo, n in (("m1", big, 32), ("m32", big32, 8)):
+            f4[k + "_gu"] = Figure(torch, f"cfg4 {k} gate/up", mo.gate_up, range(n),
+                                   mo.bytes_of(2))
+            f4[k + "_gu_ceil"] = Figure(torch, f"cfg4 {k} gate/up ceiling", mo.ceiling([0, 1]),
+                                        range(n), mo.bytes_of(2))
         run_rounds(list(f4.values()), R)
-        for k in ("m1", "m32"):
+        for k, kern in (("m1", "fused gate/up id-GEMV + SiLU (vector units, pair mode)"),
+                        ("m32", "bucketed gate/up + SiLU (matrix cores, pre-built buckets)")):
             s, c = f4[k].summary(), f4[k + "_ceil"].summary()
+            g, gc = f4[k + "_gu"].summary(), f4[k + "_gu_ceil"].summary()
             c4[k] = {"us_per_layer": s["us"], "us_q1": s["us_q1"], "us_q3": s["us_q3"],
                      "gbs": s["gbs"], "frac_hbm_peak": s["frac_hbm_peak"],
-                     "bytes_per_layer": s["bytes_per_step"], "ceiling_gbs": c["gbs"]}
+                     "bytes_per_layer": s["bytes_per_step"], "ceiling_gbs": c["gbs"],
+                     "roofline": {"bound": "hbm", "kernel": kern, "achieved": g["gbs"],
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(g["gbs"] / HBM_PEAK_GBS, 4),
+                                  "us_per_launch": g["us"], "us_q1": g["us_q1"],
+                                  "us_q3": g["us_q3"], "bytes_per_launch": g["bytes_per_step"],
+                                  "ceiling": gc["gbs"],
+                                  "frac_of_ceiling": round(g["gbs"] / gc["gbs"], 4)}}
         c4["workload"] = ("large-expert layer: hidden 7168, inter 2048, 256 experts, top_k 8, "
                           "unscaled shared expert (8 replicas); m=1 over 32 uniform draws of "
                           "distinct experts (a graph reads ~4 GB), m=32 over 8 draws")
