@@ -442,44 +442,118 @@ __device__ __forceinline__ void mfma_item(const GemvArgs &a, bool shared, int bk
 
 // ------------------------------------------------------- self-bucketing ---
 // The bucketing of the ids (moeflux expert_forward.rs, encode_moe_gather_id_fuse
-// step 1) done by every workgroup in LDS, so that a layer needs no separate
-// bucketing launch: histogram of the ids over E + 1 buckets (bucket E takes
-// ids outside [0, E)), chunks of at most kMP pairs per bucket in bucket order,
-// the pairs of a bucket in ascending pair order.  This is the chunk list the
-// bucketing kernel writes, in the same order, so an item computes exactly what
-// it computes from that list.
-constexpr int kSelfMaxPairs = 4 * kThreads;    // pairs 4 tid .. 4 tid + 3 per thread
-constexpr int kSelfMaxBuckets = 4 * kThreads;  // buckets 4 tid .. 4 tid + 3 per thread
-// chunks: at most one partial chunk per non-empty bucket plus P / kMP full ones
-constexpr int kSelfMaxChunks = kSelfMaxBuckets + kSelfMaxPairs / kMP;
+// step 1) done inside the launch, so that a layer needs no separate bucketing
+// launch.  Buckets are the experts plus one (bucket E takes ids outside
+// [0, E)); a bucket of c pairs has ceil(c / kMP) chunks; chunks are numbered
+// in bucket order, and chunk i of a bucket holds its pairs of ranks
+// kMP i .. kMP i + kMP - 1 in ascending pair order.  That is the chunk list
+// the bucketing kernel writes, in the same order, so an item computes exactly
+// what it computes from that list.
+//
+// One wave of each workgroup does it, with no barrier until it is done: its
+// LDS operations execute in program order, so the counters it zeroes, adds
+// to and reads need no synchronisation among themselves.
+constexpr int kSelfMaxPairs = 1024;
+constexpr int kSelfMaxBuckets = 1024;
+constexpr int kSelfIdRegs = kSelfMaxPairs / 64;   // ids per lane of the bucketing wave
 static_assert(kSelfMaxPairs == kSelfBucketMaxPairs && kSelfMaxBuckets == kSelfBucketMaxBuckets,
               "self-bucketing limits");
 static_assert(kSelfMaxBuckets * 4 <= mfma_lds_bytes(1), "self-bucketing scratch");
 
-// Exclusive sum over the workgroup of v (in thread order); wsum is 4 words of
-// LDS that no thread reads until this returns.
-__device__ __forceinline__ int block_exclusive_sum(int v, int *wsum) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int inc = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(inc, off, 64);
-        if (lane >= off)
-            inc += t;
-    }
-    if (lane == 63)
-        wsum[wave] = inc;
-    lds_barrier();
-    int base = 0;
-#pragma unroll
-    for (int w = 0; w < kThreads / 64; w++)
-        base += w < wave ? wsum[w] : 0;
-    return base + inc - v;
+struct SelfBuckets {
+    int chunk_start[kSelfMaxBuckets + 1];   // first chunk of each bucket; [B] = routed chunks
+    int pair_bucket[kSelfMaxPairs];         // bucket of each pair
+    int pairs[2][kMP];                      // the current item's pairs (two buffers)
+    int info[2][2];                         // the current item's bucket and pair count
+};
+
+// Inclusive sum over the lanes of a wave, in lane order: a shift-and-add
+// ladder inside each row of 16 lanes, then the totals of the rows before.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+    const int lane = threadIdx.x & 63;
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+              r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = lane >> 4;
+    return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
-// Chunk list entry: bucket (11 bits), chunk index within the bucket (13 bits),
-// pair count (<= kMP).
-__device__ __forceinline__ int chunk_pack(int b, int i, int c) { return b | (i << 11) | (c << 24); }
+// Bucketing wave: the buckets of all pairs (kept in LDS), their counts (in
+// the scratch `counts`, B words), and the chunk starts.  Returns the number
+// of routed chunks (every lane).
+__device__ __forceinline__ int self_bucket(const GemvArgs &a, SelfBuckets &sb, int *counts) {
+    const int lane = threadIdx.x & 63;
+    const int E = a.num_experts, P = a.n_pairs, B = E + 1;
+    // all the ids first, unconditional with a clamped index (no branch for
+    // the wait to join at), so their loads are in flight together
+    int raw[kSelfIdRegs];
+#pragma unroll
+    for (int j = 0; j < kSelfIdRegs; j++) {
+        const int q = 64 * j + lane;
+        raw[j] = a.ids[q < P ? q : P - 1];
+    }
+    for (int b = lane; b < B; b += 64)
+        counts[b] = 0;
+#pragma unroll
+    for (int j = 0; j < kSelfIdRegs; j++) {
+        if (64 * j >= P)   // uniform
+            break;
+        const int q = 64 * j + lane;
+        const int bk = q < P ? ((unsigned)raw[j] < (unsigned)E ? raw[j] : E) : -1;
+        sb.pair_bucket[q] = bk;
+        if (bk >= 0)
+            atomicAdd(&counts[bk], 1);
+    }
+    // chunk starts: exclusive sum of ceil(count / kMP) in bucket order
+    int run = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {   // uniform
+        const int b = b0 + lane;
+        const int ch = b < B ? (counts[b] + kMP - 1) / kMP : 0;
+        const int inc = wave_inclusive_sum(ch);
+        if (b < B)
+            sb.chunk_start[b] = run + inc - ch;
+        run += __builtin_amdgcn_readlane(inc, 63);
+    }
+    if (lane == 0)
+        sb.chunk_start[B] = run;
+    return run;
+}
+
+// Bucketing wave: bucket, pair count and pairs of routed chunk y into
+// buffer buf.
+__device__ __forceinline__ void self_pick(const GemvArgs &a, SelfBuckets &sb, int y, int buf) {
+    const int lane = threadIdx.x & 63;
+    const int P = a.n_pairs, B = a.num_experts + 1;
+    int b = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {   // uniform
+        const int bb = b0 + lane;
+        const bool hit = bb < B && sb.chunk_start[bb] <= y && y < sb.chunk_start[bb + 1];
+        const uint64_t m = __ballot(hit);
+        if (m) {
+            b = b0 + __builtin_ctzll(m);
+            break;
+        }
+    }
+    const int r0 = kMP * (y - sb.chunk_start[b]);
+    int rank = 0;
+    for (int q0 = 0; q0 < P; q0 += 64) {   // uniform
+        const int q = q0 + lane;
+        const bool in = q < P && sb.pair_bucket[q] == b;
+        const uint64_t m = __ballot(in);
+        const int r = rank + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (in && r >= r0 && r < r0 + kMP)
+            sb.pairs[buf][r - r0] = q;
+        rank += __popcll(m);
+    }
+    if (lane == 0) {
+        sb.info[buf][0] = b;
+        sb.info[buf][1] = rank - r0 < kMP ? rank - r0 : kMP;
+    }
+}
 
 // Persistent grid over the items (chunk, row tile), chunk-major, the shared
 // expert's chunks of 8 tokens after the routed ones.  The host cannot know the
@@ -488,71 +562,47 @@ __device__ __forceinline__ int chunk_pack(int b, int i, int c) { return b | (i <
 // grid holds as many workgroups as are resident at once and workgroup w takes
 // items w, w + G, ...  With a bucket workspace the chunk list and pair lists
 // come from it (the bucketing kernel's output); without one the workgroup
-// builds them (self-bucketing).
+// builds them (self-bucketing, above).
 template <int NT, int EPI, int SB, bool VEC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SB <= 4 ? 3 : 2)))
 void k_bucket_mfma(GemvArgs a, int tiles) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_b[];
-    __shared__ int chunk_list[kSelfMaxChunks];
-    __shared__ int chunk_pairs[kMP];
-    __shared__ int wsum[8];
+    __shared__ SelfBuckets sbk;
     __shared__ int n_chunks_lds;
     fetch_args(a);
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6;
     const int E = a.num_experts, P = a.n_pairs;
     const bool self = a.bucket == nullptr;
-    const BucketView bv(self ? chunk_list : a.bucket, E, P);   // workspace mode only
-    // 1. self-bucketing: the bucket of each of this thread's pairs
-    //    4 tid .. 4 tid + 3 (-1 past P), from clamped unconditional loads
-    int b[4] = {-1, -1, -1, -1};
+    const BucketView bv(self ? sbk.chunk_start : a.bucket, E, P);   // workspace mode only
     int n_chunks;
     if (self) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int p = 4 * tid + j;
-            const int e = a.ids[p < P ? p : P - 1];
-            b[j] = p < P ? ((unsigned)e < (unsigned)E ? e : E) : -1;
+        if (wave == 0) {
+            const int nc = self_bucket(a, sbk, (int *)lds_b);
+            if ((int)blockIdx.x / tiles < nc)
+                self_pick(a, sbk, (int)blockIdx.x / tiles, 0);
+            if ((tid & 63) == 0)
+                n_chunks_lds = nc;
         }
-        // 2. histogram (scratch in the staging LDS, free until the first item)
-        int *counts = (int *)lds_b;
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-            counts[4 * tid + j] = 0;
-        lds_barrier();
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-            if (b[j] >= 0)
-                atomicAdd(&counts[b[j]], 1);
-        lds_barrier();
-        // 3. chunk list: buckets 4 tid .. 4 tid + 3, ceil(count / kMP) chunks each
-        int c[4], hs = 0;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int bb = 4 * tid + j;
-            c[j] = bb <= E ? counts[bb] : 0;
-            hs += (c[j] + kMP - 1) / kMP;
-        }
-        int run = block_exclusive_sum(hs, wsum);
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-            for (int i = 0; i * kMP < c[j]; i++) {
-                const int n = c[j] - i * kMP < kMP ? c[j] - i * kMP : kMP;
-                chunk_list[run++] = chunk_pack(4 * tid + j, i, n);
-            }
-        if (tid == kThreads - 1)
-            n_chunks_lds = run;
         lds_barrier();
         n_chunks = n_chunks_lds;
     } else {
         n_chunks = *bv.n_chunks;
     }
     const int n_items = (n_chunks + (a.m_sh + kMP - 1) / kMP) * tiles;
-    // 4. the items of this workgroup
-    for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+    int kit = 0;
+    for (int it = blockIdx.x; it < n_items; it += gridDim.x, kit++) {
         const int y = it / tiles, x = it - y * tiles;
         const bool shared = y >= n_chunks;
+        const int buf = kit & 1;
+        if (self && kit > 0) {
+            // the other buffer holds the previous item's pairs, still read
+            // by waves that have not finished it
+            if (wave == 0 && !shared)
+                self_pick(a, sbk, y, buf);
+            lds_barrier();
+        }
         int bkt = 0, cnt, first = 0;
-        const int32_t *pl = chunk_pairs;
+        const int32_t *pl = sbk.pairs[buf];
         if (shared) {
             first = (y - n_chunks) * kMP;
             cnt = a.m_sh - first < kMP ? a.m_sh - first : kMP;
@@ -562,25 +612,8 @@ void k_bucket_mfma(GemvArgs a, int tiles) {
             cnt = packed >> 24;
             pl = bv.pairs + (packed & 0xFFFFFF);
         } else {
-            const int e = chunk_list[y];
-            bkt = e & 0x7FF;
-            cnt = e >> 24;
-            const int i0 = ((e >> 11) & 0x1FFF) * kMP;
-            // ranks of the bucket's pairs (ascending pair order); the
-            // previous item has read chunk_pairs before the scan's barrier
-            int f = 0;
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                f += b[j] == bkt ? 1 : 0;
-            int rank = block_exclusive_sum(f, wsum + 4);
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                if (b[j] == bkt) {
-                    if (rank >= i0 && rank < i0 + kMP)
-                        chunk_pairs[rank - i0] = 4 * tid + j;
-                    rank++;
-                }
-            lds_barrier();
+            bkt = sbk.info[buf][0];
+            cnt = sbk.info[buf][1];
         }
         mfma_item<NT, EPI, SB, VEC>(a, shared, bkt, cnt, pl, first, x * item_rows(EPI), lds_b);
     }
