@@ -314,11 +314,25 @@ def section_walk(torch, q4, wl, n_layers, rounds):
         for (r, c), t, y in zip(shapes, ts, ys):
             q4.q4tp_matvec(t, x, y, r, c)
 
+    # the read ceiling of the same access pattern: a plain read of each merged
+    # group's tensors, one launch per group, in the same order
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    reads = []
+    for ts in reps:
+        reads.append([(ts[g[0]], torch.tensor([ts[j].data_ptr() - ts[g[0]].data_ptr() for j in g],
+                                               dtype=torch.int64, device=dev),
+                       len(g), q4.q4tp_tensor_bytes(*shapes[g[0]])) for g in groups])
+
+    def ceiling(i):
+        for base, offs, n, nb in reads[i % 2]:
+            q4.q4k_ceiling_read(base, offs, n, nb, sink)
+
     nbytes = sum(q4.q4tp_tensor_bytes(r, c) for r, c in shapes)
     figs = [Figure(torch, "walk merged", merged, range(4), lambda i: nbytes),
-            Figure(torch, "walk single", single, range(4), lambda i: nbytes)]
+            Figure(torch, "walk single", single, range(4), lambda i: nbytes),
+            Figure(torch, "walk ceiling", ceiling, range(4), lambda i: nbytes)]
     run_rounds(figs, rounds)
-    m, s = figs[0].summary(), figs[1].summary()
+    m, s, c = figs[0].summary(), figs[1].summary(), figs[2].summary()
     return {
         "workload": f"dense Q4TiledP decode walk: {n_layers} layers of q, k, v, o 4096x4096, "
                     "gate and up 14336x4096, down 4096x14336, then the head 32000x4096, "
@@ -327,6 +341,8 @@ def section_walk(torch, q4, wl, n_layers, rounds):
         "bytes_per_walk": int(nbytes), "us_per_walk": m["us"], "us_q1": m["us_q1"],
         "us_q3": m["us_q3"], "gbs": m["gbs"], "frac_hbm_peak": m["frac_hbm_peak"],
         "us_per_walk_one_launch_per_tensor": s["us"], "gbs_one_launch_per_tensor": s["gbs"],
+        "ceiling_gbs": c["gbs"], "us_per_walk_ceiling": c["us"],
+        "frac_of_ceiling": round(m["gbs"] / c["gbs"], 4),
     }
 
 

@@ -9,9 +9,10 @@
 //   scale(r,g) = 2^(base + code*step).
 // y[r] = sum_g scale(r,g) * (sum_j nib*x[32g+j] - 8*sum_j x[32g+j]).
 //
-// LPR lanes (a power of two >= gpr, at most 256) cover a row, one 16-byte
-// group per lane (two when a row has more than 256 groups); x is staged in LDS
-// with per-group sums.  The group scale uses the hardware exp2 (about one
+// LPR lanes (a power of two >= gpr, at most 64) cover a row, one 16-byte
+// group per lane, or NG = ceil(gpr / 64) when a row has more than 64 groups:
+// a row never spans two waves, so its sum is one wave-wide DPP reduction; x is
+// staged in LDS with per-group sums.  The group scale uses the hardware exp2 (about one
 // ulp), as the page's kernel does.
 #include <type_traits>
 
@@ -53,13 +54,11 @@ __global__ __launch_bounds__(TPB) void k_q4tp_matvec(TpSegs sg, const float *__r
     const int rows = sg.rows[seg];
     float *__restrict__ y = yall + sg.yoff[seg];
     const int tile = (int)blockIdx.x - (seg ? sg.tile_end[seg - 1] : 0);
+    static_assert(LPR <= 64, "a row within one wave");
     constexpr int RPI = TPB / LPR;
-    constexpr int WL = LPR < 64 ? LPR : 64;
-    constexpr int WPR = LPR / WL;
     constexpr int XU = (LPR * NG + TPB - 1) / TPB;   // staging tasks per thread
     const int gpr = cols >> 5;
-    float *red = lds;           // cross-wave row sums (one per wave, at most 16)
-    float *xs = lds + 16;       // padded activations
+    float *xs = lds;            // padded activations
     float *sx = xs + 36 * gpr;  // group sums
     const int tid = threadIdx.x;
 
@@ -159,37 +158,26 @@ __global__ __launch_bounds__(TPB) void k_q4tp_matvec(TpSegs sg, const float *__r
             const float part = scale * __builtin_fmaf(-8.0f, sx[g], dot);
             acc += gok ? part : 0.0f;
         }
-        acc = group_sum<WL>(acc);
-        if constexpr (WPR > 1) {
-            const int wave = tid >> 6;
-            if ((tid & 63) == 0)
-                red[wave] = acc;
-            lds_barrier();
-            if (u == 0) {
-                float sum = red[wave];
-                for (int w = 1; w < WPR; w++)
-                    sum += red[wave + w];
-                acc = sum;
-            }
-            lds_barrier();
-        }
+        acc = group_sum<LPR>(acc);
         const int r = row0 + it * RPI + rsub;
         if (u == 0 && r < rows)
             y[r] = acc;
     }
 }
 
+// Lanes per row: the smallest power of two, at least 4, that covers the
+// row's groups, at most 64.
 static int tp_lanes(int gpr) {
     int l = 4;
-    while (l < gpr && l < 256)
+    while (l < gpr && l < 64)
         l <<= 1;
     return l;
 }
 
 // Row groups per workgroup (tpb / LPR rows each): the fewest whose weight
 // bytes are at least twice the staged activations (4 cols bytes, read from the
-// cache by every workgroup), at most 8 (4 with two groups per lane), while the
-// grid still gives every CU a workgroup.
+// cache by every workgroup), at most kMaxIt (fewer as a lane holds more
+// groups of a row), while the grid still gives every CU a workgroup.
 static int tp_iters(int tpb, int lpr, int max_it, int64_t row_bytes, int cols, int64_t total_rows,
                     int64_t cus) {
     const int rpi = tpb / lpr;
@@ -215,7 +203,7 @@ static hipError_t tp_launch(const void *const *ts, const int64_t *rows, int nseg
     int64_t total_rows = 0;
     for (int i = 0; i < nseg; i++)
         total_rows += rows[i];
-    constexpr int kMaxIt = NG == 1 ? 8 : 4;
+    constexpr int kMaxIt = NG == 1 ? 8 : (NG == 2 ? 4 : (NG <= 4 ? 2 : 1));
     int tpb = 512;
     if (NG == 1 && gpr <= 128) {
         const int it1k = tp_iters(1024, LPR, kMaxIt, row_bytes, cols, total_rows, cus);
@@ -225,7 +213,7 @@ static hipError_t tp_launch(const void *const *ts, const int64_t *rows, int nseg
     }
     const int RPI = tpb / LPR;
     const int it = tp_iters(tpb, LPR, kMaxIt, row_bytes, cols, total_rows, cus);
-    const size_t lds = (size_t)(16 + 36 * gpr + gpr) * sizeof(float);
+    const size_t lds = (size_t)(36 * gpr + gpr) * sizeof(float);
     auto go = [&](auto kern, int iters) {
         TpSegs sg{};
         int tiles = 0, yoff = 0;
@@ -244,22 +232,30 @@ static hipError_t tp_launch(const void *const *ts, const int64_t *rows, int nseg
     };
     // float4 activation loads need a 16-byte aligned x
     const bool xv = ((uintptr_t)x & 15) == 0;
+    // tp_iters returns a power of two no larger than kMaxIt: only those
+    // instantiations exist
     auto pick = [&](auto tpbc) -> hipError_t {
         constexpr int T = decltype(tpbc)::value;
-        switch (it) {
-        case 1: return xv ? go(k_q4tp_matvec<LPR, NG, 1, true, T>, 1) : go(k_q4tp_matvec<LPR, NG, 1, false, T>, 1);
-        case 2: return xv ? go(k_q4tp_matvec<LPR, NG, 2, true, T>, 2) : go(k_q4tp_matvec<LPR, NG, 2, false, T>, 2);
-        case 4: return xv ? go(k_q4tp_matvec<LPR, NG, 4, true, T>, 4) : go(k_q4tp_matvec<LPR, NG, 4, false, T>, 4);
-        default:
-            return xv ? go(k_q4tp_matvec<LPR, NG, (NG == 1 ? 8 : 4), true, T>, kMaxIt)
-                      : go(k_q4tp_matvec<LPR, NG, (NG == 1 ? 8 : 4), false, T>, kMaxIt);
-        }
+        auto run = [&](auto itc) {
+            constexpr int I = decltype(itc)::value;
+            return xv ? go(k_q4tp_matvec<LPR, NG, I, true, T>, I)
+                      : go(k_q4tp_matvec<LPR, NG, I, false, T>, I);
+        };
+        if constexpr (kMaxIt >= 8)
+            if (it >= 8)
+                return run(std::integral_constant<int, 8>{});
+        if constexpr (kMaxIt >= 4)
+            if (it >= 4)
+                return run(std::integral_constant<int, 4>{});
+        if constexpr (kMaxIt >= 2)
+            if (it >= 2)
+                return run(std::integral_constant<int, 2>{});
+        return run(std::integral_constant<int, 1>{});
     };
-    if (tpb == 1024)
-        return pick(std::integral_constant<int, 1024>{});
-    if (tpb == 512)
-        return pick(std::integral_constant<int, 512>{});
-    return pick(std::integral_constant<int, 256>{});
+    if constexpr (NG == 1)
+        if (tpb == 1024)
+            return pick(std::integral_constant<int, 1024>{});
+    return pick(std::integral_constant<int, 512>{});
 }
 
 hipError_t launch_q4tp_matvec_multi(const void *const *ts, const int64_t *rows, int nseg,
@@ -271,12 +267,17 @@ hipError_t launch_q4tp_matvec_multi(const void *const *ts, const int64_t *rows, 
     case 8: return tp_launch<8, 1>(ts, rows, nseg, x, y, c, st);
     case 16: return tp_launch<16, 1>(ts, rows, nseg, x, y, c, st);
     case 32: return tp_launch<32, 1>(ts, rows, nseg, x, y, c, st);
-    case 64: return tp_launch<64, 1>(ts, rows, nseg, x, y, c, st);
-    case 128: return tp_launch<128, 1>(ts, rows, nseg, x, y, c, st);
     default:
-        if (gpr <= 256)
-            return tp_launch<256, 1>(ts, rows, nseg, x, y, c, st);
-        return tp_launch<256, 2>(ts, rows, nseg, x, y, c, st);
+        switch ((gpr + 63) / 64) {   // groups per lane
+        case 1: return tp_launch<64, 1>(ts, rows, nseg, x, y, c, st);
+        case 2: return tp_launch<64, 2>(ts, rows, nseg, x, y, c, st);
+        case 3: return tp_launch<64, 3>(ts, rows, nseg, x, y, c, st);
+        case 4: return tp_launch<64, 4>(ts, rows, nseg, x, y, c, st);
+        case 5: return tp_launch<64, 5>(ts, rows, nseg, x, y, c, st);
+        case 6: return tp_launch<64, 6>(ts, rows, nseg, x, y, c, st);
+        case 7: return tp_launch<64, 7>(ts, rows, nseg, x, y, c, st);
+        default: return tp_launch<64, 8>(ts, rows, nseg, x, y, c, st);
+        }
     }
 }
 
