@@ -40,6 +40,15 @@ struct TpSegs {
     int nseg;
 };
 
+// A weight group, read once per launch: marked non-temporal so that the
+// streamed weights do not push the staged activations, which every workgroup
+// on the CU reads, out of the CU's cache.
+__device__ __forceinline__ uint4 load_stream(const uint8_t *p) {
+    typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+    const u4v w = __builtin_nontemporal_load((const u4v *)p);
+    return make_uint4(w.x, w.y, w.z, w.w);
+}
+
 template <int LPR, int NG, int ITERS, bool XV, int TPB>
 __global__ __launch_bounds__(TPB) void k_q4tp_matvec(TpSegs sg, const float *__restrict__ x,
                                                      float *__restrict__ yall, int cols) {
@@ -98,7 +107,7 @@ __global__ __launch_bounds__(TPB) void k_q4tp_matvec(TpSegs sg, const float *__r
             const int cb = (5 * g) >> 3;
             c0[it][j] = cp[cb];
             c1[it][j] = cp[cb + 1 < stride ? cb + 1 : cb];
-            qv[it][j] = *(const uint4 *)(t + ((int64_t)r * gpr + g) * 16);
+            qv[it][j] = load_stream(t + ((int64_t)r * gpr + g) * 16);
         }
     }
 
