@@ -19,7 +19,10 @@
 
 namespace q4k {
 
-enum { EPI_STORE = 0, EPI_SWIGLU = 1 };
+// Epilogues of the vector-unit kernels: store the row value, store
+// silu(gate) * up of the two matrices, or (a single matrix) store the values of
+// two row groups of it.
+enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_ROWPAIR = 2 };
 
 struct GemvArgs {
     const uint8_t *w0, *w1;   // routed stacks (w1: the up stack of the fused kernel)

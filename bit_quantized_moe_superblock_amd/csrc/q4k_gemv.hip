@@ -73,21 +73,28 @@ __global__ __launch_bounds__(64 * kClasses) void k_rows(GemvArgs a) {
     // register, and so waits for it, right after its load)
     asm volatile("" : "+v"(e_raw));
     const PairRef pr = pair_ref_id(a, q, e_raw, x);
-    const int64_t row0 = (int64_t)blockIdx.x * (2 * kTileRows);
+    // a workgroup covers RPW pairs of row groups: its half-waves' row groups,
+    // and with EPI_ROWPAIR the two row groups after them as the second matrix
+    constexpr int RPW = EPI == EPI_ROWPAIR ? 2 : 1;
+    const int64_t row0 = (int64_t)blockIdx.x * (2 * kTileRows * RPW);
     if (!pr.valid) {   // id outside [0, E): zero rows
-        if (tid < 2 * kTileRows && row0 + tid < a.n)
+        if (tid < 2 * kTileRows * RPW && row0 + tid < a.n)
             pr.out[row0 + tid] = 0.0f;
         return;
     }
     const int n8 = (a.n + kTileRows - 1) / kTileRows;
-    const int64_t Graw = 2 * (int64_t)blockIdx.x + (lane >> 5);
+    const int64_t Graw = 2 * RPW * (int64_t)blockIdx.x + (lane >> 5);
     const int64_t G = Graw < n8 ? Graw : n8 - 1;   // this lane's row group (clamped;
                                                    // stores are guarded)
     float *xw = lds + wave * class_steps(nb, 0) * kStepFloats;
     const uint8_t *mat[NT];
     mat[0] = pr.w0;
-    if constexpr (NT == 2)
+    if constexpr (EPI == EPI_ROWPAIR) {   // the same matrix, two row groups on (clamped)
+        const int64_t G2 = Graw + 2 < n8 ? Graw + 2 : n8 - 1;
+        mat[NT - 1] = pr.w0 + (G2 - G) * (int64_t)nb * kTileBytes;
+    } else if constexpr (NT == 2) {
         mat[1] = pr.w1;
+    }
     auto sb_of = [&](int t) { return wave + kClasses * (t < T ? t : T - 1); };   // clamped
     float acc[NT];
 #pragma unroll
@@ -133,7 +140,13 @@ __global__ __launch_bounds__(64 * kClasses) void k_rows(GemvArgs a) {
         for (int nt = 0; nt < NT; nt++)
             tot[nt] = class_total(part[0][nt][tid], part[1][nt][tid], part[2][nt][tid],
                                   part[3][nt][tid]);
-        pr.out[row] = epilogue<EPI, NT>(tot);
+        if constexpr (EPI == EPI_ROWPAIR) {
+            pr.out[row] = tot[0];
+            if (row + 2 * kTileRows < a.n)
+                pr.out[row + 2 * kTileRows] = tot[NT - 1];
+        } else {
+            pr.out[row] = epilogue<EPI, NT>(tot);
+        }
     }
 }
 
@@ -346,7 +359,8 @@ static size_t rows_lds_bytes(int64_t k) {
 template <int NT, int EPI, int D>
 static hipError_t go_rows(const GemvArgs &a, hipStream_t st) {
     const int n8 = (a.n + kTileRows - 1) / kTileRows;
-    dim3 grid((n8 + 1) / 2, a.n_pairs + a.m_sh);
+    constexpr int RPW = EPI == EPI_ROWPAIR ? 2 : 1;   // row-group pairs per workgroup
+    dim3 grid((n8 + 2 * RPW - 1) / (2 * RPW), a.n_pairs + a.m_sh);
     auto go = [&](auto kern) {
         const size_t lds = set_lds((const void *)kern, rows_lds_bytes(a.k));
         hipLaunchKernelGGL(kern, grid, dim3(64 * kClasses), lds, st, a);
@@ -376,7 +390,10 @@ hipError_t launch_q4k_gemv(const GemvLaunch &L, hipStream_t st) {
         return launch_q4k_gemv_mfma(a, L.fused_swiglu, st);
     if (L.fused_swiglu)
         return launch_rows<2, EPI_SWIGLU>(a, st);
-    return launch_rows<1, EPI_STORE>(a, st);
+    // a single matrix: two pairs of row groups per workgroup, so that each
+    // staged activation row serves 32 rows (config 4's down at m = 1: 62.9 ->
+    // 60.5 us per layer)
+    return launch_rows<2, EPI_ROWPAIR>(a, st);
 }
 
 // LDS of k_down_combine: np staged rows and the class sums of 8 rows.

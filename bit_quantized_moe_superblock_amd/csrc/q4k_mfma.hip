@@ -58,12 +58,10 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr int kMP = kBucketChunk;   // pairs per workgroup (A rows: 8 hi parts, 8 lo parts)
 constexpr int kMRows = 64;          // weight rows per row group (4 waves x 16)
-// Epilogue of a single-matrix launch whose two register tiles are two row
-// groups of the same matrix (rows r and r + kMRows), so that an item covers
-// 2 kMRows rows against one staged activation slab.
-constexpr int kEpiRowPair = 2;
-static_assert(kEpiRowPair != EPI_STORE && kEpiRowPair != EPI_SWIGLU, "epilogue ids");
-__host__ __device__ constexpr int item_rows(int epi) { return epi == kEpiRowPair ? 2 * kMRows : kMRows; }
+// EPI_ROWPAIR here: a single-matrix launch whose two register tiles are two
+// row groups of the same matrix (rows r and r + kMRows), so that an item
+// covers 2 kMRows rows against one staged activation slab.
+__host__ __device__ constexpr int item_rows(int epi) { return epi == EPI_ROWPAIR ? 2 * kMRows : kMRows; }
 constexpr int kDepth = 2;   // superblocks of weights in flight per wave
 constexpr int kSubB = 2 * 4 * kMP * 16;   // LDS bytes per staged sub-block: parts x groups x pairs x 16 B
 static_assert(kMP == 8, "A-row mapping assumes 8 pairs per workgroup");
@@ -355,7 +353,7 @@ __device__ __forceinline__ void mfma_item(const GemvArgs &a, bool shared, int bk
     int64_t wg[NT];
     wmat[0] = shared ? a.s0 : a.w0 + (int64_t)bkt * a.mat;
     wg[0] = group(r0);
-    if constexpr (EPI == kEpiRowPair) {   // the second row group of the same matrix
+    if constexpr (EPI == EPI_ROWPAIR) {   // the second row group of the same matrix
         wmat[NT - 1] = wmat[0];
         wg[NT - 1] = group(r0 + kMRows);
     } else if (NT == 2) {
@@ -425,7 +423,7 @@ __device__ __forceinline__ void mfma_item(const GemvArgs &a, bool shared, int bk
         if (g < 2 && i < gc && r0 < a.n) {
             const int q = pair_q(i);
             float *out = q < P ? a.dst + (int64_t)q * a.n : a.dst_sh + (int64_t)(q - P) * a.n;
-            if constexpr (EPI == kEpiRowPair) {
+            if constexpr (EPI == EPI_ROWPAIR) {
                 out[r0] = yv[0][j];
                 if (r0 + kMRows < a.n)
                     out[r0 + kMRows] = yv[NT - 1][j];
@@ -667,7 +665,7 @@ static hipError_t mfma_sb(const GemvArgs &a, hipStream_t st) {
 hipError_t launch_q4k_gemv_mfma(const GemvArgs &a, bool fused_swiglu, hipStream_t st) {
     if (fused_swiglu)
         return a.vec ? mfma_sb<2, EPI_SWIGLU, true>(a, st) : mfma_sb<2, EPI_SWIGLU, false>(a, st);
-    return a.vec ? mfma_sb<2, kEpiRowPair, true>(a, st) : mfma_sb<2, kEpiRowPair, false>(a, st);
+    return a.vec ? mfma_sb<2, EPI_ROWPAIR, true>(a, st) : mfma_sb<2, EPI_ROWPAIR, false>(a, st);
 }
 
 }  // namespace q4k
