@@ -151,13 +151,14 @@ __global__ __launch_bounds__(64 * kClasses) void k_rows(GemvArgs a) {
 }
 
 // ---------------------------------------------------- down + combine mode ----
-// Workgroup = (row group G, token t), W waves.  The token's np pairs (0..top_k-1
+// Workgroup = (RP row groups from G = RP*blockIdx.x, token t), W waves.  The token's np pairs (0..top_k-1
 // routed, top_k the shared expert) go in pair pairs (2pp, 2pp + 1; an odd last
 // one repeats its pair and stores nothing for it); pair pairs times the row's
 // C = min(4, nb) classes make the tasks, and wave w takes tasks w, w + W, ...
-// (task = pp*C + c), each the class's superblocks of the two pairs, and leaves
-// the class sums of the 8 rows in LDS.  Then thread r forms each pair's row
-// value (class_total) and applies
+// (task = pp*C + c), each the class's superblocks of the two pairs in the RP
+// row groups (RP register tiles per step: the staged activations serve 8*RP
+// rows), and leaves the class sums of the 8*RP rows in LDS.  Then thread r
+// forms each pair's row value (class_total) and applies
 // out[t,r] = h_mid[t,r] + sum_s w[t,s]*y_s[r] + g_t*y_sh[r]
 // with the same fma order as the combine kernel.
 
@@ -168,7 +169,7 @@ struct CombineArgs {
     int shared_mode;
 };
 
-template <bool VEC, int D, int W>
+template <bool VEC, int D, int W, int RP>
 __global__ __launch_bounds__(64 * W) void k_down_combine(GemvArgs a, CombineArgs cb) {
     extern __shared__ float lds[];
     fetch_args(a);
@@ -179,10 +180,15 @@ __global__ __launch_bounds__(64 * W) void k_down_combine(GemvArgs a, CombineArgs
     const int K = a.top_k;
     const int np = K + (a.m_sh > 0 ? 1 : 0);   // pairs of this token
     const int rl = row_lds_floats(a.k);
-    float *part = lds + np * rl;                // [np][kClasses][8]
+    constexpr int R = RP * kTileRows;           // rows of the workgroup
+    float *part = lds + np * rl;                // [np][kClasses][R]
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
-    const int64_t G = blockIdx.x;
+    const int64_t G = (int64_t)RP * blockIdx.x;
+    // the second row group's tiles (clamped to the last group: reloads it and
+    // stores nothing for it)
+    const int n8 = (a.n + kTileRows - 1) / kTileRows;
+    const int64_t dG = RP > 1 && G + 1 < n8 ? 1 : 0;
     // 1. the token's ids, then the combine's routing weights, gate logit and
     //    h_mid, loaded here so that the combine at the end waits on no memory
     //    (one load per thread, unconditional with a clamped index)
@@ -193,8 +199,8 @@ __global__ __launch_bounds__(64 * W) void k_down_combine(GemvArgs a, CombineArgs
     const float rw_own = cb.route_w[own];
     const bool gated = a.m_sh > 0 && cb.shared_mode == 1;   // uniform
     const float logit = gated ? cb.shared_logit[tok] : 0.0f;
-    const int64_t orow = G * kTileRows + (tid < kTileRows ? tid : 0);
-    const bool rowok = tid < kTileRows && orow < a.n;
+    const int64_t orow = G * kTileRows + (tid < R ? tid : 0);
+    const bool rowok = tid < R && orow < a.n;
     const int64_t o = (int64_t)tok * a.n + (orow < a.n ? orow : a.n - 1);
     const float hm = cb.h_mid[o];
     // The first staging batch of the token's activation rows (routed rows,
@@ -242,9 +248,13 @@ __global__ __launch_bounds__(64 * W) void k_down_combine(GemvArgs a, CombineArgs
         return a.w0 + (int64_t)(e >= 0 ? e : 0) * a.mat;
     };
     int lj = 0, lt = 0, ls = 0;   // load cursor: task lj, its superblock lt
-    auto load_next = [&](Step<1> &b) {
-        const uint8_t *m[1] = {mat_of(task_pp(lj))};
-        load_step<1>(m, G, task_c(lj) + kClasses * lt, nb, b);
+    auto load_next = [&](Step<RP> &b) {
+        const uint8_t *m0 = mat_of(task_pp(lj));
+        const uint8_t *m[RP];
+#pragma unroll
+        for (int r = 0; r < RP; r++)
+            m[r] = m0 + r * dG * nb * kTileBytes;
+        load_step<RP>(m, G, task_c(lj) + kClasses * lt, nb, b);
         if (ls + 1 < S) {   // advance, or stay on the last (clamped reload)
             ls++;
             if (++lt == class_steps(nb, task_c(lj))) {
@@ -253,7 +263,7 @@ __global__ __launch_bounds__(64 * W) void k_down_combine(GemvArgs a, CombineArgs
             }
         }
     };
-    Step<1> buf[D];
+    Step<RP> buf[D];
     if (S > 0) {
 #pragma unroll
         for (int d = 0; d < D; d++)
@@ -266,7 +276,10 @@ __global__ __launch_bounds__(64 * W) void k_down_combine(GemvArgs a, CombineArgs
     lds_barrier();
     // 4. the superblocks; at the end of a task its class sums go to part
     const int c = (lane >> 3) & 3;
-    float acc[1] = {0.0f};
+    float acc[RP];
+#pragma unroll
+    for (int r = 0; r < RP; r++)
+        acc[r] = 0.0f;
     int cj = 0, ct = 0;
     for (int s0 = 0; s0 < S; s0 += D) {
 #pragma unroll
@@ -276,12 +289,15 @@ __global__ __launch_bounds__(64 * W) void k_down_combine(GemvArgs a, CombineArgs
                 const int p = pair_of(pp);
                 const int u = 4 * (cl + kClasses * ct) + c;
                 const float *xrow = lds + p * rl;
-                step_units<1>(buf[d], xrow + 68 * u, xrow + xpad_len(a.k) + 2 * u, acc);
+                step_units<RP>(buf[d], xrow + 68 * u, xrow + xpad_len(a.k) + 2 * u, acc);
                 if (++ct == class_steps(nb, cl)) {
-                    const float v = chunk_sum(acc[0]);
-                    if ((lane & 24) == 0 && 2 * pp + jh < np)
-                        part[(p * kClasses + cl) * kTileRows + (lane & 7)] = v;
-                    acc[0] = 0.0f;
+#pragma unroll
+                    for (int r = 0; r < RP; r++) {
+                        const float v = chunk_sum(acc[r]);
+                        if ((lane & 24) == 0 && 2 * pp + jh < np)
+                            part[(p * kClasses + cl) * R + r * kTileRows + (lane & 7)] = v;
+                        acc[r] = 0.0f;
+                    }
                     ct = 0;
                     cj++;
                 }
@@ -294,9 +310,9 @@ __global__ __launch_bounds__(64 * W) void k_down_combine(GemvArgs a, CombineArgs
     // 5. the combine, one thread per row, slots in order
     if (rowok) {
         auto y_of = [&](int p) {
-            const float *pp = part + p * kClasses * kTileRows + tid;
-            return class_total(pp[0], C > 1 ? pp[kTileRows] : 0.0f,
-                               C > 2 ? pp[2 * kTileRows] : 0.0f, C > 3 ? pp[3 * kTileRows] : 0.0f);
+            const float *pp = part + p * kClasses * R + tid;
+            return class_total(pp[0], C > 1 ? pp[R] : 0.0f, C > 2 ? pp[2 * R] : 0.0f,
+                               C > 3 ? pp[3 * R] : 0.0f);
         };
         float accr = hm;
         for (int s = 0; s < K; s++) {
@@ -396,9 +412,9 @@ hipError_t launch_q4k_gemv(const GemvLaunch &L, hipStream_t st) {
     return launch_rows<2, EPI_ROWPAIR>(a, st);
 }
 
-// LDS of k_down_combine: np staged rows and the class sums of 8 rows.
-static size_t dc_lds_bytes(int64_t k, int np) {
-    return ((size_t)np * row_lds_floats((int)k) + (size_t)np * kClasses * kTileRows) *
+// LDS of k_down_combine: np staged rows and the class sums of 8*rp rows.
+static size_t dc_lds_bytes(int64_t k, int np, int rp) {
+    return ((size_t)np * row_lds_floats((int)k) + (size_t)np * kClasses * kTileRows * rp) *
            sizeof(float);
 }
 
@@ -406,30 +422,30 @@ static size_t dc_lds_bytes(int64_t k, int np) {
 // (e.g. top_k 8 at k = 2048: 80 KB) the launch runs in latency-bound rounds
 // of one workgroup per CU, slower than pair mode plus the combine.
 bool q4k_down_combine_ok(int64_t k, int64_t top_k, bool shared) {
-    return dc_lds_bytes(k, (int)top_k + (shared ? 1 : 0)) <= 48 * 1024;
+    return dc_lds_bytes(k, (int)top_k + (shared ? 1 : 0), 2) <= 48 * 1024;
 }
 
-template <int D, int W>
+template <int D, int W, int RP>
 static hipError_t go_dc(const GemvArgs &a, const CombineArgs &cb, hipStream_t st) {
     const int np = a.top_k + (a.m_sh > 0 ? 1 : 0);
     const int n8 = (a.n + kTileRows - 1) / kTileRows;
-    dim3 grid(n8, (int)(a.n_pairs / a.top_k));
+    dim3 grid((n8 + RP - 1) / RP, (int)(a.n_pairs / a.top_k));
     auto go = [&](auto kern) {
-        const size_t lds = set_lds((const void *)kern, dc_lds_bytes(a.k, np));
+        const size_t lds = set_lds((const void *)kern, dc_lds_bytes(a.k, np, RP));
         hipLaunchKernelGGL(kern, grid, dim3(64 * W), lds, st, a, cb);
         return hipGetLastError();
     };
-    return a.vec ? go(k_down_combine<true, D, W>) : go(k_down_combine<false, D, W>);
+    return a.vec ? go(k_down_combine<true, D, W, RP>) : go(k_down_combine<false, D, W, RP>);
 }
 
 // Steps in flight: a wave's whole share up to 4.
-template <int W>
+template <int W, int RP>
 static hipError_t dc_depth(const GemvArgs &a, const CombineArgs &cb, int most, hipStream_t st) {
     switch (most < 4 ? most : 4) {
-    case 4: return go_dc<4, W>(a, cb, st);
-    case 3: return go_dc<3, W>(a, cb, st);
-    case 2: return go_dc<2, W>(a, cb, st);
-    default: return go_dc<1, W>(a, cb, st);
+    case 4: return go_dc<4, W, RP>(a, cb, st);
+    case 3: return go_dc<3, W, RP>(a, cb, st);
+    case 2: return go_dc<2, W, RP>(a, cb, st);
+    default: return go_dc<1, W, RP>(a, cb, st);
     }
 }
 
@@ -443,11 +459,15 @@ hipError_t launch_q4k_down_combine(const GemvLaunch &L, const float *h_mid, cons
     const int nb = a.k >> 8;
     const int C = nb < kClasses ? nb : kClasses;
     const int tasks = (a.top_k + (a.m_sh > 0 ? 1 : 0) + 1) / 2 * C;
-    const int64_t wgs = (a.n + kTileRows - 1) / kTileRows * (a.n_pairs / a.top_k);
+    const int64_t tokens = a.n_pairs / a.top_k;
+    const int RP = tokens >= 2 ? 2 : 1;
+    const int64_t wgs = ((a.n + kTileRows - 1) / kTileRows + RP - 1) / RP * tokens;
     const int W = tasks > 8 && wgs * 4 < 8 * (int64_t)cu_count() ? 8 : 4;
     // superblocks of the busiest wave: its tasks times the longest class
     const int most = (tasks + W - 1) / W * class_steps(nb, 0);
-    return W == 4 ? dc_depth<4>(a, cb, most, st) : dc_depth<8>(a, cb, most, st);
+    if (RP == 2)
+        return W == 4 ? dc_depth<4, 2>(a, cb, most, st) : dc_depth<8, 2>(a, cb, most, st);
+    return W == 4 ? dc_depth<4, 1>(a, cb, most, st) : dc_depth<8, 1>(a, cb, most, st);
 }
 
 }  // namespace q4k
