@@ -151,14 +151,15 @@ __global__ __launch_bounds__(64 * kClasses) void k_rows(GemvArgs a) {
 }
 
 // ---------------------------------------------------- down + combine mode ----
-// Workgroup = (RP row groups from G = RP*blockIdx.x, token t), W waves.  The token's np pairs (0..top_k-1
-// routed, top_k the shared expert) go in pair pairs (2pp, 2pp + 1; an odd last
-// one repeats its pair and stores nothing for it); pair pairs times the row's
-// C = min(4, nb) classes make the tasks, and wave w takes tasks w, w + W, ...
-// (task = pp*C + c), each the class's superblocks of the two pairs in the RP
-// row groups (RP register tiles per step: the staged activations serve 8*RP
-// rows), and leaves the class sums of the 8*RP rows in LDS.  Then thread r
-// forms each pair's row value (class_total) and applies
+// Workgroup = (RP row groups from G = RP*blockIdx.x, token t), W waves.  The
+// token's np pairs (0..top_k-1 routed, top_k the shared expert) go in pair
+// pairs (2pp, 2pp + 1; an odd last one repeats its pair and stores nothing for
+// it); pair pairs times the row's C = min(4, nb) classes make the tasks, and
+// wave w takes tasks w, w + W, ... (task = pp*C + c), each the class's
+// superblocks of the two pairs in the RP row groups (RP register tiles per
+// step: the staged activations serve 8*RP rows), and leaves the class sums of
+// the 8*RP rows in LDS.  Then thread r forms each pair's row value
+// (class_total) and applies
 // out[t,r] = h_mid[t,r] + sum_s w[t,s]*y_s[r] + g_t*y_sh[r]
 // with the same fma order as the combine kernel.
 
