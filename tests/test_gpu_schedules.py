@@ -8,6 +8,9 @@
   vector units, through every entry point that takes activations;
 - vector-unit bucketing equal bit for bit to pair mode, and AUTO picking pair
   mode below Q4K_AUTO_BUCKET_MIN_TOKENS tokens and the matrix cores from there;
+- the layer's token mode at two and three tokens of the decode shape (the
+  fused down + combine with two row groups per workgroup) against vector-unit
+  bucketing, bit for bit, and the oracle;
 - the layer's token mode when the down + combine kernel's staged rows do not
   fit one workgroup, and a bucketed layer past the in-kernel bucketing limit
   (more than 1024 pairs) with unaligned activations.
@@ -259,6 +262,32 @@ def test_auto_threshold_and_vector_bucketing_bitwise(dev):
         want = _oracle_layer(h_st, sh, a.h_post[:m], a.h_mid[:m], ids, a.route_w[:m * K],
                              a.shared_logit[:m], H, I, E, m, K, cfg.shared_mode)
         band_rows(lay[ON], want, f"layer m={m}, matrix cores")
+
+
+@pytest.mark.parametrize("m,mode", [(2, q4.MOE_SHARED_SIGMOID), (3, q4.MOE_SHARED_NONE),
+                                    (2, q4.MOE_SHARED_UNSCALED)])
+def test_token_mode_two_row_groups_per_workgroup(dev, m, mode):
+    """From two tokens on, the layer's fused down + combine covers two row
+    groups per workgroup (eight waves at two tokens of the decode shape, four
+    from three); at hidden 2048, inter 768 and top_k 8, with each shared-expert
+    mode, it gives the bits of vector-unit bucketing (pair mode and the
+    combine launch) and holds the band against the oracle."""
+    cfg = wl.CFG3
+    H, I, E, K = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k
+    say(f"token mode, two row groups per workgroup: m={m} shared mode {mode}")
+    a, ids_all, d_st, h_st = _ffn_case(cfg, dev)
+    sd, sh = _shared_stacks(cfg, dev)
+    if mode == q4.MOE_SHARED_NONE:
+        sd = (None, None, None)
+    ids = ids_all[:m * K].copy()
+    args = (d_st, sd, T(a.h_post[:m], dev), T(a.h_mid[:m], dev), T(ids, dev),
+            T(a.route_w[:m * K], dev), T(a.shared_logit[:m], dev), H, I, E, m, K, mode)
+    tok = _layer(dev, *args, OFF)
+    assert np.array_equal(bits(tok), bits(_layer(dev, *args, VEC)))
+    assert np.array_equal(bits(tok), bits(_layer(dev, *args, AUTO)))
+    want = _oracle_layer(h_st, sh, a.h_post[:m], a.h_mid[:m], ids, a.route_w[:m * K],
+                         a.shared_logit[:m], H, I, E, m, K, mode)
+    band_rows(tok, want, f"token mode m={m}")
 
 
 def _random_stacks(g, E, H, I):
