@@ -673,13 +673,14 @@ def test_gate_up_with_shared_rides_along(dev):
 
 
 def test_layer_invalid_ids_and_token_mode_edges(dev):
-    """Few-token path with an invalid id (zero contribution), top_k 1 and 16,
-    hidden sizes that are not multiples of the tile, and an inter size whose
+    """Few-token path with an invalid id (zero contribution), top_k 1 and 16
+    (at one and two tokens), hidden sizes that are not multiples of the tile,
+    three tokens at hidden 1792 and top_k 5, and an inter size whose
     activation rows are too large for the fused down + combine (pair mode and
     the combine launch instead)."""
     g = np.random.default_rng(50)
     for H, I, E, K, m in [(512, 256, 6, 3, 2), (1280, 512, 20, 16, 1), (768, 768, 3, 1, 2),
-                          (1024, 2048, 5, 8, 1)]:
+                          (1024, 2048, 5, 8, 1), (1024, 512, 20, 16, 2), (1792, 768, 9, 5, 3)]:
         say(f"layer edges H={H} I={I} E={E} K={K} m={m}")
         st = [np.concatenate(quantize_many([(g.standard_normal((r, c)) * 0.05).astype(np.float32)
                                             for _ in range(E)]))
