@@ -568,8 +568,8 @@ def main():
                     help="only run a plain device copy of MIB MiB (counter yardstick)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this path has no multi-GPU mode and every box here "
-              f"has one MI355X (asked for --gpus {args.gpus}).", file=sys.stderr)
+        print(f"bench.py measures one GPU: the path has no multi-GPU mode (asked for --gpus "
+              f"{args.gpus}).", file=sys.stderr)
         sys.exit(2)
     want = set(s for s in args.only.split(",") if s) or \
         {"m1", "m16", "sweep", "cfg4", "walk", "mlx4", "cpu"}

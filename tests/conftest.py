@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests only run where a GPU is visible; on a CPU host they are skipped
-    # rather than failed, so `-m gpu` on a CPU machine reports skips, not errors.
+    # rather than failed, so `-m gpu` on a machine without a GPU reports skips, not errors.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
